@@ -1,0 +1,166 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each mutant is a copy of the oracle's C source with one planted mistake
+(a dropped term, a wrong index, an inverted test, a transposed operand),
+compiled into a temporary library. The pins used here (hand-worked examples
+and exhaustive comparison with the independent readers) must reject every one.
+The oracle's own source is never modified.
+"""
+import ctypes
+import itertools
+import json
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import lex_closure
+from tests.rd_reader import read_t5, read_t6
+
+HERE = os.path.dirname(__file__)
+ORACLE_DIR = os.path.join(os.path.dirname(HERE), "oracle")
+
+CSV_MUTANTS = {
+    "length_plus_one": ("len_out[nf] = (uint32_t)(i - field_start);", "len_out[nf] = (uint32_t)(i - field_start + 1);"),
+    "start_at_terminator": ("field_start = i + 1;", "field_start = i;"),
+    "no_column_advance": ("                col++;\n", "\n"),
+    "no_column_reset": ("                col = 0;\n", "\n"),
+    "final_rule_field": ("last_tag != TAG_RECORD", "last_tag != TAG_FIELD"),
+    "error_at_n_minus_1": ("err = (int64_t)n;", "err = (int64_t)n - 1;"),
+    "last_invalid_not_first": ("if (t == TAG_INVALID && err < 0)", "if (t == TAG_INVALID)"),
+    "accept_inverted": ("if (err < 0 && !((accept_mask >> s) & 1u))", "if (err < 0 && ((accept_mask >> s) & 1u))"),
+    "final_record_not_counted": ("        nf++;\n        rec++;\n    }\n    if (err", "        nf++;\n    }\n    if (err"),
+    "table_transposed": ("uint32_t t = tag[s * n_classes + c];", "uint32_t t = tag[c * n_classes + s];"),
+    "next_from_old_state": ("        s = s_next;\n", "        s = next[s_next * n_classes + c];\n"),
+    "record_index_after_bump": ("rec_out[nf] = (uint32_t)rec;\n                col_out", "rec_out[nf] = (uint32_t)(rec + (t == TAG_RECORD));\n                col_out"),
+}
+
+LEX_MUTANTS = {
+    "restart_from_current": ("q = (uint32_t)delta[(uint64_t)q0 * 256 + b];", "q = (uint32_t)delta[(uint64_t)q * 256 + b] < 0 ? q0 : q;"),
+    "kind_of_new_state": ("put(kind, start, len, cap, &nt, kind_of[q], tok_start, i - tok_start);\n            tok_start = i;",
+                          "tok_start = i;\n            put(kind, start, len, cap, &nt, kind_of[delta[(uint64_t)q0 * 256 + b]], tok_start, i - tok_start);"),
+    "no_final_token": ("    if (n > 0) put(kind, start, len, cap, &nt, kind_of[q], tok_start, n - tok_start);\n", "\n"),
+    "fold_operands_swapped": ("uint16_t m = merge[(uint64_t)prev * k + x];", "uint16_t m = merge[(uint64_t)x * k + prev];"),
+    "fold_kind_of_current": ("put(kind, start, len, cap, &nt, final_[prev], tok_start, i - tok_start);",
+                             "put(kind, start, len, cap, &nt, final_[m & id_mask], tok_start, i - tok_start);"),
+    "fold_flag_not_masked": ("        prev = m & id_mask;", "        prev = m;"),
+}
+
+
+def _compile(src_name, subst, tmp):
+    src = open(os.path.join(ORACLE_DIR, src_name)).read()
+    old, new = subst
+    assert src.count(old) == 1, (src_name, old)
+    path = os.path.join(tmp, "m.c")
+    open(path, "w").write(src.replace(old, new))
+    so = os.path.join(tmp, "m%d.so" % abs(hash(old + new)))
+    subprocess.run(["gcc", "-O1", "-shared", "-fPIC", "-o", so, path], check=True, capture_output=True)
+    return ctypes.CDLL(so)
+
+
+def _csv_run(L, t, b):
+    n = len(b)
+    cap = n + 2
+    arr = np.frombuffer(b + b"\0", dtype=np.uint8)
+    nxt = np.array(t["next"], dtype=np.uint8)
+    tag = np.array(t["tag"], dtype=np.uint8)
+    cm = np.frombuffer(t["class_map"], dtype=np.uint8)
+    out = [np.zeros(cap, dtype=np.uint32) for _ in range(4)]
+    nf, nr, err, es = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_int64(), ctypes.c_uint32()
+    P = ctypes.c_void_p
+    L.oracle_csv_parse.argtypes = [P, ctypes.c_uint64] + [ctypes.c_uint32] * 4 + [P] * 7 + [ctypes.c_uint64] + [P] * 4
+    L.oracle_csv_parse(arr.ctypes.data, n, t["n_states"], t["n_classes"], t["start"], t["accept_mask"],
+                       nxt.ctypes.data, tag.ctypes.data, cm.ctypes.data, *[o.ctypes.data for o in out], cap,
+                       ctypes.byref(nf), ctypes.byref(nr), ctypes.byref(err), ctypes.byref(es))
+    k = min(int(nf.value), cap)
+    return [tuple(int(o[i]) for o in out) for i in range(k)], int(nr.value), int(err.value)
+
+
+def _csv_pins_pass(L):
+    """golden examples + exhaustive comparison with the readers (short inputs)"""
+    for line in open(os.path.join(HERE, "golden", "csv_examples.jsonl")):
+        c = json.loads(line)
+        got = _csv_run(L, W.table(c["table"]), c["input"].encode("latin-1"))
+        if got != ([tuple(f) for f in c["fields"]], c["n_records"], c["error_pos"]):
+            return False
+    for name, alpha, reader, max_len in (("T5", b',\n"a', read_t5, 5), ("T6", b'\t\n"#a', read_t6, 4)):
+        t = W.table(name)
+        for L_ in range(max_len + 1):
+            for s in itertools.product(alpha, repeat=L_):
+                s = bytes(s)
+                if _csv_run(L, t, s) != reader(s):
+                    return False
+    return True
+
+
+@pytest.mark.parametrize("mutant", sorted(CSV_MUTANTS))
+def test_csv_mutant_is_caught(mutant):
+    with tempfile.TemporaryDirectory() as tmp:
+        L = _compile("csv_oracle.c", CSV_MUTANTS[mutant], tmp)
+        assert not _csv_pins_pass(L), "pins did not catch mutant %s" % mutant
+
+
+def test_unmutated_csv_source_passes_same_pins():
+    with tempfile.TemporaryDirectory() as tmp:
+        L = _compile("csv_oracle.c", ("int oracle_csv_parse(", "int oracle_csv_parse("), tmp)
+        assert _csv_pins_pass(L)
+
+
+def _lex_tokens(L, fn, d, tables, b):
+    n = len(b)
+    cap = n + 2
+    arr = np.frombuffer(b + b"\0", dtype=np.uint8)
+    out = [np.zeros(cap, dtype=np.uint32) for _ in range(3)]
+    nt = ctypes.c_uint64()
+    P = ctypes.c_void_p
+    if fn == "restart":
+        delta = np.ascontiguousarray(d["delta"], dtype=np.int16)
+        kind = np.ascontiguousarray(d["kind"], dtype=np.uint16)
+        L.oracle_lex_restart.argtypes = [P, ctypes.c_uint64, ctypes.c_uint32, P, P, P, P, P, ctypes.c_uint64, P]
+        L.oracle_lex_restart(arr.ctypes.data, n, d["q0"], delta.ctypes.data, kind.ctypes.data,
+                             *[o.ctypes.data for o in out], cap, ctypes.byref(nt))
+    else:
+        init, merge, fin, k = tables
+        L.oracle_lex_fold.argtypes = [P, ctypes.c_uint64, P, P, P, ctypes.c_uint32, ctypes.c_uint16, P, P, P,
+                                      ctypes.c_uint64, P]
+        L.oracle_lex_fold(arr.ctypes.data, n, init.ctypes.data, merge.ctypes.data, fin.ctypes.data, k, 0x8000,
+                          *[o.ctypes.data for o in out], cap, ctypes.byref(nt))
+    m = min(int(nt.value), cap)
+    return [(int(out[0][i]), int(out[1][i]), int(out[2][i])) for i in range(m)]
+
+
+def _lex_pins_pass(L):
+    d = W.toy_dfa()
+    t = lex_closure.build_tables(d)
+    tables = (np.array(t["initial_state"], dtype=np.uint16), np.array(t["merge_table"], dtype=np.uint16),
+              np.array(t["final_states"], dtype=np.uint16), t["k"])
+    names = {nm: i for i, nm in enumerate(d["kind_names"])}
+    for line in open(os.path.join(HERE, "golden", "lex_examples.jsonl")):
+        c = json.loads(line)
+        if c["grammar"] != "toy":
+            continue
+        want = [(names[k], s, ln) for k, s, ln in c["tokens"]]
+        if _lex_tokens(L, "restart", d, None, c["input"].encode()) != want:
+            return False
+    for L_ in range(6):
+        for s in itertools.product(b"a1 #", repeat=L_):
+            s = bytes(s)
+            if _lex_tokens(L, "restart", d, None, s) != _lex_tokens(L, "fold", d, tables, s):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("mutant", sorted(LEX_MUTANTS))
+def test_lex_mutant_is_caught(mutant):
+    with tempfile.TemporaryDirectory() as tmp:
+        L = _compile("lex_oracle.c", LEX_MUTANTS[mutant], tmp)
+        assert not _lex_pins_pass(L), "pins did not catch mutant %s" % mutant
+
+
+def test_unmutated_lex_source_passes_same_pins():
+    with tempfile.TemporaryDirectory() as tmp:
+        L = _compile("lex_oracle.c", ("int oracle_lex_fold(", "int oracle_lex_fold("), tmp)
+        assert _lex_pins_pass(L)
