@@ -1,0 +1,368 @@
+"""Data-parallel DFA parsing of delimiter-separated bytes and table-driven lexing
+on AMD Instinct MI355X (gfx950).
+
+Thin binding over the C ABI of ``libppr.so`` (``include/ppr.h``): it marshals
+arguments and nothing else. Every step of the parse runs in the library's HIP
+kernels; PyTorch only provides device memory and the stream. There is no CPU
+fallback: if the library is missing, importing this package fails.
+
+    import dfa_parsing_delimiter_amd as ppr
+    res = ppr.parse(bytes_tensor_on_cuda, table)          # per-field arrays
+    tables = ppr.LexTables.from_dfa(token_dfa)            # lexer tables (device)
+    toks = ppr.lex(bytes_tensor_on_cuda, tables)          # (kind, start, length)
+
+A DFA table is a dict with keys n_states, n_classes, next[s][c], tag[s][c]
+(0 value, 1 field delimiter, 2 record delimiter, 3 invalid), start,
+accept_mask and class_map (256 bytes). A token DFA is a dict with delta
+(n_states x 256, -1 = undefined; the start state's row total), kind
+(n_states), q0.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libppr.so")
+
+PPR_OK, PPR_EINVAL, PPR_ECAPACITY, PPR_ETOOBIG, PPR_EHIP, PPR_EWORKSPACE = 0, -1, -2, -3, -4, -5
+_ERRNAMES = {-1: "PPR_EINVAL", -2: "PPR_ECAPACITY", -3: "PPR_ETOOBIG", -4: "PPR_EHIP", -5: "PPR_EWORKSPACE"}
+TAG_VALUE, TAG_FIELD, TAG_RECORD, TAG_INVALID = 0, 1, 2, 3
+
+
+class PprError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__("%s failed: %s (%d)" % (where, _ERRNAMES.get(code, "?"), code))
+        self.code = code
+
+
+class Dfa(ctypes.Structure):
+    _fields_ = [("n_states", ctypes.c_uint32), ("n_classes", ctypes.c_uint32), ("start_state", ctypes.c_uint32),
+                ("accept_mask", ctypes.c_uint32), ("next", (ctypes.c_uint8 * 16) * 8),
+                ("tag", (ctypes.c_uint8 * 16) * 8)]
+
+
+class ParseOut(ctypes.Structure):
+    _fields_ = [("record_idx", ctypes.c_void_p), ("column_ids", ctypes.c_void_p),
+                ("field_offsets", ctypes.c_void_p), ("field_lengths", ctypes.c_void_p),
+                ("cap_fields", ctypes.c_uint64), ("n_fields", ctypes.c_uint64), ("n_records", ctypes.c_uint64),
+                ("error_pos", ctypes.c_int64), ("end_state", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+class ParseOpts(ctypes.Structure):
+    _fields_ = [("chunk_bytes", ctypes.c_uint32), ("reserved", ctypes.c_uint32 * 3)]
+
+
+class LexTablesC(ctypes.Structure):
+    _fields_ = [("initial_state", ctypes.c_void_p), ("merge_table", ctypes.c_void_p),
+                ("final_states", ctypes.c_void_p), ("k", ctypes.c_uint32), ("identity", ctypes.c_uint16),
+                ("flag_mask", ctypes.c_uint16)]
+
+
+class LexPrepared(ctypes.Structure):
+    _fields_ = [("d_fold", ctypes.c_void_p), ("k", ctypes.c_uint32), ("m", ctypes.c_uint32),
+                ("identity", ctypes.c_uint16), ("flag_mask", ctypes.c_uint16), ("column_of", ctypes.c_uint8 * 256)]
+
+
+class TokensOut(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_void_p), ("start", ctypes.c_void_p), ("length", ctypes.c_void_p),
+                ("cap_tokens", ctypes.c_uint64), ("n_tokens", ctypes.c_uint64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libppr.so is not built (run: python dfa_parsing_delimiter_amd/build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, U64, U32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32
+    L.ppr_parse_workspace_bytes.argtypes = [U64, ctypes.POINTER(ParseOpts)]
+    L.ppr_parse_workspace_bytes.restype = ctypes.c_size_t
+    for f in ("ppr_parse", "ppr_parse_async"):
+        getattr(L, f).argtypes = [P, U64, ctypes.POINTER(Dfa), ctypes.c_char_p, ctypes.POINTER(ParseOut), P,
+                                  ctypes.c_size_t, ctypes.POINTER(ParseOpts), P]
+        getattr(L, f).restype = ctypes.c_int
+    L.ppr_parse_results.argtypes = [P, U64, ctypes.POINTER(ParseOut), P]
+    L.ppr_parse_results.restype = ctypes.c_int
+    L.ppr_lex_fold_bytes.argtypes = [U32]
+    L.ppr_lex_fold_bytes.restype = ctypes.c_size_t
+    L.ppr_lex_prepare.argtypes = [ctypes.POINTER(LexTablesC), ctypes.POINTER(LexPrepared), P]
+    L.ppr_lex_prepare.restype = ctypes.c_int
+    L.ppr_lex_workspace_bytes.argtypes = [U64, ctypes.POINTER(ParseOpts)]
+    L.ppr_lex_workspace_bytes.restype = ctypes.c_size_t
+    for f in ("ppr_lex", "ppr_lex_async"):
+        getattr(L, f).argtypes = [P, U64, ctypes.POINTER(LexTablesC), ctypes.POINTER(LexPrepared),
+                                  ctypes.POINTER(TokensOut), P, ctypes.c_size_t, ctypes.POINTER(ParseOpts), P]
+        getattr(L, f).restype = ctypes.c_int
+    L.ppr_lex_results.argtypes = [P, U64, ctypes.POINTER(TokensOut), P]
+    L.ppr_lex_results.restype = ctypes.c_int
+    L.ppr_lex_build_tables.argtypes = [P, P, U32, U32, U32, ctypes.POINTER(U32), P, P, P, ctypes.POINTER(ctypes.c_uint16)]
+    L.ppr_lex_build_tables.restype = ctypes.c_int
+    L.ppr_version.argtypes = []
+    L.ppr_version.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def version() -> str:
+    return lib.ppr_version().decode()
+
+
+def _check(code: int, where: str):
+    if code != PPR_OK:
+        raise PprError(code, where)
+
+
+def _stream_handle(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _opts(chunk_bytes):
+    o = ParseOpts()
+    o.chunk_bytes = int(chunk_bytes or 0)
+    return o
+
+
+def make_dfa(table: dict):
+    """(Dfa struct, class map bytes) from a DFA table dict."""
+    d = Dfa()
+    d.n_states = table["n_states"]
+    d.n_classes = table["n_classes"]
+    d.start_state = table["start"]
+    d.accept_mask = table["accept_mask"]
+    for s in range(table["n_states"]):
+        for c in range(table["n_classes"]):
+            d.next[s][c] = table["next"][s][c]
+            d.tag[s][c] = table["tag"][s][c]
+    cm = bytes(table["class_map"])
+    assert len(cm) == 256
+    return d, cm
+
+
+def _check_input(data: torch.Tensor):
+    if not (isinstance(data, torch.Tensor) and data.is_cuda and data.dtype == torch.uint8 and data.dim() == 1
+            and data.is_contiguous()):
+        raise TypeError("input must be a contiguous 1-D torch.uint8 tensor on a CUDA (HIP) device")
+
+
+@dataclass
+class ParseResult:
+    record_idx: torch.Tensor     # int32 view of the uint32 arrays, length n_fields
+    column_ids: torch.Tensor
+    field_offsets: torch.Tensor
+    field_lengths: torch.Tensor
+    n_fields: int
+    n_records: int
+    error_pos: int
+    end_state: int
+
+
+class Parser:
+    """Reusable workspace and output buffers for inputs of up to max_n bytes."""
+
+    def __init__(self, table: dict, max_n: int, capacity: int | None = None, chunk_bytes: int | None = None,
+                 device=None):
+        self.dfa, self.class_map = make_dfa(table)
+        self.opts = _opts(chunk_bytes)
+        self.device = torch.device("cuda") if device is None else torch.device(device)
+        self.max_n = int(max_n)
+        ws = lib.ppr_parse_workspace_bytes(self.max_n, ctypes.byref(self.opts))
+        if ws == 0:
+            raise PprError(PPR_EINVAL, "ppr_parse_workspace_bytes")
+        # zero-filled before first use, as the ABI requires
+        self.ws = torch.zeros(ws + 256, dtype=torch.uint8, device=self.device)
+        self.ws_off = (-self.ws.data_ptr()) % 256
+        self.ws_bytes = ws
+        self._alloc(self.max_n + 1 if capacity is None else int(capacity))
+
+    def _alloc(self, cap):
+        self.cap = max(int(cap), 1)
+        self.out_arrays = [torch.empty(self.cap, dtype=torch.int32, device=self.device) for _ in range(4)]
+
+    def _out(self):
+        o = ParseOut()
+        o.record_idx, o.column_ids, o.field_offsets, o.field_lengths = [a.data_ptr() for a in self.out_arrays]
+        o.cap_fields = self.cap
+        return o
+
+    def _ws_ptr(self):
+        return ctypes.c_void_p(self.ws.data_ptr() + self.ws_off)
+
+    def launch(self, data: torch.Tensor, stream=None):
+        """enqueue one parse without waiting (for timing loops)"""
+        _check_input(data)
+        n = data.numel()
+        if n > self.max_n:
+            raise ValueError("input larger than the parser's max_n")
+        o = self._out()
+        _check(lib.ppr_parse_async(ctypes.c_void_p(data.data_ptr()), n, ctypes.byref(self.dfa), self.class_map,
+                                   ctypes.byref(o), self._ws_ptr(), self.ws_bytes, ctypes.byref(self.opts),
+                                   _stream_handle(stream)), "ppr_parse_async")
+
+    def results(self, n: int, stream=None) -> ParseOut:
+        o = self._out()
+        rc = lib.ppr_parse_results(self._ws_ptr(), n, ctypes.byref(o), _stream_handle(stream))
+        if rc not in (PPR_OK, PPR_ECAPACITY):
+            raise PprError(rc, "ppr_parse_results")
+        return o
+
+    def __call__(self, data: torch.Tensor, stream=None) -> ParseResult:
+        _check_input(data)
+        n = data.numel()
+        if n > self.max_n:
+            raise ValueError("input larger than the parser's max_n")
+        for _ in range(2):
+            o = self._out()
+            rc = lib.ppr_parse(ctypes.c_void_p(data.data_ptr()), n, ctypes.byref(self.dfa), self.class_map,
+                               ctypes.byref(o), self._ws_ptr(), self.ws_bytes, ctypes.byref(self.opts),
+                               _stream_handle(stream))
+            if rc == PPR_ECAPACITY:  # size, then fill
+                self._alloc(o.n_fields)
+                continue
+            _check(rc, "ppr_parse")
+            k = int(o.n_fields)
+            return ParseResult(*[a[:k] for a in self.out_arrays], k, int(o.n_records), int(o.error_pos),
+                               int(o.end_state))
+        raise PprError(PPR_ECAPACITY, "ppr_parse")
+
+
+def parse(data: torch.Tensor, table: dict, chunk_bytes: int | None = None, capacity: int | None = None,
+          stream=None) -> ParseResult:
+    """Parse one input (device uint8 tensor) with a DFA table."""
+    _check_input(data)
+    n = data.numel()
+    cap = capacity if capacity is not None else min(n + 1, max(4096, n // 4))
+    return Parser(table, n, cap, chunk_bytes, data.device)(data, stream)
+
+
+# ------------------------------------------------------------------ lexer
+
+class LexTables:
+    """Device-resident lexer tables plus their prepared fold table."""
+
+    def __init__(self, initial_state: np.ndarray, merge_table: np.ndarray, final_states: np.ndarray, k: int,
+                 identity: int = 0, device=None):
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        self.k = int(k)
+        self.identity = int(identity)
+        self.h_initial = np.ascontiguousarray(initial_state, dtype=np.uint16).reshape(256)
+        self.h_merge = np.ascontiguousarray(merge_table, dtype=np.uint16).reshape(self.k * self.k)
+        self.h_final = np.ascontiguousarray(final_states, dtype=np.uint16).reshape(self.k)
+        as_dev = lambda a: torch.from_numpy(a.view(np.int16)).to(dev)
+        self.initial_state, self.merge_table, self.final_states = (as_dev(self.h_initial), as_dev(self.h_merge),
+                                                                   as_dev(self.h_final))
+        self.c = LexTablesC(self.initial_state.data_ptr(), self.merge_table.data_ptr(), self.final_states.data_ptr(),
+                            self.k, self.identity, 0x8000)
+        self.fold = torch.empty(lib.ppr_lex_fold_bytes(self.k) // 2, dtype=torch.int16, device=dev)
+        self.prep = LexPrepared()
+        self.prep.d_fold = self.fold.data_ptr()
+        _check(lib.ppr_lex_prepare(ctypes.byref(self.c), ctypes.byref(self.prep), _stream_handle()),
+               "ppr_lex_prepare")
+
+    @staticmethod
+    def build_host(dfa: dict, max_k: int = 32768):
+        """(initial_state, merge_table, final_states, k, identity) built by the library's host builder."""
+        delta = np.ascontiguousarray(dfa["delta"], dtype=np.int16)
+        kind = np.ascontiguousarray(dfa["kind"], dtype=np.uint16)
+        Q = delta.shape[0]
+        k = ctypes.c_uint32()
+        ident = ctypes.c_uint16()
+        _check(lib.ppr_lex_build_tables(delta.ctypes.data, kind.ctypes.data, Q, dfa["q0"], max_k, ctypes.byref(k),
+                                        None, None, None, None), "ppr_lex_build_tables")
+        kk = int(k.value)
+        init = np.zeros(256, dtype=np.uint16)
+        merge = np.zeros(kk * kk, dtype=np.uint16)
+        fin = np.zeros(kk, dtype=np.uint16)
+        _check(lib.ppr_lex_build_tables(delta.ctypes.data, kind.ctypes.data, Q, dfa["q0"], max_k, ctypes.byref(k),
+                                        init.ctypes.data, merge.ctypes.data, fin.ctypes.data, ctypes.byref(ident)),
+               "ppr_lex_build_tables")
+        return init, merge.reshape(kk, kk), fin, kk, int(ident.value)
+
+    @classmethod
+    def from_dfa(cls, dfa: dict, device=None):
+        init, merge, fin, k, ident = cls.build_host(dfa)
+        return cls(init, merge, fin, k, ident, device)
+
+
+@dataclass
+class LexResult:
+    kind: torch.Tensor
+    start: torch.Tensor
+    length: torch.Tensor
+    n_tokens: int
+
+
+class Lexer:
+    """Reusable workspace and token buffers for inputs of up to max_n bytes."""
+
+    def __init__(self, tables: LexTables, max_n: int, capacity: int | None = None, chunk_bytes: int | None = None):
+        self.t = tables
+        self.opts = _opts(chunk_bytes)
+        self.max_n = int(max_n)
+        dev = tables.merge_table.device
+        ws = lib.ppr_lex_workspace_bytes(self.max_n, ctypes.byref(self.opts))
+        if ws == 0:
+            raise PprError(PPR_EINVAL, "ppr_lex_workspace_bytes")
+        self.ws = torch.zeros(ws + 256, dtype=torch.uint8, device=dev)
+        self.ws_off = (-self.ws.data_ptr()) % 256
+        self.ws_bytes = ws
+        self.device = dev
+        self._alloc(self.max_n + 1 if capacity is None else int(capacity))
+
+    def _alloc(self, cap):
+        self.cap = max(int(cap), 1)
+        self.out_arrays = [torch.empty(self.cap, dtype=torch.int32, device=self.device) for _ in range(3)]
+
+    def _out(self):
+        o = TokensOut()
+        o.kind, o.start, o.length = [a.data_ptr() for a in self.out_arrays]
+        o.cap_tokens = self.cap
+        return o
+
+    def _ws_ptr(self):
+        return ctypes.c_void_p(self.ws.data_ptr() + self.ws_off)
+
+    def launch(self, data: torch.Tensor, stream=None):
+        _check_input(data)
+        o = self._out()
+        _check(lib.ppr_lex_async(ctypes.c_void_p(data.data_ptr()), data.numel(), ctypes.byref(self.t.c),
+                                 ctypes.byref(self.t.prep), ctypes.byref(o), self._ws_ptr(), self.ws_bytes,
+                                 ctypes.byref(self.opts), _stream_handle(stream)), "ppr_lex_async")
+
+    def results(self, n: int, stream=None) -> TokensOut:
+        o = self._out()
+        rc = lib.ppr_lex_results(self._ws_ptr(), n, ctypes.byref(o), _stream_handle(stream))
+        if rc not in (PPR_OK, PPR_ECAPACITY):
+            raise PprError(rc, "ppr_lex_results")
+        return o
+
+    def __call__(self, data: torch.Tensor, stream=None) -> LexResult:
+        _check_input(data)
+        n = data.numel()
+        if n > self.max_n:
+            raise ValueError("input larger than the lexer's max_n")
+        for _ in range(2):
+            o = self._out()
+            rc = lib.ppr_lex(ctypes.c_void_p(data.data_ptr()), n, ctypes.byref(self.t.c), ctypes.byref(self.t.prep),
+                             ctypes.byref(o), self._ws_ptr(), self.ws_bytes, ctypes.byref(self.opts),
+                             _stream_handle(stream))
+            if rc == PPR_ECAPACITY:
+                self._alloc(o.n_tokens)
+                continue
+            _check(rc, "ppr_lex")
+            k = int(o.n_tokens)
+            return LexResult(*[a[:k] for a in self.out_arrays], k)
+        raise PprError(PPR_ECAPACITY, "ppr_lex")
+
+
+def lex(data: torch.Tensor, tables: LexTables, chunk_bytes: int | None = None, capacity: int | None = None,
+        stream=None) -> LexResult:
+    _check_input(data)
+    n = data.numel()
+    cap = capacity if capacity is not None else min(n + 1, max(4096, n // 3))
+    return Lexer(tables, n, cap, chunk_bytes)(data, stream)

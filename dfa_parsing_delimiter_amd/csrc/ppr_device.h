@@ -1,0 +1,111 @@
+// Device-side building blocks shared by the CSV and lexer kernels (gfx950).
+//
+// State-transition vectors [ParPaRaw, Sec. 3, Fig. 2]: entry i is the state a
+// chunk ends in when it starts in state i. With at most 8 states, a vector is
+// 8 bytes in two VGPRs (entries 0-3 in `lo`, 4-7 in `hi`), so the composite of
+// two vectors is two v_perm_b32 byte selects — the register-resident array that
+// ParPaRaw builds with bit-field insert/extract (multi-fragment in-register
+// array, Fig. 8) becomes one byte permute per four entries on CDNA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ppr {
+
+constexpr int kWave = 64;
+
+struct Vec {
+    uint32_t lo, hi;
+};
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
+{
+    // v_perm_b32: byte k of the result is byte sel.k of the 64-bit value {hi, lo} (0-3: lo, 4-7: hi)
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ Vec vec_identity() { return {0x03020100u, 0x07060504u}; }
+
+// composite: a earlier, b later; result[i] = b[a[i]]
+__device__ __forceinline__ Vec compose(Vec a, Vec b) { return {perm(b.hi, b.lo, a.lo), perm(b.hi, b.lo, a.hi)}; }
+
+__device__ __forceinline__ uint32_t vec_at(Vec v, uint32_t s)
+{
+    uint32_t w = s < 4 ? v.lo : v.hi;
+    return (w >> ((s & 3u) * 8u)) & 0xffu;
+}
+
+// 8 entries of 3 bits (values < 8) <-> nibble-packed 32-bit word
+__device__ __forceinline__ uint32_t vec_pack(Vec v)
+{
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r |= ((v.lo >> (8 * i)) & 0xfu) << (4 * i);
+        r |= ((v.hi >> (8 * i)) & 0xfu) << (4 * (i + 4));
+    }
+    return r;
+}
+
+__device__ __forceinline__ Vec vec_unpack(uint32_t p)
+{
+    Vec v{0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v.lo |= ((p >> (4 * i)) & 0xfu) << (8 * i);
+        v.hi |= ((p >> (4 * (i + 4))) & 0xfu) << (8 * i);
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------- atomics (agent scope)
+
+__device__ __forceinline__ uint64_t ld_relaxed(const uint64_t* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_acquire(const uint64_t* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(uint64_t* p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_release(uint64_t* p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------- look-back status words
+//
+// Decoupled look-back (single-pass prefix scan with a per-tile status that is
+// either the tile's own aggregate or its inclusive prefix). A status word is
+// [63:34] call epoch, [33:32] flag, [31:0] payload. Statuses left over from an
+// earlier call carry another epoch and read as "not yet published", so the
+// status arrays never need clearing between calls.
+
+constexpr uint32_t kFlagAgg = 1;
+constexpr uint32_t kFlagIncl = 2;
+constexpr uint32_t kEpochMask = 0x3fffffffu;
+
+__device__ __forceinline__ uint64_t status_word(uint32_t epoch, uint32_t flag, uint32_t payload)
+{
+    return ((uint64_t)(epoch & kEpochMask) << 34) | ((uint64_t)flag << 32) | payload;
+}
+__device__ __forceinline__ uint32_t status_flag(uint64_t w, uint32_t epoch)
+{
+    return (uint32_t)(w >> 34) == (epoch & kEpochMask) ? (uint32_t)(w >> 32) & 3u : 0u;
+}
+__device__ __forceinline__ uint32_t status_payload(uint64_t w) { return (uint32_t)w; }
+
+// ---------------------------------------------------------------- wave shuffles
+
+__device__ __forceinline__ uint32_t shfl_up(uint32_t v, int d) { return (uint32_t)__shfl_up((int)v, d, kWave); }
+__device__ __forceinline__ uint32_t shfl_down(uint32_t v, int d) { return (uint32_t)__shfl_down((int)v, d, kWave); }
+__device__ __forceinline__ uint32_t shfl(uint32_t v, int src) { return (uint32_t)__shfl((int)v, src, kWave); }
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+}  // namespace ppr

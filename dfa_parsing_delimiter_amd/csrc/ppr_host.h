@@ -1,0 +1,56 @@
+// Host/device structures shared by the library's entry points.
+#pragma once
+
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+namespace ppr {
+
+// Start of every workspace (256 bytes reserved): the tile counter of the
+// running call and the scalar results the last tile writes.
+struct WsHeader {
+    uint32_t tile_counter;
+    uint32_t end_state;
+    uint64_t n_fields;  // n_tokens for the lexer
+    uint64_t n_records;
+    int64_t error_pos;
+    uint32_t fault;     // set when a look-back wait gave up (never expected)
+    uint32_t reserved;
+};
+
+// Upper bound on look-back polls per tile; beyond it the kernel records a fault
+// and finishes instead of waiting forever.
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+// Count-carry status of one tile (second look-back): a flag word and two
+// write-once payloads, the tile's own aggregate and its inclusive prefix. They
+// must not share storage: a reader that saw the aggregate flag may read the
+// payload after the tile has gone on to publish its inclusive prefix.
+struct StatB {
+    uint64_t flag;
+    uint32_t agg[6];
+    uint32_t incl[6];
+    uint32_t pad[2];
+};
+static_assert(sizeof(StatB) == 64, "StatB layout");
+
+struct WsLayout {
+    uint64_t tiles, off_a, off_b, total;
+};
+
+inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+// Call epochs tag look-back statuses so stale ones from earlier calls read as
+// unpublished. 0 never occurs (a zero-filled workspace holds no valid status).
+inline uint32_t next_epoch()
+{
+    static std::atomic<uint32_t> ctr{0};
+    for (;;) {
+        uint32_t e = (ctr.fetch_add(1, std::memory_order_relaxed) + 1u) & 0x3fffffffu;
+        if (e) return e;
+    }
+}
+
+}  // namespace ppr

@@ -1,0 +1,503 @@
+// Table-driven data-parallel lexer on gfx950.
+//
+// Method: "Lexing on the GPU: the scan is the easy part", section "A lexer is a
+// prefix scan": bytes map to identifiers of partially applied transition
+// functions, composition is one load from a k x k table of 16-bit identifiers,
+// and the lexer state after every prefix is an inclusive scan under that
+// composition. A flag bit on a merged identifier marks a token boundary; the
+// final-state table gives the kind of the token ending just before it (section
+// "Does it produce the same tokens?").
+//
+// MI355X mapping (not the page's Futhark map/scan/filter/gather pipeline, which
+// materialises ~20 bytes of state per input byte):
+//   * nothing per byte is materialised in HBM: a tile of 256*L bytes is staged
+//     once into LDS, each thread folds its chunk sequentially (a chunk only ever
+//     merges with single-byte elements, so the fold reads a k x m "fold" table —
+//     the merge table restricted to the m distinct byte identifiers — that fits
+//     in L2, instead of the k x k table);
+//   * chunk identifiers are scanned in the workgroup with the merge table, then
+//     across tiles by decoupled look-back (16-bit payloads);
+//   * each thread re-folds its chunk from its true prefix identifier, marks token
+//     boundaries in a bitmap, and a second look-back scans token counts; tokens
+//     are written as (kind, start, length) directly.
+#include "ppr.h"
+#include "ppr_device.h"
+#include "ppr_host.h"
+
+namespace ppr {
+
+constexpr int kLexBlock = 256;
+constexpr int kLexWaves = kLexBlock / kWave;
+constexpr int kLexMaxChunk = 64;
+
+struct LexParams {
+    const uint8_t* in;
+    uint32_t n, L, tile_bytes, num_tiles, epoch;
+    uint32_t k, m;
+    uint32_t id_mask, flag_mask;
+    uint32_t identity, reserved;
+    const uint16_t* merge;  // k x k
+    const uint16_t* fold;   // k x m
+    const uint16_t* final_;
+    uint32_t* kind;
+    uint32_t* start;
+    uint32_t* len;
+    uint64_t cap;
+    WsHeader* hdr;
+    uint64_t* statA;
+    StatB* statB;  // payload words: token count, last boundary
+    uint8_t col[256];
+};
+
+__device__ __forceinline__ uint32_t merge_ids(const LexParams& p, uint32_t a, uint32_t b)
+{
+    return (uint32_t)p.merge[(uint64_t)a * p.k + b] & p.id_mask;
+}
+
+// token-count carry: nt tokens ended, lb = last boundary position (0 when none:
+// the first token starts at 0 either way). Both combine commutatively.
+struct TokCarry {
+    uint32_t nt, lb;
+};
+
+__device__ void block_scan_ids(const LexParams& p, uint32_t x, uint32_t& excl, uint32_t& total, uint32_t* s_wave)
+{
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    uint32_t inc = x;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        uint32_t o = shfl_up(inc, d);
+        if (lane >= d) inc = merge_ids(p, o, inc);
+    }
+    if (lane == kWave - 1) s_wave[w] = inc;
+    __syncthreads();
+    uint32_t pre = p.identity, tot = p.identity;
+#pragma unroll
+    for (int i = 0; i < kLexWaves; ++i) {
+        uint32_t a = s_wave[i];
+        if (i < w) pre = merge_ids(p, pre, a);
+        tot = merge_ids(p, tot, a);
+    }
+    uint32_t ex = shfl_up(inc, 1);
+    if (lane == 0) ex = p.identity;
+    excl = merge_ids(p, pre, ex);
+    total = tot;
+}
+
+__device__ void block_scan_tok(TokCarry c, TokCarry& excl, TokCarry& total, TokCarry* s_wave)
+{
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    TokCarry inc = c;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        uint32_t ont = shfl_up(inc.nt, d), olb = shfl_up(inc.lb, d);
+        if (lane >= d) {
+            inc.nt += ont;
+            inc.lb = max(inc.lb, olb);
+        }
+    }
+    if (lane == kWave - 1) s_wave[w] = inc;
+    __syncthreads();
+    TokCarry pre{0, 0}, tot{0, 0};
+#pragma unroll
+    for (int i = 0; i < kLexWaves; ++i) {
+        TokCarry a = s_wave[i];
+        if (i < w) {
+            pre.nt += a.nt;
+            pre.lb = max(pre.lb, a.lb);
+        }
+        tot.nt += a.nt;
+        tot.lb = max(tot.lb, a.lb);
+    }
+    uint32_t ent = shfl_up(inc.nt, 1), elb = shfl_up(inc.lb, 1);
+    if (lane == 0) ent = elb = 0;
+    excl = {pre.nt + ent, max(pre.lb, elb)};
+    total = tot;
+}
+
+// Wave 0 only: identifier of all bytes before `tile` (tile > 0).
+__device__ uint32_t lookback_id(const LexParams& p, uint32_t tile)
+{
+    const int lane = lane_id();
+    uint32_t acc = p.identity;
+    int64_t base = (int64_t)tile - 1;
+    uint32_t spins = 0;
+    for (;;) {
+        const int64_t u = base - lane;
+        const bool valid = u >= 0;
+        uint64_t w = 0;
+        uint32_t f = kFlagIncl;
+        if (valid) {
+            w = ld_relaxed(&p.statA[u]);
+            f = status_flag(w, p.epoch);
+        }
+        while (!__all(f != 0)) {
+            if (++spins > kSpinLimit) {
+                if (lane == 0) atomicOr(&p.hdr->fault, 1u);
+                return p.identity;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            if (f == 0) {
+                w = ld_relaxed(&p.statA[u]);
+                f = status_flag(w, p.epoch);
+            }
+        }
+        const uint64_t incl = __ballot(valid && f == kFlagIncl);
+        const int j = incl ? __ffsll((unsigned long long)incl) - 1 : kWave;
+        uint32_t a = (valid && lane <= j) ? status_payload(w) : p.identity;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            uint32_t o = shfl_down(a, d);
+            if (lane + d < kWave) a = merge_ids(p, o, a);
+        }
+        acc = merge_ids(p, shfl(a, 0), acc);
+        if (j < kWave) return acc;
+        base -= kWave;
+    }
+}
+
+__device__ TokCarry lookback_tok(const LexParams& p, uint32_t tile)
+{
+    const int lane = lane_id();
+    TokCarry acc{0, 0};
+    int64_t base = (int64_t)tile - 1;
+    uint32_t spins = 0;
+    for (;;) {
+        const int64_t u = base - lane;
+        const bool valid = u >= 0;
+        uint32_t f = kFlagIncl;
+        if (valid) f = status_flag(ld_acquire(&p.statB[u].flag), p.epoch);
+        while (!__all(f != 0)) {
+            if (++spins > kSpinLimit) {
+                if (lane == 0) atomicOr(&p.hdr->fault, 2u);
+                return TokCarry{0, 0};
+            }
+            __builtin_amdgcn_s_sleep(1);
+            if (f == 0) f = status_flag(ld_acquire(&p.statB[u].flag), p.epoch);
+        }
+        const uint64_t incl = __ballot(valid && f == kFlagIncl);
+        const int j = incl ? __ffsll((unsigned long long)incl) - 1 : kWave;
+        uint32_t nt = 0, lb = 0;
+        if (valid && lane <= j) {
+            const uint32_t* v = f == kFlagIncl ? p.statB[u].incl : p.statB[u].agg;
+            nt = v[0];
+            lb = v[1];
+        }
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            nt += shfl_down(nt, d) * (lane + d < kWave ? 1u : 0u);
+            lb = max(lb, lane + d < kWave ? shfl_down(lb, d) : 0u);
+        }
+        acc.nt += shfl(nt, 0);
+        acc.lb = max(acc.lb, shfl(lb, 0));
+        if (j < kWave) return acc;
+        base -= kWave;
+    }
+}
+
+__device__ __forceinline__ void publish_tok(StatB& s, TokCarry c, uint32_t epoch, uint32_t flag)
+{
+    uint32_t* v = flag == kFlagIncl ? s.incl : s.agg;
+    v[0] = c.nt;
+    v[1] = c.lb;
+    st_release(&s.flag, status_word(epoch, flag, 0));
+}
+
+__global__ void lex_reset_kernel(WsHeader* hdr)
+{
+    if (threadIdx.x == 0) {
+        hdr->tile_counter = 0;
+        hdr->n_fields = 0;
+        hdr->fault = 0;
+    }
+}
+
+__global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
+{
+    __shared__ __align__(16) uint8_t s_bytes[kLexBlock * kLexMaxChunk];
+    __shared__ uint16_t s_kind[kLexBlock * kLexMaxChunk];
+    __shared__ uint8_t s_col[256];
+    __shared__ uint32_t s_wid[kLexWaves];
+    __shared__ TokCarry s_wtok[kLexWaves];
+    __shared__ uint32_t s_tile, s_prefix_id;
+    __shared__ TokCarry s_prefix;
+
+    const int tid = threadIdx.x;
+    if (tid == 0) s_tile = atomicAdd(&p.hdr->tile_counter, 1u);
+    s_col[tid] = p.col[tid];
+    __syncthreads();
+    const uint32_t tile = s_tile;
+    const uint32_t tile_start = tile * p.tile_bytes;
+    const uint32_t tile_len = min(p.tile_bytes, p.n - tile_start);
+
+    const uint8_t* src = p.in + tile_start;
+    if ((((uintptr_t)src) & 15u) == 0) {
+        const uint32_t nvec = tile_len >> 4;
+        const uint4* s4 = reinterpret_cast<const uint4*>(src);
+        uint4* d4 = reinterpret_cast<uint4*>(s_bytes);
+        for (uint32_t i = tid; i < nvec; i += kLexBlock) d4[i] = s4[i];
+        for (uint32_t i = (nvec << 4) + tid; i < tile_len; i += kLexBlock) s_bytes[i] = src[i];
+    } else {
+        for (uint32_t i = tid; i < tile_len; i += kLexBlock) s_bytes[i] = src[i];
+    }
+    __syncthreads();
+
+    const uint32_t L = p.L;
+    const uint32_t pos0 = tid * L;
+    const uint32_t my_len = pos0 < tile_len ? min(L, tile_len - pos0) : 0u;
+    const uint32_t chunk_abs = tile_start + pos0;
+    const uint32_t m = p.m;
+
+    // pass 1: fold the chunk from the identity (flags are ignored here)
+    uint32_t x = p.identity;
+    for (uint32_t j = 0; j < my_len; ++j) x = (uint32_t)p.fold[x * m + s_col[s_bytes[pos0 + j]]] & p.id_mask;
+    uint32_t excl, tot;
+    block_scan_ids(p, x, excl, tot, s_wid);
+
+    if (tile == 0) {
+        if (tid == 0) {
+            s_prefix_id = p.identity;
+            st_relaxed(&p.statA[0], status_word(p.epoch, kFlagIncl, tot));
+        }
+    } else {
+        if (tid == 0) st_relaxed(&p.statA[tile], status_word(p.epoch, kFlagAgg, tot));
+        if (tid < kWave) {
+            const uint32_t pre = lookback_id(p, tile);
+            if (tid == 0) {
+                s_prefix_id = pre;
+                st_relaxed(&p.statA[tile], status_word(p.epoch, kFlagIncl, merge_ids(p, pre, tot)));
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t tile_prefix = s_prefix_id;
+
+    // pass 2: re-fold from the true prefix and mark boundaries
+    uint32_t prev = merge_ids(p, tile_prefix, excl);
+    uint64_t B = 0;
+    for (uint32_t j = 0; j < my_len; ++j) {
+        const uint32_t y = p.fold[prev * m + s_col[s_bytes[pos0 + j]]];
+        if ((y & p.flag_mask) && (chunk_abs + j) != 0u) {
+            B |= 1ull << j;
+            s_kind[pos0 + j] = p.final_[prev];
+        }
+        prev = y & p.id_mask;
+    }
+    TokCarry c{(uint32_t)__popcll(B), B ? chunk_abs + (uint32_t)(63 - __clzll((long long)B)) : 0u};
+    TokCarry cex, ctot;
+    block_scan_tok(c, cex, ctot, s_wtok);
+
+    if (tile == 0) {
+        if (tid == 0) {
+            s_prefix = TokCarry{0, 0};
+            publish_tok(p.statB[0], ctot, p.epoch, kFlagIncl);
+        }
+    } else {
+        if (tid == 0) publish_tok(p.statB[tile], ctot, p.epoch, kFlagAgg);
+        if (tid < kWave) {
+            TokCarry pre = lookback_tok(p, tile);
+            if (tid == 0) {
+                s_prefix = pre;
+                publish_tok(p.statB[tile], TokCarry{pre.nt + ctot.nt, max(pre.lb, ctot.lb)}, p.epoch, kFlagIncl);
+            }
+        }
+    }
+    __syncthreads();
+    const TokCarry P = s_prefix;
+
+    {
+        uint64_t ti = (uint64_t)P.nt + cex.nt;
+        uint32_t st = max(P.lb, cex.lb);
+        uint64_t bits = B;
+        while (bits) {
+            const uint32_t j = (uint32_t)__ffsll((unsigned long long)bits) - 1u;
+            const uint32_t pos = chunk_abs + j;
+            if (ti < p.cap) {
+                p.kind[ti] = s_kind[pos0 + j];
+                p.start[ti] = st;
+                p.len[ti] = pos - st;
+            }
+            ++ti;
+            st = pos;
+            bits &= bits - 1;
+        }
+    }
+
+    if (tile == p.num_tiles - 1 && tid == 0) {
+        const uint32_t nt = P.nt + ctot.nt;
+        const uint32_t lb = max(P.lb, ctot.lb);
+        const uint32_t last = merge_ids(p, tile_prefix, tot);
+        if (nt < p.cap) {
+            p.kind[nt] = p.final_[last];
+            p.start[nt] = lb;
+            p.len[nt] = p.n - lb;
+        }
+        p.hdr->n_fields = (uint64_t)nt + 1u;
+    }
+}
+
+// sets *bad if any merge entry's identifier is >= k
+__global__ void lex_check_kernel(const uint16_t* merge, uint64_t count, uint32_t k, uint32_t id_mask, uint32_t* bad)
+{
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count && ((uint32_t)merge[i] & id_mask) >= k) atomicOr(bad, 1u);
+}
+
+struct ColumnIds {
+    uint16_t id[256];
+};
+
+// fold[x][j] = merge[x][identifier of column j]
+__global__ void lex_fold_kernel(const uint16_t* merge, uint32_t k, ColumnIds cols, uint32_t m, uint16_t* fold)
+{
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (uint64_t)k * m) return;
+    const uint64_t x = i / m, j = i % m;
+    fold[i] = merge[x * k + cols.id[j]];
+}
+
+static uint32_t lex_chunk_of(const ppr_parse_opts_t* o)
+{
+    uint32_t L = o ? o->chunk_bytes : 0u;
+    if (L == 0) L = 32;
+    return L <= (uint32_t)kLexMaxChunk ? L : 0u;
+}
+
+static WsLayout lex_layout(uint64_t n, uint32_t L)
+{
+    const uint64_t tile = (uint64_t)kLexBlock * L;
+    const uint64_t tiles = (n + tile - 1) / tile;
+    WsLayout w;
+    w.tiles = tiles;
+    w.off_a = 256;
+    w.off_b = align_up(w.off_a + tiles * sizeof(uint64_t), 256);
+    w.total = align_up(w.off_b + tiles * sizeof(StatB), 256);
+    return w;
+}
+
+}  // namespace ppr
+
+using namespace ppr;
+
+extern "C" size_t ppr_lex_fold_bytes(uint32_t k) { return (size_t)k * 256u * sizeof(uint16_t); }
+
+extern "C" int ppr_lex_prepare(const ppr_lex_tables_t* t, ppr_lex_prepared_t* prep, void* stream)
+{
+    if (!t || !prep || !t->initial_state || !t->merge_table || !t->final_states || !prep->d_fold) return PPR_EINVAL;
+    if (t->k == 0 || t->k > t->flag_mask || t->flag_mask != 0x8000u || t->identity >= t->k) return PPR_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    uint16_t init[256];
+    if (hipMemcpyAsync(init, t->initial_state, sizeof init, hipMemcpyDeviceToHost, s) != hipSuccess) return PPR_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return PPR_EHIP;
+    ColumnIds cols;
+    memset(&cols, 0, sizeof cols);
+    uint32_t m = 0;
+    for (int b = 0; b < 256; ++b) {
+        const uint16_t id = (uint16_t)(init[b] & (uint16_t)~t->flag_mask);
+        if (id >= t->k) return PPR_EINVAL;
+        uint32_t j = 0;
+        while (j < m && cols.id[j] != id) ++j;
+        if (j == m) cols.id[m++] = id;
+        prep->column_of[b] = (uint8_t)j;
+    }
+    prep->k = t->k;
+    prep->m = m;
+    prep->identity = t->identity;
+    prep->flag_mask = t->flag_mask;
+    {
+        // every merge entry must name an identifier below k; the prepared fold
+        // buffer's first word serves as the flag (it is overwritten below)
+        uint32_t* d_bad = reinterpret_cast<uint32_t*>(prep->d_fold);
+        uint32_t bad = 0;
+        if (hipMemsetAsync(d_bad, 0, sizeof(uint32_t), s) != hipSuccess) return PPR_EHIP;
+        const uint64_t count = (uint64_t)t->k * t->k;
+        hipLaunchKernelGGL(lex_check_kernel, dim3((uint32_t)((count + 255) / 256)), dim3(256), 0, s, t->merge_table,
+                           count, t->k, (uint32_t)(uint16_t)~t->flag_mask, d_bad);
+        if (hipGetLastError() != hipSuccess) return PPR_EHIP;
+        if (hipMemcpyAsync(&bad, d_bad, sizeof bad, hipMemcpyDeviceToHost, s) != hipSuccess) return PPR_EHIP;
+        if (hipStreamSynchronize(s) != hipSuccess) return PPR_EHIP;
+        if (bad) return PPR_EINVAL;
+    }
+    const uint64_t total = (uint64_t)t->k * m;
+    const uint32_t blocks = (uint32_t)((total + 255) / 256);
+    hipLaunchKernelGGL(lex_fold_kernel, dim3(blocks), dim3(256), 0, s, t->merge_table, t->k, cols, m, prep->d_fold);
+    if (hipGetLastError() != hipSuccess) return PPR_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return PPR_EHIP;
+    return PPR_OK;
+}
+
+extern "C" size_t ppr_lex_workspace_bytes(uint64_t n, const ppr_parse_opts_t* opts)
+{
+    const uint32_t L = lex_chunk_of(opts);
+    if (!L || n >= 0xffffffffull) return 0;
+    return (size_t)lex_layout(n, L).total;
+}
+
+extern "C" int ppr_lex_async(const uint8_t* d_bytes, uint64_t n, const ppr_lex_tables_t* t,
+                             const ppr_lex_prepared_t* prep, const ppr_tokens_out_t* out, void* d_ws, size_t ws_bytes,
+                             const ppr_parse_opts_t* opts, void* stream)
+{
+    if (!t || !prep || !out || !d_ws || (n && !d_bytes)) return PPR_EINVAL;
+    if (!t->merge_table || !t->final_states || !prep->d_fold || prep->k != t->k || prep->m == 0) return PPR_EINVAL;
+    if (t->k == 0 || t->flag_mask != 0x8000u || t->identity >= t->k) return PPR_EINVAL;
+    if (out->cap_tokens && (!out->kind || !out->start || !out->length)) return PPR_EINVAL;
+    if (n >= 0xffffffffull) return PPR_ETOOBIG;
+    const uint32_t L = lex_chunk_of(opts);
+    if (!L) return PPR_EINVAL;
+    const WsLayout lay = lex_layout(n, L);
+    if (ws_bytes < lay.total || ((uintptr_t)d_ws & 255u)) return PPR_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)d_ws;
+    WsHeader* hdr = (WsHeader*)ws;
+    hipLaunchKernelGGL(lex_reset_kernel, dim3(1), dim3(64), 0, s, hdr);
+    if (hipGetLastError() != hipSuccess) return PPR_EHIP;
+    if (n == 0) return PPR_OK;
+    LexParams p;
+    memset(&p, 0, sizeof p);
+    p.in = d_bytes;
+    p.n = (uint32_t)n;
+    p.L = L;
+    p.tile_bytes = kLexBlock * L;
+    p.num_tiles = (uint32_t)lay.tiles;
+    p.epoch = next_epoch();
+    p.k = t->k;
+    p.m = prep->m;
+    p.flag_mask = t->flag_mask;
+    p.id_mask = (uint32_t)(uint16_t)~t->flag_mask;
+    p.identity = t->identity;
+    p.merge = t->merge_table;
+    p.fold = prep->d_fold;
+    p.final_ = t->final_states;
+    p.kind = out->kind;
+    p.start = out->start;
+    p.len = out->length;
+    p.cap = out->cap_tokens;
+    p.hdr = hdr;
+    p.statA = (uint64_t*)(ws + lay.off_a);
+    p.statB = (StatB*)(ws + lay.off_b);
+    memcpy(p.col, prep->column_of, 256);
+    hipLaunchKernelGGL(lex_kernel, dim3(p.num_tiles), dim3(kLexBlock), 0, s, p);
+    if (hipGetLastError() != hipSuccess) return PPR_EHIP;
+    return PPR_OK;
+}
+
+extern "C" int ppr_lex_results(const void* d_ws, uint64_t n, ppr_tokens_out_t* out, void* stream)
+{
+    (void)n;
+    if (!d_ws || !out) return PPR_EINVAL;
+    WsHeader h;
+    hipStream_t s = (hipStream_t)stream;
+    if (hipMemcpyAsync(&h, d_ws, sizeof h, hipMemcpyDeviceToHost, s) != hipSuccess) return PPR_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return PPR_EHIP;
+    out->n_tokens = h.n_fields;
+    if (h.fault) return PPR_EHIP;
+    return out->n_tokens > out->cap_tokens ? PPR_ECAPACITY : PPR_OK;
+}
+
+extern "C" int ppr_lex(const uint8_t* d_bytes, uint64_t n, const ppr_lex_tables_t* t, const ppr_lex_prepared_t* prep,
+                       ppr_tokens_out_t* out, void* d_ws, size_t ws_bytes, const ppr_parse_opts_t* opts, void* stream)
+{
+    int rc = ppr_lex_async(d_bytes, n, t, prep, out, d_ws, ws_bytes, opts, stream);
+    if (rc) return rc;
+    return ppr_lex_results(d_ws, n, out, stream);
+}

@@ -1,0 +1,222 @@
+/*
+ * ppr.h — data-parallel DFA parsing of delimiter-separated bytes and
+ * table-driven lexing on one AMD Instinct MI355X (gfx950).
+ *
+ * Method sources:
+ *   [P] "ParPaRaw: Massively Parallel Parsing of Delimiter-Separated Raw Data":
+ *       Sec. 3 (parsing context: one DFA instance per state per chunk, the
+ *       state-transition vector, its composite and the exclusive scan seeded with
+ *       the identity vector, Fig. 2; tagging: record and field delimiter bitmaps;
+ *       offsets: record counts and relative/absolute column offsets, Fig. 4) and
+ *       "validating format" (invalid transitions, non-accepting end state).
+ *   [L] "Lexing on the GPU: the scan is the easy part": "A lexer is a prefix
+ *       scan" (composition of partially applied transition functions as a scan,
+ *       every reachable composition numbered, composition as a k x k table of
+ *       16-bit identifiers, a produces-a-token flag bit masked off both operands)
+ *       and "Does it produce the same tokens?" (the final-state table gives the
+ *       kind of the token ending at a flagged position; bytes index unsigned).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named d_* are device pointers (hipMalloc or torch CUDA memory) of
+ *     the current HIP device; all other pointers are host pointers.
+ *   - The caller owns every buffer. The library allocates nothing on the device
+ *     in these calls; the workspace is caller-provided.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued on
+ *     it; calls sharing one workspace must be ordered on one stream.
+ *   - Return value: PPR_OK or a negative PPR_E* code. A malformed input is data,
+ *     not an error: it is reported through error_pos with PPR_OK.
+ *   - Blocking calls (ppr_parse, ppr_lex) return after the scalar results have
+ *     been copied back; the *_async forms leave them in the workspace for
+ *     ppr_*_results to read.
+ */
+#ifndef PPR_H
+#define PPR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PPR_MAX_STATES 8
+#define PPR_MAX_CLASSES 16
+
+/* Per-byte tags, the Mealy output of reading a symbol class in a state [P Sec. 3, tagging]. */
+enum ppr_tag { PPR_TAG_VALUE = 0, PPR_TAG_FIELD = 1, PPR_TAG_RECORD = 2, PPR_TAG_INVALID = 3 };
+
+enum ppr_status {
+    PPR_OK = 0,
+    PPR_EINVAL = -1,     /* bad table, bad option, NULL pointer */
+    PPR_ECAPACITY = -2,  /* output arrays too small; the counts are still reported */
+    PPR_ETOOBIG = -3,    /* n too large for one call */
+    PPR_EHIP = -4,       /* a HIP runtime call failed */
+    PPR_EWORKSPACE = -5  /* workspace too small or misaligned */
+};
+
+/*
+ * DFA over symbol classes [P Sec. 3, Fig. 3; symbol groups, Table 1].
+ *   n_states in [1, 8], n_classes in [1, 16]; states and classes are indices.
+ *   next[s][c]: state after reading a byte of class c in state s (< n_states).
+ *   tag[s][c]:  ppr_tag of that byte.
+ *   start_state: state before the first byte.
+ *   accept_mask: bit s set if s is an accepting end state.
+ * Entries for s >= n_states or c >= n_classes are ignored.
+ */
+typedef struct ppr_dfa {
+    uint32_t n_states;
+    uint32_t n_classes;
+    uint32_t start_state;
+    uint32_t accept_mask;
+    uint8_t next[PPR_MAX_STATES][PPR_MAX_CLASSES];
+    uint8_t tag[PPR_MAX_STATES][PPR_MAX_CLASSES];
+} ppr_dfa_t;
+
+/*
+ * Per-field output [P Sec. 3, offsets and tagging, Fig. 4], one entry per field
+ * in input order. A field ends at each FIELD or RECORD byte; if the input is
+ * non-empty and its last byte is not tagged RECORD, the unterminated rest is one
+ * more field (and record).
+ *   record_idx[i]    records completed before field i,
+ *   column_ids[i]    FIELD bytes since the last RECORD byte (or the start),
+ *   field_offsets[i] first byte of the raw span (byte after the previous terminator, or 0),
+ *   field_lengths[i] bytes from the offset up to (not including) the terminator, or to n.
+ * Device arrays of cap_fields entries each. Entries beyond cap_fields are not
+ * written; n_fields reports the full count.
+ */
+typedef struct ppr_parse_out {
+    uint32_t* record_idx;
+    uint32_t* column_ids;
+    uint32_t* field_offsets;
+    uint32_t* field_lengths;
+    uint64_t cap_fields;
+    uint64_t n_fields;  /* out */
+    uint64_t n_records; /* out */
+    int64_t error_pos;  /* out: first INVALID byte; else n if the end state is not accepting; else -1 */
+    uint32_t end_state; /* out: DFA state after the last byte */
+    uint32_t reserved;
+} ppr_parse_out_t;
+
+/* Launch options. chunk_bytes: bytes each thread simulates (1..64, 0 = default 32). */
+typedef struct ppr_parse_opts {
+    uint32_t chunk_bytes;
+    uint32_t reserved[3];
+} ppr_parse_opts_t;
+
+/*
+ * Workspace bytes ppr_parse needs for n input bytes (opts may be NULL).
+ * The workspace must be 256-byte aligned and zero-filled before its first use
+ * (afterwards the library keeps it consistent); 0 on invalid arguments.
+ */
+size_t ppr_parse_workspace_bytes(uint64_t n, const ppr_parse_opts_t* opts);
+
+/*
+ * Parse n bytes at d_bytes with the DFA and the 256-entry class map (host
+ * pointers, validated and copied at the call). n must be below 2^32 - 1
+ * (PPR_ETOOBIG otherwise). d_bytes needs no particular alignment.
+ * Blocking: returns with out->n_fields, n_records, error_pos, end_state set.
+ * Returns PPR_ECAPACITY (with the counts set) if n_fields > cap_fields.
+ */
+int ppr_parse(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, const uint8_t class_map[256],
+              ppr_parse_out_t* out, void* d_ws, size_t ws_bytes, const ppr_parse_opts_t* opts, void* stream);
+
+/* Enqueue the same work without waiting; ppr_parse_results completes it. */
+int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, const uint8_t class_map[256],
+                    const ppr_parse_out_t* out, void* d_ws, size_t ws_bytes, const ppr_parse_opts_t* opts,
+                    void* stream);
+
+/* Wait on `stream` and copy the scalars of the last ppr_parse_async on d_ws into out. */
+int ppr_parse_results(const void* d_ws, uint64_t n, ppr_parse_out_t* out, void* stream);
+
+/* ------------------------------------------------------------------ lexer */
+
+/*
+ * Lexer tables [L, "A lexer is a prefix scan"]. Device pointers.
+ *   initial_state[256]: element identifier of each byte (flag bit allowed).
+ *   merge_table[k*k]:   row a, column b = identifier of "a then b" with the flag
+ *                       bit set when its last byte ends a token; a is the earlier
+ *                       operand. Flag bits are masked off both operands first.
+ *   final_states[k]:    token kind of the token ending at a prefix whose
+ *                       identifier is x.
+ *   identity:           identifier of the empty string (neutral on both sides).
+ *   flag_mask:          the flag bit (0x8000); identifiers are < k <= flag_mask.
+ */
+typedef struct ppr_lex_tables {
+    const uint16_t* initial_state;
+    const uint16_t* merge_table;
+    const uint16_t* final_states;
+    uint32_t k;
+    uint16_t identity;
+    uint16_t flag_mask;
+} ppr_lex_tables_t;
+
+/*
+ * Prepared form of the tables for the kernels, filled by ppr_lex_prepare:
+ * bytes with the same initial identifier share a column, and d_fold holds,
+ * for every identifier x and column j, merge_table[x][column j's identifier]
+ * (k * m entries, device memory the caller provides).
+ */
+typedef struct ppr_lex_prepared {
+    uint16_t* d_fold;      /* caller-provided device buffer of ppr_lex_fold_bytes(k) bytes */
+    uint32_t k;
+    uint32_t m;            /* out: number of columns */
+    uint16_t identity;
+    uint16_t flag_mask;
+    uint8_t column_of[256]; /* out: column of each byte */
+} ppr_lex_prepared_t;
+
+/* Device bytes the prepared fold table needs (k * 256 * 2 at most). */
+size_t ppr_lex_fold_bytes(uint32_t k);
+
+/* Build the prepared tables (reads initial_state back; blocking). */
+int ppr_lex_prepare(const ppr_lex_tables_t* tables, ppr_lex_prepared_t* prep, void* stream);
+
+/*
+ * Token output, one entry per token in input order: kind = final_states of the
+ * prefix ending at the token's last byte, start, length. Every byte belongs to
+ * exactly one token; a token ends before each byte whose merged identifier has
+ * the flag bit (position 0 excepted) and at n.
+ */
+typedef struct ppr_tokens_out {
+    uint32_t* kind;
+    uint32_t* start;
+    uint32_t* length;
+    uint64_t cap_tokens;
+    uint64_t n_tokens; /* out */
+} ppr_tokens_out_t;
+
+size_t ppr_lex_workspace_bytes(uint64_t n, const ppr_parse_opts_t* opts);
+
+/* Lex n bytes (n < 2^32 - 1). Blocking. PPR_ECAPACITY if n_tokens > cap_tokens. */
+int ppr_lex(const uint8_t* d_bytes, uint64_t n, const ppr_lex_tables_t* tables, const ppr_lex_prepared_t* prep,
+            ppr_tokens_out_t* out, void* d_ws, size_t ws_bytes, const ppr_parse_opts_t* opts, void* stream);
+
+int ppr_lex_async(const uint8_t* d_bytes, uint64_t n, const ppr_lex_tables_t* tables, const ppr_lex_prepared_t* prep,
+                  const ppr_tokens_out_t* out, void* d_ws, size_t ws_bytes, const ppr_parse_opts_t* opts,
+                  void* stream);
+
+int ppr_lex_results(const void* d_ws, uint64_t n, ppr_tokens_out_t* out, void* stream);
+
+/*
+ * Build lexer tables from a token DFA [L, "A lexer is a prefix scan"]: the element
+ * of byte c maps state q to delta[q][c] when defined and otherwise restarts from
+ * q0 (delta[q0][c]), flagging that a token ended; elements compose left to
+ * right; the empty string is the identity. Host memory throughout.
+ *   delta: [n_states][256], -1 = undefined; delta[q0][*] must all be defined.
+ *   kind:  [n_states] token kind accepted in each state.
+ * First call with merge_table == NULL to get k (in *k_out); then call again with
+ * initial_state[256], merge_table[k*k], final_states[k] allocated.
+ * PPR_ECAPACITY if the closure exceeds max_k (then *k_out = max_k + 1).
+ */
+int ppr_lex_build_tables(const int16_t* delta, const uint16_t* kind, uint32_t n_states, uint32_t q0,
+                         uint32_t max_k, uint32_t* k_out, uint16_t* initial_state, uint16_t* merge_table,
+                         uint16_t* final_states, uint16_t* identity_out);
+
+/* Library version string. */
+const char* ppr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PPR_H */

@@ -1,0 +1,184 @@
+"""GPU parity: ppr_parse (HIP path, through the C ABI) against the CPU oracle.
+
+Bit-exact on every output array and scalar. Covers hand-worked and exhaustive
+short inputs, chunk sizes from 1 byte (every byte its own chunk, so the scans do
+all the work) to 64, inputs spanning several tiles with ragged tails, unaligned
+input pointers, error and capacity paths, and every delimiter-separated
+workload at its full size in the configuration the benchmark times.
+"""
+import itertools
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "csv_examples.jsonl")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def ppr():
+    import torch
+    assert torch.cuda.is_available()
+    import dfa_parsing_delimiter_amd as m
+    return m
+
+
+def _dev(b):
+    import torch
+    arr = np.frombuffer(bytes(b), dtype=np.uint8) if not isinstance(b, np.ndarray) else b
+    return torch.from_numpy(np.array(arr, dtype=np.uint8, copy=True)).to("cuda")
+
+
+def _np(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def _same(g, r, what=""):
+    assert g.n_fields == r["n_fields"], (what, g.n_fields, r["n_fields"])
+    assert g.n_records == r["n_records"], (what, g.n_records, r["n_records"])
+    assert g.error_pos == r["error_pos"], (what, g.error_pos, r["error_pos"])
+    assert g.end_state == r["end_state"], (what, g.end_state, r["end_state"])
+    for name, key in (("record_idx", "rec"), ("column_ids", "col"), ("field_offsets", "off"),
+                      ("field_lengths", "len")):
+        a = _np(getattr(g, name))
+        if not np.array_equal(a, r[key]):
+            bad = np.nonzero(a != r[key])[0]
+            raise AssertionError("%s %s differs at %d of %d (first %d: gpu %d oracle %d)" % (
+                what, name, bad.size, a.size, bad[0], a[bad[0]], r[key][bad[0]]))
+
+
+def test_golden(ppr):
+    for line in open(GOLDEN):
+        c = json.loads(line)
+        t = W.table(c["table"])
+        b = c["input"].encode("latin-1")
+        for chunk in (1, 2, 3, 32):
+            _say("golden", repr(b), chunk)
+            g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=len(b) + 1)
+            _same(g, oracle.csv_parse(b, t), (b, chunk))
+
+
+@pytest.mark.parametrize("name,alphabet,max_len", [("T5", b',\n"a', 5), ("T6", b'\t\n"#a', 4)])
+def test_exhaustive_short(ppr, name, alphabet, max_len):
+    t = W.table(name)
+    inputs = [bytes(s) for L in range(1, max_len + 1) for s in itertools.product(alphabet, repeat=L)]
+    refs = oracle.csv_parse_many(inputs, t)
+    _say("exhaustive", name, len(inputs))
+    parsers = {c: ppr.Parser(t, max_n=16, chunk_bytes=c) for c in (1, 3)}
+    for s, r in zip(inputs, refs):
+        for c, P in parsers.items():
+            _same(P(_dev(s)), r, (s, c))
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 5, 16, 31, 32, 33, 63, 64])
+def test_random_mixed_inputs_every_chunk_size(ppr, chunk):
+    rng = np.random.default_rng(chunk)
+    for name in ("T5", "T6"):
+        t = W.table(name)
+        alpha = np.frombuffer(b',\n"ab' if name == "T5" else b'\t\n"#ab', dtype=np.uint8)
+        P = ppr.Parser(t, max_n=70000, chunk_bytes=chunk)
+        for it in range(12):
+            n = int(rng.integers(0, 70000))
+            # mostly valid text with rare quotes, so that errors do not end everything early
+            p = np.array([0.08, 0.05, 0.01, 0.43, 0.43] if name == "T5" else [0.08, 0.04, 0.01, 0.01, 0.43, 0.43])
+            b = alpha[rng.choice(alpha.size, n, p=p / p.sum())]
+            _say("random", name, chunk, n)
+            _same(P(_dev(b)), oracle.csv_parse(b, t), (name, chunk, n))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+@pytest.mark.parametrize("chunk", [1, 8, 31, 32, 64])
+def test_workloads_several_tiles_ragged(ppr, cfg, chunk):
+    t = W.table(W.CONFIGS[cfg]["table"])
+    n = (3 << 20) + 12345
+    b = W.generate(cfg, n=n, seed=77 + cfg)
+    _say("workload", cfg, chunk, n)
+    g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=n + 1)
+    _same(g, oracle.csv_parse(b, t), (cfg, chunk))
+
+
+def test_unaligned_input_and_subviews(ppr):
+    import torch
+    t = W.table("T5")
+    b = W.generate(3, n=1 << 20, seed=5)
+    d = _dev(b)
+    for off in (1, 3, 7, 15):
+        _say("unaligned", off)
+        view = d[off:]
+        g = ppr.parse(view, t, capacity=b.size)
+        _same(g, oracle.csv_parse(b[off:], t), off)
+
+
+def test_edge_cases(ppr):
+    t5, t6 = W.table("T5"), W.table("T6")
+    cases = [
+        (t5, b""), (t5, b","), (t5, b"\n"), (t5, b'"'), (t5, b"x"),
+        (t5, b"," * 100000), (t5, b"\n" * 100001), (t5, b"a" * 300000),
+        (t5, b'"' + b"a,\n" * 70000),            # one quoted field left open: error at n
+        (t5, b'a"' + b"b" * 90000),              # invalid at byte 1, the rest one field
+        (t5, (b'"x""y",' * 9000) + b'"z'),
+        (t6, b"#" + b"\t\"" * 50000 + b"\n"),     # one long comment record
+        (t6, b"\t" * 70000), (t6, b"\n#\n#x\n"),
+    ]
+    for t, b in cases:
+        for chunk in (1, 7, 31, 64):
+            _say("edge", t["name"], len(b), chunk)
+            g = ppr.parse(_dev(b) if b else _dev(b"\0")[:0], t, chunk_bytes=chunk, capacity=len(b) + 2)
+            _same(g, oracle.csv_parse(b, t), (t["name"], len(b), chunk))
+
+
+def test_capacity_reported(ppr):
+    import ctypes
+    t = W.table("T5")
+    b = W.generate(1, n=1 << 18, seed=9)
+    r = oracle.csv_parse(b, t)
+    P = ppr.Parser(t, max_n=b.size, capacity=100)
+    out = P._out()
+    rc = ppr.lib.ppr_parse(ctypes.c_void_p(_dev(b).data_ptr()), b.size, ctypes.byref(P.dfa), P.class_map,
+                           ctypes.byref(out), P._ws_ptr(), P.ws_bytes, ctypes.byref(P.opts), None)
+    assert rc == ppr.PPR_ECAPACITY
+    assert out.n_fields == r["n_fields"] and out.n_records == r["n_records"]
+    first = _np(P.out_arrays[2][:100])
+    assert np.array_equal(first, r["off"][:100])
+    # the binding sizes, then fills
+    g = P(_dev(b))
+    _same(g, r, "resized")
+
+
+def test_repeatable(ppr):
+    t = W.table("T5")
+    b = W.generate(3, n=(8 << 20) + 3, seed=11)
+    r = oracle.csv_parse(b, t)
+    P = ppr.Parser(t, max_n=b.size, chunk_bytes=31)
+    d = _dev(b)
+    for i in range(5):
+        _say("repeat", i)
+        _same(P(d), r, i)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_full_size_workloads(ppr, cfg):
+    """every output array at the workload's full size, in the benchmark's launch configuration"""
+    t = W.table(W.CONFIGS[cfg]["table"])
+    chunk = W.CONFIGS[cfg].get("chunk_bytes")
+    _say("full", cfg, "generate")
+    b = W.generate(cfg)
+    _say("full", cfg, "oracle")
+    r = oracle.csv_parse(b, t)
+    _say("full", cfg, "gpu", r["n_fields"])
+    g = ppr.Parser(t, max_n=b.size, capacity=r["n_fields"], chunk_bytes=chunk)(_dev(b))
+    _same(g, r, ("full", cfg))
+    del b
