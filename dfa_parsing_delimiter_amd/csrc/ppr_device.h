@@ -100,6 +100,10 @@ __device__ __forceinline__ uint32_t status_flag(uint64_t w, uint32_t epoch)
 }
 __device__ __forceinline__ uint32_t status_payload(uint64_t w) { return (uint32_t)w; }
 
+// self-validating status word: call epoch in the high half, value in the low half
+__device__ __forceinline__ uint64_t ew(uint32_t epoch, uint32_t v) { return ((uint64_t)epoch << 32) | v; }
+__device__ __forceinline__ bool ew_ok(uint64_t w, uint32_t epoch) { return (uint32_t)(w >> 32) == epoch; }
+
 // ---------------------------------------------------------------- wave shuffles
 
 __device__ __forceinline__ uint32_t shfl_up(uint32_t v, int d) { return (uint32_t)__shfl_up((int)v, d, kWave); }

@@ -15,24 +15,24 @@ struct WsHeader {
     uint32_t end_state;
     uint64_t n_fields;  // n_tokens for the lexer
     uint64_t n_records;
-    int64_t error_pos;
+    int64_t error_pos;  // written by the host from err_min and the end state
     uint32_t fault;     // set when a look-back wait gave up (never expected)
-    uint32_t reserved;
+    uint32_t err_min;   // first INVALID byte (atomic minimum over tiles), 0xffffffff: none
 };
 
 // Upper bound on look-back polls per tile; beyond it the kernel records a fault
 // and finishes instead of waiting forever.
 constexpr uint32_t kSpinLimit = 1u << 22;
 
-// Count-carry status of one tile (second look-back): a flag word and two
-// write-once payloads, the tile's own aggregate and its inclusive prefix. They
-// must not share storage: a reader that saw the aggregate flag may read the
-// payload after the tile has gone on to publish its inclusive prefix.
+// Count-carry status of one tile (second look-back). Every word is a relaxed
+// 64-bit atomic holding the call epoch (high half) and one 32-bit value, so a
+// word is valid on its own and no release/acquire ordering between words is
+// needed (on gfx950 an agent-scope release writes back the L2 and an acquire
+// invalidates it). agg: the tile's own carry, incl: its inclusive prefix.
 struct StatB {
-    uint64_t flag;
-    uint32_t agg[6];
-    uint32_t incl[6];
-    uint32_t pad[2];
+    uint64_t agg[3];
+    uint64_t incl[4];
+    uint64_t pad;
 };
 static_assert(sizeof(StatB) == 64, "StatB layout");
 

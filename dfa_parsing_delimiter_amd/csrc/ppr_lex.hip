@@ -23,6 +23,7 @@
 #include "ppr.h"
 #include "ppr_device.h"
 #include "ppr_host.h"
+#include "ppr_scan.h"
 
 namespace ppr {
 
@@ -60,147 +61,61 @@ struct TokCarry {
     uint32_t nt, lb;
 };
 
-__device__ void block_scan_ids(const LexParams& p, uint32_t x, uint32_t& excl, uint32_t& total, uint32_t* s_wave)
-{
-    const int lane = lane_id(), w = threadIdx.x / kWave;
-    uint32_t inc = x;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        uint32_t o = shfl_up(inc, d);
-        if (lane >= d) inc = merge_ids(p, o, inc);
+struct IdComb {
+    const uint16_t* merge;
+    uint32_t k, id_mask;
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const
+    {
+        return (uint32_t)merge[(uint64_t)a * k + b] & id_mask;
     }
-    if (lane == kWave - 1) s_wave[w] = inc;
-    __syncthreads();
-    uint32_t pre = p.identity, tot = p.identity;
-#pragma unroll
-    for (int i = 0; i < kLexWaves; ++i) {
-        uint32_t a = s_wave[i];
-        if (i < w) pre = merge_ids(p, pre, a);
-        tot = merge_ids(p, tot, a);
+};
+struct TokComb {
+    __device__ TokCarry operator()(const TokCarry& a, const TokCarry& b) const
+    {
+        return {a.nt + b.nt, max(a.lb, b.lb)};
     }
-    uint32_t ex = shfl_up(inc, 1);
-    if (lane == 0) ex = p.identity;
-    excl = merge_ids(p, pre, ex);
-    total = tot;
-}
+};
 
-__device__ void block_scan_tok(TokCarry c, TokCarry& excl, TokCarry& total, TokCarry* s_wave)
-{
-    const int lane = lane_id(), w = threadIdx.x / kWave;
-    TokCarry inc = c;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        uint32_t ont = shfl_up(inc.nt, d), olb = shfl_up(inc.lb, d);
-        if (lane >= d) {
-            inc.nt += ont;
-            inc.lb = max(inc.lb, olb);
-        }
+// one tile's identifier status: aggregate = the tile's identifier, inclusive =
+// the identifier of everything through the tile
+struct IdPoll {
+    const uint64_t* statA;
+    uint32_t epoch;
+    __device__ uint32_t operator()(int64_t u, uint32_t& out) const
+    {
+        const uint64_t w = ld_relaxed(&statA[u]);
+        const uint32_t f = status_flag(w, epoch);
+        if (f) out = status_payload(w);
+        return f;
     }
-    if (lane == kWave - 1) s_wave[w] = inc;
-    __syncthreads();
-    TokCarry pre{0, 0}, tot{0, 0};
-#pragma unroll
-    for (int i = 0; i < kLexWaves; ++i) {
-        TokCarry a = s_wave[i];
-        if (i < w) {
-            pre.nt += a.nt;
-            pre.lb = max(pre.lb, a.lb);
-        }
-        tot.nt += a.nt;
-        tot.lb = max(tot.lb, a.lb);
-    }
-    uint32_t ent = shfl_up(inc.nt, 1), elb = shfl_up(inc.lb, 1);
-    if (lane == 0) ent = elb = 0;
-    excl = {pre.nt + ent, max(pre.lb, elb)};
-    total = tot;
-}
+};
 
-// Wave 0 only: identifier of all bytes before `tile` (tile > 0).
-__device__ uint32_t lookback_id(const LexParams& p, uint32_t tile)
-{
-    const int lane = lane_id();
-    uint32_t acc = p.identity;
-    int64_t base = (int64_t)tile - 1;
-    uint32_t spins = 0;
-    for (;;) {
-        const int64_t u = base - lane;
-        const bool valid = u >= 0;
-        uint64_t w = 0;
-        uint32_t f = kFlagIncl;
-        if (valid) {
-            w = ld_relaxed(&p.statA[u]);
-            f = status_flag(w, p.epoch);
+// one tile's token-count status (two self-validating words per kind)
+struct TokPoll {
+    const StatB* statB;
+    uint32_t epoch;
+    __device__ uint32_t operator()(int64_t u, TokCarry& out) const
+    {
+        const StatB& s = statB[u];
+        const uint64_t i0 = ld_relaxed(&s.incl[0]), i1 = ld_relaxed(&s.incl[1]);
+        if (ew_ok(i0, epoch) && ew_ok(i1, epoch)) {
+            out = {(uint32_t)i0, (uint32_t)i1};
+            return kFlagIncl;
         }
-        while (!__all(f != 0)) {
-            if (++spins > kSpinLimit) {
-                if (lane == 0) atomicOr(&p.hdr->fault, 1u);
-                return p.identity;
-            }
-            __builtin_amdgcn_s_sleep(1);
-            if (f == 0) {
-                w = ld_relaxed(&p.statA[u]);
-                f = status_flag(w, p.epoch);
-            }
+        const uint64_t a0 = ld_relaxed(&s.agg[0]), a1 = ld_relaxed(&s.agg[1]);
+        if (ew_ok(a0, epoch) && ew_ok(a1, epoch)) {
+            out = {(uint32_t)a0, (uint32_t)a1};
+            return kFlagAgg;
         }
-        const uint64_t incl = __ballot(valid && f == kFlagIncl);
-        const int j = incl ? __ffsll((unsigned long long)incl) - 1 : kWave;
-        uint32_t a = (valid && lane <= j) ? status_payload(w) : p.identity;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            uint32_t o = shfl_down(a, d);
-            if (lane + d < kWave) a = merge_ids(p, o, a);
-        }
-        acc = merge_ids(p, shfl(a, 0), acc);
-        if (j < kWave) return acc;
-        base -= kWave;
+        return 0;
     }
-}
-
-__device__ TokCarry lookback_tok(const LexParams& p, uint32_t tile)
-{
-    const int lane = lane_id();
-    TokCarry acc{0, 0};
-    int64_t base = (int64_t)tile - 1;
-    uint32_t spins = 0;
-    for (;;) {
-        const int64_t u = base - lane;
-        const bool valid = u >= 0;
-        uint32_t f = kFlagIncl;
-        if (valid) f = status_flag(ld_acquire(&p.statB[u].flag), p.epoch);
-        while (!__all(f != 0)) {
-            if (++spins > kSpinLimit) {
-                if (lane == 0) atomicOr(&p.hdr->fault, 2u);
-                return TokCarry{0, 0};
-            }
-            __builtin_amdgcn_s_sleep(1);
-            if (f == 0) f = status_flag(ld_acquire(&p.statB[u].flag), p.epoch);
-        }
-        const uint64_t incl = __ballot(valid && f == kFlagIncl);
-        const int j = incl ? __ffsll((unsigned long long)incl) - 1 : kWave;
-        uint32_t nt = 0, lb = 0;
-        if (valid && lane <= j) {
-            const uint32_t* v = f == kFlagIncl ? p.statB[u].incl : p.statB[u].agg;
-            nt = v[0];
-            lb = v[1];
-        }
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            nt += shfl_down(nt, d) * (lane + d < kWave ? 1u : 0u);
-            lb = max(lb, lane + d < kWave ? shfl_down(lb, d) : 0u);
-        }
-        acc.nt += shfl(nt, 0);
-        acc.lb = max(acc.lb, shfl(lb, 0));
-        if (j < kWave) return acc;
-        base -= kWave;
-    }
-}
+};
 
 __device__ __forceinline__ void publish_tok(StatB& s, TokCarry c, uint32_t epoch, uint32_t flag)
 {
-    uint32_t* v = flag == kFlagIncl ? s.incl : s.agg;
-    v[0] = c.nt;
-    v[1] = c.lb;
-    st_release(&s.flag, status_word(epoch, flag, 0));
+    uint64_t* w = flag == kFlagIncl ? s.incl : s.agg;
+    st_relaxed(&w[0], ew(epoch, c.nt));
+    st_relaxed(&w[1], ew(epoch, c.lb));
 }
 
 __global__ void lex_reset_kernel(WsHeader* hdr)
@@ -217,13 +132,14 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
     __shared__ __align__(16) uint8_t s_bytes[kLexBlock * kLexMaxChunk];
     __shared__ uint16_t s_kind[kLexBlock * kLexMaxChunk];
     __shared__ uint8_t s_col[256];
-    __shared__ uint32_t s_wid[kLexWaves];
-    __shared__ TokCarry s_wtok[kLexWaves];
+    __shared__ uint32_t s_wid[kLexWaves], s_pid[kLexWaves];
+    __shared__ TokCarry s_wtok[kLexWaves], s_ptok[kLexWaves];
+    __shared__ int s_first[kLexWaves];
     __shared__ uint32_t s_tile, s_prefix_id;
     __shared__ TokCarry s_prefix;
 
     const int tid = threadIdx.x;
-    if (tid == 0) s_tile = atomicAdd(&p.hdr->tile_counter, 1u);
+    if (tid == 0) s_tile = blockIdx.x;
     s_col[tid] = p.col[tid];
     __syncthreads();
     const uint32_t tile = s_tile;
@@ -251,8 +167,9 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
     // pass 1: fold the chunk from the identity (flags are ignored here)
     uint32_t x = p.identity;
     for (uint32_t j = 0; j < my_len; ++j) x = (uint32_t)p.fold[x * m + s_col[s_bytes[pos0 + j]]] & p.id_mask;
+    const IdComb idc{p.merge, p.k, p.id_mask};
     uint32_t excl, tot;
-    block_scan_ids(p, x, excl, tot, s_wid);
+    block_scan<kLexWaves>(x, p.identity, excl, tot, s_wid, idc);
 
     if (tile == 0) {
         if (tid == 0) {
@@ -261,12 +178,11 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
         }
     } else {
         if (tid == 0) st_relaxed(&p.statA[tile], status_word(p.epoch, kFlagAgg, tot));
-        if (tid < kWave) {
-            const uint32_t pre = lookback_id(p, tile);
-            if (tid == 0) {
-                s_prefix_id = pre;
-                st_relaxed(&p.statA[tile], status_word(p.epoch, kFlagIncl, merge_ids(p, pre, tot)));
-            }
+        const uint32_t pre = lookback<kLexWaves>(tile, p.identity, IdPoll{p.statA, p.epoch}, idc, s_pid, s_first,
+                                                 &p.hdr->fault);
+        if (tid == 0) {
+            s_prefix_id = pre;
+            st_relaxed(&p.statA[tile], status_word(p.epoch, kFlagIncl, merge_ids(p, pre, tot)));
         }
     }
     __syncthreads();
@@ -285,7 +201,7 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
     }
     TokCarry c{(uint32_t)__popcll(B), B ? chunk_abs + (uint32_t)(63 - __clzll((long long)B)) : 0u};
     TokCarry cex, ctot;
-    block_scan_tok(c, cex, ctot, s_wtok);
+    block_scan<kLexWaves>(c, TokCarry{0, 0}, cex, ctot, s_wtok, TokComb{});
 
     if (tile == 0) {
         if (tid == 0) {
@@ -294,12 +210,11 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
         }
     } else {
         if (tid == 0) publish_tok(p.statB[tile], ctot, p.epoch, kFlagAgg);
-        if (tid < kWave) {
-            TokCarry pre = lookback_tok(p, tile);
-            if (tid == 0) {
-                s_prefix = pre;
-                publish_tok(p.statB[tile], TokCarry{pre.nt + ctot.nt, max(pre.lb, ctot.lb)}, p.epoch, kFlagIncl);
-            }
+        const TokCarry pre = lookback<kLexWaves>(tile, TokCarry{0, 0}, TokPoll{p.statB, p.epoch}, TokComb{}, s_ptok,
+                                                 s_first, &p.hdr->fault);
+        if (tid == 0) {
+            s_prefix = pre;
+            publish_tok(p.statB[tile], TokCarry{pre.nt + ctot.nt, max(pre.lb, ctot.lb)}, p.epoch, kFlagIncl);
         }
     }
     __syncthreads();

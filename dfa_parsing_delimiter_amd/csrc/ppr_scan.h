@@ -1,0 +1,161 @@
+// Wave/workgroup scans and the device-wide decoupled look-back, generic over the
+// carried value (state-transition vectors, count carries, lexer identifiers).
+//
+// ParPaRaw (Sec. 3) computes the chunks' start states and offsets with
+// exclusive scans over associative operators; here every such scan is a
+// single-pass scan: each workgroup scans its own threads, publishes its tile
+// aggregate, then finds its tile's exclusive prefix by looking back over its
+// predecessors' published statuses (aggregate or inclusive prefix).
+//
+// gfx950 specifics:
+//   * wave scans use DPP lane moves (row_shr within rows of 16 lanes, then
+//     row_bcast:15 and row_bcast:31 across rows) fused into the VALU, not LDS
+//     shuffles; the exclusive shift is wave_shr:1;
+//   * every wave of the workgroup takes part in a look-back round, so one round
+//     (one trip to memory and back, about a microsecond across XCDs) covers
+//     64 x waves predecessors, and a wave only waits for the statuses it needs
+//     (those between the nearest inclusive prefix and the tile);
+//   * statuses are relaxed agent-scope atomics (coherent across XCDs) whose
+//     words carry the call epoch, so no release/acquire fences (L2 writeback and
+//     invalidate on this target) are needed.
+#pragma once
+
+#include "ppr_device.h"
+#include "ppr_host.h"
+
+namespace ppr {
+
+template <int CTRL, int ROW_MASK, typename T>
+__device__ __forceinline__ T dpp_t(const T& old, const T& src)
+{
+    static_assert(sizeof(T) % 4 == 0, "32-bit words");
+    constexpr int N = sizeof(T) / 4;
+    uint32_t o[N], s[N], r[N];
+    __builtin_memcpy(o, &old, sizeof(T));
+    __builtin_memcpy(s, &src, sizeof(T));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        r[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)o[i], (int)s[i], CTRL, ROW_MASK, 0xf, false);
+    T out;
+    __builtin_memcpy(&out, r, sizeof(T));
+    return out;
+}
+
+template <typename T>
+__device__ __forceinline__ T readlane_t(const T& v, int lane)
+{
+    constexpr int N = sizeof(T) / 4;
+    uint32_t s[N], r[N];
+    __builtin_memcpy(s, &v, sizeof(T));
+#pragma unroll
+    for (int i = 0; i < N; ++i) r[i] = (uint32_t)__builtin_amdgcn_readlane((int)s[i], lane);
+    T out;
+    __builtin_memcpy(&out, r, sizeof(T));
+    return out;
+}
+
+// inclusive scan over the 64 lanes of a wave in lane order (comb(a, b): a earlier)
+template <typename T, typename Comb>
+__device__ __forceinline__ T wave_scan(T x, const T& id, const Comb& comb)
+{
+    x = comb(dpp_t<0x111, 0xf>(id, x), x);  // row_shr:1
+    x = comb(dpp_t<0x112, 0xf>(id, x), x);  // row_shr:2
+    x = comb(dpp_t<0x114, 0xf>(id, x), x);  // row_shr:4
+    x = comb(dpp_t<0x118, 0xf>(id, x), x);  // row_shr:8
+    x = comb(dpp_t<0x142, 0xa>(id, x), x);  // row_bcast:15 into rows 1 and 3
+    x = comb(dpp_t<0x143, 0xc>(id, x), x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// value of the previous lane (lane 0: id)
+template <typename T>
+__device__ __forceinline__ T wave_shr1(const T& id, const T& x)
+{
+    return dpp_t<0x138, 0xf>(id, x);
+}
+
+// Exclusive scan over the workgroup in thread order (comb(a, b): a earlier).
+// `total` is the combination of all threads. Uses s_wave[NW]; the caller
+// synchronises before reusing it.
+template <int NW, typename T, typename Comb>
+__device__ void block_scan(const T& v, const T& ident, T& excl, T& total, T* s_wave, const Comb& comb)
+{
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    const T inc = wave_scan(v, ident, comb);
+    if (lane == kWave - 1) s_wave[w] = inc;
+    __syncthreads();
+    T pre = ident, tot = ident;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const T a = s_wave[i];
+        if (i < w) pre = comb(pre, a);
+        tot = comb(tot, a);
+    }
+    excl = comb(pre, wave_shr1(ident, inc));
+    total = tot;
+}
+
+// Decoupled look-back; every thread of the workgroup calls it, tile > 0.
+// poll(u, out) returns kFlagIncl (out = inclusive prefix through tile u),
+// kFlagAgg (out = tile u's aggregate) or 0 (not yet published). Returns the
+// combination of all tiles before `tile`. Lane 63 of wave 0 reads the nearest
+// predecessor. Gives up after kSpinLimit polls per wave, recording a fault, so
+// the kernel always finishes.
+template <int NW, typename T, typename Poll, typename Comb>
+__device__ T lookback(uint32_t tile, const T& ident, const Poll& poll, const Comb& comb, T* s_part, int* s_found,
+                      uint32_t* fault)
+{
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    T acc = ident;
+    int64_t base = (int64_t)tile - 1;
+    uint32_t spins = 0;
+    for (;;) {
+        const int64_t u = base - (int64_t)(w * kWave + (kWave - 1 - lane));
+        const bool valid = u >= 0;
+        T v = ident;
+        uint32_t f = 0;
+        if (valid) f = poll(u, v);
+        const uint64_t vmask = __ballot(valid);
+        for (;;) {
+            const uint64_t ready = __ballot(f != 0);
+            const uint64_t inclm = __ballot(f == kFlagIncl);
+            // statuses needed: from the nearest inclusive prefix up to the tile
+            const uint64_t need = inclm ? vmask & (~0ull << (63 - __clzll((long long)inclm))) : vmask;
+            if ((ready & need) == need) break;
+            if (++spins > kSpinLimit) {
+                if (lane == 0) atomicOr(fault, 1u);
+                if (valid && f == 0) {
+                    f = kFlagAgg;
+                    v = ident;
+                }
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            if (valid && f == 0) f = poll(u, v);
+        }
+        const uint64_t inclm = __ballot(f == kFlagIncl);
+        const int j = inclm ? 63 - __clzll((long long)inclm) : -1;
+        if (!(valid && lane >= j)) v = ident;
+        const T part = readlane_t(wave_scan(v, ident, comb), kWave - 1);
+        if (lane == 0) {
+            s_part[w] = part;
+            s_found[w] = j >= 0;
+        }
+        __syncthreads();
+        // wave i covers tiles base-64i-63 .. base-64i; the nearest wave holding an
+        // inclusive prefix ends the walk, and farther waves are not needed
+        int wi = NW;
+#pragma unroll
+        for (int i = NW - 1; i >= 0; --i)
+            if (s_found[i]) wi = i;
+        const int last = wi < NW ? wi : NW - 1;
+        T r = s_part[last];
+        for (int i = last - 1; i >= 0; --i) r = comb(r, s_part[i]);
+        acc = comb(r, acc);
+        __syncthreads();
+        if (wi < NW) return acc;
+        base -= (int64_t)NW * kWave;
+    }
+}
+
+}  // namespace ppr

@@ -64,7 +64,7 @@ def test_golden(ppr):
         c = json.loads(line)
         t = W.table(c["table"])
         b = c["input"].encode("latin-1")
-        for chunk in (1, 2, 3, 32):
+        for chunk in (1, 2, 3, 32, 64):
             _say("golden", repr(b), chunk)
             g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=len(b) + 1)
             _same(g, oracle.csv_parse(b, t), (b, chunk))
@@ -76,7 +76,7 @@ def test_exhaustive_short(ppr, name, alphabet, max_len):
     inputs = [bytes(s) for L in range(1, max_len + 1) for s in itertools.product(alphabet, repeat=L)]
     refs = oracle.csv_parse_many(inputs, t)
     _say("exhaustive", name, len(inputs))
-    parsers = {c: ppr.Parser(t, max_n=16, chunk_bytes=c) for c in (1, 3)}
+    parsers = {c: ppr.Parser(t, max_n=16, chunk_bytes=c) for c in (1, 3, 64)}
     for s, r in zip(inputs, refs):
         for c, P in parsers.items():
             _same(P(_dev(s)), r, (s, c))
@@ -107,6 +107,49 @@ def test_workloads_several_tiles_ragged(ppr, cfg, chunk):
     _say("workload", cfg, chunk, n)
     g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=n + 1)
     _same(g, oracle.csv_parse(b, t), (cfg, chunk))
+
+
+def _random_table(rng, absorbing, n_special):
+    S = int(rng.integers(1, 9))
+    C = int(rng.integers(1, 17))
+    nxt = rng.integers(0, S, (S, C)).tolist()
+    tag = rng.integers(0, 4, (S, C)).tolist()
+    # mostly value/terminator tags so that inputs stay valid for a while
+    for s_ in range(S):
+        for c in range(C):
+            if tag[s_][c] == 3 and rng.random() < 0.8:
+                tag[s_][c] = int(rng.integers(0, 3))
+    if absorbing and S > 1:
+        a = int(rng.integers(0, S))
+        nxt[a] = [a] * C
+        tag[a] = [3] * C
+    K = int(rng.integers(0, C))
+    cm = bytearray([K] * 256)
+    others = [c for c in range(C) if c != K]
+    if others:
+        for b in rng.choice(256, size=min(n_special, 256), replace=False):
+            cm[int(b)] = int(rng.choice(others))
+    return {"name": "rand", "n_states": S, "n_classes": C, "next": nxt, "tag": tag, "start": int(rng.integers(0, S)),
+            "accept_mask": int(rng.integers(0, 1 << S)), "class_map": bytes(cm)}
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_tables(ppr, seed):
+    """random DFAs: every fast-path variant (symbol code widths 2/3/4, 4- and 8-entry
+    vectors, with and without an absorbing state) and the generic fallback (many
+    special bytes), against the oracle"""
+    rng = np.random.default_rng(1000 + seed)
+    for trial in range(6):
+        t = _random_table(rng, absorbing=bool(trial % 2), n_special=int(rng.choice([1, 3, 8, 8, 20])))
+        specials = [b for b in range(256) if t["class_map"][b] != max(set(t["class_map"]), key=t["class_map"].count)]
+        pool = np.array(specials + [ord("a"), ord("b"), ord("z")], dtype=np.uint8)
+        for n in (1, 63, 64, 65, 16384, 16385, 100000):
+            b = pool[rng.integers(0, pool.size, n)]
+            r = oracle.csv_parse(b, t)
+            for chunk in (64, 13):
+                _say("table", seed, trial, t["n_states"], t["n_classes"], len(specials), n, chunk)
+                g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=n + 1)
+                _same(g, r, (seed, trial, n, chunk))
 
 
 def test_unaligned_input_and_subviews(ppr):
