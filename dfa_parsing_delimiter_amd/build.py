@@ -21,6 +21,7 @@ FLAGS = [
     "-fPIC",
     "-shared",
     "-Wall",
+    "-fvisibility=hidden",
     # no packed fp32 instructions in any generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

@@ -18,6 +18,8 @@ struct WsHeader {
     int64_t error_pos;  // written by the host from err_min and the end state
     uint32_t fault;     // set when a look-back wait gave up (never expected)
     uint32_t err_min;   // first INVALID byte (atomic minimum over tiles), 0xffffffff: none
+    uint32_t last_rec;  // the input's last byte is a record delimiter (multi-kernel parse)
+    uint32_t reserved;
 };
 
 // Upper bound on look-back polls per tile; beyond it the kernel records a fault

@@ -74,25 +74,75 @@ __device__ __forceinline__ T wave_shr1(const T& id, const T& x)
     return dpp_t<0x138, 0xf>(id, x);
 }
 
+// inclusive scan over lanes 0..N-1 of each row of 16 (N <= 16)
+template <int N, typename T, typename Comb>
+__device__ __forceinline__ T row_scan(T x, const T& id, const Comb& comb)
+{
+    static_assert(N <= 16, "one row");
+    if constexpr (N > 1) x = comb(dpp_t<0x111, 0xf>(id, x), x);
+    if constexpr (N > 2) x = comb(dpp_t<0x112, 0xf>(id, x), x);
+    if constexpr (N > 4) x = comb(dpp_t<0x114, 0xf>(id, x), x);
+    if constexpr (N > 8) x = comb(dpp_t<0x118, 0xf>(id, x), x);
+    return x;
+}
+
+// cond ? a : b, word by word (a conditional between two objects can otherwise
+// become a select between their addresses, in different address spaces)
+template <typename T>
+__device__ __forceinline__ T select_t(bool cond, const T& a, const T& b)
+{
+    constexpr int N = sizeof(T) / 4;
+    uint32_t x[N], y[N];
+    __builtin_memcpy(x, &a, sizeof(T));
+    __builtin_memcpy(y, &b, sizeof(T));
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = cond ? x[i] : y[i];
+    T out;
+    __builtin_memcpy(&out, x, sizeof(T));
+    return out;
+}
+
+// s_wave[lane] in lanes 0..NW-1, id elsewhere. The load is unconditional (a
+// clamped index) and the choice is made per word, so that no pointer select
+// between LDS and a private copy of id appears.
+template <int NW, typename T>
+__device__ __forceinline__ T lane_value(const T* s_wave, const T& id)
+{
+    const int lane = lane_id();
+    const T v = s_wave[lane < NW ? lane : NW - 1];
+    return select_t(lane < NW, v, id);
+}
+
 // Exclusive scan over the workgroup in thread order (comb(a, b): a earlier).
-// `total` is the combination of all threads. Uses s_wave[NW]; the caller
+// `total` is the combination of all threads. The wave totals go through LDS and
+// are scanned by the first NW lanes of every wave. Uses s_wave[NW]; the caller
 // synchronises before reusing it.
 template <int NW, typename T, typename Comb>
 __device__ void block_scan(const T& v, const T& ident, T& excl, T& total, T* s_wave, const Comb& comb)
+{
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const T inc = wave_scan(v, ident, comb);
+    if (lane == kWave - 1) s_wave[w] = inc;
+    __syncthreads();
+    const T ws = row_scan<NW>(lane_value<NW>(s_wave, ident), ident, comb);
+    T pre = ident;
+    if (w) pre = readlane_t(ws, w - 1);
+    total = readlane_t(ws, NW - 1);
+    excl = comb(pre, wave_shr1(ident, inc));
+}
+
+// Combination of the values of all threads of the workgroup in thread order,
+// returned to every thread. Uses s_wave[NW]; the caller synchronises before
+// reusing it.
+template <int NW, typename T, typename Comb>
+__device__ T block_reduce(const T& v, const T& ident, T* s_wave, const Comb& comb)
 {
     const int lane = lane_id(), w = threadIdx.x / kWave;
     const T inc = wave_scan(v, ident, comb);
     if (lane == kWave - 1) s_wave[w] = inc;
     __syncthreads();
-    T pre = ident, tot = ident;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        const T a = s_wave[i];
-        if (i < w) pre = comb(pre, a);
-        tot = comb(tot, a);
-    }
-    excl = comb(pre, wave_shr1(ident, inc));
-    total = tot;
+    return readlane_t(row_scan<NW>(lane_value<NW>(s_wave, ident), ident, comb), NW - 1);
 }
 
 // Decoupled look-back; every thread of the workgroup calls it, tile > 0.

@@ -39,6 +39,9 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden visibility; only these entry points are exported. */
+#define PPR_API __attribute__((visibility("default")))
+
 #define PPR_MAX_STATES 8
 #define PPR_MAX_CLASSES 16
 
@@ -108,7 +111,7 @@ typedef struct ppr_parse_opts {
  * The workspace must be 256-byte aligned and zero-filled before its first use
  * (afterwards the library keeps it consistent); 0 on invalid arguments.
  */
-size_t ppr_parse_workspace_bytes(uint64_t n, const ppr_parse_opts_t* opts);
+PPR_API size_t ppr_parse_workspace_bytes(uint64_t n, const ppr_parse_opts_t* opts);
 
 /*
  * Parse n bytes at d_bytes with the DFA and the 256-entry class map (host
@@ -117,16 +120,16 @@ size_t ppr_parse_workspace_bytes(uint64_t n, const ppr_parse_opts_t* opts);
  * Blocking: returns with out->n_fields, n_records, error_pos, end_state set.
  * Returns PPR_ECAPACITY (with the counts set) if n_fields > cap_fields.
  */
-int ppr_parse(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, const uint8_t class_map[256],
+PPR_API int ppr_parse(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, const uint8_t class_map[256],
               ppr_parse_out_t* out, void* d_ws, size_t ws_bytes, const ppr_parse_opts_t* opts, void* stream);
 
 /* Enqueue the same work without waiting; ppr_parse_results completes it. */
-int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, const uint8_t class_map[256],
+PPR_API int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, const uint8_t class_map[256],
                     const ppr_parse_out_t* out, void* d_ws, size_t ws_bytes, const ppr_parse_opts_t* opts,
                     void* stream);
 
 /* Wait on `stream` and copy the scalars of the last ppr_parse_async on d_ws into out. */
-int ppr_parse_results(const void* d_ws, uint64_t n, ppr_parse_out_t* out, void* stream);
+PPR_API int ppr_parse_results(const void* d_ws, uint64_t n, ppr_parse_out_t* out, void* stream);
 
 /* ------------------------------------------------------------------ lexer */
 
@@ -166,10 +169,10 @@ typedef struct ppr_lex_prepared {
 } ppr_lex_prepared_t;
 
 /* Device bytes the prepared fold table needs (k * 256 * 2 at most). */
-size_t ppr_lex_fold_bytes(uint32_t k);
+PPR_API size_t ppr_lex_fold_bytes(uint32_t k);
 
 /* Build the prepared tables (reads initial_state back; blocking). */
-int ppr_lex_prepare(const ppr_lex_tables_t* tables, ppr_lex_prepared_t* prep, void* stream);
+PPR_API int ppr_lex_prepare(const ppr_lex_tables_t* tables, ppr_lex_prepared_t* prep, void* stream);
 
 /*
  * Token output, one entry per token in input order: kind = final_states of the
@@ -185,17 +188,17 @@ typedef struct ppr_tokens_out {
     uint64_t n_tokens; /* out */
 } ppr_tokens_out_t;
 
-size_t ppr_lex_workspace_bytes(uint64_t n, const ppr_parse_opts_t* opts);
+PPR_API size_t ppr_lex_workspace_bytes(uint64_t n, const ppr_parse_opts_t* opts);
 
 /* Lex n bytes (n < 2^32 - 1). Blocking. PPR_ECAPACITY if n_tokens > cap_tokens. */
-int ppr_lex(const uint8_t* d_bytes, uint64_t n, const ppr_lex_tables_t* tables, const ppr_lex_prepared_t* prep,
+PPR_API int ppr_lex(const uint8_t* d_bytes, uint64_t n, const ppr_lex_tables_t* tables, const ppr_lex_prepared_t* prep,
             ppr_tokens_out_t* out, void* d_ws, size_t ws_bytes, const ppr_parse_opts_t* opts, void* stream);
 
-int ppr_lex_async(const uint8_t* d_bytes, uint64_t n, const ppr_lex_tables_t* tables, const ppr_lex_prepared_t* prep,
+PPR_API int ppr_lex_async(const uint8_t* d_bytes, uint64_t n, const ppr_lex_tables_t* tables, const ppr_lex_prepared_t* prep,
                   const ppr_tokens_out_t* out, void* d_ws, size_t ws_bytes, const ppr_parse_opts_t* opts,
                   void* stream);
 
-int ppr_lex_results(const void* d_ws, uint64_t n, ppr_tokens_out_t* out, void* stream);
+PPR_API int ppr_lex_results(const void* d_ws, uint64_t n, ppr_tokens_out_t* out, void* stream);
 
 /*
  * Build lexer tables from a token DFA [L, "A lexer is a prefix scan"]: the element
@@ -208,12 +211,12 @@ int ppr_lex_results(const void* d_ws, uint64_t n, ppr_tokens_out_t* out, void* s
  * initial_state[256], merge_table[k*k], final_states[k] allocated.
  * PPR_ECAPACITY if the closure exceeds max_k (then *k_out = max_k + 1).
  */
-int ppr_lex_build_tables(const int16_t* delta, const uint16_t* kind, uint32_t n_states, uint32_t q0,
+PPR_API int ppr_lex_build_tables(const int16_t* delta, const uint16_t* kind, uint32_t n_states, uint32_t q0,
                          uint32_t max_k, uint32_t* k_out, uint16_t* initial_state, uint16_t* merge_table,
                          uint16_t* final_states, uint16_t* identity_out);
 
 /* Library version string. */
-const char* ppr_version(void);
+PPR_API const char* ppr_version(void);
 
 #ifdef __cplusplus
 }
