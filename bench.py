@@ -3,17 +3,28 @@
 
 Default workload: the quote-heavy CSV, 1 GiB, 12 columns, 60% quoted fields
 with doubled quotes and embedded newlines, geometric field lengths (mean 40 B,
-max 4 KiB), parsed with the five-state RFC 4180 DFA. One step is one ppr_parse
-call over the whole input (every step of the path: per-chunk multi-DFA,
-composite scan, re-simulation and tagging, offset scans, field emission), with
-the input already resident in HBM and output buffers preallocated.
+max 4 KiB), parsed with the five-state RFC 4180 DFA. One step is one blocking
+ppr_parse call over the whole input (every step of the path: per-chunk
+multi-DFA, composite scan, re-simulation and tagging, offset scans, field
+emission, scalar read-back), with the input already resident in HBM and the
+output buffers preallocated.
 
-    python bench.py [--steps K] [--warmup W] [--workload csv3|csv1|csv2|csv4|lex5]
+    python bench.py [--steps K] [--warmup W] [--workload csv3|csv1|csv2|csv4|lex5] [--chunk L]
 
-Prints one JSON line.
+Prints one JSON line. Two more modes serve the counter-based traffic figure:
+
+    rocprofv3 --pmc FETCH_SIZE -d DIR1 -o run --output-format csv -- python bench.py --copy-calibration ...
+    rocprofv3 --pmc WRITE_SIZE -d DIR2 -o run --output-format csv -- python bench.py --copy-calibration ...
+    python bench.py --summarize-pmc DIR1 DIR2 [--workload ...]
+
+--copy-calibration also times a plain 1 GiB device-to-device copy after the
+parse, so that each counter can be scaled by what it reads for a copy of known
+size; --summarize-pmc writes profiles/hbm_counters_<workload>_chunk<L>.json.
 """
 import argparse
 import concurrent.futures as cf
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -27,43 +38,53 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 METRIC = "input GB/s parsed end-to-end (1 GiB CSV) and % of MI355X HBM peak"
 WORKLOADS = {"csv1": 1, "csv2": 2, "csv3": 3, "csv4": 4, "lex5": 5}
-KERNEL_SRC = {"csv": "dfa_parsing_delimiter_amd/csrc/ppr_csv.hip", "lex": "dfa_parsing_delimiter_amd/csrc/ppr_lex.hip"}
-KERNEL_NAME = {"csv": "csv_parse_kernel", "lex": "lex_kernel"}
+COPY_BYTES = 1 << 30
+# kernels of each path, in launch order (the library records an event before
+# the first and after each one)
+STAGES = {1: ["csv_fast_tables_kernel", "csv_codes_kernel", "csv_carries_kernel", "csv_emit_kernel"],
+          2: ["csv_reset_kernel", "csv_generic_kernel"],
+          "lex": ["lex_reset_kernel", "lex_kernel"]}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def src_sha(kind):
+def source_sha():
+    """hash of every kernel source file: counter summaries taken on other sources are stale"""
     h = hashlib.sha256()
-    for p in (KERNEL_SRC[kind], "dfa_parsing_delimiter_amd/csrc/ppr_device.h", "dfa_parsing_delimiter_amd/csrc/ppr_host.h"):
-        h.update(open(os.path.join(ROOT, p), "rb").read())
+    for p in sorted(glob.glob(os.path.join(ROOT, "dfa_parsing_delimiter_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kind, workload, chunk):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
-    were taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", "counters_%s_%s_c%d.json" % (KERNEL_NAME[kind], workload, chunk))
-    if not os.path.exists(path):
-        return None
-    c = json.load(open(path))
-    if c.get("source_sha") != src_sha(kind):
-        return None
-    return c.get("hbm_bytes_per_launch")
+def counters_path(workload, chunk):
+    return os.path.join(ROOT, "profiles", "hbm_counters_%s_chunk%d.json" % (workload, chunk))
 
 
-def cpu_oracle_baseline(kind, data, table_or_dfa, max_seconds=30.0):
+def algorithmic_bytes(stage, n, n_out, out_bytes_per_item):
+    """The bytes the method itself must move, attributed to the kernel that moves
+    them: the input read once (by the first kernel that reads it), the outputs
+    written once (by the kernel that writes them). Intermediates are not counted."""
+    if stage in ("csv_codes_kernel",):
+        return n
+    if stage in ("csv_emit_kernel",):
+        return out_bytes_per_item * n_out
+    if stage in ("csv_generic_kernel", "lex_kernel"):
+        return n + out_bytes_per_item * n_out
+    return 0
+
+
+def cpu_oracle_baseline(kind, data, spec, max_seconds=30.0):
     """The oracle as it stands, on the host: one thread over the whole input
     (median of up to 3 runs within the time bound), and all host threads (at
     most 16) each parsing its own contiguous slice as an independent input."""
     import oracle
     runs, res = [], None
     t_end = time.time() + max_seconds
-    for i in range(3):
+    for _ in range(3):
         t0 = time.perf_counter()
-        res = oracle.csv_parse(data, table_or_dfa) if kind == "csv" else oracle.lex_restart(data, table_or_dfa)
+        res = oracle.csv_parse(data, spec) if kind == "csv" else oracle.lex_restart(data, spec)
         runs.append(time.perf_counter() - t0)
         if time.time() + runs[-1] > t_end:
             break
@@ -73,9 +94,9 @@ def cpu_oracle_baseline(kind, data, table_or_dfa, max_seconds=30.0):
 
     def one(s):
         if kind == "csv":
-            oracle.csv_parse(s, table_or_dfa)
+            oracle.csv_parse(s, spec)
         else:
-            oracle.lex_restart(s, table_or_dfa)
+            oracle.lex_restart(s, spec)
 
     with cf.ThreadPoolExecutor(cores) as ex:
         t0 = time.perf_counter()
@@ -85,7 +106,89 @@ def cpu_oracle_baseline(kind, data, table_or_dfa, max_seconds=30.0):
                  "sample": "the whole %d-byte input, sequential C oracle (gcc -O2), median of %d run(s)" % (
                      data.size, len(runs))}, {
         "value": round(data.size / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-        "sample": "the same input cut into %d contiguous slices parsed as independent inputs, one thread each" % cores}
+        "sample": "the same input cut into %d contiguous slices parsed as independent inputs, one thread each"
+                  % cores}
+
+
+def read_pmc(d, counter):
+    """counter value of every dispatch, by kernel name, from a rocprofv3 csv output directory"""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under " + d)
+    per_dispatch = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
+            per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    by_kernel = {}
+    for (name, _), v in per_dispatch.items():
+        by_kernel.setdefault(name, []).append(v)
+    return by_kernel
+
+
+def short_name(kernel_name):
+    for names in STAGES.values():
+        for s in names:
+            if s + "<" in kernel_name or s + "(" in kernel_name:
+                return s
+    return None
+
+
+def summarize_pmc(args, chunk):
+    fetch = read_pmc(args.summarize_pmc[0], "FETCH_SIZE")
+    write = read_pmc(args.summarize_pmc[1], "WRITE_SIZE")
+
+    def copies(by_kernel):  # the largest single dispatch of a copy kernel: the 1 GiB calibration copy
+        v = [x for k, xs in by_kernel.items() if "ppr" not in k and "copy" in k.lower() for x in xs]
+        return max(v) if v else None
+
+    copy_f, copy_w = copies(fetch), copies(write)
+    if not copy_f or not copy_w:
+        raise SystemExit("no copy kernel in the counter output (run the parse with --copy-calibration)")
+    fetch = {k: statistics.median(v) for k, v in fetch.items()}
+    write = {k: statistics.median(v) for k, v in write.items()}
+    # the copy kernel moves COPY_BYTES in each direction; the counters read in KiB
+    f_scale = COPY_BYTES / (copy_f * 1024.0)
+    w_scale = COPY_BYTES / (copy_w * 1024.0)
+    kernels = {}
+    for k in set(fetch) | set(write):
+        s = short_name(k)
+        if s is None:
+            continue
+        fb = fetch.get(k, 0.0) * 1024.0 * f_scale
+        wb = write.get(k, 0.0) * 1024.0 * w_scale
+        kernels[s] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "hbm_bytes": round(fb + wb),
+                      "fetch_kib_raw": round(fetch.get(k, 0.0), 1), "write_kib_raw": round(write.get(k, 0.0), 1)}
+    out = {"workload": args.workload, "chunk_bytes": chunk, "source_sha": source_sha(),
+           "copy_calibration": {"bytes_each_way": COPY_BYTES, "fetch_kib_raw": round(copy_f, 1),
+                                "write_kib_raw": round(copy_w, 1), "fetch_scale": round(f_scale, 4),
+                                "write_scale": round(w_scale, 4)},
+           "kernels": kernels,
+           "commands": ["rocprofv3 --pmc %s -d %s -o run --output-format csv -- python bench.py --workload %s "
+                        "--chunk %d --no-cpu --steps 3 --warmup 1 --copy-calibration" % (c, d, args.workload, chunk)
+                        for c, d in zip(("FETCH_SIZE", "WRITE_SIZE"), args.summarize_pmc)]
+                       + ["python bench.py --workload %s --chunk %d --summarize-pmc %s %s" % (
+                           args.workload, chunk, *args.summarize_pmc)]}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    path = counters_path(args.workload, chunk)
+    json.dump(out, open(path, "w"), indent=1, sort_keys=True)
+    print(json.dumps(out))
+    log("wrote", path)
+
+
+def measured_traffic(workload, chunk, stage):
+    """HBM bytes per launch of one kernel from the committed counter summary,
+    if it was taken on the current kernel sources (else None)."""
+    path = counters_path(workload, chunk)
+    if not os.path.exists(path):
+        return None
+    c = json.load(open(path))
+    if c.get("source_sha") != source_sha():
+        return None
+    k = c.get("kernels", {}).get(stage)
+    return None if k is None else k["hbm_bytes"]
 
 
 def main():
@@ -94,13 +197,21 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="csv3", choices=sorted(WORKLOADS))
-    ap.add_argument("--chunk", type=int, default=None, help="bytes per thread (default: the workload's, else 32)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline and the parity check")
+    ap.add_argument("--chunk", type=int, default=None, help="bytes per thread (default: the library's, 64)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline and the full-size parity check")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/hbm_counters_<workload>_chunk<L>.json from two rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+    chunk = args.chunk or 64
+    if args.summarize_pmc:
+        summarize_pmc(args, chunk)
+        return
 
     import numpy as np
     import torch
@@ -111,7 +222,6 @@ def main():
     cfg_id = WORKLOADS[args.workload]
     cfg = W.CONFIGS[cfg_id]
     kind = "csv" if cfg["kind"] == "csv" else "lex"
-    chunk = args.chunk or cfg.get("chunk_bytes") or 32
     dev = torch.device("cuda:0")
     log("generating", cfg["name"], cfg["n"], "bytes")
     t0 = time.time()
@@ -126,42 +236,67 @@ def main():
         runner = ppr.Parser(table, max_n=n, capacity=max(4096, n // 8), chunk_bytes=chunk, device=dev)
         first = runner(d)
         runner._alloc(first.n_fields)
-        n_out = first.n_fields
+        n_out, path = first.n_fields, first.path
+        stages = STAGES[path]
         out_bytes_per_item = 16
         spec = table
     else:
         dfa = W.lexer_dfa()
         tabs = ppr.LexTables.from_dfa(dfa, dev)
-        runner = ppr.Lexer(tabs, max_n=n, capacity=max(4096, n // 3), chunk_bytes=chunk)
+        runner = ppr.Lexer(tabs, max_n=n, capacity=max(4096, n // 3), chunk_bytes=args.chunk)
         first = runner(d)
         runner._alloc(first.n_tokens)
-        n_out = first.n_tokens
+        n_out, path = first.n_tokens, None
+        stages = STAGES["lex"]
         out_bytes_per_item = 12
         spec = dfa
-    log("first call:", n_out, "items")
+    log("first call: %d items, kernels %s" % (n_out, stages))
+    stream = torch.cuda.current_stream()
+
+    def step():  # one blocking call: enqueue every kernel, read the scalars back
+        runner.launch(d)
+        return runner.results(n)
 
     for _ in range(args.warmup):
-        runner.launch(d)
+        step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
+
+    # (1) the metric: K blocking calls, timed on the stream
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_wall = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        runner.launch(d)
+        o = step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms = ev0.elapsed_time(ev1) / args.steps
-    o = runner.results(n)
     got = int(o.n_fields if kind == "csv" else o.n_tokens)
     assert got == n_out, (got, n_out)
 
+    # (2) per-kernel durations: K back-to-back calls with the library recording
+    # an event before, between and after its kernels on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record(stream)  # creates the events
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for row in evs:
+        runner.launch(d, stage_events=row)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_pipelined = e0.elapsed_time(e1) / args.steps
+    stage_ms = {s: statistics.mean(row[i].elapsed_time(row[i + 1]) for row in evs) for i, s in enumerate(stages)}
+    dominant = max(stage_ms, key=stage_ms.get)
+    t_dom = stage_ms[dominant] * 1e-3
+
     gbs = n / (ms * 1e-3) / 1e9
-    alg_bytes = n + out_bytes_per_item * n_out
-    achieved = alg_bytes / (ms * 1e-3) / 1e9
-    traffic = measured_traffic(kind, args.workload, chunk)
+    alg_dom = algorithmic_bytes(dominant, n, n_out, out_bytes_per_item)
+    alg_step = n + out_bytes_per_item * n_out
+    traffic = measured_traffic(args.workload, chunk, dominant) if kind == "csv" else None
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -178,20 +313,42 @@ def main():
         "pct_of_hbm_peak_input": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "config": {"workload": "%s_%dMiB" % (cfg["name"], n >> 20), "n_bytes": n, "chunk_bytes": chunk,
                    "table": cfg.get("table", "lexer_40_rules"), "items": n_out, "seed": W.seed_of(cfg_id),
-                   "input_sha256": sha[:16]},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if traffic is None else round(traffic / (ms * 1e-3) / 1e9, 2),
-                     "kernel": KERNEL_NAME[kind], "algorithmic_bytes_per_launch": alg_bytes,
-                     "timing": "HIP events on the launch stream over %d back-to-back calls; wall %.3fs" % (
-                         args.steps, wall)},
+                   "input_sha256": sha[:16], "kernels": stages},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(alg_dom / t_dom / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(alg_dom / t_dom / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic / t_dom / 1e9, 2),
+                     "traffic_bytes_per_launch": traffic,
+                     "algorithmic_bytes_per_launch": alg_dom, "kernel_ms": round(stage_ms[dominant], 4),
+                     "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+                     "step": {"algorithmic_bytes": alg_step,
+                              "achieved": round(alg_step / (ms * 1e-3) / 1e9, 2),
+                              "frac": round(alg_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                     "ms_per_step_pipelined": round(ms_pipelined, 4),
+                     "timing": "HIP events on the launch stream: %d blocking calls (wall %.3fs); per-kernel events "
+                               "recorded by the library over %d pipelined calls" % (args.steps, wall, args.steps)},
     }
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(5):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cms = c0.elapsed_time(c1) / 5
+        line["copy_calibration"] = {"bytes_each_way": COPY_BYTES, "ms": round(cms, 4),
+                                    "GBps_read_plus_write": round(2 * COPY_BYTES / (cms * 1e-3) / 1e9, 1)}
+        del src, dst
     if not args.no_cpu:
         log("cpu oracle baseline")
         ref, single, allcore = cpu_oracle_baseline(kind, data, spec)
         line["cpu_baseline"] = single
         line["cpu_baseline_all_threads"] = allcore
-        # bit-exact check of the timed configuration against the oracle
+        # bit-exact check of the timed configuration against the oracle, every output array
         keys = (("record_idx", "rec"), ("column_ids", "col"), ("field_offsets", "off"), ("field_lengths", "len")) \
             if kind == "csv" else (("kind", "kind"), ("start", "start"), ("length", "length"))
         res = runner(d)

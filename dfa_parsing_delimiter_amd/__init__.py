@@ -30,6 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PPR_LIB_PATH") or os.path.join(_HERE, "libppr.so")
 
 PPR_OK, PPR_EINVAL, PPR_ECAPACITY, PPR_ETOOBIG, PPR_EHIP, PPR_EWORKSPACE = 0, -1, -2, -3, -4, -5
+PPR_PATH_STREAMING, PPR_PATH_SINGLE_PASS = 1, 2
 _ERRNAMES = {-1: "PPR_EINVAL", -2: "PPR_ECAPACITY", -3: "PPR_ETOOBIG", -4: "PPR_EHIP", -5: "PPR_EWORKSPACE"}
 TAG_VALUE, TAG_FIELD, TAG_RECORD, TAG_INVALID = 0, 1, 2, 3
 
@@ -50,11 +51,12 @@ class ParseOut(ctypes.Structure):
     _fields_ = [("record_idx", ctypes.c_void_p), ("column_ids", ctypes.c_void_p),
                 ("field_offsets", ctypes.c_void_p), ("field_lengths", ctypes.c_void_p),
                 ("cap_fields", ctypes.c_uint64), ("n_fields", ctypes.c_uint64), ("n_records", ctypes.c_uint64),
-                ("error_pos", ctypes.c_int64), ("end_state", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+                ("error_pos", ctypes.c_int64), ("end_state", ctypes.c_uint32), ("path", ctypes.c_uint32)]
 
 
 class ParseOpts(ctypes.Structure):
-    _fields_ = [("chunk_bytes", ctypes.c_uint32), ("reserved", ctypes.c_uint32 * 3)]
+    _fields_ = [("chunk_bytes", ctypes.c_uint32), ("n_stage_events", ctypes.c_uint32),
+                ("stage_events", ctypes.c_void_p)]
 
 
 class LexTablesC(ctypes.Structure):
@@ -128,6 +130,21 @@ def _opts(chunk_bytes):
     return o
 
 
+def _opts_with_events(opts, events):
+    """A copy of opts that records the given (already created) torch.cuda.Event
+    objects between the call's kernels; returns (opts, the handle array to keep alive)."""
+    o = ParseOpts()
+    o.chunk_bytes = opts.chunk_bytes
+    if not events:
+        return o, None
+    handles = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
+    if not all(handles):
+        raise ValueError("stage events must have been recorded once (created) before use")
+    o.n_stage_events = len(events)
+    o.stage_events = ctypes.cast(handles, ctypes.c_void_p)
+    return o, handles
+
+
 def make_dfa(table: dict):
     """(Dfa struct, class map bytes) from a DFA table dict."""
     d = Dfa()
@@ -160,6 +177,7 @@ class ParseResult:
     n_records: int
     error_pos: int
     end_state: int
+    path: int                    # PPR_PATH_STREAMING or PPR_PATH_SINGLE_PASS
 
 
 class Parser:
@@ -193,16 +211,19 @@ class Parser:
     def _ws_ptr(self):
         return ctypes.c_void_p(self.ws.data_ptr() + self.ws_off)
 
-    def launch(self, data: torch.Tensor, stream=None):
-        """enqueue one parse without waiting (for timing loops)"""
+    def launch(self, data: torch.Tensor, stream=None, stage_events=None):
+        """enqueue one parse without waiting (for timing loops); stage_events:
+        optional torch.cuda.Event list recorded before/between/after the kernels"""
         _check_input(data)
         n = data.numel()
         if n > self.max_n:
             raise ValueError("input larger than the parser's max_n")
         o = self._out()
+        opts, keep = _opts_with_events(self.opts, stage_events)
         _check(lib.ppr_parse_async(ctypes.c_void_p(data.data_ptr()), n, ctypes.byref(self.dfa), self.class_map,
-                                   ctypes.byref(o), self._ws_ptr(), self.ws_bytes, ctypes.byref(self.opts),
+                                   ctypes.byref(o), self._ws_ptr(), self.ws_bytes, ctypes.byref(opts),
                                    _stream_handle(stream)), "ppr_parse_async")
+        del keep
 
     def results(self, n: int, stream=None) -> ParseOut:
         o = self._out()
@@ -227,7 +248,7 @@ class Parser:
             _check(rc, "ppr_parse")
             k = int(o.n_fields)
             return ParseResult(*[a[:k] for a in self.out_arrays], k, int(o.n_records), int(o.error_pos),
-                               int(o.end_state))
+                               int(o.end_state), int(o.path))
         raise PprError(PPR_ECAPACITY, "ppr_parse")
 
 
@@ -327,12 +348,14 @@ class Lexer:
     def _ws_ptr(self):
         return ctypes.c_void_p(self.ws.data_ptr() + self.ws_off)
 
-    def launch(self, data: torch.Tensor, stream=None):
+    def launch(self, data: torch.Tensor, stream=None, stage_events=None):
         _check_input(data)
         o = self._out()
+        opts, keep = _opts_with_events(self.opts, stage_events)
         _check(lib.ppr_lex_async(ctypes.c_void_p(data.data_ptr()), data.numel(), ctypes.byref(self.t.c),
                                  ctypes.byref(self.t.prep), ctypes.byref(o), self._ws_ptr(), self.ws_bytes,
-                                 ctypes.byref(self.opts), _stream_handle(stream)), "ppr_lex_async")
+                                 ctypes.byref(opts), _stream_handle(stream)), "ppr_lex_async")
+        del keep
 
     def results(self, n: int, stream=None) -> TokensOut:
         o = self._out()

@@ -229,6 +229,7 @@ __global__ void csv_reset_kernel(WsHeader* hdr, uint32_t n, uint32_t start_state
         hdr->fault = 0;
         hdr->err_min = 0xffffffffu;
         hdr->last_rec = 0;
+        hdr->path = PPR_PATH_SINGLE_PASS;
         if (n == 0) {  // nothing to parse: the results of an empty input
             hdr->n_fields = 0;
             hdr->n_records = 0;
@@ -343,7 +344,7 @@ static int validate_dfa(const ppr_dfa_t* d, const uint8_t* cm)
 static uint32_t chunk_of(const ppr_parse_opts_t* o)
 {
     uint32_t L = o ? o->chunk_bytes : 0u;
-    if (L == 0) L = kFastChunk;
+    if (L == 0) L = kFastChunk;  // the default: 64 bytes per thread
     return L <= (uint32_t)kMaxChunk ? L : 0u;
 }
 
@@ -523,13 +524,15 @@ extern "C" int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa
             f.range_vec = (uint64_t*)(ws + fl.range_vec);
             f.range_state = (uint32_t*)(ws + fl.range_state);
             f.range_carry = (uint4*)(ws + fl.range_carry);
-            return launch_csv_fast(f, cb, v8, s);
+            return launch_csv_fast(f, cb, v8, opts, s);
         }
     }
 
     const WsLayout lay = csv_layout(n, L);
     if (ws_bytes < lay.total) return PPR_EWORKSPACE;
+    stage_event(opts, 0, s);
     hipLaunchKernelGGL(csv_reset_kernel, dim3(1), dim3(64), 0, s, hdr, (uint32_t)n, dfa->start_state, accept);
+    stage_event(opts, 1, s);
     if (hipGetLastError() != hipSuccess) return PPR_EHIP;
     if (n == 0) return PPR_OK;
     LookCtx lc{hdr, (uint64_t*)(ws + lay.off_a), (StatB*)(ws + lay.off_b), next_epoch()};
@@ -561,6 +564,7 @@ extern "C" int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa
                               : (uint8_t)st;
     memcpy(p.cls, class_map, 256);
     hipLaunchKernelGGL(csv_generic_kernel, dim3(p.num_tiles), dim3(kBlock), 0, s, p);
+    stage_event(opts, 2, s);
     if (hipGetLastError() != hipSuccess) return PPR_EHIP;
     return PPR_OK;
 }
@@ -578,6 +582,7 @@ extern "C" int ppr_parse_results(const void* d_ws, uint64_t n, ppr_parse_out_t* 
     // the first INVALID byte wins over a non-accepting end state
     out->error_pos = h.err_min != 0xffffffffu ? (int64_t)h.err_min : h.error_pos;
     out->end_state = h.end_state;
+    out->path = h.path;
     if (h.fault) return PPR_EHIP;
     return out->n_fields > out->cap_fields ? PPR_ECAPACITY : PPR_OK;
 }

@@ -150,6 +150,6 @@ inline FastLayout fast_layout(uint64_t n)
 }
 
 // Enqueue the fast path (CB symbol-code bits, V8: more than 4 tracked states).
-int launch_csv_fast(const FastParams& f, int cb, bool v8, hipStream_t s);
+int launch_csv_fast(const FastParams& f, int cb, bool v8, const ppr_parse_opts_t* opts, hipStream_t s);
 
 }  // namespace ppr

@@ -333,6 +333,7 @@ __global__ void csv_fast_tables_kernel(FastParams p)
         p.hdr->fault = 0;
         p.hdr->err_min = kNone;
         p.hdr->last_rec = 0;
+        p.hdr->path = PPR_PATH_STREAMING;
     }
     __syncthreads();
     uint32_t* tabs = p.tabs;
@@ -703,20 +704,25 @@ __global__ void __launch_bounds__(kFastBlock) csv_emit_kernel(FastParams p)
 }
 
 template <int CB, bool V8>
-static void launch(const FastParams& f, hipStream_t s)
+static void launch(const FastParams& f, const ppr_parse_opts_t* o, hipStream_t s)
 {
     const dim3 grid(f.num_ranges), block(kFastBlock);
+    stage_event(o, 0, s);
     hipLaunchKernelGGL((csv_fast_tables_kernel<CB, V8>), dim3(1), dim3(256), 0, s, f);
+    stage_event(o, 1, s);
     hipLaunchKernelGGL((csv_codes_kernel<CB, V8>), grid, block, 0, s, f);
+    stage_event(o, 2, s);
     hipLaunchKernelGGL((csv_carries_kernel<CB, V8>), grid, block, 0, s, f);
+    stage_event(o, 3, s);
     hipLaunchKernelGGL((csv_emit_kernel<CB, V8>), grid, block, 0, s, f);
+    stage_event(o, 4, s);
 }
 
-int launch_csv_fast(const FastParams& f, int cb, bool v8, hipStream_t s)
+int launch_csv_fast(const FastParams& f, int cb, bool v8, const ppr_parse_opts_t* o, hipStream_t s)
 {
-    if (cb == 2) v8 ? launch<2, true>(f, s) : launch<2, false>(f, s);
-    else if (cb == 3) v8 ? launch<3, true>(f, s) : launch<3, false>(f, s);
-    else v8 ? launch<4, true>(f, s) : launch<4, false>(f, s);
+    if (cb == 2) v8 ? launch<2, true>(f, o, s) : launch<2, false>(f, o, s);
+    else if (cb == 3) v8 ? launch<3, true>(f, o, s) : launch<3, false>(f, o, s);
+    else v8 ? launch<4, true>(f, o, s) : launch<4, false>(f, o, s);
     return hipGetLastError() == hipSuccess ? PPR_OK : PPR_EHIP;
 }
 

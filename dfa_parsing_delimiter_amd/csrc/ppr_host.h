@@ -6,6 +6,10 @@
 
 #include <atomic>
 
+#include <hip/hip_runtime.h>
+
+#include "ppr.h"
+
 namespace ppr {
 
 // Start of every workspace (256 bytes reserved): the tile counter of the
@@ -19,8 +23,15 @@ struct WsHeader {
     uint32_t fault;     // set when a look-back wait gave up (never expected)
     uint32_t err_min;   // first INVALID byte (atomic minimum over tiles), 0xffffffff: none
     uint32_t last_rec;  // the input's last byte is a record delimiter (multi-kernel parse)
-    uint32_t reserved;
+    uint32_t path;      // which kernels ran (PPR_PATH_*)
 };
+
+// Records stage event i of the call on the stream, if the caller asked for it.
+inline void stage_event(const ppr_parse_opts_t* o, uint32_t i, hipStream_t s)
+{
+    if (o && o->stage_events && i < o->n_stage_events && o->stage_events[i])
+        (void)hipEventRecord((hipEvent_t)o->stage_events[i], s);
+}
 
 // Upper bound on look-back polls per tile; beyond it the kernel records a fault
 // and finishes instead of waiting forever.

@@ -364,7 +364,9 @@ extern "C" int ppr_lex_async(const uint8_t* d_bytes, uint64_t n, const ppr_lex_t
     hipStream_t s = (hipStream_t)stream;
     uint8_t* ws = (uint8_t*)d_ws;
     WsHeader* hdr = (WsHeader*)ws;
+    stage_event(opts, 0, s);
     hipLaunchKernelGGL(lex_reset_kernel, dim3(1), dim3(64), 0, s, hdr);
+    stage_event(opts, 1, s);
     if (hipGetLastError() != hipSuccess) return PPR_EHIP;
     if (n == 0) return PPR_OK;
     LexParams p;
@@ -392,6 +394,7 @@ extern "C" int ppr_lex_async(const uint8_t* d_bytes, uint64_t n, const ppr_lex_t
     p.statB = (StatB*)(ws + lay.off_b);
     memcpy(p.col, prep->column_of, 256);
     hipLaunchKernelGGL(lex_kernel, dim3(p.num_tiles), dim3(kLexBlock), 0, s, p);
+    stage_event(opts, 2, s);
     if (hipGetLastError() != hipSuccess) return PPR_EHIP;
     return PPR_OK;
 }

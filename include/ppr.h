@@ -97,13 +97,33 @@ typedef struct ppr_parse_out {
     uint64_t n_records; /* out */
     int64_t error_pos;  /* out: first INVALID byte; else n if the end state is not accepting; else -1 */
     uint32_t end_state; /* out: DFA state after the last byte */
-    uint32_t reserved;
+    uint32_t path;      /* out: the kernels that ran, PPR_PATH_STREAMING or PPR_PATH_SINGLE_PASS */
 } ppr_parse_out_t;
 
-/* Launch options. chunk_bytes: bytes each thread simulates (1..64, 0 = default 32). */
+/*
+ * Which kernels a parse runs (chosen at the call, reported in ppr_parse_out_t.path):
+ *   PPR_PATH_STREAMING   chunk_bytes 64, 16-byte aligned input, a class map with one
+ *                        catch-all class and at most 8 other bytes that a 3-bit hash of
+ *                        two bit fields separates: 4 kernels (step tables, codes,
+ *                        carries, emit), no waiting between workgroups;
+ *   PPR_PATH_SINGLE_PASS any table and chunk size: 2 kernels (reset, one single-pass
+ *                        kernel with decoupled look-back scans).
+ */
+enum { PPR_PATH_STREAMING = 1, PPR_PATH_SINGLE_PASS = 2 };
+
+/*
+ * Launch options (opts may be NULL: all defaults).
+ *   chunk_bytes:    bytes each thread simulates, 1..64; 0 = 64.
+ *   stage_events:   optional array of n_stage_events hipEvent_t (caller-created):
+ *                   event 0 is recorded on the stream before the first kernel of the
+ *                   call and event i after its i-th kernel, as far as the array
+ *                   reaches (streaming parse: 4 kernels; single-pass parse and the
+ *                   lexer: 2). For per-kernel timing; NULL: none.
+ */
 typedef struct ppr_parse_opts {
     uint32_t chunk_bytes;
-    uint32_t reserved[3];
+    uint32_t n_stage_events;
+    void* const* stage_events;
 } ppr_parse_opts_t;
 
 /*

@@ -200,28 +200,77 @@ def test_capacity_reported(ppr):
     _same(g, r, "resized")
 
 
-def test_repeatable(ppr):
+@pytest.mark.parametrize("chunk", [31, None])
+def test_repeatable(ppr, chunk):
+    """the same workspace reused: nothing left over from the previous call leaks in"""
     t = W.table("T5")
     b = W.generate(3, n=(8 << 20) + 3, seed=11)
     r = oracle.csv_parse(b, t)
-    P = ppr.Parser(t, max_n=b.size, chunk_bytes=31)
+    P = ppr.Parser(t, max_n=b.size, chunk_bytes=chunk)
     d = _dev(b)
     for i in range(5):
-        _say("repeat", i)
+        _say("repeat", chunk, i)
         _same(P(d), r, i)
+    # a shorter input on the same workspace, then the long one again
+    short = b[: (1 << 20) + 77]
+    _same(P(_dev(short)), oracle.csv_parse(short, t), "short")
+    _same(P(d), r, "again")
+
+
+def test_path_reported(ppr):
+    """the streaming kernels run for 64-byte chunks on aligned input with an encodable class map; the
+    single-pass kernel otherwise"""
+    for name in ("T5", "T6"):
+        t = W.table(name)
+        b = W.generate(1 if name == "T5" else 4, n=300000, seed=5)
+        g = ppr.parse(_dev(b), t, capacity=b.size + 1)
+        assert g.path == ppr.PPR_PATH_STREAMING, name
+        g31 = ppr.parse(_dev(b), t, chunk_bytes=31, capacity=b.size + 1)
+        assert g31.path == ppr.PPR_PATH_SINGLE_PASS, name
+    # more than 8 non-catch-all bytes: not encodable by the streaming classifier
+    rng = np.random.default_rng(3)
+    t = _random_table(rng, True, 40)
+    b = rng.integers(0, 256, 5000).astype(np.uint8)
+    g = ppr.parse(_dev(b), t, capacity=b.size + 1)
+    assert g.path == ppr.PPR_PATH_SINGLE_PASS
+    _same(g, oracle.csv_parse(b, t), "40 specials")
+
+
+def test_stage_events(ppr):
+    """per-kernel HIP events recorded by the library between its kernels"""
+    import torch
+    t = W.table("T5")
+    b = W.generate(3, n=(4 << 20), seed=2)
+    d = _dev(b)
+    P = ppr.Parser(t, max_n=b.size)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    P.launch(d, stage_events=ev)
+    torch.cuda.synchronize()
+    o = P.results(b.size)
+    assert o.path == ppr.PPR_PATH_STREAMING
+    times = [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+    assert all(x >= 0 for x in times) and sum(times) > 0, times
+    assert o.n_fields == oracle.csv_parse(b, t)["n_fields"]
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_full_size_workloads(ppr, cfg):
-    """every output array at the workload's full size, in the benchmark's launch configuration"""
+    """every output array at the workload's full size: in the launch configuration the benchmark times
+    (the default 64-byte chunks, streaming kernels) and at the workload's own chunk size if it names one"""
     t = W.table(W.CONFIGS[cfg]["table"])
-    chunk = W.CONFIGS[cfg].get("chunk_bytes")
     _say("full", cfg, "generate")
     b = W.generate(cfg)
     _say("full", cfg, "oracle")
     r = oracle.csv_parse(b, t)
-    _say("full", cfg, "gpu", r["n_fields"])
-    g = ppr.Parser(t, max_n=b.size, capacity=r["n_fields"], chunk_bytes=chunk)(_dev(b))
-    _same(g, r, ("full", cfg))
-    del b
+    d = _dev(b)
+    for chunk in [None] + ([W.CONFIGS[cfg]["chunk_bytes"]] if W.CONFIGS[cfg].get("chunk_bytes") else []):
+        _say("full", cfg, "gpu chunk", chunk, r["n_fields"])
+        g = ppr.Parser(t, max_n=b.size, capacity=r["n_fields"], chunk_bytes=chunk)(d)
+        if chunk is None:
+            assert g.path == ppr.PPR_PATH_STREAMING
+        _same(g, r, ("full", cfg, chunk))
+    del b, d
