@@ -519,7 +519,8 @@ extern "C" int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa
             f.idx = ws + fl.idx;
             f.cvec_lo = (uint32_t*)(ws + fl.cvec_lo);
             f.cvec_hi = (uint32_t*)(ws + fl.cvec_hi);
-            f.num_ranges = (uint32_t)std::min<uint64_t>(fl.tiles, kMaxRanges);
+            f.num_super = (uint32_t)((fl.tiles + 1) / 2);
+            f.num_ranges = (uint32_t)std::min<uint64_t>(f.num_super, kMaxRanges);
             f.tile_vec = (uint64_t*)(ws + fl.tile_vec);
             f.range_vec = (uint64_t*)(ws + fl.range_vec);
             f.range_state = (uint32_t*)(ws + fl.range_state);

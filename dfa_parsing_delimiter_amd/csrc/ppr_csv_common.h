@@ -113,7 +113,8 @@ struct FastParams {
     OutArrays out;
     WsHeader* hdr;
     uint32_t* tabs;        // step tables built for this call
-    uint32_t num_ranges;   // workgroups of the streaming kernels, each owning a contiguous run of tiles
+    uint32_t num_super;    // super-tiles: pairs of tiles (the last may hold one)
+    uint32_t num_ranges;   // workgroups of the streaming kernels, each owning a contiguous run of super-tiles
     uint8_t* idx;          // group indices, NI bytes per full chunk
     uint32_t* cvec_lo;     // per chunk: vector of the tile's bytes before it (entries 0-3)
     uint32_t* cvec_hi;     // (entries 4-7)

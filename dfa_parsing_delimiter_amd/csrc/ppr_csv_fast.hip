@@ -27,6 +27,7 @@
 // An absorbing state (such as INV) is the byte 0xFF in a vector, which v_perm
 // maps to itself, so it needs no vector entry.
 #include <algorithm>
+#include <type_traits>
 
 #include "ppr_csv_common.h"
 #include "ppr_scan.h"
@@ -45,14 +46,10 @@ struct Geo {
 };
 
 
-// Count carries [ParPaRaw Sec. 3, offsets, Fig. 4] in the fast path's
-// encodings. Inside a tile (at most 2^15 bytes): nfr = terminators |
-// record delimiters << 16, col = column offset handed on (bit 31: absolute, a
-// record delimiter was seen), lt = 1 + position of the last terminator (0:
-// none). Across tiles the two counts get a word each.
-struct TCarry {
-    uint32_t nfr, col, lt;
-};
+// Count carries [ParPaRaw Sec. 3, offsets, Fig. 4] of a run of bytes: nf
+// terminators, nr record delimiters, col the column offset handed on (bit 31:
+// absolute, a record delimiter was seen), lt = 1 + position of the last
+// terminator (0: none).
 struct GCarry {
     uint32_t nf, nr, col, lt;
 };
@@ -61,12 +58,6 @@ struct GCarry {
 // (the earlier offset's absolute flag stays in bit 31)
 __device__ __forceinline__ uint32_t col_op(uint32_t x, uint32_t y) { return (int32_t)y < 0 ? y : x + y; }
 
-struct TCarryComb {
-    __device__ TCarry operator()(const TCarry& x, const TCarry& y) const
-    {
-        return {x.nfr + y.nfr, col_op(x.col, y.col), max(x.lt, y.lt)};
-    }
-};
 struct GCarryComb {
     __device__ GCarry operator()(const GCarry& x, const GCarry& y) const
     {
@@ -74,20 +65,62 @@ struct GCarryComb {
     }
 };
 
-// the carry of one chunk from its terminator and record-delimiter bitmaps
-__device__ __forceinline__ TCarry chunk_carry(uint64_t T, uint64_t RD, uint32_t chunk_abs)
+struct AddComb {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct MaxComb {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
+};
+
+// Count carries of a workgroup's spans without a 4-word scan: each lane's
+// terminator and record counts (packed, a span holds at most 128 of each), the
+// 1 + position of its last terminator, and the 1-based index among its
+// terminators of its last record delimiter; per wave a sum scan of the packed
+// counts and two max reductions give the wave's carry (its column carry is the
+// terminators after its last record delimiter), and the waves' carries are
+// combined through LDS.
+struct SpanCarry {
+    uint32_t excl_nf;  // terminators in the wave's earlier lanes
+    uint32_t mine;     // this lane's terminators
+    GCarry wave_excl;  // carry of the tile's earlier waves
+    GCarry total;      // carry of the whole tile
+};
+
+__device__ __forceinline__ SpanCarry span_carry(const uint64_t (&T)[2], const uint64_t (&RD)[2], uint32_t abs,
+                                                GCarry* s_wave)
 {
-    TCarry c;
-    c.nfr = (uint32_t)__popcll(T) | ((uint32_t)__popcll(RD) << 16);
-    if (RD) {
-        const int hi = 63 - __clzll((long long)RD);
-        const uint64_t above = hi == 63 ? 0ull : (~0ull << (hi + 1));
-        c.col = (uint32_t)__popcll(T & above) | 0x80000000u;
-    } else {
-        c.col = (uint32_t)__popcll(T);
+    const uint32_t n0 = (uint32_t)__popcll(T[0]), n1 = (uint32_t)__popcll(T[1]);
+    const uint32_t nf = n0 + n1, nr = (uint32_t)(__popcll(RD[0]) + __popcll(RD[1]));
+    uint32_t lt = 0, rdl = 0;
+    if (T[1]) lt = abs + kFastChunk + (uint32_t)(63 - __clzll((long long)T[1])) + 1u;
+    else if (T[0]) lt = abs + (uint32_t)(63 - __clzll((long long)T[0])) + 1u;
+    if (RD[1]) {
+        const int h = 63 - __clzll((long long)RD[1]);
+        rdl = n0 + (uint32_t)__popcll(T[1] & (h == 63 ? ~0ull : ((2ull << h) - 1ull)));
+    } else if (RD[0]) {
+        const int h = 63 - __clzll((long long)RD[0]);
+        rdl = (uint32_t)__popcll(T[0] & (h == 63 ? ~0ull : ((2ull << h) - 1ull)));
     }
-    c.lt = T ? chunk_abs + (uint32_t)(63 - __clzll((long long)T)) + 1u : 0u;
-    return c;
+    const uint32_t inc = wave_scan(nf | (nr << 16), 0u, AddComb{});
+    const uint32_t excl = wave_shr1(0u, inc);
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane(inc, kWave - 1);
+    const uint32_t rdg = rdl ? (excl & 0xffffu) + rdl : 0u;  // 1-based wave-local index of the lane's last record field
+    const uint32_t max_rd = (uint32_t)__builtin_amdgcn_readlane(wave_scan(rdg, 0u, MaxComb{}), kWave - 1);
+    const uint32_t max_lt = (uint32_t)__builtin_amdgcn_readlane(wave_scan(lt, 0u, MaxComb{}), kWave - 1);
+    const uint32_t wnf = tot & 0xffffu;
+    const GCarry wc{wnf, tot >> 16, max_rd ? (wnf - max_rd) | 0x80000000u : wnf, max_lt};
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    if (lane_id() == 0) s_wave[w] = wc;
+    __syncthreads();
+    const GCarry zero{0, 0, 0, 0};
+    const GCarry ws = row_scan<kFastWaves>(lane_value<kFastWaves>(s_wave, zero), zero, GCarryComb{});
+    SpanCarry r;
+    r.excl_nf = excl & 0xffffu;
+    r.mine = nf;
+    r.wave_excl = zero;
+    if (w) r.wave_excl = readlane_t(ws, w - 1);
+    r.total = readlane_t(ws, kFastWaves - 1);
+    return r;
 }
 
 // symbol codes of four bytes: a 3-bit slot from two bit fields of each byte, the
@@ -201,100 +234,144 @@ __device__ __forceinline__ void nibbles_to_bits(uint32_t w0, uint32_t w1, uint32
     r32 = perm(r1, r0, 0x06040200u);
 }
 
-// Pass 2 over a full chunk from state code s: a chain of pass-2 lookups, one per
-// group, each addressed by the previous entry's row offset. Returns the OR of
+// Pass 2 over a thread's span of two full chunks (2 NI groups, packed four
+// index bytes per word in pw) from state code s: a chain of pass-2 lookups, one
+// per group, each addressed by the previous entry's row offset. T[h] / RD[h]:
+// terminator / record bitmaps of chunk h (bit j = byte j). Returns the OR of
 // the entries (bit 31: some byte is INVALID).
 template <int CB>
-__device__ __forceinline__ uint32_t pass2_full(const uint32_t (&idx)[Geo<CB>::NI], uint32_t s, uint32_t nt,
-                                               const uint32_t* s_t2, uint64_t& T, uint64_t& RD)
+__device__ __forceinline__ uint32_t pass2_pair(const uint32_t (&pw)[2 * Geo<CB>::NP], uint32_t s, uint32_t nt,
+                                               const uint32_t* s_t2, uint64_t (&T)[2], uint64_t (&RD)[2])
 {
-    constexpr int E = Geo<CB>::E, NI = Geo<CB>::NI, G = Geo<CB>::G;
+    constexpr int E = Geo<CB>::E, NG = 2 * Geo<CB>::NI, G = Geo<CB>::G;
     constexpr uint32_t GM = Geo<CB>::GM;
     const char* base = reinterpret_cast<const char*>(s_t2);
     uint32_t row = min(s, nt) * (uint32_t)(E * 4);
-    uint32_t e[NI], any = 0;
-#pragma unroll
-    for (int k = 0; k < NI; ++k) {
-        e[k] = *reinterpret_cast<const uint32_t*>(base + row + idx[k] * 4u);
-        row = e[k] & kRowMask;
-        any |= e[k];
-    }
+    uint32_t any = 0;
     if constexpr (G == 4) {
-        uint32_t w[NI / 4];
+        // the tag byte (bits 16-23) of four consecutive entries gathered into one word;
+        // the four index bytes of pw[q] spread into two words of 16-bit halves times 4
+        // (byte offsets), so that each step's address is one add of two halves
+        uint32_t w[NG / 4];
 #pragma unroll
-        for (int q = 0; q < NI / 4; ++q)
-            w[q] = perm(e[4 * q + 1], e[4 * q], 0x0c0c0602u) | perm(e[4 * q + 3], e[4 * q + 2], 0x06020c0cu);
-        uint32_t tl, th, rl, rh;
-        nibbles_to_bits(w[0], w[1], tl, rl);
-        nibbles_to_bits(w[2], w[3], th, rh);
-        T = (uint64_t)tl | ((uint64_t)th << 32);
-        RD = (uint64_t)rl | ((uint64_t)rh << 32);
-    } else {
-        uint32_t tw[2] = {0u, 0u}, rw[2] = {0u, 0u};
+        for (int q = 0; q < NG / 4; ++q) {
+            const uint32_t x01 = perm(0u, pw[q], 0x0c010c00u) << 2, x23 = perm(0u, pw[q], 0x0c030c02u) << 2;
+            const uint32_t off[4] = {x01 & 0xffffu, x01 >> 16, x23 & 0xffffu, x23 >> 16};
+            uint32_t e[4];
 #pragma unroll
-        for (int k = 0; k < NI; ++k) {
-            tw[(G * k) / 32] |= ((e[k] >> 16) & GM) << ((G * k) % 32);
-            rw[(G * k) / 32] |= ((e[k] >> 20) & GM) << ((G * k) % 32);
+            for (int i = 0; i < 4; ++i) {
+                e[i] = *reinterpret_cast<const uint32_t*>(base + (row & kRowMask) + off[i]);
+                row = e[i];
+                any |= e[i];
+            }
+            w[q] = perm(e[1], e[0], 0x0c0c0602u) | perm(e[3], e[2], 0x06020c0cu);
         }
-        T = (uint64_t)tw[0] | ((uint64_t)tw[1] << 32);
-        RD = (uint64_t)rw[0] | ((uint64_t)rw[1] << 32);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t tl, th, rl, rh;
+            nibbles_to_bits(w[4 * h], w[4 * h + 1], tl, rl);
+            nibbles_to_bits(w[4 * h + 2], w[4 * h + 3], th, rh);
+            T[h] = (uint64_t)tl | ((uint64_t)th << 32);
+            RD[h] = (uint64_t)rl | ((uint64_t)rh << 32);
+        }
+    } else {
+        uint32_t tw[4] = {0u, 0u, 0u, 0u}, rw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+            const uint32_t ix = (pw[k / 4] >> (8 * (k % 4))) & 0xffu;
+            const uint32_t e = *reinterpret_cast<const uint32_t*>(base + row + ix * 4u);
+            row = e & kRowMask;
+            any |= e;
+            tw[(G * k) / 32] |= ((e >> 16) & GM) << ((G * k) % 32);
+            rw[(G * k) / 32] |= ((e >> 20) & GM) << ((G * k) % 32);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            T[h] = (uint64_t)tw[2 * h] | ((uint64_t)tw[2 * h + 1] << 32);
+            RD[h] = (uint64_t)rw[2 * h] | ((uint64_t)rw[2 * h + 1] << 32);
+        }
     }
     return any;
 }
 
-// position of the first INVALID byte of a full chunk known to hold one
+// position of the first INVALID byte of a full two-chunk span known to hold one
 template <int CB>
-__device__ uint32_t first_invalid(const uint32_t (&idx)[Geo<CB>::NI], uint32_t s, uint32_t nt, const uint32_t* s_t2,
-                                  uint32_t chunk_abs)
+__device__ uint32_t first_invalid(const uint32_t (&pw)[2 * Geo<CB>::NP], uint32_t s, uint32_t nt,
+                                  const uint32_t* s_t2, uint32_t abs)
 {
-    constexpr int E = Geo<CB>::E, NI = Geo<CB>::NI, G = Geo<CB>::G;
+    constexpr int E = Geo<CB>::E, NG = 2 * Geo<CB>::NI, G = Geo<CB>::G;
     const char* base = reinterpret_cast<const char*>(s_t2);
-    uint32_t row = min(s, nt) * (uint32_t)(E * 4);
-    for (int k = 0; k < NI; ++k) {
-        const uint32_t e = *reinterpret_cast<const uint32_t*>(base + row + idx[k] * 4u);
-        if (e >> 31) return chunk_abs + (uint32_t)(G * k) + ((e >> 24) & 7u);
+    uint32_t row = min(s, nt) * (uint32_t)(E * 4), first = kNone;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {  // (no early exit: indices into pw stay compile-time constants)
+        const uint32_t ix = (pw[k / 4] >> (8 * (k % 4))) & 0xffu;
+        const uint32_t e = *reinterpret_cast<const uint32_t*>(base + row + ix * 4u);
+        if ((e >> 31) && first == kNone) first = abs + (uint32_t)(G * k) + ((e >> 24) & 7u);
         row = e & kRowMask;
     }
-    return kNone;
+    return first;
 }
 
-// pass 2 over the ragged last chunk, one byte at a time
-template <int CB>
-__device__ void pass2_ragged(const FastParams& p, const ChunkPos& c, uint32_t s, uint32_t nt, const uint8_t* s_nxt,
-                             const uint8_t* s_tag, uint64_t& T, uint64_t& RD, uint32_t& err)
+// where a thread of the carries and emit kernels works: super-tile st (two
+// tiles of the codes kernel, 64 KiB), bytes [abs, abs + my_len) of at most 128,
+// which are the codes kernel's chunks 2 (tid mod 256) and 2 (tid mod 256) + 1 of
+// its tile 2 st + tid / 256
+struct PairPos {
+    uint32_t st, tile, abs, my_len;
+    size_t pair;  // global pair index: tile * 256 + tid mod 256
+    bool valid, full;
+};
+
+__device__ __forceinline__ PairPos pair_pos(const FastParams& p, uint32_t st)
 {
-    T = 0;
-    RD = 0;
+    PairPos c;
+    c.st = st;
+    c.tile = 2 * st + threadIdx.x / (kFastBlock / 2);
+    c.valid = c.tile < p.num_tiles;
+    c.abs = st * (uint32_t)(2 * kFastTile) + threadIdx.x * (uint32_t)(2 * kFastChunk);
+    c.my_len = c.abs < p.n ? min((uint32_t)(2 * kFastChunk), p.n - c.abs) : 0u;
+    c.full = c.my_len == (uint32_t)(2 * kFastChunk);
+    c.pair = (size_t)c.tile * (kFastBlock / 2) + threadIdx.x % (kFastBlock / 2);
+    return c;
+}
+
+// pass 2 over a ragged span (the input's last bytes), one byte at a time
+template <int CB>
+__device__ void pass2_ragged(const FastParams& p, const PairPos& c, uint32_t s, uint32_t nt, const uint8_t* s_nxt,
+                             const uint8_t* s_tag, uint64_t (&T)[2], uint64_t (&RD)[2], uint32_t& err)
+{
+    T[0] = T[1] = RD[0] = RD[1] = 0;
     for (uint32_t j = 0; j < c.my_len; ++j) {
-        const uint32_t code = classify4<CB>(p.in[c.chunk_abs + j] * 0x01010101u, p) & Geo<CB>::CM;
+        const uint32_t code = classify4<CB>(p.in[c.abs + j] * 0x01010101u, p) & Geo<CB>::CM;
         const uint32_t row = min(s, nt);
         const uint32_t t = s_tag[row * 16 + code];
         s = s_nxt[row * 16 + code];
-        T |= (uint64_t)(t == PPR_TAG_FIELD || t == PPR_TAG_RECORD) << j;
-        RD |= (uint64_t)(t == PPR_TAG_RECORD) << j;
-        if (t == PPR_TAG_INVALID && err == kNone) err = c.chunk_abs + j;
+        T[j >> 6] |= (uint64_t)(t == PPR_TAG_FIELD || t == PPR_TAG_RECORD) << (j & 63);
+        RD[j >> 6] |= (uint64_t)(t == PPR_TAG_RECORD) << (j & 63);
+        if (t == PPR_TAG_INVALID && err == kNone) err = c.abs + j;
     }
 }
 
-// What the carries and emit kernels read per chunk: its group indices (NI
-// bytes, 16-byte loads) and its vector of the tile's earlier bytes. Loaded one
-// tile ahead of use.
+// What the carries and emit kernels read per thread: the group indices of its
+// two chunks (2 NI bytes, 16-byte loads) and the first chunk's vector of its
+// tile's earlier bytes. Loaded one super-tile ahead of use.
 template <int CB, bool V8>
 struct IdxIn {
-    uint32_t pw[Geo<CB>::NP];
+    uint32_t pw[2 * Geo<CB>::NP];
     uint32_t cvlo, cvhi;
+    uint64_t tvl;  // lane l: tile vector 2 st + (l & 1) (kept per lane until used, see span_state)
 };
 
-template <int CB, bool V8>
-__device__ __forceinline__ IdxIn<CB, V8> load_in(const FastParams& p, const ChunkPos& c)
+// FULL: the span is known to be full (no branch around the loads)
+template <int CB, bool V8, bool FULL>
+__device__ __forceinline__ IdxIn<CB, V8> load_in(const FastParams& p, const PairPos& c)
 {
     constexpr int NI = Geo<CB>::NI, NP = Geo<CB>::NP;
     IdxIn<CB, V8> in;
-    const size_t ci = (size_t)c.tile * kFastBlock + threadIdx.x;
-    if (c.full) {
-        const uint4* src = reinterpret_cast<const uint4*>(p.idx + ci * NI);
+    if (FULL || c.full) {
+        const uint4* src = reinterpret_cast<const uint4*>(p.idx + c.pair * (2 * NI));
 #pragma unroll
-        for (int q = 0; q < NP / 4; ++q) {
+        for (int q = 0; q < NP / 2; ++q) {
             const uint4 x = src[q];
             in.pw[4 * q] = x.x;
             in.pw[4 * q + 1] = x.y;
@@ -302,16 +379,11 @@ __device__ __forceinline__ IdxIn<CB, V8> load_in(const FastParams& p, const Chun
             in.pw[4 * q + 3] = x.w;
         }
     }
+    const size_t ci = c.valid ? 2 * c.pair : 0;  // the span's first (even) chunk
     in.cvlo = p.cvec_lo[ci];
     in.cvhi = V8 ? p.cvec_hi[ci] : 0xffffffffu;
+    in.tvl = p.tile_vec[min(2 * c.st + (threadIdx.x & 1u), p.num_tiles - 1)];
     return in;
-}
-
-template <int CB, bool V8>
-__device__ __forceinline__ void unpack_idx(const IdxIn<CB, V8>& in, uint32_t (&idx)[Geo<CB>::NI])
-{
-#pragma unroll
-    for (int k = 0; k < Geo<CB>::NI; ++k) idx[k] = (in.pw[k / 4] >> (8 * (k % 4))) & 0xffu;
 }
 
 // Pass-1 table: entry e (the codes of G bytes) -> composite vector from every
@@ -369,24 +441,25 @@ __global__ void csv_fast_tables_kernel(FastParams p)
 }
 
 // The streaming kernels run num_ranges workgroups; workgroup b owns the
-// contiguous tiles [t0, t1) below and walks them in order, loading the next
-// tile's inputs while it works on the current one. Along its range it carries
-// the state (carries, emit) and the count carry (emit) from tile to tile, so
-// the device-wide scans only run over the num_ranges range aggregates, in each
+// contiguous super-tiles [s0, s1) below (a super-tile is two tiles of the codes
+// kernel, 64 KiB) and walks them in order, loading the next one's inputs while
+// it works on the current one. Along its range it carries the state (carries,
+// emit) and the count carry (emit) from super-tile to super-tile, so the
+// device-wide scans only run over the num_ranges range aggregates, in each
 // workgroup's prologue.
-__device__ __forceinline__ void range_of(const FastParams& p, uint32_t b, uint32_t& t0, uint32_t& t1)
+__device__ __forceinline__ void range_of(const FastParams& p, uint32_t b, uint32_t& s0, uint32_t& s1)
 {
-    t0 = (uint32_t)((uint64_t)b * p.num_tiles / p.num_ranges);
-    t1 = (uint32_t)((uint64_t)(b + 1) * p.num_tiles / p.num_ranges);
+    s0 = (uint32_t)((uint64_t)b * p.num_super / p.num_ranges);
+    s1 = (uint32_t)((uint64_t)(b + 1) * p.num_super / p.num_ranges);
 }
 
 __device__ __forceinline__ Vec unpack_vec(uint64_t x) { return Vec{(uint32_t)x, (uint32_t)(x >> 32)}; }
 
-// composite of the range vectors of ranges 0..b-1 (thread i takes ranges 2i, 2i+1)
+// composite of the range vectors of ranges 0..b-1 (thread i takes ranges 2i, 2i+1;
+// loads from clamped indices, then word-wise selects)
 template <bool V8>
 __device__ Vec ranges_before(const FastParams& p, uint32_t b, const Vec& ident, Vec* s_wave)
 {
-    // (loads from clamped indices, then word-wise selects)
     const uint32_t i0 = 2 * threadIdx.x, i1 = i0 + 1;
     const Vec a = unpack_vec(p.range_vec[min(i0, kMaxRanges - 1)]);
     const Vec c = unpack_vec(p.range_vec[min(i1, kMaxRanges - 1)]);
@@ -406,8 +479,13 @@ __device__ GCarry carries_before(const FastParams& p, uint32_t b, GCarry* s_wave
     return block_reduce<kFastWaves>(c, zero, s_wave, comb);
 }
 
-// codes: symbol codes -> group indices (stored); each chunk's vector of the
-// tile's bytes before it, the tile vectors and the range vector (stored)
+// codes: symbol codes -> group indices (stored); the vector of the tile's bytes
+// before each even chunk, the tile vectors and the range vector (stored).
+//
+// The loop runs over the range's entirely full tiles with no per-chunk
+// branch, so that the next tile's loads stay in flight while the current one is
+// worked on; the input's ragged last tile, if the range holds it, is done after
+// the loop by the same body with the per-chunk checks.
 template <int CB, bool V8>
 __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
 {
@@ -419,78 +497,109 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
     __shared__ Vec s_wave[2][kFastWaves];
 
     const int tid = threadIdx.x;
-    uint32_t t0, t1;
-    range_of(p, blockIdx.x, t0, t1);
-    auto load_raw = [&](const ChunkPos& c, uint32_t (&w)[ND]) {
-        if (c.full) {
-            const uint4* src = reinterpret_cast<const uint4*>(p.in + c.chunk_abs);
+    // workgroup b takes tiles b, b + G, b + 2G, ... (G = the grid): the workgroups
+    // in flight read one contiguous window of the input
+    const uint32_t stride = gridDim.x;
+    const uint32_t tfull_all = p.n / (uint32_t)kFastTile;  // tiles [0, tfull_all) are entirely full
+    auto load_full = [&](uint32_t tile, uint32_t (&w)[ND]) {
+        const uint4* src = reinterpret_cast<const uint4*>(p.in + (size_t)tile * kFastTile + tid * kFastChunk);
 #pragma unroll
-            for (int q = 0; q < ND / 4; ++q) {
-                const uint4 x = src[q];
-                w[4 * q] = x.x;
-                w[4 * q + 1] = x.y;
-                w[4 * q + 2] = x.z;
-                w[4 * q + 3] = x.w;
-            }
+        for (int q = 0; q < ND / 4; ++q) {
+            const uint4 x = src[q];
+            w[4 * q] = x.x;
+            w[4 * q + 1] = x.y;
+            w[4 * q + 2] = x.z;
+            w[4 * q + 3] = x.w;
         }
     };
-    uint32_t tile = t0;
-    ChunkPos c = chunk_pos(p.n, tile);
     uint32_t w[ND];
-    load_raw(c, w);
+    const uint32_t t0 = blockIdx.x;
+    if (t0 < tfull_all) load_full(t0, w);
     for (int i = tid; i < T1W; i += kFastBlock) s_t1[i] = p.tabs[i];
     if (tid < 9 * 16) s_nxt[tid] = (&p.nxt[0][0])[tid];
     __syncthreads();
     const Vec ident = fast_ident<V8>(p.nt);
-    Vec rv = ident;
 
-    for (uint32_t it = 0;; ++it) {
-        const uint32_t next = tile + 1;
-        const ChunkPos cn = chunk_pos(p.n, next < t1 ? next : tile);
-        uint32_t wn[ND];
-        if (next < t1) load_raw(cn, wn);
-
-        Vec v = ident;
-        if (c.full) {
-            uint32_t idx[NI];
+    // classify, store the indices, the chunk's vector
+    auto full_chunk = [&](uint32_t tile, const uint32_t (&wc)[ND]) {
+        uint32_t idx[NI];
 #pragma unroll
-            for (int k = 0; k < ND; ++k) {
-                const uint32_t code = classify4<CB>(w[k], p);
-                if constexpr (Gm::G == 4) {
-                    idx[k] = __builtin_amdgcn_udot4(code, 0x40100401u, 0u, false);
-                } else {
-                    constexpr uint32_t W = 1u << CB;
-                    idx[2 * k] = __builtin_amdgcn_udot4(code, 0x00000001u | (W << 8), 0u, false);
-                    idx[2 * k + 1] = __builtin_amdgcn_udot4(code, 0x00010000u | (W << 24), 0u, false);
-                }
+        for (int k = 0; k < ND; ++k) {
+            const uint32_t code = classify4<CB>(wc[k], p);
+            if constexpr (Gm::G == 4) {
+                idx[k] = __builtin_amdgcn_udot4(code, 0x40100401u, 0u, false);
+            } else {
+                constexpr uint32_t W = 1u << CB;
+                idx[2 * k] = __builtin_amdgcn_udot4(code, 0x00000001u | (W << 8), 0u, false);
+                idx[2 * k + 1] = __builtin_amdgcn_udot4(code, 0x00010000u | (W << 24), 0u, false);
             }
-            uint32_t pw[NP];
-#pragma unroll
-            for (int q = 0; q < NP; ++q)
-                pw[q] = idx[4 * q] | (idx[4 * q + 1] << 8) | (idx[4 * q + 2] << 16) | (idx[4 * q + 3] << 24);
-            uint4* dst = reinterpret_cast<uint4*>(p.idx + ((size_t)tile * kFastBlock + tid) * NI);
-#pragma unroll
-            for (int q = 0; q < NP / 4; ++q)
-                dst[q] = make_uint4(pw[4 * q], pw[4 * q + 1], pw[4 * q + 2], pw[4 * q + 3]);
-            v = tree_vector<CB, V8>(idx, s_t1);
-        } else if (c.my_len) {
-            v = ragged_vector<CB, V8>(p, c, v, s_nxt);
         }
+        uint32_t pw[NP];
+#pragma unroll
+        for (int q = 0; q < NP; ++q)
+            pw[q] = idx[4 * q] | (idx[4 * q + 1] << 8) | (idx[4 * q + 2] << 16) | (idx[4 * q + 3] << 24);
+        uint4* dst = reinterpret_cast<uint4*>(p.idx + ((size_t)tile * kFastBlock + tid) * NI);
+#pragma unroll
+        for (int q = 0; q < NP / 4; ++q)
+            dst[q] = make_uint4(pw[4 * q], pw[4 * q + 1], pw[4 * q + 2], pw[4 * q + 3]);
+        return tree_vector<CB, V8>(idx, s_t1);
+    };
+    // scan the tile's chunk vectors, store them and the tile vector
+    auto finish = [&](uint32_t tile, const Vec& v, uint32_t it) {
         Vec excl, tot;
         block_scan<kFastWaves>(v, ident, excl, tot, s_wave[it & 1], VecComb<V8>{});
         const size_t ci = (size_t)tile * kFastBlock + tid;
         p.cvec_lo[ci] = excl.lo;
         if (V8) p.cvec_hi[ci] = excl.hi;
         if (tid == 0) p.tile_vec[tile] = (uint64_t)tot.lo | ((uint64_t)tot.hi << 32);
-        rv = comp<V8>(rv, tot);
+    };
 
-        if (next >= t1) break;
-        tile = next;
-        c = cn;
-#pragma unroll
-        for (int k = 0; k < ND; ++k) w[k] = wn[k];
+    // Two register buffers used in turn, and an unconditional prefetch (the
+    // last full tile is read again at the end): no copy of a register still
+    // being loaded and no branch around a load, either of which would make the
+    // compiler wait for the prefetch before the current tile's work.
+    uint32_t w2[ND];
+    uint32_t tile = t0;
+    // the last full tile this workgroup takes
+    const uint32_t tlast = tfull_all > t0 ? t0 + (tfull_all - 1 - t0) / stride * stride : t0;
+    while (tile < tfull_all) {
+        load_full(min(tile + stride, tlast), w2);
+        finish(tile, full_chunk(tile, w), 0);
+        tile += stride;
+        if (tile >= tfull_all) break;
+        load_full(min(tile + stride, tlast), w);
+        finish(tile, full_chunk(tile, w2), 1);
+        tile += stride;
     }
-    if (tid == 0) p.range_vec[blockIdx.x] = (uint64_t)rv.lo | ((uint64_t)rv.hi << 32);
+    if (tile < p.num_tiles) {  // the input's ragged last tile
+        const ChunkPos c = chunk_pos(p.n, tile);
+        Vec v = ident;
+        if (c.full) {
+            load_full(tile, w);
+            v = full_chunk(tile, w);
+        } else if (c.my_len) {
+            v = ragged_vector<CB, V8>(p, c, v, s_nxt);
+        }
+        finish(tile, v, 0);
+    }
+}
+
+// range vectors: one wave per range composes the range's tile vectors, 64 at a
+// time (coalesced loads, a DPP wave scan)
+template <bool V8>
+__global__ void __launch_bounds__(kWave) csv_range_vec_kernel(FastParams p)
+{
+    uint32_t s0, s1;
+    range_of(p, blockIdx.x, s0, s1);
+    const uint32_t t0 = 2 * s0, t1 = min(2 * s1, p.num_tiles);
+    const Vec ident = fast_ident<V8>(p.nt);
+    Vec rv = ident;
+    for (uint32_t t = t0; t < t1; t += kWave) {
+        const uint32_t i = t + threadIdx.x;
+        const Vec x = i < t1 ? unpack_vec(p.tile_vec[i]) : ident;
+        rv = comp<V8>(rv, readlane_t(wave_scan(x, ident, VecComb<V8>{}), kWave - 1));
+    }
+    if (threadIdx.x == 0) p.range_vec[blockIdx.x] = (uint64_t)rv.lo | ((uint64_t)rv.hi << 32);
 }
 
 // pass-2 table rows (tracked states + the absorbing row) and the byte tables
@@ -513,66 +622,102 @@ __device__ __forceinline__ void load_pass2(const FastParams& p, Pass2Shared<V8, 
     }
 }
 
-// carries: the range's start state (stored), tags from each chunk's start
-// state, the range's count carry (stored); the last range stores the end state
+// The tile vectors of super-tile st from the lane-wise prefetch (the second is
+// the identity if the super-tile has one tile). Broadcast only here, at their
+// use: moving a loaded value to a scalar register at the prefetch would make
+// the compiler wait for every load in flight.
+template <bool V8>
+__device__ __forceinline__ void super_vecs(const FastParams& p, uint32_t st, uint64_t tvl, const Vec& ident, Vec& v0,
+                                           Vec& v1)
+{
+    const uint32_t lo = (uint32_t)tvl, hi = (uint32_t)(tvl >> 32);
+    v0 = Vec{(uint32_t)__builtin_amdgcn_readlane(lo, 0), (uint32_t)__builtin_amdgcn_readlane(hi, 0)};
+    v1 = Vec{(uint32_t)__builtin_amdgcn_readlane(lo, 1), (uint32_t)__builtin_amdgcn_readlane(hi, 1)};
+    if (2 * st + 1 >= p.num_tiles) v1 = ident;
+}
+
+// Pass 2 for this thread's span: tags as bitmaps, the first INVALID byte (if
+// wanted). ts0 / ts1: the state before the super-tile's first / second tile.
+template <int CB, bool V8, bool FULL>
+__device__ __forceinline__ void span_tags(const FastParams& p, const PairPos& c, const IdxIn<CB, V8>& in,
+                                          uint32_t ts0, uint32_t ts1, const Pass2Shared<V8, Geo<CB>::E>& sh,
+                                          uint64_t (&T)[2], uint64_t (&RD)[2], uint32_t* err)
+{
+    const uint32_t nt = p.nt;
+    const uint32_t s = vat(Vec{in.cvlo, in.cvhi}, threadIdx.x < kFastBlock / 2 ? ts0 : ts1);
+    T[0] = T[1] = RD[0] = RD[1] = 0;
+    if (FULL || c.full) {
+        const uint32_t any = pass2_pair<CB>(in.pw, s, nt, sh.t2, T, RD);
+        if (err && (any >> 31)) *err = first_invalid<CB>(in.pw, s, nt, sh.t2, c.abs);
+    } else if (c.my_len) {
+        uint32_t e = kNone;
+        pass2_ragged<CB>(p, c, s, nt, sh.nxt, sh.tag, T, RD, e);
+        if (err) *err = e;
+    }
+}
+
+// Runs body(st, in, it) over the range's super-tiles [s0, s1) in order: the
+// entirely full ones [s0, sfull) with two register buffers used in turn and an
+// unconditional prefetch (the last full super-tile is read again at the end),
+// then the input's ragged last super-tile, if the range holds it.
+template <int CB, bool V8, typename FullBody, typename TailBody>
+__device__ __forceinline__ void walk_supers(const FastParams& p, uint32_t s0, uint32_t s1, const FullBody& full,
+                                            const TailBody& tail)
+{
+    const uint32_t sfull = min(s1, p.n / (uint32_t)(2 * kFastTile));
+    uint32_t st = s0;
+    IdxIn<CB, V8> a, b;
+    if (st < sfull) a = load_in<CB, V8, true>(p, pair_pos(p, st));
+    while (st < sfull) {
+        b = load_in<CB, V8, true>(p, pair_pos(p, min(st + 1, sfull - 1)));
+        full(st, a, 0u);
+        if (++st >= sfull) break;
+        a = load_in<CB, V8, true>(p, pair_pos(p, min(st + 1, sfull - 1)));
+        full(st, b, 1u);
+        ++st;
+    }
+    if (st < s1) tail(st, load_in<CB, V8, false>(p, pair_pos(p, st)), 0u);
+}
+
+// carries: the range's start state (stored), tags from each span's start state,
+// the range's count carry (stored); the last range stores the end state
 template <int CB, bool V8>
 __global__ void __launch_bounds__(kFastBlock) csv_carries_kernel(FastParams p)
 {
     using Gm = Geo<CB>;
-    constexpr int NI = Gm::NI;
     __shared__ Pass2Shared<V8, Gm::E> sh;
-    __shared__ TCarry s_wc[2][kFastWaves];
+    __shared__ GCarry s_wc[2][kFastWaves];
     __shared__ Vec s_wv[kFastWaves];
 
     const uint32_t b = blockIdx.x;
-    uint32_t t0, t1;
-    range_of(p, b, t0, t1);
-    uint32_t tile = t0;
-    ChunkPos c = chunk_pos(p.n, tile);
-    IdxIn<CB, V8> in = load_in<CB, V8>(p, c);
-    uint64_t tv = p.tile_vec[tile];
+    uint32_t s0, s1;
+    range_of(p, b, s0, s1);
     const uint32_t nt = p.nt;
-    load_pass2<CB, V8>(p, sh);
     const Vec ident = fast_ident<V8>(nt);
+    load_pass2<CB, V8>(p, sh);
     uint32_t run = vat(ranges_before<V8>(p, b, ident, s_wv), p.start_code);  // (its barrier publishes sh)
     if (threadIdx.x == 0) p.range_state[b] = run;
     const GCarryComb gcomb;
     GCarry rc{0, 0, 0, 0};
 
-    for (uint32_t it = 0;; ++it) {
-        const uint32_t next = tile + 1;
-        const ChunkPos cn = chunk_pos(p.n, next < t1 ? next : tile);
-        IdxIn<CB, V8> inn;
-        uint64_t tvn = 0;
-        if (next < t1) {
-            inn = load_in<CB, V8>(p, cn);
-            tvn = p.tile_vec[next];
-        }
-
-        const uint32_t s = vat(Vec{in.cvlo, in.cvhi}, run);
-        uint64_t T = 0, RD = 0;
+    auto step = [&](auto full_tag, uint32_t st, const IdxIn<CB, V8>& in, uint32_t it) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const PairPos c = pair_pos(p, st);
+        Vec v0, v1;
+        super_vecs<V8>(p, st, in.tvl, ident, v0, v1);
+        const uint32_t ts1 = vat(v0, run);
+        uint64_t T[2], RD[2];
         uint32_t err = kNone;
-        if (c.full) {
-            uint32_t idx[NI];
-            unpack_idx<CB, V8>(in, idx);
-            if (pass2_full<CB>(idx, s, nt, sh.t2, T, RD) >> 31)
-                err = first_invalid<CB>(idx, s, nt, sh.t2, c.chunk_abs);
-        } else if (c.my_len) {
-            pass2_ragged<CB>(p, c, s, nt, sh.nxt, sh.tag, T, RD, err);
-        }
+        span_tags<CB, V8, FULL>(p, c, in, run, ts1, sh, T, RD, &err);
         if (err != kNone) atomicMin(&p.hdr->err_min, err);
-        if (c.my_len && c.chunk_abs + c.my_len == p.n) p.hdr->last_rec = (uint32_t)((RD >> (c.my_len - 1)) & 1u);
-        const TCarry ct =
-            block_reduce<kFastWaves>(chunk_carry(T, RD, c.chunk_abs), TCarry{0, 0, 0}, s_wc[it & 1], TCarryComb{});
-        rc = gcomb(rc, GCarry{ct.nfr & 0xffffu, ct.nfr >> 16, ct.col, ct.lt});
-        run = vat(unpack_vec(tv), run);
-
-        if (next >= t1) break;
-        tile = next;
-        c = cn;
-        in = inn;
-        tv = tvn;
-    }
+        if (c.my_len && c.abs + c.my_len == p.n)  // the thread holding the input's last byte
+            p.hdr->last_rec = (uint32_t)((RD[(c.my_len - 1) >> 6] >> ((c.my_len - 1) & 63)) & 1u);
+        rc = gcomb(rc, span_carry(T, RD, c.abs, s_wc[it & 1]).total);
+        run = vat(v1, ts1);
+    };
+    walk_supers<CB, V8>(
+        p, s0, s1, [&](uint32_t st, const IdxIn<CB, V8>& in, uint32_t it) { step(std::true_type{}, st, in, it); },
+        [&](uint32_t st, const IdxIn<CB, V8>& in, uint32_t it) { step(std::false_type{}, st, in, it); });
     if (threadIdx.x == 0) {
         p.range_carry[b] = make_uint4(rc.nf, rc.nr, rc.col, rc.lt);
         if (b == p.num_ranges - 1) {
@@ -583,114 +728,127 @@ __global__ void __launch_bounds__(kFastBlock) csv_carries_kernel(FastParams p)
     }
 }
 
-// fields staged in LDS per round, so that the four output arrays are written
-// with consecutive addresses across the lanes
-constexpr int kStage = 2048;
+// a 64-bit value the whole wave holds, in scalar registers (a store to
+// base + uniform + lane then takes a scalar base and a 32-bit lane offset)
+__device__ __forceinline__ uint64_t uniform64(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
 
-// emit: tags from each chunk's start state; every field's record, column,
+// Per-wave list of the wave's terminators (LDS): entry = position within the
+// super-tile << 1 | record-delimiter bit, in field order.
+constexpr int kWaveList = 1024;
+
+// emit: tags from each span's start state; every field's record, column,
 // offset and length; the last range writes the unterminated final field and
-// the result counts
+// the result counts.
+//
+// Fields are written by waves, 64 consecutive fields per round: each lane first
+// lists its terminators in the wave's LDS list, then lane l of a round takes
+// field r + l: its record and column follow from a ballot of the record bits
+// of the round's fields, its offset from the previous field's terminator (the
+// lane before, by DPP). The four output arrays are written with consecutive
+// addresses across the lanes.
 template <int CB, bool V8>
 __global__ void __launch_bounds__(kFastBlock) csv_emit_kernel(FastParams p)
 {
     using Gm = Geo<CB>;
-    constexpr int NI = Gm::NI;
     __shared__ Pass2Shared<V8, Gm::E> sh;
-    __shared__ TCarry s_wc[2][kFastWaves];
+    __shared__ GCarry s_wc[2][kFastWaves];
     __shared__ GCarry s_wg[kFastWaves];
-    __shared__ uint32_t s_stage[4][kStage];
+    __shared__ uint32_t s_list[kFastWaves][kWaveList];
 
-    const int tid = threadIdx.x;
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t wv = threadIdx.x / kWave;
     const uint32_t b = blockIdx.x;
-    uint32_t t0, t1;
-    range_of(p, b, t0, t1);
-    uint32_t tile = t0;
-    ChunkPos c = chunk_pos(p.n, tile);
-    IdxIn<CB, V8> in = load_in<CB, V8>(p, c);
-    uint64_t tv = p.tile_vec[tile];
+    uint32_t s0, s1;
+    range_of(p, b, s0, s1);
+    const Vec ident = fast_ident<V8>(p.nt);
     uint32_t run = p.range_state[b];
-    const uint32_t nt = p.nt;
     const OutArrays& o = p.out;
+    uint32_t* list = s_list[wv];
     load_pass2<CB, V8>(p, sh);
     const GCarryComb gcomb;
     // the input starts at column 0 of record 0: an absolute zero column offset
     GCarry P = gcomb(GCarry{0u, 0u, 0x80000000u, 0u}, carries_before(p, b, s_wg));  // (its barrier publishes sh)
 
-    for (uint32_t it = 0;; ++it) {
-        const uint32_t next = tile + 1;
-        const ChunkPos cn = chunk_pos(p.n, next < t1 ? next : tile);
-        IdxIn<CB, V8> inn;
-        uint64_t tvn = 0;
-        if (next < t1) {
-            inn = load_in<CB, V8>(p, cn);
-            tvn = p.tile_vec[next];
-        }
+    auto step = [&](auto full_tag, uint32_t st, const IdxIn<CB, V8>& in, uint32_t it) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const PairPos c = pair_pos(p, st);
+        Vec v0, v1;
+        super_vecs<V8>(p, st, in.tvl, ident, v0, v1);
+        const uint32_t ts1 = vat(v0, run);
+        uint64_t T[2], RD[2];
+        span_tags<CB, V8, FULL>(p, c, in, run, ts1, sh, T, RD, nullptr);
+        const SpanCarry sc = span_carry(T, RD, c.abs, s_wc[it & 1]);
 
-        const uint32_t s = vat(Vec{in.cvlo, in.cvhi}, run);
-        uint64_t T = 0, RD = 0;
-        if (c.full) {
-            uint32_t idx[NI];
-            unpack_idx<CB, V8>(in, idx);
-            pass2_full<CB>(idx, s, nt, sh.t2, T, RD);
-        } else if (c.my_len) {
-            uint32_t err = kNone;
-            pass2_ragged<CB>(p, c, s, nt, sh.nxt, sh.tag, T, RD, err);
-        }
-        TCarry cex, ctot;
-        block_scan<kFastWaves>(chunk_carry(T, RD, c.chunk_abs), TCarry{0, 0, 0}, cex, ctot, s_wc[it & 1],
-                               TCarryComb{});
-
-        const uint32_t first = cex.nfr & 0xffffu, mine = (uint32_t)__popcll(T), tile_nf = ctot.nfr & 0xffffu;
-        for (uint32_t r0 = 0; r0 < tile_nf; r0 += kStage) {
-            const uint32_t r1 = min(r0 + (uint32_t)kStage, tile_nf);
-            if (mine && first < r1 && first + mine > r0) {
-                uint32_t li = first, rec = P.nr + (cex.nfr >> 16);
-                uint32_t col = col_op(P.col, cex.col) & 0x7fffffffu;
-                uint32_t off = max(P.lt, cex.lt);
-                uint64_t bits = T;
-                while (bits && li < r1) {
-                    const uint32_t j = (uint32_t)__ffsll((unsigned long long)bits) - 1u;
-                    const uint32_t pos = c.chunk_abs + j;
-                    if (li >= r0) {
-                        s_stage[0][li - r0] = rec;
-                        s_stage[1][li - r0] = col;
-                        s_stage[2][li - r0] = off;
-                        s_stage[3][li - r0] = pos - off;
+        // the wave's fields: super-tile-local indices [wfirst, wend); the state at its first field
+        const uint32_t mine = sc.mine, first = sc.wave_excl.nf + sc.excl_nf;
+        const uint32_t wfirst = sc.wave_excl.nf;
+        const uint32_t wend = __builtin_amdgcn_readlane(first + mine, kWave - 1);
+        uint32_t rec_run = P.nr + sc.wave_excl.nr;
+        uint32_t col_run = col_op(P.col, sc.wave_excl.col) & 0x7fffffffu;
+        uint32_t off_run = max(P.lt, sc.wave_excl.lt);
+        const uint32_t st_abs = st * (uint32_t)(2 * kFastTile);
+        const uint32_t rel0 = c.abs - st_abs;
+        for (uint32_t w0 = wfirst; w0 < wend; w0 += kWaveList) {
+            const uint32_t w1 = min(w0 + (uint32_t)kWaveList, wend);
+            // (1) each lane lists its terminators that fall in [w0, w1)
+            if (mine && first < w1 && first + mine > w0) {
+                uint32_t li = first;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    uint32_t bits = (uint32_t)(T[q >> 1] >> (32 * (q & 1)));
+                    const uint32_t rdw = (uint32_t)(RD[q >> 1] >> (32 * (q & 1)));
+                    while (bits && li < w1) {
+                        const uint32_t j = (uint32_t)__builtin_ctz(bits);
+                        if (li >= w0) list[li - w0] = ((rel0 + 32u * q + j) << 1) | ((rdw >> j) & 1u);
+                        ++li;
+                        bits &= bits - 1u;
                     }
-                    ++li;
-                    off = pos + 1;
-                    if ((RD >> j) & 1u) {
-                        ++rec;
-                        col = 0;
-                    } else {
-                        ++col;
-                    }
-                    bits &= bits - 1;
                 }
             }
-            __syncthreads();
-            const uint64_t g0 = (uint64_t)P.nf + r0;
-            for (uint32_t i = tid; i < r1 - r0; i += kFastBlock) {
-                const uint64_t gi = g0 + i;
-                if (gi < o.cap) {
-                    o.rec[gi] = s_stage[0][i];
-                    o.col[gi] = s_stage[1][i];
-                    o.off[gi] = s_stage[2][i];
-                    o.len[gi] = s_stage[3][i];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // (2) rounds of 64 fields: the round's output slices are uniform base pointers,
+            // each lane stores at its own 4-byte offset
+            for (uint32_t r = w0; r < w1; r += kWave) {
+                const uint32_t cnt = min((uint32_t)kWave, w1 - r);
+                const uint32_t e = list[r - w0 + min(lane, cnt - 1u)];
+                const uint32_t pos = st_abs + (e >> 1);
+                const uint64_t m = __ballot(lane < cnt && (e & 1u));
+                const uint64_t below = m & ((1ull << lane) - 1ull);
+                const uint32_t rec = rec_run + (uint32_t)__popcll(below);
+                const uint32_t col =
+                    below ? lane - (uint32_t)(63 - __clzll((long long)below)) - 1u : col_run + lane;
+                const uint32_t prev = dpp_t<0x138, 0xf>(0u, pos);  // wave_shr:1: the previous lane's terminator
+                const uint32_t off = lane ? prev + 1u : off_run;
+                const uint64_t g0 = uniform64((uint64_t)P.nf + r);
+                const uint32_t room = g0 < o.cap ? (uint32_t)min<uint64_t>(o.cap - g0, (uint64_t)cnt) : 0u;
+                if (lane < room) {
+                    (o.rec + g0)[lane] = rec;
+                    (o.col + g0)[lane] = col;
+                    (o.off + g0)[lane] = off;
+                    (o.len + g0)[lane] = pos - off;
                 }
+                rec_run += (uint32_t)__popcll(m);
+                col_run = m ? (cnt - 1u) - (uint32_t)(63 - __clzll((long long)m)) : col_run + cnt;
+                off_run = __builtin_amdgcn_readlane(pos, cnt - 1) + 1u;
             }
-            __syncthreads();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-        P = gcomb(P, GCarry{ctot.nfr & 0xffffu, ctot.nfr >> 16, ctot.col, ctot.lt});
-        run = vat(unpack_vec(tv), run);
-
-        if (next >= t1) break;
-        tile = next;
-        c = cn;
-        in = inn;
-        tv = tvn;
-    }
-    if (tid == 0 && b == p.num_ranges - 1) {
+        P = gcomb(P, sc.total);
+        run = vat(v1, ts1);
+    };
+    walk_supers<CB, V8>(
+        p, s0, s1, [&](uint32_t st, const IdxIn<CB, V8>& in, uint32_t it) { step(std::true_type{}, st, in, it); },
+        [&](uint32_t st, const IdxIn<CB, V8>& in, uint32_t it) { step(std::false_type{}, st, in, it); });
+    if (threadIdx.x == 0 && b == p.num_ranges - 1) {
         const uint32_t final_field = p.hdr->last_rec ? 0u : 1u;
         if (final_field && P.nf < o.cap) {
             o.rec[P.nf] = P.nr;
@@ -703,6 +861,9 @@ __global__ void __launch_bounds__(kFastBlock) csv_emit_kernel(FastParams p)
     }
 }
 
+// workgroups of the codes kernel (all resident at once: 4 per CU)
+constexpr uint32_t kCodesGrid = 1024;
+
 template <int CB, bool V8>
 static void launch(const FastParams& f, const ppr_parse_opts_t* o, hipStream_t s)
 {
@@ -710,7 +871,8 @@ static void launch(const FastParams& f, const ppr_parse_opts_t* o, hipStream_t s
     stage_event(o, 0, s);
     hipLaunchKernelGGL((csv_fast_tables_kernel<CB, V8>), dim3(1), dim3(256), 0, s, f);
     stage_event(o, 1, s);
-    hipLaunchKernelGGL((csv_codes_kernel<CB, V8>), grid, block, 0, s, f);
+    hipLaunchKernelGGL((csv_codes_kernel<CB, V8>), dim3(std::min<uint32_t>(f.num_tiles, kCodesGrid)), block, 0, s, f);
+    hipLaunchKernelGGL((csv_range_vec_kernel<V8>), grid, dim3(kWave), 0, s, f);
     stage_event(o, 2, s);
     hipLaunchKernelGGL((csv_carries_kernel<CB, V8>), grid, block, 0, s, f);
     stage_event(o, 3, s);
