@@ -249,19 +249,16 @@ __device__ __forceinline__ uint32_t pass2_pair(const uint32_t (&pw)[2 * Geo<CB>:
     uint32_t row = min(s, nt) * (uint32_t)(E * 4);
     uint32_t any = 0;
     if constexpr (G == 4) {
-        // the tag byte (bits 16-23) of four consecutive entries gathered into one word;
-        // the four index bytes of pw[q] spread into two words of 16-bit halves times 4
-        // (byte offsets), so that each step's address is one add of two halves
+        // the tag byte (bits 16-23) of four consecutive entries gathered into one word
         uint32_t w[NG / 4];
 #pragma unroll
         for (int q = 0; q < NG / 4; ++q) {
-            const uint32_t x01 = perm(0u, pw[q], 0x0c010c00u) << 2, x23 = perm(0u, pw[q], 0x0c030c02u) << 2;
-            const uint32_t off[4] = {x01 & 0xffffu, x01 >> 16, x23 & 0xffffu, x23 >> 16};
             uint32_t e[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                e[i] = *reinterpret_cast<const uint32_t*>(base + (row & kRowMask) + off[i]);
-                row = e[i];
+                const uint32_t ix = (pw[q] >> (8 * i)) & 0xffu;
+                e[i] = *reinterpret_cast<const uint32_t*>(base + row + ix * 4u);
+                row = e[i] & kRowMask;
                 any |= e[i];
             }
             w[q] = perm(e[1], e[0], 0x0c0c0602u) | perm(e[3], e[2], 0x06020c0cu);
