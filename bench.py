@@ -10,6 +10,7 @@ emission, scalar read-back), with the input already resident in HBM and the
 output buffers preallocated.
 
     python bench.py [--steps K] [--warmup W] [--workload csv3|csv1|csv2|csv4|lex5] [--chunk L]
+                    [--path auto|fused|streaming|single-pass]
 
 Prints one JSON line. Two more modes serve the counter-based traffic figure:
 
@@ -43,6 +44,7 @@ COPY_BYTES = 1 << 30
 # the first and after each one)
 STAGES = {1: ["csv_fast_tables_kernel", "csv_codes_kernel", "csv_carries_kernel", "csv_emit_kernel"],
           2: ["csv_reset_kernel", "csv_generic_kernel"],
+          3: ["csv_fast_tables_kernel", "csv_fused_kernel"],
           "lex": ["lex_reset_kernel", "lex_kernel"]}
 
 
@@ -70,7 +72,7 @@ def algorithmic_bytes(stage, n, n_out, out_bytes_per_item):
         return n
     if stage in ("csv_emit_kernel",):
         return out_bytes_per_item * n_out
-    if stage in ("csv_generic_kernel", "lex_kernel"):
+    if stage in ("csv_generic_kernel", "csv_fused_kernel", "lex_kernel"):
         return n + out_bytes_per_item * n_out
     return 0
 
@@ -198,6 +200,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="csv3", choices=sorted(WORKLOADS))
     ap.add_argument("--chunk", type=int, default=None, help="bytes per thread (default: the library's, 64)")
+    ap.add_argument("--path", choices=["auto", "fused", "streaming", "single-pass"], default="auto",
+                    help="parse kernels to ask the library for (default: its automatic choice)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline and the full-size parity check")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -233,7 +237,9 @@ def main():
 
     if kind == "csv":
         table = W.table(cfg["table"])
-        runner = ppr.Parser(table, max_n=n, capacity=max(4096, n // 8), chunk_bytes=chunk, device=dev)
+        want = {"auto": None, "fused": ppr.PPR_PATH_FUSED, "streaming": ppr.PPR_PATH_STREAMING,
+                "single-pass": ppr.PPR_PATH_SINGLE_PASS}[args.path]
+        runner = ppr.Parser(table, max_n=n, capacity=max(4096, n // 8), chunk_bytes=chunk, device=dev, path=want)
         first = runner(d)
         runner._alloc(first.n_fields)
         n_out, path = first.n_fields, first.path

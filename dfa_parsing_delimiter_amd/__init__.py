@@ -30,7 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PPR_LIB_PATH") or os.path.join(_HERE, "libppr.so")
 
 PPR_OK, PPR_EINVAL, PPR_ECAPACITY, PPR_ETOOBIG, PPR_EHIP, PPR_EWORKSPACE = 0, -1, -2, -3, -4, -5
-PPR_PATH_STREAMING, PPR_PATH_SINGLE_PASS = 1, 2
+PPR_PATH_STREAMING, PPR_PATH_SINGLE_PASS, PPR_PATH_FUSED = 1, 2, 3
 _ERRNAMES = {-1: "PPR_EINVAL", -2: "PPR_ECAPACITY", -3: "PPR_ETOOBIG", -4: "PPR_EHIP", -5: "PPR_EWORKSPACE"}
 TAG_VALUE, TAG_FIELD, TAG_RECORD, TAG_INVALID = 0, 1, 2, 3
 
@@ -56,7 +56,7 @@ class ParseOut(ctypes.Structure):
 
 class ParseOpts(ctypes.Structure):
     _fields_ = [("chunk_bytes", ctypes.c_uint32), ("n_stage_events", ctypes.c_uint32),
-                ("stage_events", ctypes.c_void_p)]
+                ("stage_events", ctypes.c_void_p), ("path", ctypes.c_uint32)]
 
 
 class LexTablesC(ctypes.Structure):
@@ -124,9 +124,10 @@ def _stream_handle(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _opts(chunk_bytes):
+def _opts(chunk_bytes, path=None):
     o = ParseOpts()
     o.chunk_bytes = int(chunk_bytes or 0)
+    o.path = int(path or 0)
     return o
 
 
@@ -135,6 +136,7 @@ def _opts_with_events(opts, events):
     objects between the call's kernels; returns (opts, the handle array to keep alive)."""
     o = ParseOpts()
     o.chunk_bytes = opts.chunk_bytes
+    o.path = opts.path
     if not events:
         return o, None
     handles = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
@@ -177,16 +179,16 @@ class ParseResult:
     n_records: int
     error_pos: int
     end_state: int
-    path: int                    # PPR_PATH_STREAMING or PPR_PATH_SINGLE_PASS
+    path: int                    # the kernels that ran: a PPR_PATH_* value
 
 
 class Parser:
     """Reusable workspace and output buffers for inputs of up to max_n bytes."""
 
     def __init__(self, table: dict, max_n: int, capacity: int | None = None, chunk_bytes: int | None = None,
-                 device=None):
+                 device=None, path: int | None = None):
         self.dfa, self.class_map = make_dfa(table)
-        self.opts = _opts(chunk_bytes)
+        self.opts = _opts(chunk_bytes, path)
         self.device = torch.device("cuda") if device is None else torch.device(device)
         self.max_n = int(max_n)
         ws = lib.ppr_parse_workspace_bytes(self.max_n, ctypes.byref(self.opts))
@@ -253,12 +255,13 @@ class Parser:
 
 
 def parse(data: torch.Tensor, table: dict, chunk_bytes: int | None = None, capacity: int | None = None,
-          stream=None) -> ParseResult:
-    """Parse one input (device uint8 tensor) with a DFA table."""
+          stream=None, path: int | None = None) -> ParseResult:
+    """Parse one input (device uint8 tensor) with a DFA table; path: a
+    PPR_PATH_* value to ask for (None: the library's automatic choice)."""
     _check_input(data)
     n = data.numel()
     cap = capacity if capacity is not None else min(n + 1, max(4096, n // 4))
-    return Parser(table, n, cap, chunk_bytes, data.device)(data, stream)
+    return Parser(table, n, cap, chunk_bytes, data.device, path)(data, stream)
 
 
 # ------------------------------------------------------------------ lexer

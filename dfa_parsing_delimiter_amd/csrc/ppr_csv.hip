@@ -341,6 +341,9 @@ static int validate_dfa(const ppr_dfa_t* d, const uint8_t* cm)
     return PPR_OK;
 }
 
+// the table-driven path an automatic choice takes (the faster one on MI355X)
+constexpr uint32_t kDefaultTablePath = PPR_PATH_STREAMING;
+
 static uint32_t chunk_of(const ppr_parse_opts_t* o)
 {
     uint32_t L = o ? o->chunk_bytes : 0u;
@@ -501,8 +504,10 @@ extern "C" int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa
     const uint32_t accept = dfa->accept_mask & ((1u << dfa->n_states) - 1u);
     OutArrays oa{out->record_idx, out->column_ids, out->field_offsets, out->field_lengths, out->cap_fields};
 
-    // streaming path: 64-byte chunks, 16-byte aligned input, a table it can encode
-    if (n && L == (uint32_t)kFastChunk && ((uintptr_t)d_bytes & 15u) == 0) {
+    const uint32_t want = opts ? opts->path : 0u;
+    if (want > PPR_PATH_FUSED) return PPR_EINVAL;
+    // table-driven paths: 64-byte chunks, 16-byte aligned input, a table they can encode
+    if (n && want != PPR_PATH_SINGLE_PASS && L == (uint32_t)kFastChunk && ((uintptr_t)d_bytes & 15u) == 0) {
         FastParams f;
         memset(&f, 0, sizeof f);
         int cb = 0;
@@ -525,6 +530,10 @@ extern "C" int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa
             f.range_vec = (uint64_t*)(ws + fl.range_vec);
             f.range_state = (uint32_t*)(ws + fl.range_state);
             f.range_carry = (uint4*)(ws + fl.range_carry);
+            f.stat_vec = (uint64_t*)(ws + fl.stat_vec);
+            f.stat_carry = (StatB*)(ws + fl.stat_carry);
+            f.epoch = next_epoch();
+            f.path = want == PPR_PATH_STREAMING || want == PPR_PATH_FUSED ? want : kDefaultTablePath;
             return launch_csv_fast(f, cb, v8, opts, s);
         }
     }

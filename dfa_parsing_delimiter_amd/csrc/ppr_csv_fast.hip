@@ -86,21 +86,23 @@ struct SpanCarry {
     GCarry total;      // carry of the whole tile
 };
 
-__device__ __forceinline__ SpanCarry span_carry(const uint64_t (&T)[2], const uint64_t (&RD)[2], uint32_t abs,
+template <int NCH>
+__device__ __forceinline__ SpanCarry span_carry(const uint64_t (&T)[NCH], const uint64_t (&RD)[NCH], uint32_t abs,
                                                 GCarry* s_wave)
 {
-    const uint32_t n0 = (uint32_t)__popcll(T[0]), n1 = (uint32_t)__popcll(T[1]);
-    const uint32_t nf = n0 + n1, nr = (uint32_t)(__popcll(RD[0]) + __popcll(RD[1]));
-    uint32_t lt = 0, rdl = 0;
-    if (T[1]) lt = abs + kFastChunk + (uint32_t)(63 - __clzll((long long)T[1])) + 1u;
-    else if (T[0]) lt = abs + (uint32_t)(63 - __clzll((long long)T[0])) + 1u;
-    if (RD[1]) {
-        const int h = 63 - __clzll((long long)RD[1]);
-        rdl = n0 + (uint32_t)__popcll(T[1] & (h == 63 ? ~0ull : ((2ull << h) - 1ull)));
-    } else if (RD[0]) {
-        const int h = 63 - __clzll((long long)RD[0]);
-        rdl = (uint32_t)__popcll(T[0] & (h == 63 ? ~0ull : ((2ull << h) - 1ull)));
+    uint32_t nf = 0, nr = 0, lt = 0, rdl = 0, before = 0;
+#pragma unroll
+    for (int h = 0; h < NCH; ++h) {
+        const uint32_t nh = (uint32_t)__popcll(T[h]);
+        nr += (uint32_t)__popcll(RD[h]);
+        if (T[h]) lt = abs + (uint32_t)(kFastChunk * h) + (uint32_t)(63 - __clzll((long long)T[h])) + 1u;
+        if (RD[h]) {
+            const int hb = 63 - __clzll((long long)RD[h]);
+            rdl = before + (uint32_t)__popcll(T[h] & (hb == 63 ? ~0ull : ((2ull << hb) - 1ull)));
+        }
+        before += nh;
     }
+    nf = before;
     const uint32_t inc = wave_scan(nf | (nr << 16), 0u, AddComb{});
     const uint32_t excl = wave_shr1(0u, inc);
     const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane(inc, kWave - 1);
@@ -136,6 +138,29 @@ __device__ __forceinline__ uint32_t classify4(uint32_t w, const FastParams& p)
     const uint32_t t = (((d & 0x7f7f7f7fu) + 0x7f7f7f7fu) | d) & 0x80808080u;  // 0x80: not a special byte
     const uint32_t x = t >> 7;
     return c | ((x << CB) - x);
+}
+
+// the group indices of a full chunk (one byte per group of G symbol codes:
+// c0 + 4 c1 + 16 c2 + 64 c3, or c0 + 2^CB c1), also packed four per word
+template <int CB>
+__device__ __forceinline__ void chunk_codes(const uint32_t (&w)[Geo<CB>::ND], const FastParams& p,
+                                            uint32_t (&idx)[Geo<CB>::NI], uint32_t (&pw)[Geo<CB>::NP])
+{
+    using Gm = Geo<CB>;
+#pragma unroll
+    for (int k = 0; k < Gm::ND; ++k) {
+        const uint32_t code = classify4<CB>(w[k], p);
+        if constexpr (Gm::G == 4) {
+            idx[k] = __builtin_amdgcn_udot4(code, 0x40100401u, 0u, false);
+        } else {
+            constexpr uint32_t W = 1u << CB;
+            idx[2 * k] = __builtin_amdgcn_udot4(code, 0x00000001u | (W << 8), 0u, false);
+            idx[2 * k + 1] = __builtin_amdgcn_udot4(code, 0x00010000u | (W << 24), 0u, false);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < Gm::NP; ++q)
+        pw[q] = idx[4 * q] | (idx[4 * q + 1] << 8) | (idx[4 * q + 2] << 16) | (idx[4 * q + 3] << 24);
 }
 
 // identity vector over the tracked state codes; the rest is absorbing
@@ -234,16 +259,16 @@ __device__ __forceinline__ void nibbles_to_bits(uint32_t w0, uint32_t w1, uint32
     r32 = perm(r1, r0, 0x06040200u);
 }
 
-// Pass 2 over a thread's span of two full chunks (2 NI groups, packed four
-// index bytes per word in pw) from state code s: a chain of pass-2 lookups, one
-// per group, each addressed by the previous entry's row offset. T[h] / RD[h]:
-// terminator / record bitmaps of chunk h (bit j = byte j). Returns the OR of
-// the entries (bit 31: some byte is INVALID).
-template <int CB>
-__device__ __forceinline__ uint32_t pass2_pair(const uint32_t (&pw)[2 * Geo<CB>::NP], uint32_t s, uint32_t nt,
-                                               const uint32_t* s_t2, uint64_t (&T)[2], uint64_t (&RD)[2])
+// Pass 2 over NCH consecutive full chunks of a thread (NCH NI groups, packed
+// four index bytes per word in pw) from state code s: a chain of pass-2
+// lookups, one per group, each addressed by the previous entry's row offset.
+// T[h] / RD[h]: terminator / record bitmaps of chunk h (bit j = byte j).
+// Returns the OR of the entries (bit 31: some byte is INVALID).
+template <int CB, int NCH>
+__device__ __forceinline__ uint32_t pass2_run(const uint32_t (&pw)[NCH * Geo<CB>::NP], uint32_t s, uint32_t nt,
+                                              const uint32_t* s_t2, uint64_t (&T)[NCH], uint64_t (&RD)[NCH])
 {
-    constexpr int E = Geo<CB>::E, NG = 2 * Geo<CB>::NI, G = Geo<CB>::G;
+    constexpr int E = Geo<CB>::E, NG = NCH * Geo<CB>::NI, G = Geo<CB>::G;
     constexpr uint32_t GM = Geo<CB>::GM;
     const char* base = reinterpret_cast<const char*>(s_t2);
     uint32_t row = min(s, nt) * (uint32_t)(E * 4);
@@ -264,7 +289,7 @@ __device__ __forceinline__ uint32_t pass2_pair(const uint32_t (&pw)[2 * Geo<CB>:
             w[q] = perm(e[1], e[0], 0x0c0c0602u) | perm(e[3], e[2], 0x06020c0cu);
         }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < NCH; ++h) {
             uint32_t tl, th, rl, rh;
             nibbles_to_bits(w[4 * h], w[4 * h + 1], tl, rl);
             nibbles_to_bits(w[4 * h + 2], w[4 * h + 3], th, rh);
@@ -272,7 +297,9 @@ __device__ __forceinline__ uint32_t pass2_pair(const uint32_t (&pw)[2 * Geo<CB>:
             RD[h] = (uint64_t)rl | ((uint64_t)rh << 32);
         }
     } else {
-        uint32_t tw[4] = {0u, 0u, 0u, 0u}, rw[4] = {0u, 0u, 0u, 0u};
+        uint32_t tw[2 * NCH], rw[2 * NCH];
+#pragma unroll
+        for (int i = 0; i < 2 * NCH; ++i) tw[i] = rw[i] = 0u;
 #pragma unroll
         for (int k = 0; k < NG; ++k) {
             const uint32_t ix = (pw[k / 4] >> (8 * (k % 4))) & 0xffu;
@@ -283,7 +310,7 @@ __device__ __forceinline__ uint32_t pass2_pair(const uint32_t (&pw)[2 * Geo<CB>:
             rw[(G * k) / 32] |= ((e >> 20) & GM) << ((G * k) % 32);
         }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < NCH; ++h) {
             T[h] = (uint64_t)tw[2 * h] | ((uint64_t)tw[2 * h + 1] << 32);
             RD[h] = (uint64_t)rw[2 * h] | ((uint64_t)rw[2 * h + 1] << 32);
         }
@@ -291,12 +318,19 @@ __device__ __forceinline__ uint32_t pass2_pair(const uint32_t (&pw)[2 * Geo<CB>:
     return any;
 }
 
-// position of the first INVALID byte of a full two-chunk span known to hold one
 template <int CB>
-__device__ uint32_t first_invalid(const uint32_t (&pw)[2 * Geo<CB>::NP], uint32_t s, uint32_t nt,
+__device__ __forceinline__ uint32_t pass2_pair(const uint32_t (&pw)[2 * Geo<CB>::NP], uint32_t s, uint32_t nt,
+                                               const uint32_t* s_t2, uint64_t (&T)[2], uint64_t (&RD)[2])
+{
+    return pass2_run<CB, 2>(pw, s, nt, s_t2, T, RD);
+}
+
+// position of the first INVALID byte of NCH full chunks known to hold one
+template <int CB, int NCH>
+__device__ uint32_t first_invalid(const uint32_t (&pw)[NCH * Geo<CB>::NP], uint32_t s, uint32_t nt,
                                   const uint32_t* s_t2, uint32_t abs)
 {
-    constexpr int E = Geo<CB>::E, NG = 2 * Geo<CB>::NI, G = Geo<CB>::G;
+    constexpr int E = Geo<CB>::E, NG = NCH * Geo<CB>::NI, G = Geo<CB>::G;
     const char* base = reinterpret_cast<const char*>(s_t2);
     uint32_t row = min(s, nt) * (uint32_t)(E * 4), first = kNone;
 #pragma unroll
@@ -402,7 +436,7 @@ __global__ void csv_fast_tables_kernel(FastParams p)
         p.hdr->fault = 0;
         p.hdr->err_min = kNone;
         p.hdr->last_rec = 0;
-        p.hdr->path = PPR_PATH_STREAMING;
+        p.hdr->path = p.path;
     }
     __syncthreads();
     uint32_t* tabs = p.tabs;
@@ -519,22 +553,8 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
 
     // classify, store the indices, the chunk's vector
     auto full_chunk = [&](uint32_t tile, const uint32_t (&wc)[ND]) {
-        uint32_t idx[NI];
-#pragma unroll
-        for (int k = 0; k < ND; ++k) {
-            const uint32_t code = classify4<CB>(wc[k], p);
-            if constexpr (Gm::G == 4) {
-                idx[k] = __builtin_amdgcn_udot4(code, 0x40100401u, 0u, false);
-            } else {
-                constexpr uint32_t W = 1u << CB;
-                idx[2 * k] = __builtin_amdgcn_udot4(code, 0x00000001u | (W << 8), 0u, false);
-                idx[2 * k + 1] = __builtin_amdgcn_udot4(code, 0x00010000u | (W << 24), 0u, false);
-            }
-        }
-        uint32_t pw[NP];
-#pragma unroll
-        for (int q = 0; q < NP; ++q)
-            pw[q] = idx[4 * q] | (idx[4 * q + 1] << 8) | (idx[4 * q + 2] << 16) | (idx[4 * q + 3] << 24);
+        uint32_t idx[NI], pw[NP];
+        chunk_codes<CB>(wc, p, idx, pw);
         uint4* dst = reinterpret_cast<uint4*>(p.idx + ((size_t)tile * kFastBlock + tid) * NI);
 #pragma unroll
         for (int q = 0; q < NP / 4; ++q)
@@ -645,7 +665,7 @@ __device__ __forceinline__ void span_tags(const FastParams& p, const PairPos& c,
     T[0] = T[1] = RD[0] = RD[1] = 0;
     if (FULL || c.full) {
         const uint32_t any = pass2_pair<CB>(in.pw, s, nt, sh.t2, T, RD);
-        if (err && (any >> 31)) *err = first_invalid<CB>(in.pw, s, nt, sh.t2, c.abs);
+        if (err && (any >> 31)) *err = first_invalid<CB, 2>(in.pw, s, nt, sh.t2, c.abs);
     } else if (c.my_len) {
         uint32_t e = kNone;
         pass2_ragged<CB>(p, c, s, nt, sh.nxt, sh.tag, T, RD, e);
@@ -858,6 +878,352 @@ __global__ void __launch_bounds__(kFastBlock) csv_emit_kernel(FastParams p)
     }
 }
 
+// ================================================================ fused single pass
+//
+// One kernel runs every step of the method per 32 KiB tile: classify, the
+// chunk vectors and their block scan, the tile's start state by a decoupled
+// look-back over the tile vectors, pass 2 from each chunk's start state, the
+// block scan of the count carries, the tile's count prefix by a second
+// look-back, and the field emission. The input is read once and the fields are
+// written once; nothing per byte or per chunk goes to memory.
+//
+// Workgroups are persistent and take tiles in increasing order from an atomic
+// counter, so a tile only ever waits for tiles that running workgroups already
+// hold, and a workgroup never waits for one that is not resident.
+//
+// Each workgroup runs a three-stage software pipeline over its tiles. One
+// round does phase 1 of its newest tile (classify, chunk vectors, block scan,
+// publish the tile's vector aggregate), phase 2 of the previous one (vector
+// look-back, pass 2, count carries, publish their aggregate) and phase 3 of the
+// one before (count look-back, fields). A look-back thus reads statuses that
+// were published about a round earlier, instead of waiting for tiles that
+// started at the same time; and a tile's aggregate is published right after it
+// is taken, never behind a wait, so waits do not feed back into later tiles.
+
+// Count-carry statuses. Aggregate (tile-local): nf | nr << 16 (a 32 KiB tile
+// has at most 2^15 of each), col (bit 31: absolute), lt. Inclusive prefix: nf,
+// nr, col, lt, all absolute.
+__device__ __forceinline__ void publish_gagg(StatB& s, const GCarry& c, uint32_t epoch)
+{
+    st_relaxed(&s.agg[0], ew(epoch, c.nf | (c.nr << 16)));
+    st_relaxed(&s.agg[1], ew(epoch, c.col));
+    st_relaxed(&s.agg[2], ew(epoch, c.lt));
+}
+__device__ __forceinline__ void publish_gincl(StatB& s, const GCarry& c, uint32_t epoch)
+{
+    st_relaxed(&s.incl[0], ew(epoch, c.nf));
+    st_relaxed(&s.incl[1], ew(epoch, c.nr));
+    st_relaxed(&s.incl[2], ew(epoch, c.col));
+    st_relaxed(&s.incl[3], ew(epoch, c.lt));
+}
+
+// count-carry status of one tile: the seven words are loaded at once
+struct GCarryPoll {
+    const StatB* stat;
+    uint32_t epoch;
+    struct Raw {
+        uint64_t i[4], a[3];
+    };
+    __device__ __forceinline__ Raw load(int64_t u) const
+    {
+        const StatB& s = stat[u];
+        Raw r;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r.i[k] = ld_relaxed(&s.incl[k]);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) r.a[k] = ld_relaxed(&s.agg[k]);
+        return r;
+    }
+    __device__ __forceinline__ uint32_t decode(const Raw& r, GCarry& out) const
+    {
+        if (ew_ok(r.i[0], epoch) && ew_ok(r.i[1], epoch) && ew_ok(r.i[2], epoch) && ew_ok(r.i[3], epoch)) {
+            out = {(uint32_t)r.i[0], (uint32_t)r.i[1], (uint32_t)r.i[2], (uint32_t)r.i[3]};
+            return kFlagIncl;
+        }
+        if (ew_ok(r.a[0], epoch) && ew_ok(r.a[1], epoch) && ew_ok(r.a[2], epoch)) {
+            const uint32_t x0 = (uint32_t)r.a[0];
+            out = {x0 & 0xffffu, x0 >> 16, (uint32_t)r.a[1], (uint32_t)r.a[2]};
+            return kFlagAgg;
+        }
+        return 0;
+    }
+};
+
+// Vector statuses: the aggregate is the tile's packed vector, the inclusive
+// prefix the state after the tile, read back as a constant vector.
+struct FVecPoll {
+    const uint64_t* stat;
+    uint32_t epoch;
+    using Raw = uint64_t;
+    __device__ __forceinline__ Raw load(int64_t u) const { return ld_relaxed(&stat[u]); }
+    __device__ __forceinline__ uint32_t decode(Raw w, Vec& out) const
+    {
+        const uint32_t f = status_flag(w, epoch);
+        if (f == kFlagAgg) out = vunpack(status_payload(w));
+        if (f == kFlagIncl) {
+            const uint32_t k = status_payload(w) * 0x01010101u;
+            out = {k, k};
+        }
+        return f;
+    }
+};
+
+// pass 2 over a ragged chunk (the input's last bytes), one byte at a time
+template <int CB>
+__device__ void pass2_ragged_chunk(const FastParams& p, const ChunkPos& c, uint32_t s, uint32_t nt,
+                                   const uint8_t* s_nxt, const uint8_t* s_tag, uint64_t& T, uint64_t& RD,
+                                   uint32_t& err)
+{
+    T = RD = 0;
+    for (uint32_t j = 0; j < c.my_len; ++j) {
+        const uint32_t code = classify4<CB>(p.in[c.chunk_abs + j] * 0x01010101u, p) & Geo<CB>::CM;
+        const uint32_t row = min(s, nt);
+        const uint32_t t = s_tag[row * 16 + code];
+        s = s_nxt[row * 16 + code];
+        T |= (uint64_t)(t == PPR_TAG_FIELD || t == PPR_TAG_RECORD) << j;
+        RD |= (uint64_t)(t == PPR_TAG_RECORD) << j;
+        if (t == PPR_TAG_INVALID && err == kNone) err = c.chunk_abs + j;
+    }
+}
+
+constexpr int kFusedList = 1024;  // per-wave terminator list entries (LDS)
+constexpr int kFusedWavesPerSimd = 4;  // 3 resident workgroups per CU: the register budget the kernel is cut to
+
+template <int CB, bool V8>
+struct FusedShared {
+    uint32_t t1[V8 ? 2 * Geo<CB>::E : Geo<CB>::E];
+    Pass2Shared<V8, Geo<CB>::E> p2;
+    Vec wv[kFastWaves];
+    Vec pv[kFastWaves];
+    GCarry wc[kFastWaves];
+    GCarry pc[kFastWaves];
+    int first[kFastWaves];
+    uint32_t next, state, last_rec;
+    uint32_t list[kFastWaves][kFusedList];
+};
+
+template <int CB, bool V8>
+__global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kernel(FastParams p)
+{
+    using Gm = Geo<CB>;
+    constexpr int NI = Gm::NI, ND = Gm::ND, NP = Gm::NP;
+    __shared__ FusedShared<CB, V8> sh;
+
+    const int tid = threadIdx.x;
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t wv = threadIdx.x / kWave;
+    const uint32_t nt = p.nt, num_tiles = p.num_tiles;
+    const OutArrays& o = p.out;
+    const GCarryComb gcomb;
+    const GCarry zero{0u, 0u, 0u, 0u};
+    if (tid == 0) {
+        sh.next = atomicAdd(&p.hdr->tile_counter, 1u);
+        sh.last_rec = 0;
+    }
+    for (int i = tid; i < (V8 ? 2 : 1) * Gm::E; i += kFastBlock) sh.t1[i] = p.tabs[i];
+    load_pass2<CB, V8>(p, sh.p2);
+    __syncthreads();
+    const Vec ident = fast_ident<V8>(nt);
+
+    // this thread's 64 bytes of a tile, if its chunk is full (16-byte loads)
+    auto load_chunk = [&](uint32_t t, uint32_t (&w)[ND]) {
+        const uint32_t pos = t * (uint32_t)kFastTile + (uint32_t)tid * (uint32_t)kFastChunk;
+        if (pos + (uint32_t)kFastChunk <= p.n) {
+            const uint4* src = reinterpret_cast<const uint4*>(p.in + pos);
+#pragma unroll
+            for (int q = 0; q < ND / 4; ++q) {
+                const uint4 x = src[q];
+                w[4 * q] = x.x;
+                w[4 * q + 1] = x.y;
+                w[4 * q + 2] = x.z;
+                w[4 * q + 3] = x.w;
+            }
+        }
+    };
+
+    // The pipeline: t0 in phase 1 (bytes loaded), t1 in phase 2, t2 in phase 3
+    // (num_tiles: no tile). Each tile's state is handed from phase to phase in
+    // registers.
+    uint32_t t0 = sh.next, t1 = num_tiles, t2 = num_tiles;
+    uint32_t w[ND];
+    if (t0 < num_tiles) load_chunk(t0, w);
+    uint32_t pw1[NP];  // phase 2 input: group indices, vector of the tile's earlier chunks, tile vector
+    Vec excl1 = ident, tot1 = ident;
+    uint64_t T2 = 0, RD2 = 0;  // phase 3 input: tag bitmaps, count carries, end state
+    SpanCarry sc2{0u, 0u, zero, zero};
+    uint32_t end2 = 0;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) pw1[q] = 0;
+
+    const FVecPoll vpoll{p.stat_vec, p.epoch};
+    const GCarryPoll cpoll{p.stat_carry, p.epoch};
+    while (t0 < num_tiles || t1 < num_tiles || t2 < num_tiles) {
+        // ---- phase 1 (tile t0): classify, chunk vectors, block scan, aggregate
+        uint32_t pw0[NP];
+#pragma unroll
+        for (int q = 0; q < NP; ++q) pw0[q] = 0;
+        Vec excl0 = ident, tot0 = ident;
+        uint32_t tn = num_tiles;
+        if (t0 < num_tiles) {
+            if (tid == 0) sh.next = atomicAdd(&p.hdr->tile_counter, 1u);  // read after the block scan's barrier
+            const ChunkPos c = chunk_pos(p.n, t0);
+            Vec v = ident;
+            if (c.full) {
+                uint32_t idx[NI];
+                chunk_codes<CB>(w, p, idx, pw0);
+                v = tree_vector<CB, V8>(idx, sh.t1);
+            } else if (c.my_len) {
+                v = ragged_vector<CB, V8>(p, c, ident, sh.p2.nxt);
+            }
+            block_scan<kFastWaves>(v, ident, excl0, tot0, sh.wv, VecComb<V8>{});
+            tn = sh.next;
+            if (tid == 0)
+                st_relaxed(&p.stat_vec[t0], t0 == 0 ? status_word(p.epoch, kFlagIncl, vat(tot0, p.start_code))
+                                                    : status_word(p.epoch, kFlagAgg, vpack(tot0)));
+        }
+
+        // ---- phase 2 (tile t1): start state, pass 2, count carries, their aggregate
+        uint64_t T1 = 0, RD1 = 0;
+        SpanCarry sc1{0u, 0u, zero, zero};
+        uint32_t end1 = 0;
+        if (t1 < num_tiles) {
+            if (t1 == 0) {
+                if (tid == 0) sh.state = p.start_code;
+            } else {
+                const Vec acc = lookback_pre<kFastWaves>(t1, ident, vpoll, VecComb<V8>{}, sh.pv, sh.first,
+                                                         &p.hdr->fault, look_first<kFastWaves>(t1, vpoll));
+                if (tid == 0) {
+                    const uint32_t st = vat(acc, 0);  // a constant vector: the state after all earlier tiles
+                    sh.state = st;
+                    st_relaxed(&p.stat_vec[t1], status_word(p.epoch, kFlagIncl, vat(tot1, st)));
+                }
+            }
+            __syncthreads();
+            const uint32_t ts = sh.state;
+            end1 = vat(tot1, ts);
+            const ChunkPos c = chunk_pos(p.n, t1);
+            const uint32_t s = vat(excl1, ts);
+            uint32_t err = kNone;
+            uint64_t T[1] = {0}, RD[1] = {0};
+            if (c.full) {
+                const uint32_t any = pass2_run<CB, 1>(pw1, s, nt, sh.p2.t2, T, RD);
+                if (any >> 31) err = first_invalid<CB, 1>(pw1, s, nt, sh.p2.t2, c.chunk_abs);
+            } else if (c.my_len) {
+                pass2_ragged_chunk<CB>(p, c, s, nt, sh.p2.nxt, sh.p2.tag, T[0], RD[0], err);
+            }
+            if (err != kNone) atomicMin(&p.hdr->err_min, err);
+            if (c.my_len && c.chunk_abs + c.my_len == p.n)
+                sh.last_rec = (uint32_t)((RD[0] >> (c.my_len - 1)) & 1u);
+            sc1 = span_carry<1>(T, RD, c.chunk_abs, sh.wc);
+            T1 = T[0];
+            RD1 = RD[0];
+            if (tid == 0) {
+                if (t1 == 0)  // the input starts at column 0 of record 0
+                    publish_gincl(p.stat_carry[0], gcomb(GCarry{0u, 0u, 0x80000000u, 0u}, sc1.total), p.epoch);
+                else
+                    publish_gagg(p.stat_carry[t1], sc1.total, p.epoch);
+            }
+        }
+
+        // ---- phase 3 (tile t2): count prefix, fields
+        if (t2 < num_tiles) {
+            GCarry P{0u, 0u, 0x80000000u, 0u};
+            if (t2 != 0) {
+                P = lookback_pre<kFastWaves>(t2, zero, cpoll, gcomb, sh.pc, sh.first, &p.hdr->fault,
+                                             look_first<kFastWaves>(t2, cpoll));
+                if (tid == 0) publish_gincl(p.stat_carry[t2], gcomb(P, sc2.total), p.epoch);
+            }
+            const uint32_t tile_start = t2 * (uint32_t)kFastTile;
+            // the wave lists its terminators, then writes 64 fields per round
+            uint32_t* list = sh.list[wv];
+            const uint32_t mine = sc2.mine, first = sc2.wave_excl.nf + sc2.excl_nf;
+            const uint32_t wfirst = sc2.wave_excl.nf;
+            const uint32_t wend = __builtin_amdgcn_readlane(first + mine, kWave - 1);
+            uint32_t rec_run = P.nr + sc2.wave_excl.nr;
+            uint32_t col_run = col_op(P.col, sc2.wave_excl.col) & 0x7fffffffu;
+            uint32_t off_run = max(P.lt, sc2.wave_excl.lt);
+            const uint32_t rel0 = (uint32_t)tid * (uint32_t)kFastChunk;
+            for (uint32_t w0 = wfirst; w0 < wend; w0 += kFusedList) {
+                const uint32_t w1 = min(w0 + (uint32_t)kFusedList, wend);
+                if (mine && first < w1 && first + mine > w0) {
+                    uint32_t li = first;
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        uint32_t bits = (uint32_t)(T2 >> (32 * q));
+                        const uint32_t rdw = (uint32_t)(RD2 >> (32 * q));
+                        while (bits && li < w1) {
+                            const uint32_t j = (uint32_t)__builtin_ctz(bits);
+                            if (li >= w0) list[li - w0] = ((rel0 + 32u * q + j) << 1) | ((rdw >> j) & 1u);
+                            ++li;
+                            bits &= bits - 1u;
+                        }
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                for (uint32_t r = w0; r < w1; r += kWave) {
+                    const uint32_t cnt = min((uint32_t)kWave, w1 - r);
+                    const uint32_t e = list[r - w0 + min(lane, cnt - 1u)];
+                    const uint32_t pos = tile_start + (e >> 1);
+                    const uint64_t m = __ballot(lane < cnt && (e & 1u));
+                    const uint64_t below = m & ((1ull << lane) - 1ull);
+                    const uint32_t rec = rec_run + (uint32_t)__popcll(below);
+                    const uint32_t col =
+                        below ? lane - (uint32_t)(63 - __clzll((long long)below)) - 1u : col_run + lane;
+                    const uint32_t prev = dpp_t<0x138, 0xf>(0u, pos);  // wave_shr:1: the previous lane's terminator
+                    const uint32_t off = lane ? prev + 1u : off_run;
+                    const uint64_t g0 = uniform64((uint64_t)P.nf + r);
+                    const uint32_t room = g0 < o.cap ? (uint32_t)min<uint64_t>(o.cap - g0, (uint64_t)cnt) : 0u;
+                    if (lane < room) {
+                        (o.rec + g0)[lane] = rec;
+                        (o.col + g0)[lane] = col;
+                        (o.off + g0)[lane] = off;
+                        (o.len + g0)[lane] = pos - off;
+                    }
+                    rec_run += (uint32_t)__popcll(m);
+                    col_run = m ? (cnt - 1u) - (uint32_t)(63 - __clzll((long long)m)) : col_run + cnt;
+                    off_run = __builtin_amdgcn_readlane(pos, cnt - 1) + 1u;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+            // the input's last tile: the unterminated final field and the results
+            if (t2 == num_tiles - 1 && tid == 0) {
+                const GCarry I = gcomb(P, sc2.total);
+                const uint32_t final_field = sh.last_rec ? 0u : 1u;
+                if (final_field && I.nf < o.cap) {
+                    o.rec[I.nf] = I.nr;
+                    o.col[I.nf] = I.col & 0x7fffffffu;
+                    o.off[I.nf] = I.lt;
+                    o.len[I.nf] = p.n - I.lt;
+                }
+                const uint32_t e = min(end2, 8u);
+                p.hdr->n_fields = (uint64_t)I.nf + final_field;
+                p.hdr->n_records = (uint64_t)I.nr + final_field;
+                p.hdr->end_state = p.state_of[e];
+                p.hdr->error_pos = ((p.accept_codes >> e) & 1u) ? (int64_t)-1 : (int64_t)p.n;  // before err_min
+            }
+        }
+
+        // hand the tiles on
+        t2 = t1;
+        T2 = T1;
+        RD2 = RD1;
+        sc2 = sc1;
+        end2 = end1;
+        t1 = t0;
+#pragma unroll
+        for (int q = 0; q < NP; ++q) pw1[q] = pw0[q];
+        excl1 = excl0;
+        tot1 = tot0;
+        t0 = tn;
+        if (t0 < num_tiles) load_chunk(t0, w);
+        __syncthreads();  // sh.next and the scan scratch are rewritten next round
+    }
+}
+
 // workgroups of the codes kernel (all resident at once: 4 per CU)
 constexpr uint32_t kCodesGrid = 1024;
 
@@ -877,11 +1243,51 @@ static void launch(const FastParams& f, const ppr_parse_opts_t* o, hipStream_t s
     stage_event(o, 4, s);
 }
 
+// Persistent grid of the fused kernel: as many workgroups as the device holds at
+// once (more would only wait for a slot; fewer would leave CUs idle).
+template <int CB, bool V8>
+static uint32_t fused_grid()
+{
+    static int per_cu = 0;
+    static int cus = 0;
+    if (per_cu == 0) {
+        int dev = 0, b = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, csv_fused_kernel<CB, V8>, kFastBlock, 0) == hipSuccess &&
+            b > 0 && n > 0) {
+            cus = n;
+            per_cu = b;
+        } else {
+            cus = 256;
+            per_cu = 1;
+        }
+    }
+    return (uint32_t)(cus * per_cu);
+}
+
+template <int CB, bool V8>
+static void launch_fused(const FastParams& f, const ppr_parse_opts_t* o, hipStream_t s)
+{
+    stage_event(o, 0, s);
+    hipLaunchKernelGGL((csv_fast_tables_kernel<CB, V8>), dim3(1), dim3(256), 0, s, f);
+    stage_event(o, 1, s);
+    const uint32_t grid = std::min<uint32_t>(f.num_tiles, fused_grid<CB, V8>());
+    hipLaunchKernelGGL((csv_fused_kernel<CB, V8>), dim3(grid), dim3(kFastBlock), 0, s, f);
+    stage_event(o, 2, s);
+}
+
 int launch_csv_fast(const FastParams& f, int cb, bool v8, const ppr_parse_opts_t* o, hipStream_t s)
 {
-    if (cb == 2) v8 ? launch<2, true>(f, o, s) : launch<2, false>(f, o, s);
-    else if (cb == 3) v8 ? launch<3, true>(f, o, s) : launch<3, false>(f, o, s);
-    else v8 ? launch<4, true>(f, o, s) : launch<4, false>(f, o, s);
+    if (f.path == PPR_PATH_FUSED) {
+        if (cb == 2) v8 ? launch_fused<2, true>(f, o, s) : launch_fused<2, false>(f, o, s);
+        else if (cb == 3) v8 ? launch_fused<3, true>(f, o, s) : launch_fused<3, false>(f, o, s);
+        else v8 ? launch_fused<4, true>(f, o, s) : launch_fused<4, false>(f, o, s);
+    } else {
+        if (cb == 2) v8 ? launch<2, true>(f, o, s) : launch<2, false>(f, o, s);
+        else if (cb == 3) v8 ? launch<3, true>(f, o, s) : launch<3, false>(f, o, s);
+        else v8 ? launch<4, true>(f, o, s) : launch<4, false>(f, o, s);
+    }
     return hipGetLastError() == hipSuccess ? PPR_OK : PPR_EHIP;
 }
 

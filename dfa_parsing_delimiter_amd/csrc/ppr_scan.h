@@ -208,4 +208,71 @@ __device__ T lookback(uint32_t tile, const T& ident, const Poll& poll, const Com
     }
 }
 
+// Look-back whose first round of polls the caller issued earlier (look_first),
+// so that those loads travel while the caller does other work. A poller has
+// load(u) -> Raw (the status words of tile u, all loads issued at once) and
+// decode(raw, out) -> kFlagIncl / kFlagAgg / 0, as poll() above. Otherwise as
+// lookback(): every thread calls it, tile > 0, bounded by kSpinLimit.
+template <int NW, typename P>
+__device__ __forceinline__ typename P::Raw look_first(uint32_t tile, const P& poller)
+{
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    const int64_t u = (int64_t)tile - 1 - (int64_t)(w * kWave + (kWave - 1 - lane));
+    return poller.load(u >= 0 ? u : 0);  // (a tile before the first is never decoded)
+}
+
+template <int NW, typename T, typename P, typename Comb>
+__device__ T lookback_pre(uint32_t tile, const T& ident, const P& poller, const Comb& comb, T* s_part, int* s_found,
+                          uint32_t* fault, const typename P::Raw& raw0)
+{
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    T acc = ident;
+    int64_t base = (int64_t)tile - 1;
+    uint32_t spins = 0;
+    for (bool first_round = true;; first_round = false) {
+        const int64_t u = base - (int64_t)(w * kWave + (kWave - 1 - lane));
+        const bool valid = u >= 0;
+        T v = ident;
+        uint32_t f = 0;
+        if (valid) f = poller.decode(first_round ? raw0 : poller.load(u), v);
+        const uint64_t vmask = __ballot(valid);
+        for (;;) {
+            const uint64_t ready = __ballot(f != 0);
+            const uint64_t inclm = __ballot(f == kFlagIncl);
+            const uint64_t need = inclm ? vmask & (~0ull << (63 - __clzll((long long)inclm))) : vmask;
+            if ((ready & need) == need) break;
+            if (++spins > kSpinLimit) {
+                if (lane == 0) atomicOr(fault, 1u);
+                if (valid && f == 0) {
+                    f = kFlagAgg;
+                    v = ident;
+                }
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            if (valid && f == 0) f = poller.decode(poller.load(u), v);
+        }
+        const uint64_t inclm = __ballot(f == kFlagIncl);
+        const int j = inclm ? 63 - __clzll((long long)inclm) : -1;
+        if (!(valid && lane >= j)) v = ident;
+        const T part = readlane_t(wave_scan(v, ident, comb), kWave - 1);
+        if (lane == 0) {
+            s_part[w] = part;
+            s_found[w] = j >= 0;
+        }
+        __syncthreads();
+        int wi = NW;
+#pragma unroll
+        for (int i = NW - 1; i >= 0; --i)
+            if (s_found[i]) wi = i;
+        const int last = wi < NW ? wi : NW - 1;
+        T r = s_part[last];
+        for (int i = last - 1; i >= 0; --i) r = comb(r, s_part[i]);
+        acc = comb(r, acc);
+        __syncthreads();
+        if (wi < NW) return acc;
+        base -= (int64_t)NW * kWave;
+    }
+}
+
 }  // namespace ppr

@@ -97,19 +97,23 @@ typedef struct ppr_parse_out {
     uint64_t n_records; /* out */
     int64_t error_pos;  /* out: first INVALID byte; else n if the end state is not accepting; else -1 */
     uint32_t end_state; /* out: DFA state after the last byte */
-    uint32_t path;      /* out: the kernels that ran, PPR_PATH_STREAMING or PPR_PATH_SINGLE_PASS */
+    uint32_t path;      /* out: the kernels that ran, a PPR_PATH_* value */
 } ppr_parse_out_t;
 
 /*
- * Which kernels a parse runs (chosen at the call, reported in ppr_parse_out_t.path):
- *   PPR_PATH_STREAMING   chunk_bytes 64, 16-byte aligned input, a class map with one
- *                        catch-all class and at most 8 other bytes that a 3-bit hash of
- *                        two bit fields separates: 4 kernels (step tables, codes,
- *                        carries, emit), no waiting between workgroups;
- *   PPR_PATH_SINGLE_PASS any table and chunk size: 2 kernels (reset, one single-pass
- *                        kernel with decoupled look-back scans).
+ * Which kernels a parse runs (chosen at the call, reported in ppr_parse_out_t.path).
+ * The first two need chunk_bytes 64, a 16-byte aligned input and a class map with
+ * one catch-all class and at most 8 other bytes that a 3-bit hash of two bit
+ * fields separates ("table-driven" below):
+ *   PPR_PATH_FUSED       table-driven, 2 kernels (step tables, one persistent
+ *                        single-pass kernel with decoupled look-back scans over
+ *                        32 KiB tiles): the input is read once;
+ *   PPR_PATH_STREAMING   table-driven, 5 kernels (step tables, codes, range
+ *                        vectors, carries, emit), no waiting between workgroups;
+ *   PPR_PATH_SINGLE_PASS any table and chunk size: 2 kernels (reset, one
+ *                        single-pass kernel with decoupled look-back scans).
  */
-enum { PPR_PATH_STREAMING = 1, PPR_PATH_SINGLE_PASS = 2 };
+enum { PPR_PATH_STREAMING = 1, PPR_PATH_SINGLE_PASS = 2, PPR_PATH_FUSED = 3 };
 
 /*
  * Launch options (opts may be NULL: all defaults).
@@ -117,13 +121,21 @@ enum { PPR_PATH_STREAMING = 1, PPR_PATH_SINGLE_PASS = 2 };
  *   stage_events:   optional array of n_stage_events hipEvent_t (caller-created):
  *                   event 0 is recorded on the stream before the first kernel of the
  *                   call and event i after its i-th kernel, as far as the array
- *                   reaches (streaming parse: 4 kernels; single-pass parse and the
- *                   lexer: 2). For per-kernel timing; NULL: none.
+ *                   reaches (streaming parse: 4 events after the tables, codes +
+ *                   range vectors, carries and emit kernels; fused and single-pass
+ *                   parse and the lexer: 2). For per-kernel timing; NULL: none.
+ *   path:           0 = automatic (the streaming path where the table and input
+ *                   allow it, else the single-pass path); PPR_PATH_FUSED or
+ *                   PPR_PATH_STREAMING ask for that path and fall back to the
+ *                   single-pass path where it does not apply; PPR_PATH_SINGLE_PASS
+ *                   forces the generic kernel. Any other value: PPR_EINVAL. The
+ *                   lexer ignores it.
  */
 typedef struct ppr_parse_opts {
     uint32_t chunk_bytes;
     uint32_t n_stage_events;
     void* const* stage_events;
+    uint32_t path;
 } ppr_parse_opts_t;
 
 /*

@@ -4,7 +4,9 @@ Bit-exact on every output array and scalar. Covers hand-worked and exhaustive
 short inputs, chunk sizes from 1 byte (every byte its own chunk, so the scans do
 all the work) to 64, inputs spanning several tiles with ragged tails, unaligned
 input pointers, error and capacity paths, and every delimiter-separated
-workload at its full size in the configuration the benchmark times.
+workload at its full size in the configuration the benchmark times. Every
+64-byte case runs on both table-driven paths (the streaming kernels, the
+automatic choice, and the fused single-pass kernel).
 """
 import itertools
 import json
@@ -59,15 +61,28 @@ def _same(g, r, what=""):
                 what, name, bad.size, a.size, bad[0], a[bad[0]], r[key][bad[0]]))
 
 
+# (chunk_bytes, path) pairs: 64-byte chunks on each table-driven path (None: the automatic choice,
+# the streaming kernels; 3: the fused kernel)
+AUTO_PATH = 1
+FUSED = 3
+
+
+def _with_paths(chunks):
+    out = []
+    for c in chunks:
+        out += [(c, None), (c, FUSED)] if c in (None, 64) else [(c, None)]
+    return out
+
+
 def test_golden(ppr):
     for line in open(GOLDEN):
         c = json.loads(line)
         t = W.table(c["table"])
         b = c["input"].encode("latin-1")
-        for chunk in (1, 2, 3, 32, 64):
-            _say("golden", repr(b), chunk)
-            g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=len(b) + 1)
-            _same(g, oracle.csv_parse(b, t), (b, chunk))
+        for chunk, path in _with_paths((1, 2, 3, 32, 64)):
+            _say("golden", repr(b), chunk, path)
+            g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=len(b) + 1, path=path)
+            _same(g, oracle.csv_parse(b, t), (b, chunk, path))
 
 
 @pytest.mark.parametrize("name,alphabet,max_len", [("T5", b',\n"a', 5), ("T6", b'\t\n"#a', 4)])
@@ -76,19 +91,19 @@ def test_exhaustive_short(ppr, name, alphabet, max_len):
     inputs = [bytes(s) for L in range(1, max_len + 1) for s in itertools.product(alphabet, repeat=L)]
     refs = oracle.csv_parse_many(inputs, t)
     _say("exhaustive", name, len(inputs))
-    parsers = {c: ppr.Parser(t, max_n=16, chunk_bytes=c) for c in (1, 3, 64)}
+    parsers = {cp: ppr.Parser(t, max_n=16, chunk_bytes=cp[0], path=cp[1]) for cp in _with_paths((1, 3, 64))}
     for s, r in zip(inputs, refs):
         for c, P in parsers.items():
             _same(P(_dev(s)), r, (s, c))
 
 
-@pytest.mark.parametrize("chunk", [1, 2, 5, 16, 31, 32, 33, 63, 64])
-def test_random_mixed_inputs_every_chunk_size(ppr, chunk):
+@pytest.mark.parametrize("chunk,path", _with_paths([1, 2, 5, 16, 31, 32, 33, 63, 64]))
+def test_random_mixed_inputs_every_chunk_size(ppr, chunk, path):
     rng = np.random.default_rng(chunk)
     for name in ("T5", "T6"):
         t = W.table(name)
         alpha = np.frombuffer(b',\n"ab' if name == "T5" else b'\t\n"#ab', dtype=np.uint8)
-        P = ppr.Parser(t, max_n=70000, chunk_bytes=chunk)
+        P = ppr.Parser(t, max_n=70000, chunk_bytes=chunk, path=path)
         for it in range(12):
             n = int(rng.integers(0, 70000))
             # mostly valid text with rare quotes, so that errors do not end everything early
@@ -99,14 +114,14 @@ def test_random_mixed_inputs_every_chunk_size(ppr, chunk):
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
-@pytest.mark.parametrize("chunk", [1, 8, 31, 32, 64])
-def test_workloads_several_tiles_ragged(ppr, cfg, chunk):
+@pytest.mark.parametrize("chunk,path", _with_paths([1, 8, 31, 32, 64]))
+def test_workloads_several_tiles_ragged(ppr, cfg, chunk, path):
     t = W.table(W.CONFIGS[cfg]["table"])
     n = (3 << 20) + 12345
     b = W.generate(cfg, n=n, seed=77 + cfg)
-    _say("workload", cfg, chunk, n)
-    g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=n + 1)
-    _same(g, oracle.csv_parse(b, t), (cfg, chunk))
+    _say("workload", cfg, chunk, path, n)
+    g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=n + 1, path=path)
+    _same(g, oracle.csv_parse(b, t), (cfg, chunk, path))
 
 
 def _random_table(rng, absorbing, n_special):
@@ -146,10 +161,10 @@ def test_random_tables(ppr, seed):
         for n in (1, 63, 64, 65, 16384, 16385, 100000):
             b = pool[rng.integers(0, pool.size, n)]
             r = oracle.csv_parse(b, t)
-            for chunk in (64, 13):
-                _say("table", seed, trial, t["n_states"], t["n_classes"], len(specials), n, chunk)
-                g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=n + 1)
-                _same(g, r, (seed, trial, n, chunk))
+            for chunk, path in _with_paths((64, 13)):
+                _say("table", seed, trial, t["n_states"], t["n_classes"], len(specials), n, chunk, path)
+                g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=n + 1, path=path)
+                _same(g, r, (seed, trial, n, chunk, path))
 
 
 def test_unaligned_input_and_subviews(ppr):
@@ -157,11 +172,12 @@ def test_unaligned_input_and_subviews(ppr):
     t = W.table("T5")
     b = W.generate(3, n=1 << 20, seed=5)
     d = _dev(b)
-    for off in (1, 3, 7, 15):
+    for off in (1, 3, 7, 15, 16):
         _say("unaligned", off)
         view = d[off:]
         g = ppr.parse(view, t, capacity=b.size)
         _same(g, oracle.csv_parse(b[off:], t), off)
+        assert g.path == (AUTO_PATH if off == 16 else ppr.PPR_PATH_SINGLE_PASS)
 
 
 def test_edge_cases(ppr):
@@ -176,10 +192,10 @@ def test_edge_cases(ppr):
         (t6, b"\t" * 70000), (t6, b"\n#\n#x\n"),
     ]
     for t, b in cases:
-        for chunk in (1, 7, 31, 64):
-            _say("edge", t["name"], len(b), chunk)
-            g = ppr.parse(_dev(b) if b else _dev(b"\0")[:0], t, chunk_bytes=chunk, capacity=len(b) + 2)
-            _same(g, oracle.csv_parse(b, t), (t["name"], len(b), chunk))
+        for chunk, path in _with_paths((1, 7, 31, 64)):
+            _say("edge", t["name"], len(b), chunk, path)
+            g = ppr.parse(_dev(b) if b else _dev(b"\0")[:0], t, chunk_bytes=chunk, capacity=len(b) + 2, path=path)
+            _same(g, oracle.csv_parse(b, t), (t["name"], len(b), chunk, path))
 
 
 def test_capacity_reported(ppr):
@@ -200,13 +216,13 @@ def test_capacity_reported(ppr):
     _same(g, r, "resized")
 
 
-@pytest.mark.parametrize("chunk", [31, None])
-def test_repeatable(ppr, chunk):
+@pytest.mark.parametrize("chunk,path", _with_paths([31, None]))
+def test_repeatable(ppr, chunk, path):
     """the same workspace reused: nothing left over from the previous call leaks in"""
     t = W.table("T5")
     b = W.generate(3, n=(8 << 20) + 3, seed=11)
     r = oracle.csv_parse(b, t)
-    P = ppr.Parser(t, max_n=b.size, chunk_bytes=chunk)
+    P = ppr.Parser(t, max_n=b.size, chunk_bytes=chunk, path=path)
     d = _dev(b)
     for i in range(5):
         _say("repeat", chunk, i)
@@ -218,15 +234,24 @@ def test_repeatable(ppr, chunk):
 
 
 def test_path_reported(ppr):
-    """the streaming kernels run for 64-byte chunks on aligned input with an encodable class map; the
-    single-pass kernel otherwise"""
+    """the table-driven kernels run for 64-byte chunks on aligned input with an encodable class map
+    (the fused kernel unless the streaming kernels are asked for); the single-pass kernel otherwise"""
     for name in ("T5", "T6"):
         t = W.table(name)
         b = W.generate(1 if name == "T5" else 4, n=300000, seed=5)
+        r = oracle.csv_parse(b, t)
         g = ppr.parse(_dev(b), t, capacity=b.size + 1)
-        assert g.path == ppr.PPR_PATH_STREAMING, name
+        assert g.path == AUTO_PATH, name
+        for want in (ppr.PPR_PATH_FUSED, ppr.PPR_PATH_STREAMING, ppr.PPR_PATH_SINGLE_PASS):
+            g = ppr.parse(_dev(b), t, capacity=b.size + 1, path=want)
+            assert g.path == want, (name, want)
+            _same(g, r, (name, want))
         g31 = ppr.parse(_dev(b), t, chunk_bytes=31, capacity=b.size + 1)
         assert g31.path == ppr.PPR_PATH_SINGLE_PASS, name
+        g31 = ppr.parse(_dev(b), t, chunk_bytes=31, capacity=b.size + 1, path=ppr.PPR_PATH_FUSED)
+        assert g31.path == ppr.PPR_PATH_SINGLE_PASS, name
+    with pytest.raises(ppr.PprError):
+        ppr.parse(_dev(b), t, capacity=b.size + 1, path=4)
     # more than 8 non-catch-all bytes: not encodable by the streaming classifier
     rng = np.random.default_rng(3)
     t = _random_table(rng, True, 40)
@@ -236,22 +261,23 @@ def test_path_reported(ppr):
     _same(g, oracle.csv_parse(b, t), "40 specials")
 
 
-def test_stage_events(ppr):
+@pytest.mark.parametrize("path,stages", [(None, 4), (3, 2)])
+def test_stage_events(ppr, path, stages):
     """per-kernel HIP events recorded by the library between its kernels"""
     import torch
     t = W.table("T5")
     b = W.generate(3, n=(4 << 20), seed=2)
     d = _dev(b)
-    P = ppr.Parser(t, max_n=b.size)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    P = ppr.Parser(t, max_n=b.size, path=path)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(stages + 1)]
     for e in ev:
         e.record()
     torch.cuda.synchronize()
     P.launch(d, stage_events=ev)
     torch.cuda.synchronize()
     o = P.results(b.size)
-    assert o.path == ppr.PPR_PATH_STREAMING
-    times = [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+    assert o.path == (path or AUTO_PATH)
+    times = [ev[i].elapsed_time(ev[i + 1]) for i in range(stages)]
     assert all(x >= 0 for x in times) and sum(times) > 0, times
     assert o.n_fields == oracle.csv_parse(b, t)["n_fields"]
 
@@ -260,17 +286,21 @@ def test_stage_events(ppr):
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_full_size_workloads(ppr, cfg):
     """every output array at the workload's full size: in the launch configuration the benchmark times
-    (the default 64-byte chunks, streaming kernels) and at the workload's own chunk size if it names one"""
+    (the default 64-byte chunks, streaming kernels), on the fused kernel, and at the workload's own
+    chunk size if it names one"""
     t = W.table(W.CONFIGS[cfg]["table"])
     _say("full", cfg, "generate")
     b = W.generate(cfg)
     _say("full", cfg, "oracle")
     r = oracle.csv_parse(b, t)
     d = _dev(b)
-    for chunk in [None] + ([W.CONFIGS[cfg]["chunk_bytes"]] if W.CONFIGS[cfg].get("chunk_bytes") else []):
-        _say("full", cfg, "gpu chunk", chunk, r["n_fields"])
-        g = ppr.Parser(t, max_n=b.size, capacity=r["n_fields"], chunk_bytes=chunk)(d)
+    runs = [(None, None), (None, FUSED)]
+    if W.CONFIGS[cfg].get("chunk_bytes"):
+        runs.append((W.CONFIGS[cfg]["chunk_bytes"], None))
+    for chunk, path in runs:
+        _say("full", cfg, "gpu chunk", chunk, path, r["n_fields"])
+        g = ppr.Parser(t, max_n=b.size, capacity=r["n_fields"], chunk_bytes=chunk, path=path)(d)
         if chunk is None:
-            assert g.path == ppr.PPR_PATH_STREAMING
-        _same(g, r, ("full", cfg, chunk))
+            assert g.path == (path or AUTO_PATH)
+        _same(g, r, ("full", cfg, chunk, path))
     del b, d
