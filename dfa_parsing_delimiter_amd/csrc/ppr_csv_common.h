@@ -116,7 +116,7 @@ struct FastParams {
     uint32_t num_super;    // super-tiles: pairs of tiles (the last may hold one)
     uint32_t num_ranges;   // workgroups of the streaming kernels, each owning a contiguous run of super-tiles
     uint8_t* idx;          // group indices, NI bytes per full chunk
-    uint32_t* cvec_lo;     // per chunk: vector of the tile's bytes before it (entries 0-3)
+    uint32_t* cvec_lo;     // per even chunk: vector of the tile's bytes before it (entries 0-3)
     uint32_t* cvec_hi;     // (entries 4-7)
     uint64_t* tile_vec;    // per tile: state-transition vector (lo | hi << 32)
     uint64_t* range_vec;   // per range: composite of its tile vectors
@@ -151,8 +151,8 @@ inline FastLayout fast_layout(uint64_t n)
     L.stat_vec = align_up(L.range_carry + kMaxRanges * 16, 256);
     L.stat_carry = align_up(L.stat_vec + L.tiles * 8, 256);
     L.cvec_lo = align_up(L.stat_carry + L.tiles * sizeof(StatB), 256);
-    L.cvec_hi = align_up(L.cvec_lo + L.tiles * kFastBlock * 4, 256);
-    L.idx = align_up(L.cvec_hi + L.tiles * kFastBlock * 4, 256);
+    L.cvec_hi = align_up(L.cvec_lo + L.tiles * (kFastBlock / 2) * 4, 256);
+    L.idx = align_up(L.cvec_hi + L.tiles * (kFastBlock / 2) * 4, 256);
     L.total = align_up(L.idx + L.tiles * (uint64_t)kFastTile / 2, 256);
     return L;
 }

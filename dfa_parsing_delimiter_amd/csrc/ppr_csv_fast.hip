@@ -75,10 +75,12 @@ struct MaxComb {
 // Count carries of a workgroup's spans without a 4-word scan: each lane's
 // terminator and record counts (packed, a span holds at most 128 of each), the
 // 1 + position of its last terminator, and the 1-based index among its
-// terminators of its last record delimiter; per wave a sum scan of the packed
-// counts and two max reductions give the wave's carry (its column carry is the
-// terminators after its last record delimiter), and the waves' carries are
-// combined through LDS.
+// terminators of its last record delimiter. Per wave, a sum scan of the packed
+// counts gives each lane's exclusive counts; the wave's last terminator and
+// last record field are those of its last lane holding one (a ballot and a
+// readlane: positions grow with the lane); its column carry is the terminators
+// after its last record delimiter. Wave 0 then scans the waves' carries and
+// hands each wave its exclusive carry and the total through LDS.
 struct SpanCarry {
     uint32_t excl_nf;  // terminators in the wave's earlier lanes
     uint32_t mine;     // this lane's terminators
@@ -86,11 +88,13 @@ struct SpanCarry {
     GCarry total;      // carry of the whole tile
 };
 
+constexpr int kSpanScratch = 2 * kFastWaves + 1;  // GCarry entries of span_carry's LDS scratch
+
 template <int NCH>
 __device__ __forceinline__ SpanCarry span_carry(const uint64_t (&T)[NCH], const uint64_t (&RD)[NCH], uint32_t abs,
                                                 GCarry* s_wave)
 {
-    uint32_t nf = 0, nr = 0, lt = 0, rdl = 0, before = 0;
+    uint32_t nr = 0, lt = 0, rdl = 0, before = 0;
 #pragma unroll
     for (int h = 0; h < NCH; ++h) {
         const uint32_t nh = (uint32_t)__popcll(T[h]);
@@ -102,26 +106,33 @@ __device__ __forceinline__ SpanCarry span_carry(const uint64_t (&T)[NCH], const 
         }
         before += nh;
     }
-    nf = before;
+    const uint32_t nf = before;
     const uint32_t inc = wave_scan(nf | (nr << 16), 0u, AddComb{});
     const uint32_t excl = wave_shr1(0u, inc);
     const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane(inc, kWave - 1);
-    const uint32_t rdg = rdl ? (excl & 0xffffu) + rdl : 0u;  // 1-based wave-local index of the lane's last record field
-    const uint32_t max_rd = (uint32_t)__builtin_amdgcn_readlane(wave_scan(rdg, 0u, MaxComb{}), kWave - 1);
-    const uint32_t max_lt = (uint32_t)__builtin_amdgcn_readlane(wave_scan(lt, 0u, MaxComb{}), kWave - 1);
+    const uint64_t has_t = __ballot(nf != 0), has_r = __ballot(rdl != 0);
+    const uint32_t max_lt = has_t ? (uint32_t)__builtin_amdgcn_readlane(lt, 63 - __clzll((long long)has_t)) : 0u;
+    // 1-based wave-local index of the wave's last record field
+    const uint32_t max_rd =
+        has_r ? (uint32_t)__builtin_amdgcn_readlane((excl & 0xffffu) + rdl, 63 - __clzll((long long)has_r)) : 0u;
     const uint32_t wnf = tot & 0xffffu;
     const GCarry wc{wnf, tot >> 16, max_rd ? (wnf - max_rd) | 0x80000000u : wnf, max_lt};
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const GCarry zero{0, 0, 0, 0};
     if (lane_id() == 0) s_wave[w] = wc;
     __syncthreads();
-    const GCarry zero{0, 0, 0, 0};
-    const GCarry ws = row_scan<kFastWaves>(lane_value<kFastWaves>(s_wave, zero), zero, GCarryComb{});
+    if (w == 0) {  // s_wave[NW + i]: carry of the waves before wave i; s_wave[2 NW]: the total
+        const GCarry ws = row_scan<kFastWaves>(lane_value<kFastWaves>(s_wave, zero), zero, GCarryComb{});
+        const GCarry ex = wave_shr1(zero, ws);
+        if (lane_id() < kFastWaves) s_wave[kFastWaves + lane_id()] = ex;
+        if (lane_id() == kFastWaves - 1) s_wave[2 * kFastWaves] = ws;
+    }
+    __syncthreads();
     SpanCarry r;
     r.excl_nf = excl & 0xffffu;
     r.mine = nf;
-    r.wave_excl = zero;
-    if (w) r.wave_excl = readlane_t(ws, w - 1);
-    r.total = readlane_t(ws, kFastWaves - 1);
+    r.wave_excl = s_wave[kFastWaves + w];
+    r.total = s_wave[2 * kFastWaves];
     return r;
 }
 
@@ -410,7 +421,7 @@ __device__ __forceinline__ IdxIn<CB, V8> load_in(const FastParams& p, const Pair
             in.pw[4 * q + 3] = x.w;
         }
     }
-    const size_t ci = c.valid ? 2 * c.pair : 0;  // the span's first (even) chunk
+    const size_t ci = c.valid ? c.pair : 0;  // the span's first (even) chunk
     in.cvlo = p.cvec_lo[ci];
     in.cvhi = V8 ? p.cvec_hi[ci] : 0xffffffffu;
     in.tvl = p.tile_vec[min(2 * c.st + (threadIdx.x & 1u), p.num_tiles - 1)];
@@ -561,13 +572,16 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
             dst[q] = make_uint4(pw[4 * q], pw[4 * q + 1], pw[4 * q + 2], pw[4 * q + 3]);
         return tree_vector<CB, V8>(idx, s_t1);
     };
-    // scan the tile's chunk vectors, store them and the tile vector
+    // scan the tile's chunk vectors, store those of the even chunks (where the
+    // carries and emit kernels' two-chunk spans start) and the tile vector
     auto finish = [&](uint32_t tile, const Vec& v, uint32_t it) {
         Vec excl, tot;
         block_scan<kFastWaves>(v, ident, excl, tot, s_wave[it & 1], VecComb<V8>{});
-        const size_t ci = (size_t)tile * kFastBlock + tid;
-        p.cvec_lo[ci] = excl.lo;
-        if (V8) p.cvec_hi[ci] = excl.hi;
+        if ((tid & 1) == 0) {
+            const size_t ci = (size_t)tile * (kFastBlock / 2) + (uint32_t)tid / 2;
+            p.cvec_lo[ci] = excl.lo;
+            if (V8) p.cvec_hi[ci] = excl.hi;
+        }
         if (tid == 0) p.tile_vec[tile] = (uint64_t)tot.lo | ((uint64_t)tot.hi << 32);
     };
 
@@ -676,7 +690,8 @@ __device__ __forceinline__ void span_tags(const FastParams& p, const PairPos& c,
 // Runs body(st, in, it) over the range's super-tiles [s0, s1) in order: the
 // entirely full ones [s0, sfull) with two register buffers used in turn and an
 // unconditional prefetch (the last full super-tile is read again at the end),
-// then the input's ragged last super-tile, if the range holds it.
+// then the input's ragged last super-tile, if the range holds it. it = (st -
+// s0) mod 2 alternates from call to call, for LDS scratch used in turn.
 template <int CB, bool V8, typename FullBody, typename TailBody>
 __device__ __forceinline__ void walk_supers(const FastParams& p, uint32_t s0, uint32_t s1, const FullBody& full,
                                             const TailBody& tail)
@@ -693,20 +708,40 @@ __device__ __forceinline__ void walk_supers(const FastParams& p, uint32_t s0, ui
         full(st, b, 1u);
         ++st;
     }
-    if (st < s1) tail(st, load_in<CB, V8, false>(p, pair_pos(p, st)), 0u);
+    if (st < s1) tail(st, load_in<CB, V8, false>(p, pair_pos(p, st)), (st - s0) & 1u);  // (buffers keep alternating)
+}
+
+// Terminators of a 128-byte span (bitmaps T, bit j = byte j) at span
+// positions k and later, 0 <= k < 128.
+__device__ __forceinline__ uint32_t count_from(const uint64_t (&T)[2], uint32_t k)
+{
+    const uint64_t m0 = k < 64 ? ~0ull << k : 0ull;
+    const uint64_t m1 = k < 64 ? ~0ull : ~0ull << (k - 64);
+    return (uint32_t)(__popcll(T[0] & m0) + __popcll(T[1] & m1));
 }
 
 // carries: the range's start state (stored), tags from each span's start state,
-// the range's count carry (stored); the last range stores the end state
+// the range's count carry (stored); the last range stores the end state.
+//
+// The count carry needs no scan: terminator and record counts add up and the
+// last terminator is a maximum, in any order, so each thread accumulates its
+// own; the column carry (terminators after the range's last record delimiter)
+// follows from one block maximum per super-tile, the position of its last
+// record delimiter: a super-tile that has one restarts every thread's count at
+// its terminators after that position, one without adds all of them. The
+// thread sums and maxima are reduced once, at the end of the range.
 template <int CB, bool V8>
 __global__ void __launch_bounds__(kFastBlock) csv_carries_kernel(FastParams p)
 {
     using Gm = Geo<CB>;
     __shared__ Pass2Shared<V8, Gm::E> sh;
-    __shared__ GCarry s_wc[2][kFastWaves];
+    __shared__ uint32_t s_rd[2][kFastWaves];
     __shared__ Vec s_wv[kFastWaves];
+    __shared__ uint4 s_red[kFastWaves];
 
     const uint32_t b = blockIdx.x;
+    const uint32_t lane = (uint32_t)lane_id();
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     uint32_t s0, s1;
     range_of(p, b, s0, s1);
     const uint32_t nt = p.nt;
@@ -714,8 +749,7 @@ __global__ void __launch_bounds__(kFastBlock) csv_carries_kernel(FastParams p)
     load_pass2<CB, V8>(p, sh);
     uint32_t run = vat(ranges_before<V8>(p, b, ident, s_wv), p.start_code);  // (its barrier publishes sh)
     if (threadIdx.x == 0) p.range_state[b] = run;
-    const GCarryComb gcomb;
-    GCarry rc{0, 0, 0, 0};
+    uint32_t acc_nf = 0, acc_nr = 0, acc_col = 0, acc_lt = 0;
 
     auto step = [&](auto full_tag, uint32_t st, const IdxIn<CB, V8>& in, uint32_t it) {
         constexpr bool FULL = decltype(full_tag)::value;
@@ -729,14 +763,43 @@ __global__ void __launch_bounds__(kFastBlock) csv_carries_kernel(FastParams p)
         if (err != kNone) atomicMin(&p.hdr->err_min, err);
         if (c.my_len && c.abs + c.my_len == p.n)  // the thread holding the input's last byte
             p.hdr->last_rec = (uint32_t)((RD[(c.my_len - 1) >> 6] >> ((c.my_len - 1) & 63)) & 1u);
-        rc = gcomb(rc, span_carry(T, RD, c.abs, s_wc[it & 1]).total);
+        const uint32_t nf = (uint32_t)(__popcll(T[0]) + __popcll(T[1]));
+        acc_nf += nf;
+        acc_nr += (uint32_t)(__popcll(RD[0]) + __popcll(RD[1]));
+        if (T[1]) acc_lt = c.abs + (uint32_t)kFastChunk + (uint32_t)(63 - __clzll((long long)T[1])) + 1u;
+        else if (T[0]) acc_lt = c.abs + (uint32_t)(63 - __clzll((long long)T[0])) + 1u;
+        // 1 + position of the super-tile's last record delimiter (0: none)
+        uint32_t rdp = 0;
+        if (RD[1]) rdp = c.abs + (uint32_t)kFastChunk + (uint32_t)(63 - __clzll((long long)RD[1])) + 1u;
+        else if (RD[0]) rdp = c.abs + (uint32_t)(63 - __clzll((long long)RD[0])) + 1u;
+        const uint64_t has_r = __ballot(rdp != 0);
+        if (lane == 0)
+            s_rd[it & 1][w] = has_r ? (uint32_t)__builtin_amdgcn_readlane(rdp, 63 - __clzll((long long)has_r)) : 0u;
+        __syncthreads();
+        const uint4 x = reinterpret_cast<const uint4*>(s_rd[it & 1])[0];
+        const uint4 y = reinterpret_cast<const uint4*>(s_rd[it & 1])[1];
+        const uint32_t L = max(max(max(x.x, x.y), max(x.z, x.w)), max(max(y.x, y.y), max(y.z, y.w)));
+        if (L == 0) acc_col += nf;
+        else if (c.abs >= L) acc_col = nf;
+        else acc_col = c.abs + 2u * kFastChunk > L ? count_from(T, L - c.abs) : 0u;
         run = vat(v1, ts1);
     };
     walk_supers<CB, V8>(
         p, s0, s1, [&](uint32_t st, const IdxIn<CB, V8>& in, uint32_t it) { step(std::true_type{}, st, in, it); },
         [&](uint32_t st, const IdxIn<CB, V8>& in, uint32_t it) { step(std::false_type{}, st, in, it); });
+
+    // the range's carry: sums of nf, nr, col and the maximum of lt over the threads
+    const uint32_t snf = wave_scan(acc_nf, 0u, AddComb{}), snr = wave_scan(acc_nr, 0u, AddComb{});
+    const uint32_t scol = wave_scan(acc_col, 0u, AddComb{}), slt = wave_scan(acc_lt, 0u, MaxComb{});
+    if (lane == kWave - 1) s_red[w] = make_uint4(snf, snr, scol, slt);
+    __syncthreads();
     if (threadIdx.x == 0) {
-        p.range_carry[b] = make_uint4(rc.nf, rc.nr, rc.col, rc.lt);
+        uint4 r = s_red[0];
+        for (int i = 1; i < kFastWaves; ++i) {
+            const uint4 q = s_red[i];
+            r = make_uint4(r.x + q.x, r.y + q.y, r.z + q.z, max(r.w, q.w));
+        }
+        p.range_carry[b] = make_uint4(r.x, r.y, r.z | (r.y ? 0x80000000u : 0u), r.w);
         if (b == p.num_ranges - 1) {
             const uint32_t e = min(run, 8u);
             p.hdr->end_state = p.state_of[e];
@@ -752,6 +815,45 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v)
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
     return ((uint64_t)hi << 32) | lo;
+}
+
+// Lists a lane's terminators that fall in the window [w0, w1) of wave-local
+// field indices into the wave's LDS list (entry = position << 1 | record bit,
+// positions from rel0 on). The lane's fields are [first, first + mine); tw / rw:
+// its terminator / record bitmaps as 32-bit words (bit j of word q = byte
+// 32 q + j). When all of them fall in the window (the usual case) the loop
+// runs without index checks.
+template <int NWORDS>
+__device__ __forceinline__ void list_terminators(uint32_t* list, const uint32_t (&tw)[NWORDS],
+                                                 const uint32_t (&rw)[NWORDS], uint32_t rel0, uint32_t first,
+                                                 uint32_t mine, uint32_t w0, uint32_t w1)
+{
+    if (!(mine && first < w1 && first + mine > w0)) return;
+    if (first >= w0 && first + mine <= w1) {
+        uint32_t* dst = list + (first - w0);
+#pragma unroll
+        for (int q = 0; q < NWORDS; ++q) {
+            uint32_t bits = tw[q];
+            const uint32_t base2 = (rel0 + 32u * q) << 1;
+            while (bits) {
+                const uint32_t j = (uint32_t)__builtin_ctz(bits);
+                *dst++ = base2 + (j << 1) + ((rw[q] >> j) & 1u);
+                bits &= bits - 1u;
+            }
+        }
+        return;
+    }
+    uint32_t li = first;
+#pragma unroll
+    for (int q = 0; q < NWORDS; ++q) {
+        uint32_t bits = tw[q];
+        while (bits && li < w1) {
+            const uint32_t j = (uint32_t)__builtin_ctz(bits);
+            if (li >= w0) list[li - w0] = ((rel0 + 32u * q + j) << 1) | ((rw[q] >> j) & 1u);
+            ++li;
+            bits &= bits - 1u;
+        }
+    }
 }
 
 // Per-wave list of the wave's terminators (LDS): entry = position within the
@@ -773,7 +875,7 @@ __global__ void __launch_bounds__(kFastBlock) csv_emit_kernel(FastParams p)
 {
     using Gm = Geo<CB>;
     __shared__ Pass2Shared<V8, Gm::E> sh;
-    __shared__ GCarry s_wc[2][kFastWaves];
+    __shared__ GCarry s_wc[kSpanScratch];
     __shared__ GCarry s_wg[kFastWaves];
     __shared__ uint32_t s_list[kFastWaves][kWaveList];
 
@@ -799,7 +901,7 @@ __global__ void __launch_bounds__(kFastBlock) csv_emit_kernel(FastParams p)
         const uint32_t ts1 = vat(v0, run);
         uint64_t T[2], RD[2];
         span_tags<CB, V8, FULL>(p, c, in, run, ts1, sh, T, RD, nullptr);
-        const SpanCarry sc = span_carry(T, RD, c.abs, s_wc[it & 1]);
+        const SpanCarry sc = span_carry(T, RD, c.abs, s_wc);
 
         // the wave's fields: super-tile-local indices [wfirst, wend); the state at its first field
         const uint32_t mine = sc.mine, first = sc.wave_excl.nf + sc.excl_nf;
@@ -813,19 +915,11 @@ __global__ void __launch_bounds__(kFastBlock) csv_emit_kernel(FastParams p)
         for (uint32_t w0 = wfirst; w0 < wend; w0 += kWaveList) {
             const uint32_t w1 = min(w0 + (uint32_t)kWaveList, wend);
             // (1) each lane lists its terminators that fall in [w0, w1)
-            if (mine && first < w1 && first + mine > w0) {
-                uint32_t li = first;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint32_t bits = (uint32_t)(T[q >> 1] >> (32 * (q & 1)));
-                    const uint32_t rdw = (uint32_t)(RD[q >> 1] >> (32 * (q & 1)));
-                    while (bits && li < w1) {
-                        const uint32_t j = (uint32_t)__builtin_ctz(bits);
-                        if (li >= w0) list[li - w0] = ((rel0 + 32u * q + j) << 1) | ((rdw >> j) & 1u);
-                        ++li;
-                        bits &= bits - 1u;
-                    }
-                }
+            {
+                const uint32_t tw[4] = {(uint32_t)T[0], (uint32_t)(T[0] >> 32), (uint32_t)T[1], (uint32_t)(T[1] >> 32)};
+                const uint32_t rw[4] = {(uint32_t)RD[0], (uint32_t)(RD[0] >> 32), (uint32_t)RD[1],
+                                        (uint32_t)(RD[1] >> 32)};
+                list_terminators<4>(list, tw, rw, rel0, first, mine, w0, w1);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -995,7 +1089,7 @@ struct FusedShared {
     Pass2Shared<V8, Geo<CB>::E> p2;
     Vec wv[kFastWaves];
     Vec pv[kFastWaves];
-    GCarry wc[kFastWaves];
+    GCarry wc[kSpanScratch];
     GCarry pc[kFastWaves];
     int first[kFastWaves];
     uint32_t next, state, last_rec;
@@ -1145,19 +1239,10 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
             const uint32_t rel0 = (uint32_t)tid * (uint32_t)kFastChunk;
             for (uint32_t w0 = wfirst; w0 < wend; w0 += kFusedList) {
                 const uint32_t w1 = min(w0 + (uint32_t)kFusedList, wend);
-                if (mine && first < w1 && first + mine > w0) {
-                    uint32_t li = first;
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        uint32_t bits = (uint32_t)(T2 >> (32 * q));
-                        const uint32_t rdw = (uint32_t)(RD2 >> (32 * q));
-                        while (bits && li < w1) {
-                            const uint32_t j = (uint32_t)__builtin_ctz(bits);
-                            if (li >= w0) list[li - w0] = ((rel0 + 32u * q + j) << 1) | ((rdw >> j) & 1u);
-                            ++li;
-                            bits &= bits - 1u;
-                        }
-                    }
+                {
+                    const uint32_t tw[2] = {(uint32_t)T2, (uint32_t)(T2 >> 32)};
+                    const uint32_t rw[2] = {(uint32_t)RD2, (uint32_t)(RD2 >> 32)};
+                    list_terminators<2>(list, tw, rw, rel0, first, mine, w0, w1);
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
