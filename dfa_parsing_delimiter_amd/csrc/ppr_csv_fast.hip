@@ -808,53 +808,6 @@ __global__ void __launch_bounds__(kFastBlock) csv_carries_kernel(FastParams p)
     }
 }
 
-// a 64-bit value the whole wave holds, in scalar registers (a store to
-// base + uniform + lane then takes a scalar base and a 32-bit lane offset)
-__device__ __forceinline__ uint64_t uniform64(uint64_t v)
-{
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// Lists a lane's terminators that fall in the window [w0, w1) of wave-local
-// field indices into the wave's LDS list (entry = position << 1 | record bit,
-// positions from rel0 on). The lane's fields are [first, first + mine); tw / rw:
-// its terminator / record bitmaps as 32-bit words (bit j of word q = byte
-// 32 q + j). When all of them fall in the window (the usual case) the loop
-// runs without index checks.
-template <int NWORDS>
-__device__ __forceinline__ void list_terminators(uint32_t* list, const uint32_t (&tw)[NWORDS],
-                                                 const uint32_t (&rw)[NWORDS], uint32_t rel0, uint32_t first,
-                                                 uint32_t mine, uint32_t w0, uint32_t w1)
-{
-    if (!(mine && first < w1 && first + mine > w0)) return;
-    if (first >= w0 && first + mine <= w1) {
-        uint32_t* dst = list + (first - w0);
-#pragma unroll
-        for (int q = 0; q < NWORDS; ++q) {
-            uint32_t bits = tw[q];
-            const uint32_t base2 = (rel0 + 32u * q) << 1;
-            while (bits) {
-                const uint32_t j = (uint32_t)__builtin_ctz(bits);
-                *dst++ = base2 + (j << 1) + ((rw[q] >> j) & 1u);
-                bits &= bits - 1u;
-            }
-        }
-        return;
-    }
-    uint32_t li = first;
-#pragma unroll
-    for (int q = 0; q < NWORDS; ++q) {
-        uint32_t bits = tw[q];
-        while (bits && li < w1) {
-            const uint32_t j = (uint32_t)__builtin_ctz(bits);
-            if (li >= w0) list[li - w0] = ((rel0 + 32u * q + j) << 1) | ((rw[q] >> j) & 1u);
-            ++li;
-            bits &= bits - 1u;
-        }
-    }
-}
 
 // Per-wave list of the wave's terminators (LDS): entry = position within the
 // super-tile << 1 | record-delimiter bit, in field order.

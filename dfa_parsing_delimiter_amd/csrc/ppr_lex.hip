@@ -129,8 +129,12 @@ __global__ void lex_reset_kernel(WsHeader* hdr)
 
 __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
 {
-    __shared__ __align__(16) uint8_t s_bytes[kLexBlock * kLexMaxChunk];
-    __shared__ uint16_t s_kind[kLexBlock * kLexMaxChunk];
+    // dynamic LDS, sized for the call's chunk length L: the tile's bytes, then the
+    // kind of the token ending before each byte (3 L bytes per thread, so that
+    // short chunks leave room for more workgroups per CU)
+    extern __shared__ __align__(16) uint8_t s_dyn[];
+    uint8_t* s_bytes = s_dyn;
+    uint16_t* s_kind = reinterpret_cast<uint16_t*>(s_dyn + kLexBlock * p.L);
     __shared__ uint8_t s_col[256];
     __shared__ uint32_t s_wid[kLexWaves], s_pid[kLexWaves];
     __shared__ TokCarry s_wtok[kLexWaves], s_ptok[kLexWaves];
@@ -220,21 +224,46 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
     __syncthreads();
     const TokCarry P = s_prefix;
 
+    // Tokens, written by waves: each lane lists its boundaries (tile positions)
+    // in the wave's LDS list, laid over the tile's bytes (pass 2 is done with
+    // them: barriers since), then lane l of a round takes token r + l. Its end
+    // is its boundary, its start the previous one (the lane before, by DPP), so
+    // the three output arrays are written with consecutive addresses.
     {
-        uint64_t ti = (uint64_t)P.nt + cex.nt;
-        uint32_t st = max(P.lb, cex.lb);
-        uint64_t bits = B;
-        while (bits) {
-            const uint32_t j = (uint32_t)__ffsll((unsigned long long)bits) - 1u;
-            const uint32_t pos = chunk_abs + j;
-            if (ti < p.cap) {
-                p.kind[ti] = s_kind[pos0 + j];
-                p.start[ti] = st;
-                p.len[ti] = pos - st;
+        const uint32_t lane = (uint32_t)lane_id();
+        const uint32_t lcap = kLexBlock * L / 4u / kLexWaves;  // per-wave list entries over the tile's bytes
+        uint32_t* list = reinterpret_cast<uint32_t*>(s_bytes) + (tid / kWave) * lcap;
+        const uint32_t mine = c.nt;
+        const uint32_t wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)cex.nt);  // tokens before the wave
+        const uint32_t first = cex.nt - wbase;
+        const uint32_t wcnt = (uint32_t)__builtin_amdgcn_readlane((int)(first + mine), kWave - 1);
+        uint32_t off_run = max(P.lb, (uint32_t)__builtin_amdgcn_readfirstlane((int)cex.lb));
+        const uint32_t tw[2] = {(uint32_t)B, (uint32_t)(B >> 32)}, rw[2] = {0u, 0u};
+        for (uint32_t w0 = 0; w0 < wcnt; w0 += lcap) {
+            const uint32_t w1 = min(w0 + lcap, wcnt);
+            list_terminators<2>(list, tw, rw, pos0, first, mine, w0, w1);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            for (uint32_t r = w0; r < w1; r += kWave) {
+                const uint32_t cnt = min((uint32_t)kWave, w1 - r);
+                const uint32_t e = list[r - w0 + min(lane, cnt - 1u)] >> 1;
+                const uint32_t pos = tile_start + e;
+                const uint32_t prev = dpp_t<0x138, 0xf>(0u, pos);  // wave_shr:1: the previous lane's boundary
+                const uint32_t st = lane ? prev : off_run;
+                const uint32_t kd = s_kind[e];
+                const uint64_t g0 = uniform64((uint64_t)P.nt + wbase + r);
+                const uint32_t room = g0 < p.cap ? (uint32_t)min<uint64_t>(p.cap - g0, (uint64_t)cnt) : 0u;
+                if (lane < room) {
+                    (p.kind + g0)[lane] = kd;
+                    (p.start + g0)[lane] = st;
+                    (p.len + g0)[lane] = pos - st;
+                }
+                off_run = (uint32_t)__builtin_amdgcn_readlane((int)pos, (int)cnt - 1);
             }
-            ++ti;
-            st = pos;
-            bits &= bits - 1;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
 
@@ -393,7 +422,7 @@ extern "C" int ppr_lex_async(const uint8_t* d_bytes, uint64_t n, const ppr_lex_t
     p.statA = (uint64_t*)(ws + lay.off_a);
     p.statB = (StatB*)(ws + lay.off_b);
     memcpy(p.col, prep->column_of, 256);
-    hipLaunchKernelGGL(lex_kernel, dim3(p.num_tiles), dim3(kLexBlock), 0, s, p);
+    hipLaunchKernelGGL(lex_kernel, dim3(p.num_tiles), dim3(kLexBlock), (size_t)kLexBlock * L * 3u, s, p);
     stage_event(opts, 2, s);
     if (hipGetLastError() != hipSuccess) return PPR_EHIP;
     return PPR_OK;
