@@ -30,6 +30,7 @@ namespace ppr {
 constexpr int kLexBlock = 256;
 constexpr int kLexWaves = kLexBlock / kWave;
 constexpr int kLexMaxChunk = 64;
+constexpr int kLexLdsKinds = 4096;  // final-state tables up to this many entries are read from LDS
 
 struct LexParams {
     const uint8_t* in;
@@ -132,9 +133,12 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
     // dynamic LDS, sized for the call's chunk length L: the tile's bytes, then the
     // kind of the token ending before each byte (3 L bytes per thread, so that
     // short chunks leave room for more workgroups per CU)
+    // (and, when k <= kLexLdsKinds, the final-state table after them)
     extern __shared__ __align__(16) uint8_t s_dyn[];
     uint8_t* s_bytes = s_dyn;
     uint16_t* s_kind = reinterpret_cast<uint16_t*>(s_dyn + kLexBlock * p.L);
+    uint16_t* s_final = s_kind + kLexBlock * p.L;
+    const bool lds_final = p.k <= (uint32_t)kLexLdsKinds;
     __shared__ uint8_t s_col[256];
     __shared__ uint32_t s_wid[kLexWaves], s_pid[kLexWaves];
     __shared__ TokCarry s_wtok[kLexWaves], s_ptok[kLexWaves];
@@ -145,6 +149,8 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
     const int tid = threadIdx.x;
     if (tid == 0) s_tile = blockIdx.x;
     s_col[tid] = p.col[tid];
+    if (lds_final)
+        for (uint32_t i = tid; i < p.k; i += kLexBlock) s_final[i] = p.final_[i];
     __syncthreads();
     const uint32_t tile = s_tile;
     const uint32_t tile_start = tile * p.tile_bytes;
@@ -199,7 +205,7 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
         const uint32_t y = p.fold[prev * m + s_col[s_bytes[pos0 + j]]];
         if ((y & p.flag_mask) && (chunk_abs + j) != 0u) {
             B |= 1ull << j;
-            s_kind[pos0 + j] = p.final_[prev];
+            s_kind[pos0 + j] = lds_final ? s_final[prev] : p.final_[prev];
         }
         prev = y & p.id_mask;
     }
@@ -422,7 +428,8 @@ extern "C" int ppr_lex_async(const uint8_t* d_bytes, uint64_t n, const ppr_lex_t
     p.statA = (uint64_t*)(ws + lay.off_a);
     p.statB = (StatB*)(ws + lay.off_b);
     memcpy(p.col, prep->column_of, 256);
-    hipLaunchKernelGGL(lex_kernel, dim3(p.num_tiles), dim3(kLexBlock), (size_t)kLexBlock * L * 3u, s, p);
+    const size_t lds = (size_t)kLexBlock * L * 3u + (p.k <= (uint32_t)kLexLdsKinds ? (size_t)p.k * 2u : 0u);
+    hipLaunchKernelGGL(lex_kernel, dim3(p.num_tiles), dim3(kLexBlock), lds, s, p);
     stage_event(opts, 2, s);
     if (hipGetLastError() != hipSuccess) return PPR_EHIP;
     return PPR_OK;
