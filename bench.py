@@ -212,7 +212,7 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
-    chunk = args.chunk or 64
+    chunk = args.chunk or (40 if args.workload == "lex5" else 64)  # the library's defaults
     if args.summarize_pmc:
         summarize_pmc(args, chunk)
         return

@@ -67,7 +67,8 @@ class LexTablesC(ctypes.Structure):
 
 class LexPrepared(ctypes.Structure):
     _fields_ = [("d_fold", ctypes.c_void_p), ("k", ctypes.c_uint32), ("m", ctypes.c_uint32),
-                ("identity", ctypes.c_uint16), ("flag_mask", ctypes.c_uint16), ("column_of", ctypes.c_uint8 * 256)]
+                ("identity", ctypes.c_uint16), ("flag_mask", ctypes.c_uint16), ("column_of", ctypes.c_uint8 * 256),
+                ("n_states", ctypes.c_uint32)]
 
 
 class TokensOut(ctypes.Structure):

@@ -20,6 +20,9 @@
 //   * each thread re-folds its chunk from its true prefix identifier, marks token
 //     boundaries in a bitmap, and a second look-back scans token counts; tokens
 //     are written as (kind, start, length) directly.
+#include <map>
+#include <vector>
+
 #include "ppr.h"
 #include "ppr_device.h"
 #include "ppr_host.h"
@@ -31,6 +34,7 @@ constexpr int kLexBlock = 256;
 constexpr int kLexWaves = kLexBlock / kWave;
 constexpr int kLexMaxChunk = 64;
 constexpr int kLexLdsKinds = 4096;  // final-state tables up to this many entries are read from LDS
+constexpr uint32_t kLexLdsStep = 48u << 10;  // minimal automata up to this size are stepped from LDS
 
 struct LexParams {
     const uint8_t* in;
@@ -41,6 +45,10 @@ struct LexParams {
     const uint16_t* merge;  // k x k
     const uint16_t* fold;   // k x m
     const uint16_t* final_;
+    const uint16_t* state_of;  // minimal automaton (nq > 0): state of each identifier,
+    const uint32_t* step;      //   per state and column: successor | flag << 16,
+    const uint16_t* state_kind;  //   per state: token kind
+    uint32_t nq;                 // its states; 0: pass 2 re-folds the identifiers
     uint32_t* kind;
     uint32_t* start;
     uint32_t* len;
@@ -138,7 +146,10 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
     uint8_t* s_bytes = s_dyn;
     uint16_t* s_kind = reinterpret_cast<uint16_t*>(s_dyn + kLexBlock * p.L);
     uint16_t* s_final = s_kind + kLexBlock * p.L;
-    const bool lds_final = p.k <= (uint32_t)kLexLdsKinds;
+    const bool use_min = p.nq != 0;
+    const bool lds_final = !use_min && p.k <= (uint32_t)kLexLdsKinds;
+    uint32_t* s_step = reinterpret_cast<uint32_t*>(s_final);  // (use_min: in place of the final-state table)
+    uint16_t* s_qkind = reinterpret_cast<uint16_t*>(s_step + (use_min ? p.nq * p.m : 0u));
     __shared__ uint8_t s_col[256];
     __shared__ uint32_t s_wid[kLexWaves], s_pid[kLexWaves];
     __shared__ TokCarry s_wtok[kLexWaves], s_ptok[kLexWaves];
@@ -151,6 +162,10 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
     s_col[tid] = p.col[tid];
     if (lds_final)
         for (uint32_t i = tid; i < p.k; i += kLexBlock) s_final[i] = p.final_[i];
+    if (use_min) {
+        for (uint32_t i = tid; i < p.nq * p.m; i += kLexBlock) s_step[i] = p.step[i];
+        for (uint32_t i = tid; i < p.nq; i += kLexBlock) s_qkind[i] = p.state_kind[i];
+    }
     __syncthreads();
     const uint32_t tile = s_tile;
     const uint32_t tile_start = tile * p.tile_bytes;
@@ -198,16 +213,29 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
     __syncthreads();
     const uint32_t tile_prefix = s_prefix_id;
 
-    // pass 2: re-fold from the true prefix and mark boundaries
+    // pass 2: from the true prefix, mark boundaries. With the minimal automaton
+    // this steps a few states in LDS; otherwise it re-folds the identifiers.
     uint32_t prev = merge_ids(p, tile_prefix, excl);
     uint64_t B = 0;
-    for (uint32_t j = 0; j < my_len; ++j) {
-        const uint32_t y = p.fold[prev * m + s_col[s_bytes[pos0 + j]]];
-        if ((y & p.flag_mask) && (chunk_abs + j) != 0u) {
-            B |= 1ull << j;
-            s_kind[pos0 + j] = lds_final ? s_final[prev] : p.final_[prev];
+    if (use_min) {
+        uint32_t qs = p.state_of[prev];
+        for (uint32_t j = 0; j < my_len; ++j) {
+            const uint32_t e = s_step[qs * m + s_col[s_bytes[pos0 + j]]];
+            if ((e >> 16) && (chunk_abs + j) != 0u) {
+                B |= 1ull << j;
+                s_kind[pos0 + j] = s_qkind[qs];
+            }
+            qs = e & 0xffffu;
         }
-        prev = y & p.id_mask;
+    } else {
+        for (uint32_t j = 0; j < my_len; ++j) {
+            const uint32_t y = p.fold[prev * m + s_col[s_bytes[pos0 + j]]];
+            if ((y & p.flag_mask) && (chunk_abs + j) != 0u) {
+                B |= 1ull << j;
+                s_kind[pos0 + j] = lds_final ? s_final[prev] : p.final_[prev];
+            }
+            prev = y & p.id_mask;
+        }
     }
     TokCarry c{(uint32_t)__popcll(B), B ? chunk_abs + (uint32_t)(63 - __clzll((long long)B)) : 0u};
     TokCarry cex, ctot;
@@ -306,10 +334,59 @@ __global__ void lex_fold_kernel(const uint16_t* merge, uint32_t k, ColumnIds col
     fold[i] = merge[x * k + cols.id[j]];
 }
 
+// Where the minimal automaton sits in the prepared buffer (after the k x m fold
+// entries): byte offsets of the state of each identifier, the step table and the
+// state kinds, and the end. Fits when end <= ppr_lex_fold_bytes(k).
+struct MinLayout {
+    uint64_t state_of, step, kind, end;
+};
+
+static MinLayout min_layout(uint32_t k, uint32_t m, uint32_t nq)
+{
+    MinLayout L;
+    L.state_of = align_up((uint64_t)k * m * 2u, 256);
+    L.step = align_up(L.state_of + (uint64_t)k * 2u, 256);
+    L.kind = align_up(L.step + (uint64_t)nq * m * 4u, 256);
+    L.end = L.kind + (uint64_t)nq * 2u;
+    return L;
+}
+
+// Minimal automaton of the identifier fold [L, "A lexer is a prefix scan": the
+// fold is a DFA over identifiers]. States are identifiers, symbols are columns;
+// reading column j in x outputs the flag of fold[x][j] and, with the flag, the
+// kind final[x] of the token it ends; final[x] is also the kind of a last token.
+// Refinement starts from the partition by (final[x], the flags of row x) and
+// splits by successor states until no state splits. Returns the state count.
+static uint32_t lex_minimize(const std::vector<uint16_t>& fold, const std::vector<uint16_t>& fin, uint32_t k,
+                             uint32_t m, uint32_t flag, uint32_t id_mask, std::vector<uint32_t>& cls)
+{
+    cls.assign(k, 0);
+    std::vector<uint32_t> sig(m + 1);
+    std::map<std::vector<uint32_t>, uint32_t> ids;
+    for (uint32_t x = 0; x < k; ++x) {
+        sig[0] = fin[x];
+        for (uint32_t j = 0; j < m; ++j) sig[1 + j] = (fold[(size_t)x * m + j] & flag) ? 1u : 0u;
+        cls[x] = ids.emplace(sig, (uint32_t)ids.size()).first->second;
+    }
+    uint32_t n = (uint32_t)ids.size();
+    std::vector<uint32_t> next(k);
+    for (;;) {
+        std::map<std::vector<uint32_t>, uint32_t> nids;
+        for (uint32_t x = 0; x < k; ++x) {
+            sig[0] = cls[x];
+            for (uint32_t j = 0; j < m; ++j) sig[1 + j] = cls[fold[(size_t)x * m + j] & id_mask];
+            next[x] = nids.emplace(sig, (uint32_t)nids.size()).first->second;
+        }
+        if ((uint32_t)nids.size() == n) return n;  // no state split: the partition is stable
+        n = (uint32_t)nids.size();
+        cls.swap(next);
+    }
+}
+
 static uint32_t lex_chunk_of(const ppr_parse_opts_t* o)
 {
     uint32_t L = o ? o->chunk_bytes : 0u;
-    if (L == 0) L = 32;
+    if (L == 0) L = 40;  // the default: measured fastest on the 40-rule token stream (32 to 56 within 10%)
     return L <= (uint32_t)kLexMaxChunk ? L : 0u;
 }
 
@@ -373,6 +450,39 @@ extern "C" int ppr_lex_prepare(const ppr_lex_tables_t* t, ppr_lex_prepared_t* pr
     hipLaunchKernelGGL(lex_fold_kernel, dim3(blocks), dim3(256), 0, s, t->merge_table, t->k, cols, m, prep->d_fold);
     if (hipGetLastError() != hipSuccess) return PPR_EHIP;
     if (hipStreamSynchronize(s) != hipSuccess) return PPR_EHIP;
+
+    // the minimal automaton of the fold, stored after it in the same buffer
+    prep->n_states = 0;
+    std::vector<uint16_t> fold(total), fin(t->k);
+    if (hipMemcpy(fold.data(), prep->d_fold, total * 2u, hipMemcpyDeviceToHost) != hipSuccess) return PPR_EHIP;
+    if (hipMemcpy(fin.data(), t->final_states, (size_t)t->k * 2u, hipMemcpyDeviceToHost) != hipSuccess)
+        return PPR_EHIP;
+    std::vector<uint32_t> cls;
+    const uint32_t id_mask = (uint32_t)(uint16_t)~t->flag_mask;
+    const uint32_t nq = lex_minimize(fold, fin, t->k, m, t->flag_mask, id_mask, cls);
+    const MinLayout ml = min_layout(t->k, m, nq);
+    if (ml.end <= ppr_lex_fold_bytes(t->k)) {
+        std::vector<uint16_t> state_of(t->k), qkind(nq);
+        std::vector<uint32_t> step((size_t)nq * m), rep(nq, 0xffffffffu);
+        for (uint32_t x = 0; x < t->k; ++x) {
+            state_of[x] = (uint16_t)cls[x];
+            if (rep[cls[x]] == 0xffffffffu) rep[cls[x]] = x;
+        }
+        for (uint32_t q = 0; q < nq; ++q) {
+            const uint32_t x = rep[q];
+            qkind[q] = fin[x];
+            for (uint32_t j = 0; j < m; ++j) {
+                const uint32_t y = fold[(size_t)x * m + j];
+                step[(size_t)q * m + j] = cls[y & id_mask] | ((y & t->flag_mask) ? 0x10000u : 0u);
+            }
+        }
+        uint8_t* base = reinterpret_cast<uint8_t*>(prep->d_fold);
+        if (hipMemcpy(base + ml.state_of, state_of.data(), (size_t)t->k * 2u, hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemcpy(base + ml.step, step.data(), step.size() * 4u, hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemcpy(base + ml.kind, qkind.data(), (size_t)nq * 2u, hipMemcpyHostToDevice) != hipSuccess)
+            return PPR_EHIP;
+        prep->n_states = nq;
+    }
     return PPR_OK;
 }
 
@@ -428,7 +538,20 @@ extern "C" int ppr_lex_async(const uint8_t* d_bytes, uint64_t n, const ppr_lex_t
     p.statA = (uint64_t*)(ws + lay.off_a);
     p.statB = (StatB*)(ws + lay.off_b);
     memcpy(p.col, prep->column_of, 256);
-    const size_t lds = (size_t)kLexBlock * L * 3u + (p.k <= (uint32_t)kLexLdsKinds ? (size_t)p.k * 2u : 0u);
+    // the minimal automaton steps pass 2 when it fits the LDS budget
+    p.nq = 0;
+    if (prep->n_states && (uint64_t)prep->n_states * prep->m * 4u + prep->n_states * 2u <= kLexLdsStep &&
+        min_layout(prep->k, prep->m, prep->n_states).end <= ppr_lex_fold_bytes(prep->k)) {
+        const MinLayout ml = min_layout(prep->k, prep->m, prep->n_states);
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(prep->d_fold);
+        p.nq = prep->n_states;
+        p.state_of = reinterpret_cast<const uint16_t*>(base + ml.state_of);
+        p.step = reinterpret_cast<const uint32_t*>(base + ml.step);
+        p.state_kind = reinterpret_cast<const uint16_t*>(base + ml.kind);
+    }
+    const size_t lds = (size_t)kLexBlock * L * 3u +
+                       (p.nq ? (size_t)p.nq * p.m * 4u + p.nq * 2u
+                             : (p.k <= (uint32_t)kLexLdsKinds ? (size_t)p.k * 2u : 0u));
     hipLaunchKernelGGL(lex_kernel, dim3(p.num_tiles), dim3(kLexBlock), lds, s, p);
     stage_event(opts, 2, s);
     if (hipGetLastError() != hipSuccess) return PPR_EHIP;

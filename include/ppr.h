@@ -117,7 +117,7 @@ enum { PPR_PATH_STREAMING = 1, PPR_PATH_SINGLE_PASS = 2, PPR_PATH_FUSED = 3 };
 
 /*
  * Launch options (opts may be NULL: all defaults).
- *   chunk_bytes:    bytes each thread simulates, 1..64; 0 = 64.
+ *   chunk_bytes:    bytes each thread simulates, 1..64; 0 = 64 (parse) or 40 (lexer).
  *   stage_events:   optional array of n_stage_events hipEvent_t (caller-created):
  *                   event 0 is recorded on the stream before the first kernel of the
  *                   call and event i after its i-th kernel, as far as the array
@@ -189,7 +189,12 @@ typedef struct ppr_lex_tables {
  * Prepared form of the tables for the kernels, filled by ppr_lex_prepare:
  * bytes with the same initial identifier share a column, and d_fold holds,
  * for every identifier x and column j, merge_table[x][column j's identifier]
- * (k * m entries, device memory the caller provides).
+ * (k * m entries, device memory the caller provides). After those entries the
+ * same buffer holds the minimal automaton of that fold (identifiers that give
+ * the same flags and token kinds on every continuation share a state; found by
+ * partition refinement): the state of each identifier, and per state and
+ * column its successor state and flag, and its token kind. Lexing from a known
+ * prefix (the second pass over a chunk) steps through this small automaton.
  */
 typedef struct ppr_lex_prepared {
     uint16_t* d_fold;      /* caller-provided device buffer of ppr_lex_fold_bytes(k) bytes */
@@ -198,6 +203,7 @@ typedef struct ppr_lex_prepared {
     uint16_t identity;
     uint16_t flag_mask;
     uint8_t column_of[256]; /* out: column of each byte */
+    uint32_t n_states;     /* out: states of the minimal automaton (0: it does not fit the buffer; not used) */
 } ppr_lex_prepared_t;
 
 /* Device bytes the prepared fold table needs (k * 256 * 2 at most). */

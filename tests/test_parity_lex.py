@@ -63,13 +63,13 @@ def test_golden(ppr, tables):
         c = json.loads(line)
         d, T = tables[c["grammar"]]
         b = c["input"].encode()
-        for chunk in (1, 2, 32):
+        for chunk in (1, 2, 32, None):
             _say("golden", repr(b), chunk)
             g = ppr.lex(_dev(b), T, chunk_bytes=chunk, capacity=len(b) + 1)
             _same(g, oracle.lex_restart(b, d), (b, chunk))
 
 
-@pytest.mark.parametrize("chunk", [1, 3, 16, 31, 32, 64])
+@pytest.mark.parametrize("chunk", [1, 3, 16, 31, 32, 40, 64])
 def test_streams_several_tiles(ppr, tables, chunk):
     d, T = tables["lexer"]
     for seed in (1, 2):
@@ -86,10 +86,26 @@ def test_random_bytes_and_edges(ppr, tables):
     cases = [b"", b"a", b"@", b"//" + b"x" * 70000, b'"' + b"q" * 70001, b" " * 100000, b"1." * 30000]
     cases += [rng.integers(0, 256, int(rng.integers(1, 50000)), dtype=np.uint8).tobytes() for _ in range(6)]
     for b in cases:
-        for chunk in (1, 7, 32):
+        for chunk in (1, 7, 32, None):
             _say("edge", len(b), chunk)
             g = ppr.lex(_dev(b) if b else _dev(b"\0")[:0], T, chunk_bytes=chunk, capacity=len(b) + 1)
             _same(g, oracle.lex_restart(b, d), (len(b), chunk))
+
+
+def test_minimal_automaton_and_identifier_fold(ppr, tables):
+    """the second pass steps the minimal automaton of the fold when the prepared tables hold one, and re-folds
+    the identifiers otherwise; both against the oracle"""
+    d, T = tables["lexer"]
+    assert 0 < T.prep.n_states <= T.k, T.prep.n_states
+    b = W.gen_tokens(3, (1 << 20) + 5)
+    r = oracle.lex_restart(b, d)
+    _same(ppr.lex(_dev(b), T, capacity=b.size + 1), r, "minimal automaton")
+    saved = T.prep.n_states
+    T.prep.n_states = 0
+    try:
+        _same(ppr.lex(_dev(b), T, capacity=b.size + 1), r, "identifier fold")
+    finally:
+        T.prep.n_states = saved
 
 
 @pytest.mark.slow
