@@ -17,7 +17,7 @@
 //     input and a class map with one catch-all class and at most 8 other bytes:
 //     five kernels with no inter-workgroup waiting;
 //   * the generic single-pass kernel here (any table, chunk size 1..64): one
-//     workgroup per tile of 256 chunks, bytes staged through LDS, the two
+//     workgroup per tile of 1024 chunks, bytes staged through LDS, the two
 //     device-wide scans (state vectors, then count carries) as decoupled
 //     look-backs in which every wave reads 64 predecessors per round; a
 //     state-transition vector is one byte per state in two VGPRs, so a composite
@@ -266,7 +266,7 @@ __global__ void __launch_bounds__(kBlock) csv_generic_kernel(CsvParams p)
         s_tile = blockIdx.x;
         sh.last_rec = 0;
     }
-    s_cls[tid] = p.cls[tid];
+    if (tid < 256) s_cls[tid] = p.cls[tid];
     if (tid < PPR_MAX_STATES * PPR_MAX_CLASSES) s_nt[tid] = (&p.nt[0][0])[tid];
     if (tid < PPR_MAX_CLASSES) {
         s_rlo[tid] = p.row_lo[tid];

@@ -12,7 +12,8 @@
 
 namespace ppr {
 
-constexpr int kBlock = 256;      // generic path: threads per tile
+constexpr int kBlock = 1024;     // generic path: threads per tile (a look-back round covers as many tiles as the
+                                 // device holds at once: 2 workgroups per CU)
 constexpr int kWaves = kBlock / kWave;
 constexpr int kFastBlock = 512;  // fast path: threads per tile
 constexpr int kFastWaves = kFastBlock / kWave;

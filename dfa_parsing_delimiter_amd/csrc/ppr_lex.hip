@@ -10,7 +10,7 @@
 //
 // MI355X mapping (not the page's Futhark map/scan/filter/gather pipeline, which
 // materialises ~20 bytes of state per input byte):
-//   * nothing per byte is materialised in HBM: a tile of 256*L bytes is staged
+//   * nothing per byte is materialised in HBM: a tile of 512*L bytes is staged
 //     once into LDS, each thread folds its chunk sequentially (a chunk only ever
 //     merges with single-byte elements, so the fold reads a k x m "fold" table —
 //     the merge table restricted to the m distinct byte identifiers — that fits
@@ -30,7 +30,7 @@
 
 namespace ppr {
 
-constexpr int kLexBlock = 256;
+constexpr int kLexBlock = 512;  // threads per tile: a look-back round covers 512 tiles
 constexpr int kLexWaves = kLexBlock / kWave;
 constexpr int kLexMaxChunk = 64;
 constexpr int kLexLdsKinds = 4096;  // final-state tables up to this many entries are read from LDS
@@ -159,7 +159,7 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
 
     const int tid = threadIdx.x;
     if (tid == 0) s_tile = blockIdx.x;
-    s_col[tid] = p.col[tid];
+    if (tid < 256) s_col[tid] = p.col[tid];
     if (lds_final)
         for (uint32_t i = tid; i < p.k; i += kLexBlock) s_final[i] = p.final_[i];
     if (use_min) {
