@@ -254,10 +254,20 @@ __device__ Vec ragged_vector(const FastParams& p, const ChunkPos& c, Vec v, cons
     return v;
 }
 
-// Pass-2 table entry: bits 0-15 the byte offset of the next state's row,
-// 16..16+G-1 terminator bits, 20..20+G-1 record-delimiter bits, 24-26 the
-// first INVALID byte of the group, 31 some byte is INVALID.
-constexpr uint32_t kRowMask = 0xffffu;
+// Pass-2 table: one row of kRowStride entries per state code (row nt: the
+// absorbing state), entry e = the table index of a group of G symbols. Entry
+// bits 8-15 hold the next state's row, 16..16+G-1 the terminator bits,
+// 20..20+G-1 the record-delimiter bits, 24-26 the first INVALID byte of the
+// group, 31 some byte is INVALID. With the row in byte 1, the next lookup's
+// word index (row << 8 | index byte) is one v_perm of the previous entry and
+// the packed index word.
+constexpr int kRowStride = 256;
+
+// word index of the lookup for index byte i of idxw after entry prev
+__device__ __forceinline__ uint32_t p2_index(uint32_t prev, uint32_t idxw, int i)
+{
+    return perm(prev, idxw, 0x0c0c0500u | (uint32_t)i);
+}
 
 // the 64 bits of each kind from the gathered tag bytes of 8 groups of 4 bytes
 // (byte g of w0/w1 = terminator nibble | record nibble << 4 of group g / 4 + g)
@@ -272,17 +282,19 @@ __device__ __forceinline__ void nibbles_to_bits(uint32_t w0, uint32_t w1, uint32
 
 // Pass 2 over NCH consecutive full chunks of a thread (NCH NI groups, packed
 // four index bytes per word in pw) from state code s: a chain of pass-2
-// lookups, one per group, each addressed by the previous entry's row offset.
+// lookups, one per group, each addressed by the previous entry (p2_index).
 // T[h] / RD[h]: terminator / record bitmaps of chunk h (bit j = byte j).
-// Returns the OR of the entries (bit 31: some byte is INVALID).
+// Returns the OR of the entries (bit 31: some byte is INVALID). (Cutting the
+// chain into independent runs, with start states from the pass-1 table, costs
+// more instructions than the shorter LDS wait saves: these kernels are bound by
+// instruction issue.)
 template <int CB, int NCH>
 __device__ __forceinline__ uint32_t pass2_run(const uint32_t (&pw)[NCH * Geo<CB>::NP], uint32_t s, uint32_t nt,
                                               const uint32_t* s_t2, uint64_t (&T)[NCH], uint64_t (&RD)[NCH])
 {
-    constexpr int E = Geo<CB>::E, NG = NCH * Geo<CB>::NI, G = Geo<CB>::G;
+    constexpr int NG = NCH * Geo<CB>::NI, G = Geo<CB>::G;
     constexpr uint32_t GM = Geo<CB>::GM;
-    const char* base = reinterpret_cast<const char*>(s_t2);
-    uint32_t row = min(s, nt) * (uint32_t)(E * 4);
+    uint32_t prev = min(s, nt) << 8;
     uint32_t any = 0;
     if constexpr (G == 4) {
         // the tag byte (bits 16-23) of four consecutive entries gathered into one word
@@ -292,9 +304,8 @@ __device__ __forceinline__ uint32_t pass2_run(const uint32_t (&pw)[NCH * Geo<CB>
             uint32_t e[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t ix = (pw[q] >> (8 * i)) & 0xffu;
-                e[i] = *reinterpret_cast<const uint32_t*>(base + row + ix * 4u);
-                row = e[i] & kRowMask;
+                e[i] = s_t2[p2_index(prev, pw[q], i)];
+                prev = e[i];
                 any |= e[i];
             }
             w[q] = perm(e[1], e[0], 0x0c0c0602u) | perm(e[3], e[2], 0x06020c0cu);
@@ -313,9 +324,8 @@ __device__ __forceinline__ uint32_t pass2_run(const uint32_t (&pw)[NCH * Geo<CB>
         for (int i = 0; i < 2 * NCH; ++i) tw[i] = rw[i] = 0u;
 #pragma unroll
         for (int k = 0; k < NG; ++k) {
-            const uint32_t ix = (pw[k / 4] >> (8 * (k % 4))) & 0xffu;
-            const uint32_t e = *reinterpret_cast<const uint32_t*>(base + row + ix * 4u);
-            row = e & kRowMask;
+            const uint32_t e = s_t2[p2_index(prev, pw[k / 4], k % 4)];
+            prev = e;
             any |= e;
             tw[(G * k) / 32] |= ((e >> 16) & GM) << ((G * k) % 32);
             rw[(G * k) / 32] |= ((e >> 20) & GM) << ((G * k) % 32);
@@ -341,15 +351,13 @@ template <int CB, int NCH>
 __device__ uint32_t first_invalid(const uint32_t (&pw)[NCH * Geo<CB>::NP], uint32_t s, uint32_t nt,
                                   const uint32_t* s_t2, uint32_t abs)
 {
-    constexpr int E = Geo<CB>::E, NG = NCH * Geo<CB>::NI, G = Geo<CB>::G;
-    const char* base = reinterpret_cast<const char*>(s_t2);
-    uint32_t row = min(s, nt) * (uint32_t)(E * 4), first = kNone;
+    constexpr int NG = NCH * Geo<CB>::NI, G = Geo<CB>::G;
+    uint32_t prev = min(s, nt) << 8, first = kNone;
 #pragma unroll
     for (int k = 0; k < NG; ++k) {  // (no early exit: indices into pw stay compile-time constants)
-        const uint32_t ix = (pw[k / 4] >> (8 * (k % 4))) & 0xffu;
-        const uint32_t e = *reinterpret_cast<const uint32_t*>(base + row + ix * 4u);
+        const uint32_t e = s_t2[p2_index(prev, pw[k / 4], k % 4)];
         if ((e >> 31) && first == kNone) first = abs + (uint32_t)(G * k) + ((e >> 24) & 7u);
-        row = e & kRowMask;
+        prev = e;
     }
     return first;
 }
@@ -477,7 +485,7 @@ __global__ void csv_fast_tables_kernel(FastParams p)
                 if (t == PPR_TAG_INVALID && !(ent >> 31)) ent |= (1u << 31) | ((uint32_t)g << 24);
                 s = ns == kAbs ? nt : ns;
             }
-            t2[r * E + e] = ent | (s * (uint32_t)E * 4u);
+            t2[r * kRowStride + e] = ent | (s << 8);
         }
     }
 }
@@ -636,7 +644,7 @@ __global__ void __launch_bounds__(kWave) csv_range_vec_kernel(FastParams p)
 // pass-2 table rows (tracked states + the absorbing row) and the byte tables
 template <bool V8, int E>
 struct Pass2Shared {
-    uint32_t t2[(V8 ? 9 : 5) * E];
+    uint32_t t2[(V8 ? 9 : 5) * kRowStride];
     uint8_t nxt[9 * 16], tag[9 * 16];
 };
 
@@ -645,7 +653,7 @@ __device__ __forceinline__ void load_pass2(const FastParams& p, Pass2Shared<V8, 
 {
     constexpr int E = Geo<CB>::E;
     const uint32_t* t2g = p.tabs + (V8 ? 2 : 1) * E;
-    const int words = (int)(p.nt + 1) * E;
+    const int words = (int)(p.nt + 1) * kRowStride;
     for (int i = threadIdx.x; i < words; i += kFastBlock) sh.t2[i] = t2g[i];
     if (threadIdx.x < 9 * 16) {
         sh.nxt[threadIdx.x] = (&p.nxt[0][0])[threadIdx.x];
