@@ -817,6 +817,43 @@ __global__ void __launch_bounds__(kFastBlock) csv_carries_kernel(FastParams p)
 }
 
 
+// Running values of a wave's field emission (wave-uniform): the record index,
+// column and offset of its next field.
+struct FieldRun {
+    uint32_t rec, col, off;
+};
+
+// One round of at most 64 of a wave's fields: lane l writes field g0 + l (g0
+// wave-uniform) from its list entry e (position - base << 1 | record bit). The
+// record index is the running one plus the record bits of the earlier lanes
+// (mbcnt), the column counts from the last record field before the lane, the
+// offset follows the previous lane's terminator (DPP). The four arrays are
+// written through wave-uniform base pointers, so every store is one scalar
+// base plus the lane's offset. cap32: the output capacity clamped to 32 bits;
+// lt_mask: the lanes below this one.
+__device__ __forceinline__ void field_round(const OutArrays& o, uint32_t cap32, uint32_t g0, uint32_t cnt, uint32_t e,
+                                            uint32_t base, uint32_t lane, uint64_t lt_mask, FieldRun& fr)
+{
+    const uint32_t pos = base + (e >> 1);
+    const uint64_t m = __ballot(lane < cnt && (e & 1u));
+    const uint64_t below = m & lt_mask;
+    const uint32_t rec =
+        fr.rec + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    const uint32_t col = below ? lane - (uint32_t)(63 - __clzll((long long)below)) - 1u : fr.col + lane;
+    const uint32_t prev = dpp_t<0x138, 0xf>(0u, pos);  // wave_shr:1: the previous lane's terminator
+    const uint32_t off = lane ? prev + 1u : fr.off;
+    const uint32_t room = g0 < cap32 ? min(cap32 - g0, cnt) : 0u;
+    if (lane < room) {
+        store_u32(o.rec + g0, lane, rec);
+        store_u32(o.col + g0, lane, col);
+        store_u32(o.off + g0, lane, off);
+        store_u32(o.len + g0, lane, pos - off);
+    }
+    fr.rec += (uint32_t)__popcll(m);
+    fr.col = m ? (cnt - 1u) - (uint32_t)(63 - __clzll((long long)m)) : fr.col + cnt;
+    fr.off = (uint32_t)__builtin_amdgcn_readlane((int)pos, (int)cnt - 1) + 1u;
+}
+
 // Per-wave list of the wave's terminators (LDS): entry = position within the
 // super-tile << 1 | record-delimiter bit, in field order.
 constexpr int kWaveList = 1024;
@@ -848,6 +885,8 @@ __global__ void __launch_bounds__(kFastBlock) csv_emit_kernel(FastParams p)
     const Vec ident = fast_ident<V8>(p.nt);
     uint32_t run = p.range_state[b];
     const OutArrays& o = p.out;
+    const uint32_t cap32 = (uint32_t)min<uint64_t>(o.cap, 0xffffffffull);
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
     uint32_t* list = s_list[wv];
     load_pass2<CB, V8>(p, sh);
     const GCarryComb gcomb;
@@ -868,9 +907,8 @@ __global__ void __launch_bounds__(kFastBlock) csv_emit_kernel(FastParams p)
         const uint32_t mine = sc.mine, first = sc.wave_excl.nf + sc.excl_nf;
         const uint32_t wfirst = sc.wave_excl.nf;
         const uint32_t wend = __builtin_amdgcn_readlane(first + mine, kWave - 1);
-        uint32_t rec_run = P.nr + sc.wave_excl.nr;
-        uint32_t col_run = col_op(P.col, sc.wave_excl.col) & 0x7fffffffu;
-        uint32_t off_run = max(P.lt, sc.wave_excl.lt);
+        FieldRun fr{P.nr + sc.wave_excl.nr, col_op(P.col, sc.wave_excl.col) & 0x7fffffffu,
+                    (uint32_t)max(P.lt, sc.wave_excl.lt)};
         const uint32_t st_abs = st * (uint32_t)(2 * kFastTile);
         const uint32_t rel0 = c.abs - st_abs;
         for (uint32_t w0 = wfirst; w0 < wend; w0 += kWaveList) {
@@ -889,26 +927,7 @@ __global__ void __launch_bounds__(kFastBlock) csv_emit_kernel(FastParams p)
             // each lane stores at its own 4-byte offset
             for (uint32_t r = w0; r < w1; r += kWave) {
                 const uint32_t cnt = min((uint32_t)kWave, w1 - r);
-                const uint32_t e = list[r - w0 + min(lane, cnt - 1u)];
-                const uint32_t pos = st_abs + (e >> 1);
-                const uint64_t m = __ballot(lane < cnt && (e & 1u));
-                const uint64_t below = m & ((1ull << lane) - 1ull);
-                const uint32_t rec = rec_run + (uint32_t)__popcll(below);
-                const uint32_t col =
-                    below ? lane - (uint32_t)(63 - __clzll((long long)below)) - 1u : col_run + lane;
-                const uint32_t prev = dpp_t<0x138, 0xf>(0u, pos);  // wave_shr:1: the previous lane's terminator
-                const uint32_t off = lane ? prev + 1u : off_run;
-                const uint64_t g0 = uniform64((uint64_t)P.nf + r);
-                const uint32_t room = g0 < o.cap ? (uint32_t)min<uint64_t>(o.cap - g0, (uint64_t)cnt) : 0u;
-                if (lane < room) {
-                    (o.rec + g0)[lane] = rec;
-                    (o.col + g0)[lane] = col;
-                    (o.off + g0)[lane] = off;
-                    (o.len + g0)[lane] = pos - off;
-                }
-                rec_run += (uint32_t)__popcll(m);
-                col_run = m ? (cnt - 1u) - (uint32_t)(63 - __clzll((long long)m)) : col_run + cnt;
-                off_run = __builtin_amdgcn_readlane(pos, cnt - 1) + 1u;
+                field_round(o, cap32, P.nf + r, cnt, list[r - w0 + min(lane, cnt - 1u)], st_abs, lane, lt_mask, fr);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -1069,6 +1088,8 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
     const uint32_t wv = threadIdx.x / kWave;
     const uint32_t nt = p.nt, num_tiles = p.num_tiles;
     const OutArrays& o = p.out;
+    const uint32_t cap32 = (uint32_t)min<uint64_t>(o.cap, 0xffffffffull);
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
     const GCarryComb gcomb;
     const GCarry zero{0u, 0u, 0u, 0u};
     if (tid == 0) {
@@ -1194,9 +1215,8 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
             const uint32_t mine = sc2.mine, first = sc2.wave_excl.nf + sc2.excl_nf;
             const uint32_t wfirst = sc2.wave_excl.nf;
             const uint32_t wend = __builtin_amdgcn_readlane(first + mine, kWave - 1);
-            uint32_t rec_run = P.nr + sc2.wave_excl.nr;
-            uint32_t col_run = col_op(P.col, sc2.wave_excl.col) & 0x7fffffffu;
-            uint32_t off_run = max(P.lt, sc2.wave_excl.lt);
+            FieldRun fr{P.nr + sc2.wave_excl.nr, col_op(P.col, sc2.wave_excl.col) & 0x7fffffffu,
+                        (uint32_t)max(P.lt, sc2.wave_excl.lt)};
             const uint32_t rel0 = (uint32_t)tid * (uint32_t)kFastChunk;
             for (uint32_t w0 = wfirst; w0 < wend; w0 += kFusedList) {
                 const uint32_t w1 = min(w0 + (uint32_t)kFusedList, wend);
@@ -1210,26 +1230,8 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 for (uint32_t r = w0; r < w1; r += kWave) {
                     const uint32_t cnt = min((uint32_t)kWave, w1 - r);
-                    const uint32_t e = list[r - w0 + min(lane, cnt - 1u)];
-                    const uint32_t pos = tile_start + (e >> 1);
-                    const uint64_t m = __ballot(lane < cnt && (e & 1u));
-                    const uint64_t below = m & ((1ull << lane) - 1ull);
-                    const uint32_t rec = rec_run + (uint32_t)__popcll(below);
-                    const uint32_t col =
-                        below ? lane - (uint32_t)(63 - __clzll((long long)below)) - 1u : col_run + lane;
-                    const uint32_t prev = dpp_t<0x138, 0xf>(0u, pos);  // wave_shr:1: the previous lane's terminator
-                    const uint32_t off = lane ? prev + 1u : off_run;
-                    const uint64_t g0 = uniform64((uint64_t)P.nf + r);
-                    const uint32_t room = g0 < o.cap ? (uint32_t)min<uint64_t>(o.cap - g0, (uint64_t)cnt) : 0u;
-                    if (lane < room) {
-                        (o.rec + g0)[lane] = rec;
-                        (o.col + g0)[lane] = col;
-                        (o.off + g0)[lane] = off;
-                        (o.len + g0)[lane] = pos - off;
-                    }
-                    rec_run += (uint32_t)__popcll(m);
-                    col_run = m ? (cnt - 1u) - (uint32_t)(63 - __clzll((long long)m)) : col_run + cnt;
-                    off_run = __builtin_amdgcn_readlane(pos, cnt - 1) + 1u;
+                    field_round(o, cap32, P.nf + r, cnt, list[r - w0 + min(lane, cnt - 1u)], tile_start, lane,
+                                lt_mask, fr);
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();

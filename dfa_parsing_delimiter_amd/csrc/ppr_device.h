@@ -114,6 +114,7 @@ __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1
 
 // ---------------------------------------------------------------- wave-level output staging
 
+
 // a 64-bit value the whole wave holds, in scalar registers (a store to
 // base + uniform + lane then takes a scalar base and a 32-bit lane offset)
 __device__ __forceinline__ uint64_t uniform64(uint64_t v)
@@ -121,6 +122,20 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v)
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
     return ((uint64_t)hi << 32) | lo;
+}
+
+// One store of v to base[lane] with base wave-uniform: the base goes through
+// readfirstlane into scalar registers and stays a global-address-space pointer,
+// so the compiler emits global_store_dword with a scalar base and the lane's
+// 32-bit offset (and handles the VALU-to-SGPR hazard itself). Indexing the
+// kernel-argument pointer directly instead lets the compiler hoist base + lane
+// into per-lane 64-bit addresses and add the uniform part before every store.
+typedef __attribute__((address_space(1))) uint32_t global_u32;
+
+__device__ __forceinline__ void store_u32(uint32_t* base, uint32_t lane, uint32_t v)
+{
+    global_u32* const g = (global_u32*)uniform64((uint64_t)(uintptr_t)base);
+    g[lane] = v;
 }
 
 // Lists a lane's terminators that fall in the window [w0, w1) of wave-local
