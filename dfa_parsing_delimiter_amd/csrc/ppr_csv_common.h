@@ -22,7 +22,7 @@ constexpr int kFastChunk = 64;   // fast path: bytes per thread
 constexpr int kFastTile = kFastBlock * kFastChunk;
 constexpr uint32_t kNone = 0xffffffffu;
 constexpr uint32_t kAbs = 0xffu;                // state code of the absorbing state (fast path)
-constexpr int kTabWords = 2 * 256 + 9 * 256;    // largest step tables (pass 1 + pass 2), 32-bit words
+constexpr int kTabWords = 2 * 256 + 2 * 9 * 256;  // largest step tables (pass 1 + pass 2), 32-bit words
 
 // Carries of a run of bytes [ParPaRaw Sec. 3, offsets, Fig. 4]:
 //   nf terminators, nr record delimiters,

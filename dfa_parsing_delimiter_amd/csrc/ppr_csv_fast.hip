@@ -43,6 +43,7 @@ struct Geo {
     static constexpr int NI = kFastChunk / G;       // groups per chunk (index bytes)
     static constexpr int NP = NI / 4;               // index words per chunk
     static constexpr uint32_t GM = (1u << G) - 1u;
+    static constexpr int PAR = G == 4 ? 2 : 1;      // pass-2 tables used in turn (one per group parity)
 };
 
 
@@ -256,12 +257,23 @@ __device__ Vec ragged_vector(const FastParams& p, const ChunkPos& c, Vec v, cons
 
 // Pass-2 table: one row of kRowStride entries per state code (row nt: the
 // absorbing state), entry e = the table index of a group of G symbols. Entry
-// bits 8-15 hold the next state's row, 16..16+G-1 the terminator bits,
-// 20..20+G-1 the record-delimiter bits, 24-26 the first INVALID byte of the
-// group, 31 some byte is INVALID. With the row in byte 1, the next lookup's
-// word index (row << 8 | index byte) is one v_perm of the previous entry and
-// the packed index word.
+// bits 0-2 hold the first INVALID byte of the group, bit 7 is set if some byte
+// is INVALID, bits 8-15 hold the row of the next lookup. With the row in byte
+// 1, the next lookup's word index (row << 8 | index byte) is one v_perm of the
+// previous entry and the packed index word.
+//
+// G = 2: one table; bits 16..17 are the terminator bits, 20..21 the
+// record-delimiter bits (bit g: byte g of the group).
+//
+// G = 4: two tables, used by the even and the odd groups of a chunk in turn
+// (an even group's entry names a row of the odd table, rows nt+1 .. 2nt+1, and
+// the reverse). The even table holds the terminator nibble in bits 16-19 and
+// the record-delimiter nibble in 24-27, the odd table in bits 20-23 and 28-31,
+// so the OR of a pair's two entries holds the pair's 8 terminator bits in byte
+// 2 and its 8 record-delimiter bits in byte 3: one v_perm of two pairs then
+// gives the bitmaps of 16 bytes.
 constexpr int kRowStride = 256;
+constexpr uint32_t kP2Invalid = 0x80u;
 
 // word index of the lookup for index byte i of idxw after entry prev
 __device__ __forceinline__ uint32_t p2_index(uint32_t prev, uint32_t idxw, int i)
@@ -269,22 +281,11 @@ __device__ __forceinline__ uint32_t p2_index(uint32_t prev, uint32_t idxw, int i
     return perm(prev, idxw, 0x0c0c0500u | (uint32_t)i);
 }
 
-// the 64 bits of each kind from the gathered tag bytes of 8 groups of 4 bytes
-// (byte g of w0/w1 = terminator nibble | record nibble << 4 of group g / 4 + g)
-__device__ __forceinline__ void nibbles_to_bits(uint32_t w0, uint32_t w1, uint32_t& t32, uint32_t& r32)
-{
-    const uint32_t m = 0x0f0f0f0fu;
-    const uint32_t t0 = (w0 & m) | ((w0 >> 4) & ~m), t1 = (w1 & m) | ((w1 >> 4) & ~m);
-    const uint32_t r0 = ((w0 >> 4) & m) | ((w0 >> 8) & ~m), r1 = ((w1 >> 4) & m) | ((w1 >> 8) & ~m);
-    t32 = perm(t1, t0, 0x06040200u);
-    r32 = perm(r1, r0, 0x06040200u);
-}
-
 // Pass 2 over NCH consecutive full chunks of a thread (NCH NI groups, packed
 // four index bytes per word in pw) from state code s: a chain of pass-2
 // lookups, one per group, each addressed by the previous entry (p2_index).
 // T[h] / RD[h]: terminator / record bitmaps of chunk h (bit j = byte j).
-// Returns the OR of the entries (bit 31: some byte is INVALID). (Cutting the
+// Returns the OR of the entries (kP2Invalid: some byte is INVALID). (Cutting the
 // chain into independent runs, with start states from the pass-1 table, costs
 // more instructions than the shorter LDS wait saves: these kernels are bound by
 // instruction issue.)
@@ -297,26 +298,25 @@ __device__ __forceinline__ uint32_t pass2_run(const uint32_t (&pw)[NCH * Geo<CB>
     uint32_t prev = min(s, nt) << 8;
     uint32_t any = 0;
     if constexpr (G == 4) {
-        // the tag byte (bits 16-23) of four consecutive entries gathered into one word
+        // per index word (16 bytes): terminator bits in 0-15, record-delimiter bits in 16-31
         uint32_t w[NG / 4];
 #pragma unroll
         for (int q = 0; q < NG / 4; ++q) {
-            uint32_t e[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                e[i] = s_t2[p2_index(prev, pw[q], i)];
-                prev = e[i];
-                any |= e[i];
-            }
-            w[q] = perm(e[1], e[0], 0x0c0c0602u) | perm(e[3], e[2], 0x06020c0cu);
+            const uint32_t e0 = s_t2[p2_index(prev, pw[q], 0)];
+            const uint32_t e1 = s_t2[p2_index(e0, pw[q], 1)];
+            const uint32_t e2 = s_t2[p2_index(e1, pw[q], 2)];
+            const uint32_t e3 = s_t2[p2_index(e2, pw[q], 3)];
+            prev = e3;
+            const uint32_t a = e0 | e1, b = e2 | e3;
+            any |= a | b;
+            w[q] = perm(b, a, 0x07030602u);
         }
 #pragma unroll
         for (int h = 0; h < NCH; ++h) {
-            uint32_t tl, th, rl, rh;
-            nibbles_to_bits(w[4 * h], w[4 * h + 1], tl, rl);
-            nibbles_to_bits(w[4 * h + 2], w[4 * h + 3], th, rh);
-            T[h] = (uint64_t)tl | ((uint64_t)th << 32);
-            RD[h] = (uint64_t)rl | ((uint64_t)rh << 32);
+            T[h] = (uint64_t)perm(w[4 * h + 1], w[4 * h], 0x05040100u) |
+                   ((uint64_t)perm(w[4 * h + 3], w[4 * h + 2], 0x05040100u) << 32);
+            RD[h] = (uint64_t)perm(w[4 * h + 1], w[4 * h], 0x07060302u) |
+                    ((uint64_t)perm(w[4 * h + 3], w[4 * h + 2], 0x07060302u) << 32);
         }
     } else {
         uint32_t tw[2 * NCH], rw[2 * NCH];
@@ -352,11 +352,15 @@ __device__ uint32_t first_invalid(const uint32_t (&pw)[NCH * Geo<CB>::NP], uint3
                                   const uint32_t* s_t2, uint32_t abs)
 {
     constexpr int NG = NCH * Geo<CB>::NI, G = Geo<CB>::G;
+    // z is 0 (nt <= 8) but not known to the compiler, so these lookups are made
+    // again rather than shared with the common path's chain, whose entries
+    // would otherwise stay in registers for this rare case
+    const uint32_t z = nt >> 16;
     uint32_t prev = min(s, nt) << 8, first = kNone;
 #pragma unroll
     for (int k = 0; k < NG; ++k) {  // (no early exit: indices into pw stay compile-time constants)
-        const uint32_t e = s_t2[p2_index(prev, pw[k / 4], k % 4)];
-        if ((e >> 31) && first == kNone) first = abs + (uint32_t)(G * k) + ((e >> 24) & 7u);
+        const uint32_t e = s_t2[p2_index(prev, pw[k / 4], k % 4) | z];
+        if ((e & kP2Invalid) && first == kNone) first = abs + (uint32_t)(G * k) + (e & 7u);
         prev = e;
     }
     return first;
@@ -476,16 +480,21 @@ __global__ void csv_fast_tables_kernel(FastParams p)
         if (V8) tabs[E + e] = hi;
         uint32_t* t2 = tabs + (V8 ? 2 : 1) * E;
         for (uint32_t r = 0; r <= nt; ++r) {
-            uint32_t s = r, ent = 0;
+            uint32_t s = r, tb = 0, rb = 0, inv = 0;
             for (int g = 0; g < G; ++g) {
                 const uint32_t t = s_tag[s * 16 + cg[g]];
                 const uint32_t ns = s_nxt[s * 16 + cg[g]];
-                if (t == PPR_TAG_FIELD || t == PPR_TAG_RECORD) ent |= 1u << (16 + g);
-                if (t == PPR_TAG_RECORD) ent |= 1u << (20 + g);
-                if (t == PPR_TAG_INVALID && !(ent >> 31)) ent |= (1u << 31) | ((uint32_t)g << 24);
+                if (t == PPR_TAG_FIELD || t == PPR_TAG_RECORD) tb |= 1u << g;
+                if (t == PPR_TAG_RECORD) rb |= 1u << g;
+                if (t == PPR_TAG_INVALID && !inv) inv = kP2Invalid | (uint32_t)g;
                 s = ns == kAbs ? nt : ns;
             }
-            t2[r * kRowStride + e] = ent | (s << 8);
+            if constexpr (G == 4) {
+                t2[r * kRowStride + e] = inv | ((nt + 1 + s) << 8) | (tb << 16) | (rb << 24);
+                t2[(nt + 1 + r) * kRowStride + e] = inv | (s << 8) | (tb << 20) | (rb << 28);
+            } else {
+                t2[r * kRowStride + e] = inv | (s << 8) | (tb << 16) | (rb << 20);
+            }
         }
     }
 }
@@ -641,19 +650,19 @@ __global__ void __launch_bounds__(kWave) csv_range_vec_kernel(FastParams p)
     if (threadIdx.x == 0) p.range_vec[blockIdx.x] = (uint64_t)rv.lo | ((uint64_t)rv.hi << 32);
 }
 
-// pass-2 table rows (tracked states + the absorbing row) and the byte tables
-template <bool V8, int E>
+// pass-2 table rows (tracked states + the absorbing row, per table) and the byte tables
+template <bool V8, int PAR>
 struct Pass2Shared {
-    uint32_t t2[(V8 ? 9 : 5) * kRowStride];
+    uint32_t t2[PAR * (V8 ? 9 : 5) * kRowStride];
     uint8_t nxt[9 * 16], tag[9 * 16];
 };
 
 template <int CB, bool V8>
-__device__ __forceinline__ void load_pass2(const FastParams& p, Pass2Shared<V8, Geo<CB>::E>& sh)
+__device__ __forceinline__ void load_pass2(const FastParams& p, Pass2Shared<V8, Geo<CB>::PAR>& sh)
 {
     constexpr int E = Geo<CB>::E;
     const uint32_t* t2g = p.tabs + (V8 ? 2 : 1) * E;
-    const int words = (int)(p.nt + 1) * kRowStride;
+    const int words = Geo<CB>::PAR * (int)(p.nt + 1) * kRowStride;
     for (int i = threadIdx.x; i < words; i += kFastBlock) sh.t2[i] = t2g[i];
     if (threadIdx.x < 9 * 16) {
         sh.nxt[threadIdx.x] = (&p.nxt[0][0])[threadIdx.x];
@@ -679,7 +688,7 @@ __device__ __forceinline__ void super_vecs(const FastParams& p, uint32_t st, uin
 // wanted). ts0 / ts1: the state before the super-tile's first / second tile.
 template <int CB, bool V8, bool FULL>
 __device__ __forceinline__ void span_tags(const FastParams& p, const PairPos& c, const IdxIn<CB, V8>& in,
-                                          uint32_t ts0, uint32_t ts1, const Pass2Shared<V8, Geo<CB>::E>& sh,
+                                          uint32_t ts0, uint32_t ts1, const Pass2Shared<V8, Geo<CB>::PAR>& sh,
                                           uint64_t (&T)[2], uint64_t (&RD)[2], uint32_t* err)
 {
     const uint32_t nt = p.nt;
@@ -687,7 +696,7 @@ __device__ __forceinline__ void span_tags(const FastParams& p, const PairPos& c,
     T[0] = T[1] = RD[0] = RD[1] = 0;
     if (FULL || c.full) {
         const uint32_t any = pass2_pair<CB>(in.pw, s, nt, sh.t2, T, RD);
-        if (err && (any >> 31)) *err = first_invalid<CB, 2>(in.pw, s, nt, sh.t2, c.abs);
+        if (err && (any & kP2Invalid)) *err = first_invalid<CB, 2>(in.pw, s, nt, sh.t2, c.abs);
     } else if (c.my_len) {
         uint32_t e = kNone;
         pass2_ragged<CB>(p, c, s, nt, sh.nxt, sh.tag, T, RD, e);
@@ -728,6 +737,16 @@ __device__ __forceinline__ uint32_t count_from(const uint64_t (&T)[2], uint32_t 
     return (uint32_t)(__popcll(T[0] & m0) + __popcll(T[1] & m1));
 }
 
+// Register budgets of the carries and emit kernels (waves per SIMD; a
+// workgroup is two per SIMD). With 4-byte groups both wait mostly on their
+// pass-2 lookup chains and fit 64 VGPRs, four workgroups per CU. With 2-byte
+// groups they take up to 128 (the carries kernel would spill below that, and
+// the emit kernel measured slower at 80 VGPRs and three workgroups per CU).
+template <int CB>
+constexpr int kCarriesWavesPerSimd = CB == 2 ? 8 : 4;
+template <int CB>
+constexpr int kEmitWavesPerSimd = CB == 2 ? 8 : 4;
+
 // carries: the range's start state (stored), tags from each span's start state,
 // the range's count carry (stored); the last range stores the end state.
 //
@@ -739,10 +758,10 @@ __device__ __forceinline__ uint32_t count_from(const uint64_t (&T)[2], uint32_t 
 // its terminators after that position, one without adds all of them. The
 // thread sums and maxima are reduced once, at the end of the range.
 template <int CB, bool V8>
-__global__ void __launch_bounds__(kFastBlock) csv_carries_kernel(FastParams p)
+__global__ void __launch_bounds__(kFastBlock, kCarriesWavesPerSimd<CB>) csv_carries_kernel(FastParams p)
 {
     using Gm = Geo<CB>;
-    __shared__ Pass2Shared<V8, Gm::E> sh;
+    __shared__ Pass2Shared<V8, Gm::PAR> sh;
     __shared__ uint32_t s_rd[2][kFastWaves];
     __shared__ Vec s_wv[kFastWaves];
     __shared__ uint4 s_red[kFastWaves];
@@ -855,8 +874,11 @@ __device__ __forceinline__ void field_round(const OutArrays& o, uint32_t cap32, 
 }
 
 // Per-wave list of the wave's terminators (LDS): entry = position within the
-// super-tile << 1 | record-delimiter bit, in field order.
-constexpr int kWaveList = 1024;
+// super-tile << 1 | record-delimiter bit, in field order. A wave with more
+// fields in a super-tile lists and writes them in several passes. With 4-byte
+// groups the list is shorter, so that four workgroups fit a CU's LDS.
+template <int CB>
+constexpr int kWaveList = CB == 2 ? 768 : 1024;
 
 // emit: tags from each span's start state; every field's record, column,
 // offset and length; the last range writes the unterminated final field and
@@ -869,13 +891,13 @@ constexpr int kWaveList = 1024;
 // lane before, by DPP). The four output arrays are written with consecutive
 // addresses across the lanes.
 template <int CB, bool V8>
-__global__ void __launch_bounds__(kFastBlock) csv_emit_kernel(FastParams p)
+__global__ void __launch_bounds__(kFastBlock, kEmitWavesPerSimd<CB>) csv_emit_kernel(FastParams p)
 {
     using Gm = Geo<CB>;
-    __shared__ Pass2Shared<V8, Gm::E> sh;
+    __shared__ Pass2Shared<V8, Gm::PAR> sh;
     __shared__ GCarry s_wc[kSpanScratch];
     __shared__ GCarry s_wg[kFastWaves];
-    __shared__ uint32_t s_list[kFastWaves][kWaveList];
+    __shared__ uint32_t s_list[kFastWaves][kWaveList<CB>];
 
     const uint32_t lane = (uint32_t)lane_id();
     const uint32_t wv = threadIdx.x / kWave;
@@ -911,8 +933,8 @@ __global__ void __launch_bounds__(kFastBlock) csv_emit_kernel(FastParams p)
                     (uint32_t)max(P.lt, sc.wave_excl.lt)};
         const uint32_t st_abs = st * (uint32_t)(2 * kFastTile);
         const uint32_t rel0 = c.abs - st_abs;
-        for (uint32_t w0 = wfirst; w0 < wend; w0 += kWaveList) {
-            const uint32_t w1 = min(w0 + (uint32_t)kWaveList, wend);
+        for (uint32_t w0 = wfirst; w0 < wend; w0 += kWaveList<CB>) {
+            const uint32_t w1 = min(w0 + (uint32_t)kWaveList<CB>, wend);
             // (1) each lane lists its terminators that fall in [w0, w1)
             {
                 const uint32_t tw[4] = {(uint32_t)T[0], (uint32_t)(T[0] >> 32), (uint32_t)T[1], (uint32_t)(T[1] >> 32)};
@@ -1066,7 +1088,7 @@ constexpr int kFusedWavesPerSimd = 4;  // 3 resident workgroups per CU: the regi
 template <int CB, bool V8>
 struct FusedShared {
     uint32_t t1[V8 ? 2 * Geo<CB>::E : Geo<CB>::E];
-    Pass2Shared<V8, Geo<CB>::E> p2;
+    Pass2Shared<V8, Geo<CB>::PAR> p2;
     Vec wv[kFastWaves];
     Vec pv[kFastWaves];
     GCarry wc[kSpanScratch];
@@ -1183,7 +1205,7 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
             uint64_t T[1] = {0}, RD[1] = {0};
             if (c.full) {
                 const uint32_t any = pass2_run<CB, 1>(pw1, s, nt, sh.p2.t2, T, RD);
-                if (any >> 31) err = first_invalid<CB, 1>(pw1, s, nt, sh.p2.t2, c.chunk_abs);
+                if (any & kP2Invalid) err = first_invalid<CB, 1>(pw1, s, nt, sh.p2.t2, c.chunk_abs);
             } else if (c.my_len) {
                 pass2_ragged_chunk<CB>(p, c, s, nt, sh.p2.nxt, sh.p2.tag, T[0], RD[0], err);
             }

@@ -42,7 +42,7 @@ def test_workspace_sizes():
     assert L.ppr_parse_workspace_bytes(1000, ctypes.byref(o)) == 0
     o.chunk_bytes = 31
     ws = L.ppr_parse_workspace_bytes(1 << 30, ctypes.byref(o))
-    tiles = -(-(1 << 30) // (256 * 31))
+    tiles = -(-(1 << 30) // (1024 * 31))  # single-pass tiles: 1024 threads x 31 bytes
     assert ws >= 256 + tiles * 72
     assert L.ppr_parse_workspace_bytes(1 << 32, ctypes.byref(o)) == 0
 
