@@ -440,63 +440,81 @@ __device__ __forceinline__ IdxIn<CB, V8> load_in(const FastParams& p, const Pair
     return in;
 }
 
+// The workspace header's per-call fields (the first kernel of a call resets them).
+__device__ __forceinline__ void reset_header(const FastParams& p)
+{
+    p.hdr->tile_counter = 0;
+    p.hdr->fault = 0;
+    p.hdr->err_min = kNone;
+    p.hdr->last_rec = 0;
+    p.hdr->path = p.path;
+}
+
 // Pass-1 table: entry e (the codes of G bytes) -> composite vector from every
-// tracked state. Pass-2 table: row r (state code, row nt = absorbing), entry e ->
-// the next state's row offset, the group's tag bits (see pass2_full). One
-// workgroup builds them for the call and resets the workspace header.
+// tracked state (words [0, E): entries 0-3, words [E, 2E): entries 4-7). The
+// threads of a workgroup build it together from the byte step table s_nxt.
 template <int CB, bool V8>
-__global__ void csv_fast_tables_kernel(FastParams p)
+__device__ void build_pass1(uint32_t* t1, const uint8_t* s_nxt, uint32_t nt)
 {
     constexpr int G = Geo<CB>::G, E = Geo<CB>::E;
     constexpr uint32_t CM = Geo<CB>::CM;
+    for (uint32_t e = threadIdx.x; e < (uint32_t)E; e += blockDim.x) {
+        uint32_t lo = 0, hi = 0;
+        for (int i = 0; i < (V8 ? 8 : 4); ++i) {
+            uint32_t s = (uint32_t)i < nt ? (uint32_t)i : kAbs;
+            for (int g = 0; g < G; ++g)
+                if (s != kAbs) s = s_nxt[s * 16 + ((e >> (CB * g)) & CM)];
+            if (i < 4) lo |= s << (8 * i);
+            else hi |= s << (8 * (i - 4));
+        }
+        t1[e] = lo;
+        if (V8) t1[E + e] = hi;
+    }
+}
+
+// Pass-2 tables (layout above: rows of kRowStride entries, one set of nt + 1
+// rows per table), built by the threads of a workgroup from the byte tables.
+template <int CB>
+__device__ void build_pass2(uint32_t* t2, const uint8_t* s_nxt, const uint8_t* s_tag, uint32_t nt)
+{
+    constexpr int G = Geo<CB>::G, E = Geo<CB>::E;
+    constexpr uint32_t CM = Geo<CB>::CM;
+    const uint32_t cells = (nt + 1) * (uint32_t)E;
+    for (uint32_t i = threadIdx.x; i < cells; i += blockDim.x) {
+        const uint32_t r = i / (uint32_t)E, e = i % (uint32_t)E;
+        uint32_t s = r, tb = 0, rb = 0, inv = 0;
+        for (int g = 0; g < G; ++g) {
+            const uint32_t c = (e >> (CB * g)) & CM;
+            const uint32_t t = s_tag[s * 16 + c];
+            const uint32_t ns = s_nxt[s * 16 + c];
+            if (t == PPR_TAG_FIELD || t == PPR_TAG_RECORD) tb |= 1u << g;
+            if (t == PPR_TAG_RECORD) rb |= 1u << g;
+            if (t == PPR_TAG_INVALID && !inv) inv = kP2Invalid | (uint32_t)g;
+            s = ns == kAbs ? nt : ns;
+        }
+        if constexpr (G == 4) {
+            t2[r * kRowStride + e] = inv | ((nt + 1 + s) << 8) | (tb << 16) | (rb << 24);
+            t2[(nt + 1 + r) * kRowStride + e] = inv | (s << 8) | (tb << 20) | (rb << 28);
+        } else {
+            t2[r * kRowStride + e] = inv | (s << 8) | (tb << 16) | (rb << 20);
+        }
+    }
+}
+
+// The fused path's tables (in the workspace, read by every workgroup) and the
+// reset of the workspace header. One workgroup.
+template <int CB, bool V8>
+__global__ void csv_fast_tables_kernel(FastParams p)
+{
     __shared__ uint8_t s_nxt[9 * 16], s_tag[9 * 16];
     if (threadIdx.x < 9 * 16) {
         s_nxt[threadIdx.x] = (&p.nxt[0][0])[threadIdx.x];
         s_tag[threadIdx.x] = (&p.tag[0][0])[threadIdx.x];
     }
-    if (threadIdx.x == 0) {
-        p.hdr->tile_counter = 0;
-        p.hdr->fault = 0;
-        p.hdr->err_min = kNone;
-        p.hdr->last_rec = 0;
-        p.hdr->path = p.path;
-    }
+    if (threadIdx.x == 0) reset_header(p);
     __syncthreads();
-    uint32_t* tabs = p.tabs;
-    const uint32_t nt = p.nt;
-    for (uint32_t e = threadIdx.x; e < (uint32_t)E; e += blockDim.x) {
-        uint32_t cg[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) cg[g] = (e >> (CB * g)) & CM;
-        uint32_t lo = 0, hi = 0;
-        for (int i = 0; i < (V8 ? 8 : 4); ++i) {
-            uint32_t s = (uint32_t)i < nt ? (uint32_t)i : kAbs;
-            for (int g = 0; g < G; ++g)
-                if (s != kAbs) s = s_nxt[s * 16 + cg[g]];
-            if (i < 4) lo |= s << (8 * i);
-            else hi |= s << (8 * (i - 4));
-        }
-        tabs[e] = lo;
-        if (V8) tabs[E + e] = hi;
-        uint32_t* t2 = tabs + (V8 ? 2 : 1) * E;
-        for (uint32_t r = 0; r <= nt; ++r) {
-            uint32_t s = r, tb = 0, rb = 0, inv = 0;
-            for (int g = 0; g < G; ++g) {
-                const uint32_t t = s_tag[s * 16 + cg[g]];
-                const uint32_t ns = s_nxt[s * 16 + cg[g]];
-                if (t == PPR_TAG_FIELD || t == PPR_TAG_RECORD) tb |= 1u << g;
-                if (t == PPR_TAG_RECORD) rb |= 1u << g;
-                if (t == PPR_TAG_INVALID && !inv) inv = kP2Invalid | (uint32_t)g;
-                s = ns == kAbs ? nt : ns;
-            }
-            if constexpr (G == 4) {
-                t2[r * kRowStride + e] = inv | ((nt + 1 + s) << 8) | (tb << 16) | (rb << 24);
-                t2[(nt + 1 + r) * kRowStride + e] = inv | (s << 8) | (tb << 20) | (rb << 28);
-            } else {
-                t2[r * kRowStride + e] = inv | (s << 8) | (tb << 16) | (rb << 20);
-            }
-        }
-    }
+    build_pass1<CB, V8>(p.tabs, s_nxt, p.nt);
+    build_pass2<CB>(p.tabs + (V8 ? 2 : 1) * Geo<CB>::E, s_nxt, s_tag, p.nt);
 }
 
 // The streaming kernels run num_ranges workgroups; workgroup b owns the
@@ -574,8 +592,10 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
     uint32_t w[ND];
     const uint32_t t0 = blockIdx.x;
     if (t0 < tfull_all) load_full(t0, w);
-    for (int i = tid; i < T1W; i += kFastBlock) s_t1[i] = p.tabs[i];
     if (tid < 9 * 16) s_nxt[tid] = (&p.nxt[0][0])[tid];
+    if (blockIdx.x == 0 && tid == 0) reset_header(p);  // (no kernel of the call has read it yet)
+    __syncthreads();
+    build_pass1<CB, V8>(s_t1, s_nxt, p.nt);
     __syncthreads();
     const Vec ident = fast_ident<V8>(p.nt);
 
@@ -657,17 +677,17 @@ struct Pass2Shared {
     uint8_t nxt[9 * 16], tag[9 * 16];
 };
 
+// The byte tables and the pass-2 tables in LDS, built by the workgroup (the
+// caller's next barrier publishes the pass-2 tables).
 template <int CB, bool V8>
 __device__ __forceinline__ void load_pass2(const FastParams& p, Pass2Shared<V8, Geo<CB>::PAR>& sh)
 {
-    constexpr int E = Geo<CB>::E;
-    const uint32_t* t2g = p.tabs + (V8 ? 2 : 1) * E;
-    const int words = Geo<CB>::PAR * (int)(p.nt + 1) * kRowStride;
-    for (int i = threadIdx.x; i < words; i += kFastBlock) sh.t2[i] = t2g[i];
     if (threadIdx.x < 9 * 16) {
         sh.nxt[threadIdx.x] = (&p.nxt[0][0])[threadIdx.x];
         sh.tag[threadIdx.x] = (&p.tag[0][0])[threadIdx.x];
     }
+    __syncthreads();
+    build_pass2<CB>(sh.t2, sh.nxt, sh.tag, p.nt);
 }
 
 // The tile vectors of super-tile st from the lane-wise prefetch (the second is
@@ -739,13 +759,15 @@ __device__ __forceinline__ uint32_t count_from(const uint64_t (&T)[2], uint32_t 
 
 // Register budgets of the carries and emit kernels (waves per SIMD; a
 // workgroup is two per SIMD). With 4-byte groups both wait mostly on their
-// pass-2 lookup chains and fit 64 VGPRs, four workgroups per CU. With 2-byte
-// groups they take up to 128 (the carries kernel would spill below that, and
-// the emit kernel measured slower at 80 VGPRs and three workgroups per CU).
+// pass-2 lookup chains and fit 64 VGPRs, four workgroups per CU (the emit
+// kernel only with at most 4 tracked states: with more, its LDS holds three).
+// With 2-byte groups they take up to 128 (the carries kernel would spill below
+// that, and the emit kernel measured slower at 80 VGPRs and three workgroups
+// per CU).
 template <int CB>
 constexpr int kCarriesWavesPerSimd = CB == 2 ? 8 : 4;
-template <int CB>
-constexpr int kEmitWavesPerSimd = CB == 2 ? 8 : 4;
+template <int CB, bool V8>
+constexpr int kEmitWavesPerSimd = CB == 2 && !V8 ? 8 : 4;
 
 // carries: the range's start state (stored), tags from each span's start state,
 // the range's count carry (stored); the last range stores the end state.
@@ -891,7 +913,7 @@ constexpr int kWaveList = CB == 2 ? 768 : 1024;
 // lane before, by DPP). The four output arrays are written with consecutive
 // addresses across the lanes.
 template <int CB, bool V8>
-__global__ void __launch_bounds__(kFastBlock, kEmitWavesPerSimd<CB>) csv_emit_kernel(FastParams p)
+__global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_emit_kernel(FastParams p)
 {
     using Gm = Geo<CB>;
     __shared__ Pass2Shared<V8, Gm::PAR> sh;
@@ -1302,15 +1324,13 @@ static void launch(const FastParams& f, const ppr_parse_opts_t* o, hipStream_t s
 {
     const dim3 grid(f.num_ranges), block(kFastBlock);
     stage_event(o, 0, s);
-    hipLaunchKernelGGL((csv_fast_tables_kernel<CB, V8>), dim3(1), dim3(256), 0, s, f);
-    stage_event(o, 1, s);
     hipLaunchKernelGGL((csv_codes_kernel<CB, V8>), dim3(std::min<uint32_t>(f.num_tiles, kCodesGrid)), block, 0, s, f);
     hipLaunchKernelGGL((csv_range_vec_kernel<V8>), grid, dim3(kWave), 0, s, f);
-    stage_event(o, 2, s);
+    stage_event(o, 1, s);
     hipLaunchKernelGGL((csv_carries_kernel<CB, V8>), grid, block, 0, s, f);
-    stage_event(o, 3, s);
+    stage_event(o, 2, s);
     hipLaunchKernelGGL((csv_emit_kernel<CB, V8>), grid, block, 0, s, f);
-    stage_event(o, 4, s);
+    stage_event(o, 3, s);
 }
 
 // Persistent grid of the fused kernel: as many workgroups as the device holds at

@@ -121,9 +121,9 @@ enum { PPR_PATH_STREAMING = 1, PPR_PATH_SINGLE_PASS = 2, PPR_PATH_FUSED = 3 };
  *   stage_events:   optional array of n_stage_events hipEvent_t (caller-created):
  *                   event 0 is recorded on the stream before the first kernel of the
  *                   call and event i after its i-th kernel, as far as the array
- *                   reaches (streaming parse: 4 events after the tables, codes +
- *                   range vectors, carries and emit kernels; fused and single-pass
- *                   parse and the lexer: 2). For per-kernel timing; NULL: none.
+ *                   reaches (streaming parse: 3 events after the codes + range
+ *                   vectors, carries and emit kernels; fused and single-pass parse
+ *                   and the lexer: 2). For per-kernel timing; NULL: none.
  *   path:           0 = automatic (the streaming path where the table and input
  *                   allow it, else the single-pass path); PPR_PATH_FUSED or
  *                   PPR_PATH_STREAMING ask for that path and fall back to the
