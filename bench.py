@@ -45,7 +45,8 @@ COPY_BYTES = 1 << 30
 STAGES = {1: ["csv_codes_kernel", "csv_carries_kernel", "csv_emit_kernel"],
           2: ["csv_reset_kernel", "csv_generic_kernel"],
           3: ["csv_fast_tables_kernel", "csv_fused_kernel"],
-          "lex": ["lex_reset_kernel", "lex_kernel"]}
+          "lex1": ["lex_ids_kernel", "lex_count_kernel", "lex_emit_kernel"],
+          "lex2": ["lex_reset_kernel", "lex_kernel"]}
 
 
 def log(*a):
@@ -68,9 +69,9 @@ def algorithmic_bytes(stage, n, n_out, out_bytes_per_item):
     """The bytes the method itself must move, attributed to the kernel that moves
     them: the input read once (by the first kernel that reads it), the outputs
     written once (by the kernel that writes them). Intermediates are not counted."""
-    if stage in ("csv_codes_kernel",):
+    if stage in ("csv_codes_kernel", "lex_ids_kernel"):
         return n
-    if stage in ("csv_emit_kernel",):
+    if stage in ("csv_emit_kernel", "lex_emit_kernel"):
         return out_bytes_per_item * n_out
     if stage in ("csv_generic_kernel", "csv_fused_kernel", "lex_kernel"):
         return n + out_bytes_per_item * n_out
@@ -249,11 +250,13 @@ def main():
     else:
         dfa = W.lexer_dfa()
         tabs = ppr.LexTables.from_dfa(dfa, dev)
-        runner = ppr.Lexer(tabs, max_n=n, capacity=max(4096, n // 3), chunk_bytes=args.chunk)
+        want = {"auto": None, "fused": ppr.PPR_PATH_STREAMING, "streaming": ppr.PPR_PATH_STREAMING,
+                "single-pass": ppr.PPR_PATH_SINGLE_PASS}[args.path]
+        runner = ppr.Lexer(tabs, max_n=n, capacity=max(4096, n // 3), chunk_bytes=args.chunk, path=want)
         first = runner(d)
         runner._alloc(first.n_tokens)
-        n_out, path = first.n_tokens, None
-        stages = STAGES["lex"]
+        n_out, path = first.n_tokens, first.path
+        stages = STAGES["lex%d" % path]
         out_bytes_per_item = 12
         spec = dfa
     log("first call: %d items, kernels %s" % (n_out, stages))

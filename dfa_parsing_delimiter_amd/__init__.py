@@ -68,12 +68,12 @@ class LexTablesC(ctypes.Structure):
 class LexPrepared(ctypes.Structure):
     _fields_ = [("d_fold", ctypes.c_void_p), ("k", ctypes.c_uint32), ("m", ctypes.c_uint32),
                 ("identity", ctypes.c_uint16), ("flag_mask", ctypes.c_uint16), ("column_of", ctypes.c_uint8 * 256),
-                ("n_states", ctypes.c_uint32)]
+                ("n_states", ctypes.c_uint32), ("n_rows", ctypes.c_uint32), ("row0", ctypes.c_uint32)]
 
 
 class TokensOut(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_void_p), ("start", ctypes.c_void_p), ("length", ctypes.c_void_p),
-                ("cap_tokens", ctypes.c_uint64), ("n_tokens", ctypes.c_uint64)]
+                ("cap_tokens", ctypes.c_uint64), ("n_tokens", ctypes.c_uint64), ("path", ctypes.c_uint32)]
 
 
 def _load():
@@ -320,14 +320,16 @@ class LexResult:
     start: torch.Tensor
     length: torch.Tensor
     n_tokens: int
+    path: int = 0                # the kernels that ran: PPR_PATH_STREAMING or PPR_PATH_SINGLE_PASS
 
 
 class Lexer:
     """Reusable workspace and token buffers for inputs of up to max_n bytes."""
 
-    def __init__(self, tables: LexTables, max_n: int, capacity: int | None = None, chunk_bytes: int | None = None):
+    def __init__(self, tables: LexTables, max_n: int, capacity: int | None = None, chunk_bytes: int | None = None,
+                 path: int | None = None):
         self.t = tables
-        self.opts = _opts(chunk_bytes)
+        self.opts = _opts(chunk_bytes, path)
         self.max_n = int(max_n)
         dev = tables.merge_table.device
         ws = lib.ppr_lex_workspace_bytes(self.max_n, ctypes.byref(self.opts))
@@ -383,13 +385,15 @@ class Lexer:
                 continue
             _check(rc, "ppr_lex")
             k = int(o.n_tokens)
-            return LexResult(*[a[:k] for a in self.out_arrays], k)
+            return LexResult(*[a[:k] for a in self.out_arrays], k, int(o.path))
         raise PprError(PPR_ECAPACITY, "ppr_lex")
 
 
 def lex(data: torch.Tensor, tables: LexTables, chunk_bytes: int | None = None, capacity: int | None = None,
-        stream=None) -> LexResult:
+        stream=None, path: int | None = None) -> LexResult:
+    """Lex one input (device uint8 tensor); path: a PPR_PATH_* value to ask for
+    (None: automatic)."""
     _check_input(data)
     n = data.numel()
     cap = capacity if capacity is not None else min(n + 1, max(4096, n // 3))
-    return Lexer(tables, n, cap, chunk_bytes)(data, stream)
+    return Lexer(tables, n, cap, chunk_bytes, path)(data, stream)

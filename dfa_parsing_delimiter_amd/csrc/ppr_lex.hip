@@ -26,6 +26,7 @@
 #include "ppr.h"
 #include "ppr_device.h"
 #include "ppr_host.h"
+#include "ppr_lex_common.h"
 #include "ppr_scan.h"
 
 namespace ppr {
@@ -133,6 +134,7 @@ __global__ void lex_reset_kernel(WsHeader* hdr)
         hdr->tile_counter = 0;
         hdr->n_fields = 0;
         hdr->fault = 0;
+        hdr->path = PPR_PATH_SINGLE_PASS;
     }
 }
 
@@ -352,6 +354,45 @@ static MinLayout min_layout(uint32_t k, uint32_t m, uint32_t nq)
     return L;
 }
 
+// Where the fold rows of the streaming kernels sit, after the minimal
+// automaton: the next row (times m) and the identifier reached, n_rows x m
+// entries each, padded to 16 bytes.
+struct RowLayout {
+    uint64_t next_row, row_id, end;
+};
+
+static RowLayout row_layout(uint32_t k, uint32_t m, uint32_t nq, uint32_t n_rows)
+{
+    RowLayout L;
+    const uint64_t bytes = align_up((uint64_t)n_rows * m * 2u, 16);
+    L.next_row = align_up(min_layout(k, m, nq).end, 256);
+    L.row_id = align_up(L.next_row + bytes, 256);
+    L.end = L.row_id + bytes;
+    return L;
+}
+
+// Fold rows [L, "A lexer is a prefix scan": the chunk fold is a walk through
+// the fold table]: identifiers whose rows of the fold table name the same
+// identifiers share a row. Pass 1 only needs the row it is in until the last
+// byte, so it walks the (fewer) rows and reads the identifier at the end.
+// Returns the row count; row_of[x] is the row of identifier x, rep[r] one
+// identifier of row r.
+static uint32_t lex_fold_rows(const std::vector<uint16_t>& fold, uint32_t k, uint32_t m, uint32_t id_mask,
+                              std::vector<uint32_t>& row_of, std::vector<uint32_t>& rep)
+{
+    std::map<std::vector<uint16_t>, uint32_t> rows;
+    std::vector<uint16_t> key(m);
+    row_of.assign(k, 0);
+    rep.clear();
+    for (uint32_t x = 0; x < k; ++x) {
+        for (uint32_t j = 0; j < m; ++j) key[j] = (uint16_t)(fold[(size_t)x * m + j] & id_mask);
+        const auto it = rows.emplace(key, (uint32_t)rows.size());
+        if (it.second) rep.push_back(x);
+        row_of[x] = it.first->second;
+    }
+    return (uint32_t)rows.size();
+}
+
 // Minimal automaton of the identifier fold [L, "A lexer is a prefix scan": the
 // fold is a DFA over identifiers]. States are identifiers, symbols are columns;
 // reading column j in x outputs the flag of fold[x][j] and, with the flag, the
@@ -454,6 +495,8 @@ extern "C" int ppr_lex_prepare(const ppr_lex_tables_t* t, ppr_lex_prepared_t* pr
 
     // the minimal automaton of the fold, stored after it in the same buffer
     prep->n_states = 0;
+    prep->n_rows = 0;
+    prep->row0 = 0;
     std::vector<uint16_t> fold(total), fin(t->k);
     if (hipMemcpy(fold.data(), prep->d_fold, total * 2u, hipMemcpyDeviceToHost) != hipSuccess) return PPR_EHIP;
     if (hipMemcpy(fin.data(), t->final_states, (size_t)t->k * 2u, hipMemcpyDeviceToHost) != hipSuccess)
@@ -483,6 +526,30 @@ extern "C" int ppr_lex_prepare(const ppr_lex_tables_t* t, ppr_lex_prepared_t* pr
             hipMemcpy(base + ml.kind, qkind.data(), (size_t)nq * 2u, hipMemcpyHostToDevice) != hipSuccess)
             return PPR_EHIP;
         prep->n_states = nq;
+
+        // the streaming kernels' fold rows, where their tables fit the LDS budgets
+        // (the automaton's entries carry the 8-bit kinds, its states times m 16 bits)
+        uint32_t max_kind = 0;
+        for (uint32_t q = 0; q < nq; ++q) max_kind = std::max<uint32_t>(max_kind, qkind[q]);
+        std::vector<uint32_t> row_of, rrep;
+        const uint32_t nr = lex_fold_rows(fold, t->k, m, id_mask, row_of, rrep);
+        const RowLayout rl = row_layout(t->k, m, nq, nr);
+        if (max_kind < 256u && (uint64_t)nq * m * 4u <= kLexStepLds && (uint64_t)t->k * 2u <= kLexStateLds &&
+            (uint64_t)nr * m * 2u <= kLexRowLds && rl.end <= ppr_lex_fold_bytes(t->k)) {
+            const size_t cells = align_up((uint64_t)nr * m * 2u, 16) / 2u;
+            std::vector<uint16_t> next_row(cells, 0), row_id(cells, 0);
+            for (uint32_t r = 0; r < nr; ++r)
+                for (uint32_t j = 0; j < m; ++j) {
+                    const uint32_t y = fold[(size_t)rrep[r] * m + j] & id_mask;
+                    next_row[(size_t)r * m + j] = (uint16_t)(row_of[y] * m);
+                    row_id[(size_t)r * m + j] = (uint16_t)y;
+                }
+            if (hipMemcpy(base + rl.next_row, next_row.data(), cells * 2u, hipMemcpyHostToDevice) != hipSuccess ||
+                hipMemcpy(base + rl.row_id, row_id.data(), cells * 2u, hipMemcpyHostToDevice) != hipSuccess)
+                return PPR_EHIP;
+            prep->n_rows = nr;
+            prep->row0 = row_of[t->identity] * m;
+        }
     }
     return PPR_OK;
 }
@@ -491,7 +558,9 @@ extern "C" size_t ppr_lex_workspace_bytes(uint64_t n, const ppr_parse_opts_t* op
 {
     const uint32_t L = lex_chunk_of(opts);
     if (!L || n >= 0xffffffffull) return 0;
-    return (size_t)lex_layout(n, L).total;
+    uint64_t total = lex_layout(n, L).total;
+    if (L == (uint32_t)kLexFastChunk) total = std::max(total, lex_fast_layout(n).total);
+    return (size_t)total;
 }
 
 extern "C" int ppr_lex_async(const uint8_t* d_bytes, uint64_t n, const ppr_lex_tables_t* t,
@@ -505,11 +574,55 @@ extern "C" int ppr_lex_async(const uint8_t* d_bytes, uint64_t n, const ppr_lex_t
     if (n >= 0xffffffffull) return PPR_ETOOBIG;
     const uint32_t L = lex_chunk_of(opts);
     if (!L) return PPR_EINVAL;
+    const uint32_t want = opts ? opts->path : 0u;
+    if (want > PPR_PATH_FUSED) return PPR_EINVAL;
     const WsLayout lay = lex_layout(n, L);
     if (ws_bytes < lay.total || ((uintptr_t)d_ws & 255u)) return PPR_EWORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     uint8_t* ws = (uint8_t*)d_ws;
     WsHeader* hdr = (WsHeader*)ws;
+
+    // the streaming kernels: 40-byte chunks, 8-byte aligned input, prepared fold rows
+    // (and positions up to the last tile's end below 2^32)
+    if (n && n <= 0xffff0000ull && want != PPR_PATH_SINGLE_PASS && L == (uint32_t)kLexFastChunk &&
+        ((uintptr_t)d_bytes & 7u) == 0 && prep->n_rows && prep->n_states) {
+        const LexFastLayout fl = lex_fast_layout(n);
+        if (ws_bytes < fl.total) return PPR_EWORKSPACE;
+        const MinLayout ml = min_layout(prep->k, prep->m, prep->n_states);
+        const RowLayout rl = row_layout(prep->k, prep->m, prep->n_states, prep->n_rows);
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(prep->d_fold);
+        LexFastParams f;
+        memset(&f, 0, sizeof f);
+        f.in = d_bytes;
+        f.n = (uint32_t)n;
+        f.num_tiles = (uint32_t)fl.tiles;
+        f.num_ranges = (uint32_t)fl.ranges;
+        f.k = t->k;
+        f.m = prep->m;
+        f.identity = t->identity;
+        f.id_mask = (uint32_t)(uint16_t)~t->flag_mask;
+        f.row0 = prep->row0;
+        f.n_rows = prep->n_rows;
+        f.nq = prep->n_states;
+        f.merge = t->merge_table;
+        f.final_ = t->final_states;
+        f.next_row = reinterpret_cast<const uint16_t*>(base + rl.next_row);
+        f.row_id = reinterpret_cast<const uint16_t*>(base + rl.row_id);
+        f.state_of = reinterpret_cast<const uint16_t*>(base + ml.state_of);
+        f.step = reinterpret_cast<const uint32_t*>(base + ml.step);
+        f.state_kind = reinterpret_cast<const uint16_t*>(base + ml.kind);
+        f.chunk_id = reinterpret_cast<uint16_t*>(ws + fl.chunk_id);
+        f.tile_id = reinterpret_cast<uint32_t*>(ws + fl.tile_id);
+        f.range_id = reinterpret_cast<uint32_t*>(ws + fl.range_id);
+        f.range_tok = reinterpret_cast<uint2*>(ws + fl.range_tok);
+        f.kind = out->kind;
+        f.start = out->start;
+        f.len = out->length;
+        f.cap = out->cap_tokens;
+        f.hdr = hdr;
+        memcpy(f.col, prep->column_of, 256);
+        return launch_lex_fast(f, opts, s);
+    }
     stage_event(opts, 0, s);
     hipLaunchKernelGGL(lex_reset_kernel, dim3(1), dim3(64), 0, s, hdr);
     stage_event(opts, 1, s);
@@ -568,6 +681,7 @@ extern "C" int ppr_lex_results(const void* d_ws, uint64_t n, ppr_tokens_out_t* o
     if (hipMemcpyAsync(&h, d_ws, sizeof h, hipMemcpyDeviceToHost, s) != hipSuccess) return PPR_EHIP;
     if (hipStreamSynchronize(s) != hipSuccess) return PPR_EHIP;
     out->n_tokens = h.n_fields;
+    out->path = h.path;
     if (h.fault) return PPR_EHIP;
     return out->n_tokens > out->cap_tokens ? PPR_ECAPACITY : PPR_OK;
 }

@@ -1,0 +1,427 @@
+// Streaming lexer kernels on gfx950.
+//
+// Method: "Lexing on the GPU: the scan is the easy part", section "A lexer is a
+// prefix scan" (identifiers of transition functions, composed through the k x k
+// merge table; the state after each prefix is an inclusive scan) and section
+// "Does it produce the same tokens?" (a flag on a merged identifier ends a token
+// before that byte; its kind is the final-state entry of the state before it).
+//
+// Four kernels, none of which waits on another workgroup:
+//   lex_ids_kernel    pass 1: each thread folds its 40-byte chunk from the
+//                     identity through the fold rows held in LDS (identifiers
+//                     whose fold rows are equal share a row), a block scan of
+//                     the chunk identifiers under the merge table; stores each
+//                     chunk's tile-exclusive identifier and each tile's.
+//   lex_range_kernel  one wave per range (a contiguous run of tiles) composes
+//                     its tile identifiers.
+//   lex_count_kernel  per range, in tile order: each chunk's start identifier
+//                     (the range prefix, the tiles before, the chunk's tile
+//                     prefix), pass 2 through the minimal automaton in LDS,
+//                     boundary counts and the last boundary, one per range.
+//   lex_emit_kernel   the same pass 2 with token kinds, a block scan of the
+//                     counts, and the tokens written by waves, 64 per round
+//                     with consecutive addresses; the last range writes the
+//                     final token and the count.
+// The device-wide scans run over the range aggregates only, in each workgroup's
+// prologue.
+#include "ppr_lex_common.h"
+#include "ppr_scan.h"
+
+namespace ppr {
+
+// a earlier, b later
+struct LexIdComb {
+    const uint16_t* merge;
+    uint32_t k, id_mask;
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const
+    {
+        return (uint32_t)merge[(uint64_t)a * k + b] & id_mask;
+    }
+};
+
+// boundaries counted, the last one's position (0: none; position 0 is never one)
+struct LexTok {
+    uint32_t nt, lb;
+};
+
+struct LexTokComb {
+    __device__ LexTok operator()(const LexTok& a, const LexTok& b) const { return {a.nt + b.nt, max(a.lb, b.lb)}; }
+};
+
+constexpr int kLexWords = kLexFastChunk / 4;  // dwords per chunk
+constexpr int kLexList = 512;                 // per-wave token list entries (LDS)
+
+__device__ __forceinline__ uint32_t chunk_byte(const uint32_t (&w)[kLexWords], int j)
+{
+    return (w[j >> 2] >> (8 * (j & 3))) & 0xffu;
+}
+
+// A thread's chunk: full (8-byte loads) or the input's ragged end (bytes < len).
+template <bool FULL>
+__device__ __forceinline__ void load_lex_chunk(const uint8_t* src, uint32_t len, uint32_t (&w)[kLexWords])
+{
+    if constexpr (FULL) {
+        const uint2* s = reinterpret_cast<const uint2*>(src);
+#pragma unroll
+        for (int q = 0; q < kLexWords / 2; ++q) {
+            const uint2 x = s[q];
+            w[2 * q] = x.x;
+            w[2 * q + 1] = x.y;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < kLexWords; ++q) w[q] = 0;
+#pragma unroll
+        for (int j = 0; j < kLexFastChunk; ++j) {
+            const uint32_t b = (uint32_t)j < len ? (uint32_t)src[j] : 0u;
+            w[j >> 2] |= b << (8 * (j & 3));
+        }
+    }
+}
+
+// Pass 1: the chunk's identifier, folded from the identity. All but the last
+// byte step through the fold rows in LDS (entries: the next row times m); the
+// last byte reads the identifier itself from the same row in global memory.
+template <bool FULL>
+__device__ __forceinline__ uint32_t fold_lex_chunk(const LexFastParams& p, const uint32_t (&w)[kLexWords], uint32_t len,
+                                                   const uint16_t* s_rows, const uint8_t* s_col)
+{
+    if (!FULL && len == 0) return p.identity;
+    uint32_t r = p.row0, c = 0;
+#pragma unroll
+    for (int j = 0; j < kLexFastChunk; ++j) {
+        const uint32_t cj = s_col[chunk_byte(w, j)];
+        if (FULL ? j + 1 < kLexFastChunk : (uint32_t)j + 1u < len) r = s_rows[r + cj];
+        else if (FULL || (uint32_t)j + 1u == len) c = cj;
+    }
+    return p.row_id[r + c];
+}
+
+// Pass 2 from the automaton state q (times m): bit j of the result is set when
+// a token ends before byte j. With kinds, the ending token's kind (bits 24-31 of
+// the step entry: the kind of the state before the byte) goes to kinds[j].
+template <bool FULL>
+__device__ __forceinline__ uint64_t lex_pass2(const uint32_t (&w)[kLexWords], uint32_t len, uint32_t q,
+                                              const uint32_t* s_step, const uint8_t* s_col, uint8_t* kinds)
+{
+    uint32_t b0 = 0, b1 = 0;
+#pragma unroll
+    for (int j = 0; j < kLexFastChunk; ++j) {
+        if (FULL || (uint32_t)j < len) {
+            const uint32_t e = s_step[q + s_col[chunk_byte(w, j)]];
+            const uint32_t f = (e >> 16) & 1u;
+            if (kinds && f) kinds[j] = (uint8_t)(e >> 24);
+            if (j < 32) b0 |= f << j;
+            else b1 |= f << (j - 32);
+            q = e & 0xffffu;
+        }
+    }
+    return (uint64_t)b0 | ((uint64_t)b1 << 32);
+}
+
+__device__ __forceinline__ void lex_range_of(const LexFastParams& p, uint32_t b, uint32_t& t0, uint32_t& t1)
+{
+    t0 = (uint32_t)((uint64_t)b * p.num_tiles / p.num_ranges);
+    t1 = (uint32_t)((uint64_t)(b + 1) * p.num_tiles / p.num_ranges);
+}
+
+// What a thread of the count and emit kernels reads per tile: its chunk's
+// bytes, its chunk's tile-exclusive identifier and the tile's identifier.
+struct LexIn {
+    uint32_t w[kLexWords];
+    uint32_t cid, tid;
+};
+
+__device__ __forceinline__ LexIn load_lex_in(const LexFastParams& p, uint32_t tile)
+{
+    LexIn in;
+    load_lex_chunk<true>(p.in + (size_t)tile * kLexFastTile + threadIdx.x * kLexFastChunk, kLexFastChunk, in.w);
+    in.cid = p.chunk_id[(size_t)tile * kLexFastBlock + threadIdx.x];
+    in.tid = p.tile_id[tile];
+    return in;
+}
+
+// Runs full(tile, in, it) over the entirely full tiles of [t0, t1) in order,
+// with two register buffers used in turn and an unconditional prefetch (the
+// last full tile is read again at the end), then tail(tile, it) for the input's
+// ragged last tile if the range holds it. it counts the tiles from 0.
+template <typename Full, typename Tail>
+__device__ __forceinline__ void walk_lex_tiles(const LexFastParams& p, uint32_t t0, uint32_t t1, const Full& full,
+                                               const Tail& tail)
+{
+    const uint32_t tf = min(t1, p.n / (uint32_t)kLexFastTile);
+    uint32_t t = t0;
+    LexIn a, b;
+    if (t < tf) a = load_lex_in(p, t);
+    while (t < tf) {
+        b = load_lex_in(p, min(t + 1, tf - 1));
+        full(t, a, t - t0);
+        if (++t >= tf) break;
+        a = load_lex_in(p, min(t + 1, tf - 1));
+        full(t, b, t - t0);
+        ++t;
+    }
+    if (t < t1) tail(t, t - t0);
+}
+
+// identifier of the bytes of ranges 0..b-1 (thread i takes ranges 2i, 2i+1)
+__device__ uint32_t lex_ranges_before(const LexFastParams& p, uint32_t b, uint32_t* s_wave, const LexIdComb& idc)
+{
+    const uint32_t i0 = 2 * threadIdx.x, i1 = i0 + 1;
+    const uint32_t a = i0 < b ? p.range_id[i0] : p.identity;
+    const uint32_t c = i1 < b ? p.range_id[i1] : p.identity;
+    return block_reduce<kLexFastWaves>(idc(a, c), p.identity, s_wave, idc);
+}
+
+// boundaries of ranges 0..b-1
+__device__ LexTok lex_tokens_before(const LexFastParams& p, uint32_t b, LexTok* s_wave)
+{
+    const uint32_t i0 = 2 * threadIdx.x, i1 = i0 + 1;
+    const uint2 x = i0 < b ? p.range_tok[i0] : make_uint2(0u, 0u);
+    const uint2 y = i1 < b ? p.range_tok[i1] : make_uint2(0u, 0u);
+    return block_reduce<kLexFastWaves>(LexTok{x.x + y.x, max(x.y, y.y)}, LexTok{0u, 0u}, s_wave, LexTokComb{});
+}
+
+// The minimal automaton in LDS, successors times m: entry = successor * m |
+// flag << 16 | kind of the row's state << 24; and the state of each identifier,
+// times m.
+__device__ __forceinline__ void load_lex_automaton(const LexFastParams& p, uint32_t* s_step, uint16_t* s_state)
+{
+    const uint32_t m = p.m;
+    for (uint32_t i = threadIdx.x; i < p.nq * m; i += kLexFastBlock) {
+        const uint32_t e = p.step[i];
+        s_step[i] = (e & 0xffffu) * m | (e & 0x10000u) | ((uint32_t)p.state_kind[i / m] << 24);
+    }
+    for (uint32_t i = threadIdx.x; i < p.k; i += kLexFastBlock) s_state[i] = (uint16_t)(p.state_of[i] * m);
+}
+
+__global__ void __launch_bounds__(kLexFastBlock) lex_ids_kernel(LexFastParams p)
+{
+    extern __shared__ __align__(16) uint16_t s_rows[];
+    __shared__ uint8_t s_col[256];
+    __shared__ uint32_t s_wave[2][kLexFastWaves];
+    const uint32_t tid = threadIdx.x;
+    if (blockIdx.x == 0 && tid == 0) {  // (no kernel of the call has read the header yet)
+        p.hdr->tile_counter = 0;
+        p.hdr->n_fields = 0;
+        p.hdr->fault = 0;
+        p.hdr->path = PPR_PATH_STREAMING;
+    }
+    const uint32_t row_vecs = (p.n_rows * p.m + 7u) / 8u;  // (the rows are padded to 16 bytes)
+    for (uint32_t i = tid; i < row_vecs; i += kLexFastBlock)
+        reinterpret_cast<uint4*>(s_rows)[i] = reinterpret_cast<const uint4*>(p.next_row)[i];
+    if (tid < 256) s_col[tid] = p.col[tid];
+    __syncthreads();
+    const LexIdComb idc{p.merge, p.k, p.id_mask};
+    const uint32_t tfull = p.n / (uint32_t)kLexFastTile;  // tiles [0, tfull) are entirely full
+    const uint32_t stride = gridDim.x;
+    auto load = [&](uint32_t t, uint32_t (&w)[kLexWords]) {
+        load_lex_chunk<true>(p.in + (size_t)t * kLexFastTile + tid * kLexFastChunk, kLexFastChunk, w);
+    };
+    auto body = [&](uint32_t t, const uint32_t (&w)[kLexWords], uint32_t it) {
+        uint32_t excl, tot;
+        block_scan<kLexFastWaves>(fold_lex_chunk<true>(p, w, kLexFastChunk, s_rows, s_col), p.identity, excl, tot,
+                                  s_wave[it & 1], idc);
+        p.chunk_id[(size_t)t * kLexFastBlock + tid] = (uint16_t)excl;
+        if (tid == 0) p.tile_id[t] = tot;
+    };
+    // two register buffers used in turn, unconditional prefetch (the workgroup's
+    // last full tile is read again at the end)
+    uint32_t tile = blockIdx.x, it = 0;
+    const uint32_t tlast = tfull > tile ? tile + (tfull - 1 - tile) / stride * stride : tile;
+    uint32_t wa[kLexWords], wb[kLexWords];
+    if (tile < tfull) load(tile, wa);
+    while (tile < tfull) {
+        load(min(tile + stride, tlast), wb);
+        body(tile, wa, it++);
+        tile += stride;
+        if (tile >= tfull) break;
+        load(min(tile + stride, tlast), wa);
+        body(tile, wb, it++);
+        tile += stride;
+    }
+    if (tile < p.num_tiles) {  // the input's ragged last tile
+        const uint32_t pos = tile * (uint32_t)kLexFastTile + tid * (uint32_t)kLexFastChunk;
+        const uint32_t len = pos < p.n ? min((uint32_t)kLexFastChunk, p.n - pos) : 0u;
+        uint32_t w[kLexWords];
+        load_lex_chunk<false>(p.in + pos, len, w);
+        uint32_t excl, tot;
+        block_scan<kLexFastWaves>(fold_lex_chunk<false>(p, w, len, s_rows, s_col), p.identity, excl, tot,
+                                  s_wave[it & 1], idc);
+        p.chunk_id[(size_t)tile * kLexFastBlock + tid] = (uint16_t)excl;
+        if (tid == 0) p.tile_id[tile] = tot;
+    }
+}
+
+__global__ void __launch_bounds__(kWave) lex_range_kernel(LexFastParams p)
+{
+    const LexIdComb idc{p.merge, p.k, p.id_mask};
+    uint32_t t0, t1;
+    lex_range_of(p, blockIdx.x, t0, t1);
+    uint32_t rv = p.identity;
+    for (uint32_t t = t0; t < t1; t += kWave) {
+        const uint32_t i = t + threadIdx.x;
+        const uint32_t x = i < t1 ? p.tile_id[i] : p.identity;
+        rv = idc(rv, readlane_t(wave_scan(x, p.identity, idc), kWave - 1));
+    }
+    if (threadIdx.x == 0) p.range_id[blockIdx.x] = rv;
+}
+
+__global__ void __launch_bounds__(kLexFastBlock) lex_count_kernel(LexFastParams p)
+{
+    extern __shared__ __align__(16) uint32_t s_tab[];
+    uint32_t* s_step = s_tab;
+    uint16_t* s_state = reinterpret_cast<uint16_t*>(s_tab + p.nq * p.m);
+    __shared__ uint8_t s_col[256];
+    __shared__ uint32_t s_wave[kLexFastWaves];
+    __shared__ LexTok s_tw[kLexFastWaves];
+    const uint32_t tid = threadIdx.x, b = blockIdx.x;
+    load_lex_automaton(p, s_step, s_state);
+    if (tid < 256) s_col[tid] = p.col[tid];
+    const LexIdComb idc{p.merge, p.k, p.id_mask};
+    uint32_t run = lex_ranges_before(p, b, s_wave, idc);  // (its barrier publishes the tables)
+    uint32_t t0, t1;
+    lex_range_of(p, b, t0, t1);
+    LexTok acc{0u, 0u};
+    auto count = [&](uint32_t tile, uint64_t B) {
+        const uint32_t pos = tile * (uint32_t)kLexFastTile + tid * (uint32_t)kLexFastChunk;
+        if (pos == 0) B &= ~1ull;  // a flag at the input's first byte ends no token
+        acc.nt += (uint32_t)__popcll(B);
+        if (B) acc.lb = pos + (uint32_t)(63 - __clzll((long long)B));
+    };
+    walk_lex_tiles(
+        p, t0, t1,
+        [&](uint32_t tile, const LexIn& in, uint32_t) {
+            const uint32_t q = s_state[idc(run, in.cid)];
+            count(tile, lex_pass2<true>(in.w, kLexFastChunk, q, s_step, s_col, nullptr));
+            run = idc(run, in.tid);
+        },
+        [&](uint32_t tile, uint32_t) {
+            const uint32_t pos = tile * (uint32_t)kLexFastTile + tid * (uint32_t)kLexFastChunk;
+            const uint32_t len = pos < p.n ? min((uint32_t)kLexFastChunk, p.n - pos) : 0u;
+            uint32_t w[kLexWords];
+            load_lex_chunk<false>(p.in + pos, len, w);
+            const uint32_t q = s_state[idc(run, p.chunk_id[(size_t)tile * kLexFastBlock + tid])];
+            count(tile, lex_pass2<false>(w, len, q, s_step, s_col, nullptr));
+            run = idc(run, p.tile_id[tile]);
+        });
+    const LexTok r = block_reduce<kLexFastWaves>(acc, LexTok{0u, 0u}, s_tw, LexTokComb{});
+    if (tid == 0) p.range_tok[b] = make_uint2(r.nt, r.lb);
+}
+
+__global__ void __launch_bounds__(kLexFastBlock) lex_emit_kernel(LexFastParams p)
+{
+    extern __shared__ __align__(16) uint32_t s_tab[];
+    uint32_t* s_step = s_tab;
+    uint16_t* s_state = reinterpret_cast<uint16_t*>(s_tab + p.nq * p.m);
+    __shared__ uint8_t s_kind[kLexFastTile];  // kind of the token ending before each byte of the tile
+    __shared__ uint32_t s_list[kLexFastWaves][kLexList];
+    __shared__ uint8_t s_col[256];
+    __shared__ uint32_t s_wave[kLexFastWaves];
+    __shared__ LexTok s_pre[kLexFastWaves];
+    __shared__ LexTok s_tw[2][kLexFastWaves];
+    const uint32_t tid = threadIdx.x, b = blockIdx.x;
+    const uint32_t lane = (uint32_t)lane_id();
+    load_lex_automaton(p, s_step, s_state);
+    if (tid < 256) s_col[tid] = p.col[tid];
+    const LexIdComb idc{p.merge, p.k, p.id_mask};
+    uint32_t run = lex_ranges_before(p, b, s_wave, idc);  // (its barrier publishes the tables)
+    LexTok P = lex_tokens_before(p, b, s_pre);
+    const uint32_t cap32 = (uint32_t)min<uint64_t>(p.cap, 0xffffffffull);
+    uint32_t* list = s_list[tid / kWave];
+    const uint32_t pos0 = tid * (uint32_t)kLexFastChunk;  // the chunk's first byte in the tile
+    uint32_t t0, t1;
+    lex_range_of(p, b, t0, t1);
+    // one tile's tokens from its boundary bitmaps (pass 2 done, kinds in s_kind)
+    auto emit = [&](uint32_t tile, uint64_t B, uint32_t it) {
+        const uint32_t tile_start = tile * (uint32_t)kLexFastTile;
+        const uint32_t pos = tile_start + pos0;
+        if (pos == 0) B &= ~1ull;  // a flag at the input's first byte ends no token
+        const LexTok c{(uint32_t)__popcll(B), B ? pos + (uint32_t)(63 - __clzll((long long)B)) : 0u};
+        LexTok cex, ctot;
+        block_scan<kLexFastWaves>(c, LexTok{0u, 0u}, cex, ctot, s_tw[it & 1u], LexTokComb{});  // (publishes s_kind)
+
+        // Tokens, written by waves: each lane lists its boundaries (tile
+        // positions) in the wave's list, then lane l of a round takes token
+        // r + l: its end is its boundary, its start the previous boundary (the
+        // lane before, by DPP).
+        const uint32_t mine = c.nt;
+        const uint32_t wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)cex.nt);  // tile tokens before the wave
+        const uint32_t first = cex.nt - wbase;
+        const uint32_t wcnt = (uint32_t)__builtin_amdgcn_readlane((int)(first + mine), kWave - 1);
+        uint32_t off_run = max(P.lb, (uint32_t)__builtin_amdgcn_readfirstlane((int)cex.lb));
+        const uint32_t tw[2] = {(uint32_t)B, (uint32_t)(B >> 32)}, rw[2] = {0u, 0u};
+        for (uint32_t w0 = 0; w0 < wcnt; w0 += kLexList) {
+            const uint32_t w1 = min(w0 + (uint32_t)kLexList, wcnt);
+            list_terminators<2>(list, tw, rw, pos0, first, mine, w0, w1);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            for (uint32_t r = w0; r < w1; r += kWave) {
+                const uint32_t cnt = min((uint32_t)kWave, w1 - r);
+                const uint32_t e = list[r - w0 + min(lane, cnt - 1u)] >> 1;
+                const uint32_t end = tile_start + e;
+                const uint32_t prev = dpp_t<0x138, 0xf>(0u, end);  // wave_shr:1: the previous lane's boundary
+                const uint32_t st = lane ? prev : off_run;
+                const uint32_t g0 = P.nt + wbase + r;  // (token counts < n < 2^32)
+                const uint32_t room = g0 < cap32 ? min(cap32 - g0, cnt) : 0u;
+                if (lane < room) {
+                    store_u32(p.kind + g0, lane, s_kind[e]);
+                    store_u32(p.start + g0, lane, st);
+                    store_u32(p.len + g0, lane, end - st);
+                }
+                off_run = (uint32_t)__builtin_amdgcn_readlane((int)end, (int)cnt - 1);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        P = LexTokComb{}(P, ctot);
+        __syncthreads();  // the next tile's pass 2 rewrites s_kind
+    };
+    walk_lex_tiles(
+        p, t0, t1,
+        [&](uint32_t tile, const LexIn& in, uint32_t it) {
+            const uint32_t q = s_state[idc(run, in.cid)];
+            emit(tile, lex_pass2<true>(in.w, kLexFastChunk, q, s_step, s_col, s_kind + pos0), it);
+            run = idc(run, in.tid);
+        },
+        [&](uint32_t tile, uint32_t it) {
+            const uint32_t pos = tile * (uint32_t)kLexFastTile + pos0;
+            const uint32_t len = pos < p.n ? min((uint32_t)kLexFastChunk, p.n - pos) : 0u;
+            uint32_t w[kLexWords];
+            load_lex_chunk<false>(p.in + pos, len, w);
+            const uint32_t q = s_state[idc(run, p.chunk_id[(size_t)tile * kLexFastBlock + tid])];
+            emit(tile, lex_pass2<false>(w, len, q, s_step, s_col, s_kind + pos0), it);
+            run = idc(run, p.tile_id[tile]);
+        });
+    if (b == p.num_ranges - 1 && tid == 0) {  // the final token: from the last boundary to n
+        if (P.nt < p.cap) {
+            p.kind[P.nt] = p.final_[run];
+            p.start[P.nt] = P.lb;
+            p.len[P.nt] = p.n - P.lb;
+        }
+        p.hdr->n_fields = (uint64_t)P.nt + 1u;
+    }
+}
+
+// workgroups of the pass-1 kernel (two per CU hold the fold rows in LDS)
+constexpr uint32_t kLexIdsGrid = 512;
+
+int launch_lex_fast(const LexFastParams& p, const ppr_parse_opts_t* o, hipStream_t s)
+{
+    const size_t rows_lds = (size_t)(p.n_rows * p.m + 7u) / 8u * 16u;
+    const size_t tab_lds = (size_t)p.nq * p.m * 4u + (size_t)p.k * 2u;
+    stage_event(o, 0, s);
+    hipLaunchKernelGGL(lex_ids_kernel, dim3(std::min<uint32_t>(p.num_tiles, kLexIdsGrid)), dim3(kLexFastBlock), rows_lds,
+                       s, p);
+    hipLaunchKernelGGL(lex_range_kernel, dim3(p.num_ranges), dim3(kWave), 0, s, p);
+    stage_event(o, 1, s);
+    hipLaunchKernelGGL(lex_count_kernel, dim3(p.num_ranges), dim3(kLexFastBlock), tab_lds, s, p);
+    stage_event(o, 2, s);
+    hipLaunchKernelGGL(lex_emit_kernel, dim3(p.num_ranges), dim3(kLexFastBlock), tab_lds, s, p);
+    stage_event(o, 3, s);
+    return hipGetLastError() == hipSuccess ? PPR_OK : PPR_EHIP;
+}
+
+}  // namespace ppr

@@ -108,10 +108,17 @@ typedef struct ppr_parse_out {
  *   PPR_PATH_FUSED       table-driven, 2 kernels (step tables, one persistent
  *                        single-pass kernel with decoupled look-back scans over
  *                        32 KiB tiles): the input is read once;
- *   PPR_PATH_STREAMING   table-driven, 5 kernels (step tables, codes, range
- *                        vectors, carries, emit), no waiting between workgroups;
+ *   PPR_PATH_STREAMING   table-driven, 4 kernels (codes, range vectors,
+ *                        carries, emit), no waiting between workgroups;
  *   PPR_PATH_SINGLE_PASS any table and chunk size: 2 kernels (reset, one
  *                        single-pass kernel with decoupled look-back scans).
+ * The lexer has two (reported in ppr_tokens_out_t.path):
+ *   PPR_PATH_STREAMING   4 kernels (chunk identifiers through the fold rows,
+ *                        range identifiers, boundary counts, tokens), no waiting
+ *                        between workgroups; needs chunk_bytes 40, an 8-byte
+ *                        aligned input and prepared fold rows (n_rows > 0);
+ *   PPR_PATH_SINGLE_PASS any chunk size: 2 kernels (reset, one single-pass
+ *                        kernel with decoupled look-back scans).
  */
 enum { PPR_PATH_STREAMING = 1, PPR_PATH_SINGLE_PASS = 2, PPR_PATH_FUSED = 3 };
 
@@ -121,15 +128,16 @@ enum { PPR_PATH_STREAMING = 1, PPR_PATH_SINGLE_PASS = 2, PPR_PATH_FUSED = 3 };
  *   stage_events:   optional array of n_stage_events hipEvent_t (caller-created):
  *                   event 0 is recorded on the stream before the first kernel of the
  *                   call and event i after its i-th kernel, as far as the array
- *                   reaches (streaming parse: 3 events after the codes + range
- *                   vectors, carries and emit kernels; fused and single-pass parse
- *                   and the lexer: 2). For per-kernel timing; NULL: none.
+ *                   reaches (streaming parse and lexer: 3 events, after the
+ *                   first two kernels and after each of the last two; fused and
+ *                   single-pass parse and lexer: 2). For per-kernel timing;
+ *                   NULL: none.
  *   path:           0 = automatic (the streaming path where the table and input
  *                   allow it, else the single-pass path); PPR_PATH_FUSED or
  *                   PPR_PATH_STREAMING ask for that path and fall back to the
  *                   single-pass path where it does not apply; PPR_PATH_SINGLE_PASS
  *                   forces the generic kernel. Any other value: PPR_EINVAL. The
- *                   lexer ignores it.
+ *                   lexer treats PPR_PATH_FUSED as PPR_PATH_STREAMING.
  */
 typedef struct ppr_parse_opts {
     uint32_t chunk_bytes;
@@ -195,6 +203,10 @@ typedef struct ppr_lex_tables {
  * partition refinement): the state of each identifier, and per state and
  * column its successor state and flag, and its token kind. Lexing from a known
  * prefix (the second pass over a chunk) steps through this small automaton.
+ * Then the fold rows of the streaming lexer kernels: identifiers whose rows of
+ * the fold name the same identifiers share a row; per row and column, the row
+ * reached (times m) and the identifier reached. The first pass over a chunk
+ * walks these rows in LDS.
  */
 typedef struct ppr_lex_prepared {
     uint16_t* d_fold;      /* caller-provided device buffer of ppr_lex_fold_bytes(k) bytes */
@@ -204,6 +216,8 @@ typedef struct ppr_lex_prepared {
     uint16_t flag_mask;
     uint8_t column_of[256]; /* out: column of each byte */
     uint32_t n_states;     /* out: states of the minimal automaton (0: it does not fit the buffer; not used) */
+    uint32_t n_rows;       /* out: fold rows (0: the streaming kernels' tables do not fit; they are not used) */
+    uint32_t row0;         /* out: the identity's row, times m */
 } ppr_lex_prepared_t;
 
 /* Device bytes the prepared fold table needs (k * 256 * 2 at most). */
@@ -224,6 +238,7 @@ typedef struct ppr_tokens_out {
     uint32_t* length;
     uint64_t cap_tokens;
     uint64_t n_tokens; /* out */
+    uint32_t path;     /* out: the kernels that ran (PPR_PATH_STREAMING or PPR_PATH_SINGLE_PASS) */
 } ppr_tokens_out_t;
 
 PPR_API size_t ppr_lex_workspace_bytes(uint64_t n, const ppr_parse_opts_t* opts);

@@ -16,6 +16,7 @@ import workloads as W
 
 pytestmark = pytest.mark.gpu
 
+STREAMING, SINGLE_PASS = 1, 2
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "lex_examples.jsonl")
 
 
@@ -58,26 +59,33 @@ def _same(g, r, what=""):
                 what, key, bad.size, a.size, bad[0], a[bad[0]], r[key][bad[0]]))
 
 
+# (chunk, path): the default 40-byte chunks run the streaming kernels; the
+# single-pass kernel is asked for explicitly or serves other chunk sizes
+PATHS = [(1, None), (2, None), (32, None), (None, None), (None, SINGLE_PASS)]
+
+
 def test_golden(ppr, tables):
     for line in open(GOLDEN):
         c = json.loads(line)
         d, T = tables[c["grammar"]]
         b = c["input"].encode()
-        for chunk in (1, 2, 32, None):
-            _say("golden", repr(b), chunk)
-            g = ppr.lex(_dev(b), T, chunk_bytes=chunk, capacity=len(b) + 1)
-            _same(g, oracle.lex_restart(b, d), (b, chunk))
+        for chunk, path in PATHS:
+            _say("golden", repr(b), chunk, path)
+            g = ppr.lex(_dev(b), T, chunk_bytes=chunk, capacity=len(b) + 1, path=path)
+            _same(g, oracle.lex_restart(b, d), (b, chunk, path))
 
 
-@pytest.mark.parametrize("chunk", [1, 3, 16, 31, 32, 40, 64])
-def test_streams_several_tiles(ppr, tables, chunk):
+@pytest.mark.parametrize("chunk,path", [(1, None), (3, None), (16, None), (31, None), (32, None), (40, None),
+                                        (40, SINGLE_PASS), (64, None)])
+def test_streams_several_tiles(ppr, tables, chunk, path):
     d, T = tables["lexer"]
     for seed in (1, 2):
         n = (2 << 20) + 777 * seed
         b = W.gen_tokens(seed, n)
-        _say("stream", chunk, seed, n)
-        g = ppr.lex(_dev(b), T, chunk_bytes=chunk, capacity=n + 1)
-        _same(g, oracle.lex_restart(b, d), (chunk, seed))
+        _say("stream", chunk, path, seed, n)
+        g = ppr.lex(_dev(b), T, chunk_bytes=chunk, capacity=n + 1, path=path)
+        _same(g, oracle.lex_restart(b, d), (chunk, path, seed))
+        assert g.path == (path or (STREAMING if chunk == 40 else SINGLE_PASS))
 
 
 def test_random_bytes_and_edges(ppr, tables):
@@ -86,26 +94,56 @@ def test_random_bytes_and_edges(ppr, tables):
     cases = [b"", b"a", b"@", b"//" + b"x" * 70000, b'"' + b"q" * 70001, b" " * 100000, b"1." * 30000]
     cases += [rng.integers(0, 256, int(rng.integers(1, 50000)), dtype=np.uint8).tobytes() for _ in range(6)]
     for b in cases:
-        for chunk in (1, 7, 32, None):
-            _say("edge", len(b), chunk)
-            g = ppr.lex(_dev(b) if b else _dev(b"\0")[:0], T, chunk_bytes=chunk, capacity=len(b) + 1)
-            _same(g, oracle.lex_restart(b, d), (len(b), chunk))
+        for chunk, path in [(1, None), (7, None), (32, None), (None, None), (None, SINGLE_PASS)]:
+            _say("edge", len(b), chunk, path)
+            g = ppr.lex(_dev(b) if b else _dev(b"\0")[:0], T, chunk_bytes=chunk, capacity=len(b) + 1, path=path)
+            _same(g, oracle.lex_restart(b, d), (len(b), chunk, path))
+
+
+def test_streaming_ragged_tiles_and_ranges(ppr, tables):
+    """the streaming kernels at lengths around their 20 KiB tiles and 40-byte chunks (a last chunk of 1 byte,
+    a last tile of one chunk), and with more tiles than ranges (the 1024 ranges then hold one or two tiles)"""
+    d, T = tables["lexer"]
+    tile = 512 * 40
+    for n in (1, 39, 40, 41, tile - 1, tile, tile + 1, 3 * tile + 40 * 17 + 1, 1500 * tile + 12345):
+        b = W.gen_tokens(7, n)
+        _say("ragged", n)
+        g = ppr.lex(_dev(b), T, capacity=n + 1)
+        assert g.path == STREAMING
+        _same(g, oracle.lex_restart(b, d), n)
+
+
+def test_streaming_needs_aligned_input(ppr, tables):
+    """an input that does not start on 8 bytes runs the single-pass kernel, with the same tokens"""
+    d, T = tables["lexer"]
+    b = W.gen_tokens(8, 300000)
+    buf = _dev(np.concatenate([np.zeros(3, np.uint8), b]))
+    g = ppr.lex(buf[3:], T, capacity=b.size + 1)
+    assert g.path == SINGLE_PASS
+    _same(g, oracle.lex_restart(b, d), "misaligned")
+    assert ppr.lex(_dev(b), T, capacity=b.size + 1).path == STREAMING
 
 
 def test_minimal_automaton_and_identifier_fold(ppr, tables):
     """the second pass steps the minimal automaton of the fold when the prepared tables hold one, and re-folds
-    the identifiers otherwise; both against the oracle"""
+    the identifiers otherwise; both against the oracle. Without the automaton or the fold rows the streaming
+    kernels do not run."""
     d, T = tables["lexer"]
     assert 0 < T.prep.n_states <= T.k, T.prep.n_states
+    assert 0 < T.prep.n_rows <= T.k, T.prep.n_rows
     b = W.gen_tokens(3, (1 << 20) + 5)
     r = oracle.lex_restart(b, d)
-    _same(ppr.lex(_dev(b), T, capacity=b.size + 1), r, "minimal automaton")
-    saved = T.prep.n_states
-    T.prep.n_states = 0
-    try:
-        _same(ppr.lex(_dev(b), T, capacity=b.size + 1), r, "identifier fold")
-    finally:
-        T.prep.n_states = saved
+    _same(ppr.lex(_dev(b), T, capacity=b.size + 1), r, "streaming")
+    _same(ppr.lex(_dev(b), T, capacity=b.size + 1, path=SINGLE_PASS), r, "minimal automaton")
+    for field in ("n_rows", "n_states"):
+        saved = getattr(T.prep, field)
+        setattr(T.prep, field, 0)
+        try:
+            g = ppr.lex(_dev(b), T, capacity=b.size + 1)
+            assert g.path == SINGLE_PASS
+            _same(g, r, "without " + field)
+        finally:
+            setattr(T.prep, field, saved)
 
 
 @pytest.mark.slow
@@ -116,5 +154,8 @@ def test_full_size_lexer_workload(ppr, tables):
     _say("full lexer: oracle")
     r = oracle.lex_restart(b, d)
     _say("full lexer: gpu", r["n_tokens"])
-    g = ppr.Lexer(T, max_n=b.size, capacity=r["n_tokens"])(_dev(b))
-    _same(g, r, "full")
+    d_b = _dev(b)
+    for path in (None, SINGLE_PASS):
+        g = ppr.Lexer(T, max_n=b.size, capacity=r["n_tokens"], path=path)(d_b)
+        assert g.path == (path or STREAMING)
+        _same(g, r, ("full", path))
