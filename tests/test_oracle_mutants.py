@@ -9,6 +9,7 @@ The oracle's own source is never modified.
 import ctypes
 import itertools
 import json
+import multiprocessing
 import os
 import subprocess
 import tempfile
@@ -50,7 +51,7 @@ LEX_MUTANTS = {
 }
 
 
-def _compile(src_name, subst, tmp):
+def _compile_so(src_name, subst, tmp):
     src = open(os.path.join(ORACLE_DIR, src_name)).read()
     old, new = subst
     assert src.count(old) == 1, (src_name, old)
@@ -58,7 +59,32 @@ def _compile(src_name, subst, tmp):
     open(path, "w").write(src.replace(old, new))
     so = os.path.join(tmp, "m%d.so" % abs(hash(old + new)))
     subprocess.run(["gcc", "-O1", "-shared", "-fPIC", "-o", so, path], check=True, capture_output=True)
-    return ctypes.CDLL(so)
+    return so
+
+
+def _compile(src_name, subst, tmp):
+    return ctypes.CDLL(_compile_so(src_name, subst, tmp))
+
+
+def _pins_reject(src_name, subst, pins_pass):
+    """Compiles a mutant and runs the pins on it in a forked child process. A
+    mutant is caught when the pins reject it, and also when its mistake makes
+    it crash or hang (an identifier with its flag bit left on indexes far past
+    the merge table) instead of returning a wrong answer."""
+    with tempfile.TemporaryDirectory() as tmp:
+        so = _compile_so(src_name, subst, tmp)
+
+        def child():
+            os._exit(0 if pins_pass(ctypes.CDLL(so)) else 1)
+
+        proc = multiprocessing.get_context("fork").Process(target=child)
+        proc.start()
+        proc.join(300)
+        if proc.exitcode is None:
+            proc.kill()
+            proc.join()
+            return True
+        return proc.exitcode != 0
 
 
 def _csv_run(L, t, b):
@@ -98,9 +124,7 @@ def _csv_pins_pass(L):
 
 @pytest.mark.parametrize("mutant", sorted(CSV_MUTANTS))
 def test_csv_mutant_is_caught(mutant):
-    with tempfile.TemporaryDirectory() as tmp:
-        L = _compile("csv_oracle.c", CSV_MUTANTS[mutant], tmp)
-        assert not _csv_pins_pass(L), "pins did not catch mutant %s" % mutant
+    assert _pins_reject("csv_oracle.c", CSV_MUTANTS[mutant], _csv_pins_pass), "pins did not catch mutant %s" % mutant
 
 
 def test_unmutated_csv_source_passes_same_pins():
@@ -155,9 +179,7 @@ def _lex_pins_pass(L):
 
 @pytest.mark.parametrize("mutant", sorted(LEX_MUTANTS))
 def test_lex_mutant_is_caught(mutant):
-    with tempfile.TemporaryDirectory() as tmp:
-        L = _compile("lex_oracle.c", LEX_MUTANTS[mutant], tmp)
-        assert not _lex_pins_pass(L), "pins did not catch mutant %s" % mutant
+    assert _pins_reject("lex_oracle.c", LEX_MUTANTS[mutant], _lex_pins_pass), "pins did not catch mutant %s" % mutant
 
 
 def test_unmutated_lex_source_passes_same_pins():
