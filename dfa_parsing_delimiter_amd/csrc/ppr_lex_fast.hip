@@ -195,11 +195,23 @@ __device__ __forceinline__ void load_lex_automaton(const LexFastParams& p, uint3
     for (uint32_t i = threadIdx.x; i < p.k; i += kLexFastBlock) s_state[i] = (uint16_t)(p.state_of[i] * m);
 }
 
+// Two tiles' chunk identifiers, scanned together: the merges of the two scans
+// are independent gathers, so each level of the scan waits once for both.
+struct IdPair {
+    uint32_t a, b;
+};
+
+struct LexIdPairComb {
+    LexIdComb c;
+    __device__ IdPair operator()(const IdPair& x, const IdPair& y) const { return {c(x.a, y.a), c(x.b, y.b)}; }
+};
+
 __global__ void __launch_bounds__(kLexFastBlock) lex_ids_kernel(LexFastParams p)
 {
     extern __shared__ __align__(16) uint16_t s_rows[];
     __shared__ uint8_t s_col[256];
-    __shared__ uint32_t s_wave[2][kLexFastWaves];
+    __shared__ IdPair s_pair[2][kLexFastWaves];
+    __shared__ uint32_t s_wave[kLexFastWaves];
     const uint32_t tid = threadIdx.x;
     if (blockIdx.x == 0 && tid == 0) {  // (no kernel of the call has read the header yet)
         p.hdr->tile_counter = 0;
@@ -213,43 +225,56 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_ids_kernel(LexFastParams p)
     if (tid < 256) s_col[tid] = p.col[tid];
     __syncthreads();
     const LexIdComb idc{p.merge, p.k, p.id_mask};
+    const LexIdPairComb pcomb{idc};
     const uint32_t tfull = p.n / (uint32_t)kLexFastTile;  // tiles [0, tfull) are entirely full
     const uint32_t stride = gridDim.x;
-    auto load = [&](uint32_t t, uint32_t (&w)[kLexWords]) {
+    // Workgroup b takes the full tiles b, b + G, b + 2G, ... (G = the grid) two at
+    // a time: t and t + G (t itself again when t + G is not a full tile; the two
+    // halves then store the same values).
+    auto second = [&](uint32_t t) { return t + stride < tfull ? t + stride : t; };
+    auto load = [&](uint32_t t, uint32_t (&w)[kLexWords], uint32_t (&w2)[kLexWords]) {
         load_lex_chunk<true>(p.in + (size_t)t * kLexFastTile + tid * kLexFastChunk, kLexFastChunk, w);
+        load_lex_chunk<true>(p.in + (size_t)second(t) * kLexFastTile + tid * kLexFastChunk, kLexFastChunk, w2);
     };
-    auto body = [&](uint32_t t, const uint32_t (&w)[kLexWords], uint32_t it) {
-        uint32_t excl, tot;
-        block_scan<kLexFastWaves>(fold_lex_chunk<true>(p, w, kLexFastChunk, s_rows, s_col), p.identity, excl, tot,
-                                  s_wave[it & 1], idc);
-        p.chunk_id[(size_t)t * kLexFastBlock + tid] = (uint16_t)excl;
-        if (tid == 0) p.tile_id[t] = tot;
+    auto body = [&](uint32_t t, const uint32_t (&w)[kLexWords], const uint32_t (&w2)[kLexWords], uint32_t it) {
+        const uint32_t t2 = second(t);
+        const IdPair v{fold_lex_chunk<true>(p, w, kLexFastChunk, s_rows, s_col),
+                       fold_lex_chunk<true>(p, w2, kLexFastChunk, s_rows, s_col)};
+        IdPair excl, tot;
+        block_scan<kLexFastWaves>(v, IdPair{p.identity, p.identity}, excl, tot, s_pair[it & 1], pcomb);
+        p.chunk_id[(size_t)t * kLexFastBlock + tid] = (uint16_t)excl.a;
+        p.chunk_id[(size_t)t2 * kLexFastBlock + tid] = (uint16_t)excl.b;
+        if (tid == 0) {
+            p.tile_id[t] = tot.a;
+            p.tile_id[t2] = tot.b;
+        }
     };
     // two register buffers used in turn, unconditional prefetch (the workgroup's
-    // last full tile is read again at the end)
+    // last pair is read again at the end)
     uint32_t tile = blockIdx.x, it = 0;
-    const uint32_t tlast = tfull > tile ? tile + (tfull - 1 - tile) / stride * stride : tile;
-    uint32_t wa[kLexWords], wb[kLexWords];
-    if (tile < tfull) load(tile, wa);
+    const uint32_t step = 2 * stride;
+    const uint32_t tlast = tfull > tile ? tile + (tfull - 1 - tile) / step * step : tile;
+    uint32_t wa[kLexWords], wa2[kLexWords], wb[kLexWords], wb2[kLexWords];
+    if (tile < tfull) load(tile, wa, wa2);
     while (tile < tfull) {
-        load(min(tile + stride, tlast), wb);
-        body(tile, wa, it++);
-        tile += stride;
+        load(min(tile + step, tlast), wb, wb2);
+        body(tile, wa, wa2, it++);
+        tile += step;
         if (tile >= tfull) break;
-        load(min(tile + stride, tlast), wa);
-        body(tile, wb, it++);
-        tile += stride;
+        load(min(tile + step, tlast), wa, wa2);
+        body(tile, wb, wb2, it++);
+        tile += step;
     }
-    if (tile < p.num_tiles) {  // the input's ragged last tile
-        const uint32_t pos = tile * (uint32_t)kLexFastTile + tid * (uint32_t)kLexFastChunk;
+    if (tfull < p.num_tiles && blockIdx.x == tfull % stride) {  // the input's ragged last tile
+        const uint32_t pos = tfull * (uint32_t)kLexFastTile + tid * (uint32_t)kLexFastChunk;
         const uint32_t len = pos < p.n ? min((uint32_t)kLexFastChunk, p.n - pos) : 0u;
         uint32_t w[kLexWords];
         load_lex_chunk<false>(p.in + pos, len, w);
         uint32_t excl, tot;
-        block_scan<kLexFastWaves>(fold_lex_chunk<false>(p, w, len, s_rows, s_col), p.identity, excl, tot,
-                                  s_wave[it & 1], idc);
-        p.chunk_id[(size_t)tile * kLexFastBlock + tid] = (uint16_t)excl;
-        if (tid == 0) p.tile_id[tile] = tot;
+        block_scan<kLexFastWaves>(fold_lex_chunk<false>(p, w, len, s_rows, s_col), p.identity, excl, tot, s_wave,
+                                  idc);
+        p.chunk_id[(size_t)tfull * kLexFastBlock + tid] = (uint16_t)excl;
+        if (tid == 0) p.tile_id[tfull] = tot;
     }
 }
 
