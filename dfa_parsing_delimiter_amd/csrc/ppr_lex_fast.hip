@@ -195,22 +195,30 @@ __device__ __forceinline__ void load_lex_automaton(const LexFastParams& p, uint3
     for (uint32_t i = threadIdx.x; i < p.k; i += kLexFastBlock) s_state[i] = (uint16_t)(p.state_of[i] * m);
 }
 
-// Two tiles' chunk identifiers, scanned together: the merges of the two scans
-// are independent gathers, so each level of the scan waits once for both.
-struct IdPair {
-    uint32_t a, b;
+// Several tiles' chunk identifiers, scanned together: the merges of the scans
+// are independent gathers, so each level of the scan waits once for all.
+constexpr int kIdsTiles = 4;
+
+struct IdSet {
+    uint32_t v[kIdsTiles];
 };
 
-struct LexIdPairComb {
+struct LexIdSetComb {
     LexIdComb c;
-    __device__ IdPair operator()(const IdPair& x, const IdPair& y) const { return {c(x.a, y.a), c(x.b, y.b)}; }
+    __device__ IdSet operator()(const IdSet& x, const IdSet& y) const
+    {
+        IdSet r;
+#pragma unroll
+        for (int k = 0; k < kIdsTiles; ++k) r.v[k] = c(x.v[k], y.v[k]);
+        return r;
+    }
 };
 
 __global__ void __launch_bounds__(kLexFastBlock) lex_ids_kernel(LexFastParams p)
 {
     extern __shared__ __align__(16) uint16_t s_rows[];
     __shared__ uint8_t s_col[256];
-    __shared__ IdPair s_pair[2][kLexFastWaves];
+    __shared__ IdSet s_set[2][kLexFastWaves];
     __shared__ uint32_t s_wave[kLexFastWaves];
     const uint32_t tid = threadIdx.x;
     if (blockIdx.x == 0 && tid == 0) {  // (no kernel of the call has read the header yet)
@@ -225,45 +233,32 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_ids_kernel(LexFastParams p)
     if (tid < 256) s_col[tid] = p.col[tid];
     __syncthreads();
     const LexIdComb idc{p.merge, p.k, p.id_mask};
-    const LexIdPairComb pcomb{idc};
+    const LexIdSetComb scomb{idc};
     const uint32_t tfull = p.n / (uint32_t)kLexFastTile;  // tiles [0, tfull) are entirely full
     const uint32_t stride = gridDim.x;
-    // Workgroup b takes the full tiles b, b + G, b + 2G, ... (G = the grid) two at
-    // a time: t and t + G (t itself again when t + G is not a full tile; the two
-    // halves then store the same values).
-    auto second = [&](uint32_t t) { return t + stride < tfull ? t + stride : t; };
-    auto load = [&](uint32_t t, uint32_t (&w)[kLexWords], uint32_t (&w2)[kLexWords]) {
-        load_lex_chunk<true>(p.in + (size_t)t * kLexFastTile + tid * kLexFastChunk, kLexFastChunk, w);
-        load_lex_chunk<true>(p.in + (size_t)second(t) * kLexFastTile + tid * kLexFastChunk, kLexFastChunk, w2);
-    };
-    auto body = [&](uint32_t t, const uint32_t (&w)[kLexWords], const uint32_t (&w2)[kLexWords], uint32_t it) {
-        const uint32_t t2 = second(t);
-        const IdPair v{fold_lex_chunk<true>(p, w, kLexFastChunk, s_rows, s_col),
-                       fold_lex_chunk<true>(p, w2, kLexFastChunk, s_rows, s_col)};
-        IdPair excl, tot;
-        block_scan<kLexFastWaves>(v, IdPair{p.identity, p.identity}, excl, tot, s_pair[it & 1], pcomb);
-        p.chunk_id[(size_t)t * kLexFastBlock + tid] = (uint16_t)excl.a;
-        p.chunk_id[(size_t)t2 * kLexFastBlock + tid] = (uint16_t)excl.b;
-        if (tid == 0) {
-            p.tile_id[t] = tot.a;
-            p.tile_id[t2] = tot.b;
+    // Workgroup b takes the full tiles b, b + G, b + 2G, ... (G = the grid),
+    // kIdsTiles at a time: t, t + G, ... (t itself again in place of one that is
+    // not a full tile; its copy then stores the same values).
+    auto nth = [&](uint32_t t, uint32_t k) { return t + k * stride < tfull ? t + k * stride : t; };
+    uint32_t it = 0;
+    for (uint32_t tile = blockIdx.x; tile < tfull; tile += kIdsTiles * stride, ++it) {
+        uint32_t w[kIdsTiles][kLexWords];
+#pragma unroll
+        for (int k = 0; k < kIdsTiles; ++k)
+            load_lex_chunk<true>(p.in + (size_t)nth(tile, k) * kLexFastTile + tid * kLexFastChunk, kLexFastChunk,
+                                 w[k]);
+        IdSet v, ident, excl, tot;
+#pragma unroll
+        for (int k = 0; k < kIdsTiles; ++k) {
+            v.v[k] = fold_lex_chunk<true>(p, w[k], kLexFastChunk, s_rows, s_col);
+            ident.v[k] = p.identity;
         }
-    };
-    // two register buffers used in turn, unconditional prefetch (the workgroup's
-    // last pair is read again at the end)
-    uint32_t tile = blockIdx.x, it = 0;
-    const uint32_t step = 2 * stride;
-    const uint32_t tlast = tfull > tile ? tile + (tfull - 1 - tile) / step * step : tile;
-    uint32_t wa[kLexWords], wa2[kLexWords], wb[kLexWords], wb2[kLexWords];
-    if (tile < tfull) load(tile, wa, wa2);
-    while (tile < tfull) {
-        load(min(tile + step, tlast), wb, wb2);
-        body(tile, wa, wa2, it++);
-        tile += step;
-        if (tile >= tfull) break;
-        load(min(tile + step, tlast), wa, wa2);
-        body(tile, wb, wb2, it++);
-        tile += step;
+        block_scan<kLexFastWaves>(v, ident, excl, tot, s_set[it & 1], scomb);
+#pragma unroll
+        for (int k = 0; k < kIdsTiles; ++k) {
+            p.chunk_id[(size_t)nth(tile, k) * kLexFastBlock + tid] = (uint16_t)excl.v[k];
+            if (tid == 0) p.tile_id[nth(tile, k)] = tot.v[k];
+        }
     }
     if (tfull < p.num_tiles && blockIdx.x == tfull % stride) {  // the input's ragged last tile
         const uint32_t pos = tfull * (uint32_t)kLexFastTile + tid * (uint32_t)kLexFastChunk;
