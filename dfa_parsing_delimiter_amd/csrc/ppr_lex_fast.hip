@@ -49,7 +49,7 @@ struct LexTokComb {
 };
 
 constexpr int kLexWords = kLexFastChunk / 4;  // dwords per chunk
-constexpr int kLexList = 512;                 // per-wave token list entries (LDS)
+constexpr int kLexList = 1024;                // per-wave token list entries (LDS)
 
 __device__ __forceinline__ uint32_t chunk_byte(const uint32_t (&w)[kLexWords], int j)
 {
