@@ -870,10 +870,11 @@ struct FieldRun {
 // (mbcnt), the column counts from the last record field before the lane, the
 // offset follows the previous lane's terminator (DPP). The four arrays are
 // written through wave-uniform base pointers, so every store is one scalar
-// base plus the lane's offset. cap32: the output capacity clamped to 32 bits;
+// base plus the lane's offset; a field is written only below the capacity
+// (compared in 64 bits, so that no wrap-around can let a store through).
 // lt_mask: the lanes below this one.
-__device__ __forceinline__ void field_round(const OutArrays& o, uint32_t cap32, uint32_t g0, uint32_t cnt, uint32_t e,
-                                            uint32_t base, uint32_t lane, uint64_t lt_mask, FieldRun& fr)
+__device__ __forceinline__ void field_round(const OutArrays& o, uint32_t g0, uint32_t cnt, uint32_t e, uint32_t base,
+                                            uint32_t lane, uint64_t lt_mask, FieldRun& fr)
 {
     const uint32_t pos = base + (e >> 1);
     const uint64_t m = __ballot(lane < cnt && (e & 1u));
@@ -883,8 +884,7 @@ __device__ __forceinline__ void field_round(const OutArrays& o, uint32_t cap32, 
     const uint32_t col = below ? lane - (uint32_t)(63 - __clzll((long long)below)) - 1u : fr.col + lane;
     const uint32_t prev = dpp_t<0x138, 0xf>(0u, pos);  // wave_shr:1: the previous lane's terminator
     const uint32_t off = lane ? prev + 1u : fr.off;
-    const uint32_t room = g0 < cap32 ? min(cap32 - g0, cnt) : 0u;
-    if (lane < room) {
+    if (lane < cnt && (uint64_t)g0 + lane < o.cap) {
         store_u32(o.rec + g0, lane, rec);
         store_u32(o.col + g0, lane, col);
         store_u32(o.off + g0, lane, off);
@@ -929,7 +929,6 @@ __global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_e
     const Vec ident = fast_ident<V8>(p.nt);
     uint32_t run = p.range_state[b];
     const OutArrays& o = p.out;
-    const uint32_t cap32 = (uint32_t)min<uint64_t>(o.cap, 0xffffffffull);
     const uint64_t lt_mask = (1ull << lane) - 1ull;
     uint32_t* list = s_list[wv];
     load_pass2<CB, V8>(p, sh);
@@ -971,7 +970,7 @@ __global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_e
             // each lane stores at its own 4-byte offset
             for (uint32_t r = w0; r < w1; r += kWave) {
                 const uint32_t cnt = min((uint32_t)kWave, w1 - r);
-                field_round(o, cap32, P.nf + r, cnt, list[r - w0 + min(lane, cnt - 1u)], st_abs, lane, lt_mask, fr);
+                field_round(o, P.nf + r, cnt, list[r - w0 + min(lane, cnt - 1u)], st_abs, lane, lt_mask, fr);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -1132,7 +1131,6 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
     const uint32_t wv = threadIdx.x / kWave;
     const uint32_t nt = p.nt, num_tiles = p.num_tiles;
     const OutArrays& o = p.out;
-    const uint32_t cap32 = (uint32_t)min<uint64_t>(o.cap, 0xffffffffull);
     const uint64_t lt_mask = (1ull << lane) - 1ull;
     const GCarryComb gcomb;
     const GCarry zero{0u, 0u, 0u, 0u};
@@ -1274,7 +1272,7 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 for (uint32_t r = w0; r < w1; r += kWave) {
                     const uint32_t cnt = min((uint32_t)kWave, w1 - r);
-                    field_round(o, cap32, P.nf + r, cnt, list[r - w0 + min(lane, cnt - 1u)], tile_start, lane,
+                    field_round(o, P.nf + r, cnt, list[r - w0 + min(lane, cnt - 1u)], tile_start, lane,
                                 lt_mask, fr);
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

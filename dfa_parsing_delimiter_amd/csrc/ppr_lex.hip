@@ -267,7 +267,6 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
     // the three output arrays are written with consecutive addresses.
     {
         const uint32_t lane = (uint32_t)lane_id();
-        const uint32_t cap32 = (uint32_t)min<uint64_t>(p.cap, 0xffffffffull);
         const uint32_t lcap = kLexBlock * L / 4u / kLexWaves;  // per-wave list entries over the tile's bytes
         uint32_t* list = reinterpret_cast<uint32_t*>(s_bytes) + (tid / kWave) * lcap;
         const uint32_t mine = c.nt;
@@ -289,9 +288,9 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
                 const uint32_t prev = dpp_t<0x138, 0xf>(0u, pos);  // wave_shr:1: the previous lane's boundary
                 const uint32_t st = lane ? prev : off_run;
                 const uint32_t kd = s_kind[e];
-                const uint32_t g0 = P.nt + wbase + r;  // (token counts < n < 2^32)
-                const uint32_t room = g0 < cap32 ? min(cap32 - g0, cnt) : 0u;
-                if (lane < room) {
+                // the round's first token index, in 64 bits: a slot is written only below the capacity
+                const uint64_t g0 = (uint64_t)P.nt + wbase + r;
+                if (lane < cnt && g0 + lane < p.cap) {
                     store_u32(p.kind + g0, lane, kd);
                     store_u32(p.start + g0, lane, st);
                     store_u32(p.len + g0, lane, pos - st);

@@ -347,7 +347,6 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_emit_kernel(LexFastParams p
     const LexIdComb idc{p.merge, p.k, p.id_mask};
     uint32_t run = lex_ranges_before(p, b, s_wave, idc);  // (its barrier publishes the tables)
     LexTok P = lex_tokens_before(p, b, s_pre);
-    const uint32_t cap32 = (uint32_t)min<uint64_t>(p.cap, 0xffffffffull);
     uint32_t* list = s_list[tid / kWave];
     const uint32_t pos0 = tid * (uint32_t)kLexFastChunk;  // the chunk's first byte in the tile
     uint32_t t0, t1;
@@ -383,9 +382,9 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_emit_kernel(LexFastParams p
                 const uint32_t end = tile_start + e;
                 const uint32_t prev = dpp_t<0x138, 0xf>(0u, end);  // wave_shr:1: the previous lane's boundary
                 const uint32_t st = lane ? prev : off_run;
-                const uint32_t g0 = P.nt + wbase + r;  // (token counts < n < 2^32)
-                const uint32_t room = g0 < cap32 ? min(cap32 - g0, cnt) : 0u;
-                if (lane < room) {
+                // the round's first token index, in 64 bits: a slot is written only below the capacity
+                const uint64_t g0 = (uint64_t)P.nt + wbase + r;
+                if (lane < cnt && g0 + lane < p.cap) {
                     store_u32(p.kind + g0, lane, s_kind[e]);
                     store_u32(p.start + g0, lane, st);
                     store_u32(p.len + g0, lane, end - st);

@@ -65,6 +65,7 @@ def _same(g, r, what=""):
 # the streaming kernels; 3: the fused kernel)
 AUTO_PATH = 1
 FUSED = 3
+SINGLE_PASS = 2
 
 
 def _with_paths(chunks):
@@ -198,22 +199,34 @@ def test_edge_cases(ppr):
             _same(g, oracle.csv_parse(b, t), (t["name"], len(b), chunk, path))
 
 
-def test_capacity_reported(ppr):
+@pytest.mark.parametrize("path,cap", [(None, 100), (None, 20000), (FUSED, 20000), (SINGLE_PASS, 20000)])
+def test_capacity_reported(ppr, path, cap):
+    """with too few output slots: PPR_ECAPACITY, the counts set, the first cap fields written and nothing past
+    them (guard words after each array stay untouched); the binding then resizes and fills"""
     import ctypes
+    import torch
     t = W.table("T5")
-    b = W.generate(1, n=1 << 18, seed=9)
+    b = W.generate(1, n=1 << 20, seed=9)
     r = oracle.csv_parse(b, t)
-    P = ppr.Parser(t, max_n=b.size, capacity=100)
-    out = P._out()
-    rc = ppr.lib.ppr_parse(ctypes.c_void_p(_dev(b).data_ptr()), b.size, ctypes.byref(P.dfa), P.class_map,
+    assert r["n_fields"] > cap
+    P = ppr.Parser(t, max_n=b.size, capacity=cap, path=path)
+    guard = 4096
+    arrs = [torch.full((cap + guard,), -1, dtype=torch.int32, device="cuda") for _ in range(4)]
+    out = ppr.ParseOut()
+    out.record_idx, out.column_ids, out.field_offsets, out.field_lengths = [a.data_ptr() for a in arrs]
+    out.cap_fields = cap
+    d = _dev(b)
+    rc = ppr.lib.ppr_parse(ctypes.c_void_p(d.data_ptr()), b.size, ctypes.byref(P.dfa), P.class_map,
                            ctypes.byref(out), P._ws_ptr(), P.ws_bytes, ctypes.byref(P.opts), None)
     assert rc == ppr.PPR_ECAPACITY
     assert out.n_fields == r["n_fields"] and out.n_records == r["n_records"]
-    first = _np(P.out_arrays[2][:100])
-    assert np.array_equal(first, r["off"][:100])
+    assert out.path == (path or AUTO_PATH)
+    for a, key in zip(arrs, ("rec", "col", "off", "len")):
+        got = _np(a)
+        assert np.array_equal(got[:cap], r[key][:cap]), key
+        assert np.all(got[cap:] == 0xffffffff), (key, "written past the capacity")
     # the binding sizes, then fills
-    g = P(_dev(b))
-    _same(g, r, "resized")
+    _same(P(d), r, "resized")
 
 
 @pytest.mark.parametrize("chunk,path", _with_paths([31, None]))

@@ -159,3 +159,66 @@ def test_full_size_lexer_workload(ppr, tables):
         g = ppr.Lexer(T, max_n=b.size, capacity=r["n_tokens"], path=path)(d_b)
         assert g.path == (path or STREAMING)
         _same(g, r, ("full", path))
+
+
+@pytest.mark.parametrize("path,cap", [(None, 1000), (None, 100000), (SINGLE_PASS, 1000), (SINGLE_PASS, 100000)])
+def test_capacity_reported(ppr, tables, path, cap):
+    """with too few output slots: PPR_ECAPACITY, the token count set, the first cap tokens written and nothing
+    past them (guard words after each array stay untouched); the binding then resizes and fills"""
+    import ctypes
+    import torch
+    d, T = tables["lexer"]
+    b = W.gen_tokens(11, (1 << 20) + 33)
+    r = oracle.lex_restart(b, d)
+    Lx = ppr.Lexer(T, max_n=b.size, capacity=cap, path=path)
+    guard = 4096
+    arrs = [torch.full((cap + guard,), -1, dtype=torch.int32, device="cuda") for _ in range(3)]
+    o = ppr.TokensOut()
+    o.kind, o.start, o.length = [a.data_ptr() for a in arrs]
+    o.cap_tokens = cap
+    d_b = _dev(b)
+    rc = ppr.lib.ppr_lex(ctypes.c_void_p(d_b.data_ptr()), b.size, ctypes.byref(T.c), ctypes.byref(T.prep),
+                         ctypes.byref(o), Lx._ws_ptr(), Lx.ws_bytes, ctypes.byref(Lx.opts), None)
+    assert rc == ppr.PPR_ECAPACITY
+    assert o.n_tokens == r["n_tokens"] and o.path == (path or STREAMING)
+    for a, key in zip(arrs, ("kind", "start", "length")):
+        got = _np(a)
+        assert np.array_equal(got[:cap], r[key][:cap]), key
+        assert np.all(got[cap:] == 0xffffffff), (key, "written past the capacity")
+    _same(Lx(d_b), r, "resized")
+
+
+@pytest.mark.parametrize("path", [None, SINGLE_PASS])
+def test_repeatable(ppr, tables, path):
+    """the same workspace reused: nothing from the previous call leaks in (a shorter input, then the long one)"""
+    d, T = tables["lexer"]
+    b = W.gen_tokens(12, (6 << 20) + 5)
+    r = oracle.lex_restart(b, d)
+    Lx = ppr.Lexer(T, max_n=b.size, capacity=b.size + 1, path=path)
+    dev = _dev(b)
+    for i in range(3):
+        _say("lex repeat", path, i)
+        _same(Lx(dev), r, (path, i))
+    short = b[: (1 << 20) + 9]
+    _same(Lx(_dev(short)), oracle.lex_restart(short, d), "short")
+    _same(Lx(dev), r, "again")
+
+
+def test_stage_events_streaming(ppr, tables):
+    """the streaming lexer records an event before its kernels and after the first two, the count and the emit
+    kernel"""
+    import torch
+    d, T = tables["lexer"]
+    b = W.gen_tokens(13, 4 << 20)
+    Lx = ppr.Lexer(T, max_n=b.size, capacity=b.size + 1)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    Lx.launch(_dev(b), stage_events=ev)
+    torch.cuda.synchronize()
+    o = Lx.results(b.size)
+    assert o.path == STREAMING
+    times = [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
+    assert all(x >= 0 for x in times) and sum(times) > 0, times
+    assert o.n_tokens == oracle.lex_restart(b, d)["n_tokens"]
