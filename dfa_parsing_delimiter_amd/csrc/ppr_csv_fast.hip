@@ -870,11 +870,12 @@ struct FieldRun {
 // (mbcnt), the column counts from the last record field before the lane, the
 // offset follows the previous lane's terminator (DPP). The four arrays are
 // written through wave-uniform base pointers, so every store is one scalar
-// base plus the lane's offset; a field is written only below the capacity
-// (compared in 64 bits, so that no wrap-around can let a store through).
+// base plus the lane's offset. Only the window's first `slots` fields are
+// written (those below the capacity); rel: the round's offset in the window.
 // lt_mask: the lanes below this one.
-__device__ __forceinline__ void field_round(const OutArrays& o, uint32_t g0, uint32_t cnt, uint32_t e, uint32_t base,
-                                            uint32_t lane, uint64_t lt_mask, FieldRun& fr)
+__device__ __forceinline__ void field_round(const OutArrays& o, uint32_t g0, uint32_t rel, uint32_t slots,
+                                            uint32_t cnt, uint32_t e, uint32_t base, uint32_t lane, uint64_t lt_mask,
+                                            FieldRun& fr)
 {
     const uint32_t pos = base + (e >> 1);
     const uint64_t m = __ballot(lane < cnt && (e & 1u));
@@ -884,7 +885,8 @@ __device__ __forceinline__ void field_round(const OutArrays& o, uint32_t g0, uin
     const uint32_t col = below ? lane - (uint32_t)(63 - __clzll((long long)below)) - 1u : fr.col + lane;
     const uint32_t prev = dpp_t<0x138, 0xf>(0u, pos);  // wave_shr:1: the previous lane's terminator
     const uint32_t off = lane ? prev + 1u : fr.off;
-    if (lane < cnt && (uint64_t)g0 + lane < o.cap) {
+    g0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)g0);  // (wave-uniform: the store addresses stay scalar)
+    if (rel + lane < slots) {
         store_u32(o.rec + g0, lane, rec);
         store_u32(o.col + g0, lane, col);
         store_u32(o.off + g0, lane, off);
@@ -968,9 +970,11 @@ __global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_e
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             // (2) rounds of 64 fields: the round's output slices are uniform base pointers,
             // each lane stores at its own 4-byte offset
+            const uint32_t slots = slots_from(o.cap, (uint64_t)P.nf + w0, w1 - w0);
             for (uint32_t r = w0; r < w1; r += kWave) {
                 const uint32_t cnt = min((uint32_t)kWave, w1 - r);
-                field_round(o, P.nf + r, cnt, list[r - w0 + min(lane, cnt - 1u)], st_abs, lane, lt_mask, fr);
+                field_round(o, P.nf + r, r - w0, slots, cnt, list[r - w0 + min(lane, cnt - 1u)], st_abs, lane, lt_mask,
+                            fr);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -1270,10 +1274,11 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                const uint32_t slots = slots_from(o.cap, (uint64_t)P.nf + w0, w1 - w0);
                 for (uint32_t r = w0; r < w1; r += kWave) {
                     const uint32_t cnt = min((uint32_t)kWave, w1 - r);
-                    field_round(o, P.nf + r, cnt, list[r - w0 + min(lane, cnt - 1u)], tile_start, lane,
-                                lt_mask, fr);
+                    field_round(o, P.nf + r, r - w0, slots, cnt, list[r - w0 + min(lane, cnt - 1u)], tile_start,
+                                lane, lt_mask, fr);
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();

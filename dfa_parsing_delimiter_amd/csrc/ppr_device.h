@@ -138,6 +138,16 @@ __device__ __forceinline__ void store_u32(uint32_t* base, uint32_t lane, uint32_
     g[lane] = v;
 }
 
+// Output slots for `count` items written from global index `first` on: those
+// below the capacity. Computed in 64 bits once per window of items, so that the
+// per-round test (item offset in the window < slots) involves no wrap-around.
+__device__ __forceinline__ uint32_t slots_from(uint64_t cap, uint64_t first, uint32_t count)
+{
+    if (first >= cap) return 0u;
+    const uint64_t left = cap - first;
+    return left < (uint64_t)count ? (uint32_t)left : count;
+}
+
 // Lists a lane's terminators that fall in the window [w0, w1) of wave-local
 // field indices into the wave's LDS list (entry = position << 1 | record bit,
 // positions from rel0 on). The lane's fields are [first, first + mine); tw / rw:

@@ -376,15 +376,15 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_emit_kernel(LexFastParams p
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const uint32_t slots = slots_from(p.cap, (uint64_t)P.nt + wbase + w0, w1 - w0);
             for (uint32_t r = w0; r < w1; r += kWave) {
                 const uint32_t cnt = min((uint32_t)kWave, w1 - r);
                 const uint32_t e = list[r - w0 + min(lane, cnt - 1u)] >> 1;
                 const uint32_t end = tile_start + e;
                 const uint32_t prev = dpp_t<0x138, 0xf>(0u, end);  // wave_shr:1: the previous lane's boundary
                 const uint32_t st = lane ? prev : off_run;
-                // the round's first token index, in 64 bits: a slot is written only below the capacity
-                const uint64_t g0 = (uint64_t)P.nt + wbase + r;
-                if (lane < cnt && g0 + lane < p.cap) {
+                const uint32_t g0 = P.nt + wbase + r;  // (token counts < n < 2^32)
+                if (r - w0 + lane < slots) {
                     store_u32(p.kind + g0, lane, s_kind[e]);
                     store_u32(p.start + g0, lane, st);
                     store_u32(p.len + g0, lane, end - st);
