@@ -132,8 +132,9 @@ enum { PPR_PATH_STREAMING = 1, PPR_PATH_SINGLE_PASS = 2, PPR_PATH_FUSED = 3 };
  *                   first two kernels and after each of the last two; fused and
  *                   single-pass parse and lexer: 2). For per-kernel timing;
  *                   NULL: none.
- *   path:           0 = automatic (the streaming path where the table and input
- *                   allow it, else the single-pass path); PPR_PATH_FUSED or
+ *   path:           0 = automatic (where the table and input allow the
+ *                   table-driven paths: the fused kernel up to 8 MiB, the
+ *                   streaming kernels above; else the single-pass path); PPR_PATH_FUSED or
  *                   PPR_PATH_STREAMING ask for that path and fall back to the
  *                   single-pass path where it does not apply; PPR_PATH_SINGLE_PASS
  *                   forces the generic kernel. Any other value: PPR_EINVAL. The

@@ -61,17 +61,22 @@ def _same(g, r, what=""):
                 what, name, bad.size, a.size, bad[0], a[bad[0]], r[key][bad[0]]))
 
 
-# (chunk_bytes, path) pairs: 64-byte chunks on each table-driven path (None: the automatic choice,
-# the streaming kernels; 3: the fused kernel)
-AUTO_PATH = 1
+# (chunk_bytes, path) pairs: 64-byte chunks on each table-driven path (None: the automatic choice;
+# 1: the streaming kernels; 3: the fused kernel)
+STREAMING = 1
 FUSED = 3
 SINGLE_PASS = 2
+FUSED_MAX_AUTO = 8 << 20  # the automatic choice: the fused kernel up to this many bytes, streaming above
+
+
+def auto_path(n):
+    return FUSED if n <= FUSED_MAX_AUTO else STREAMING
 
 
 def _with_paths(chunks):
     out = []
     for c in chunks:
-        out += [(c, None), (c, FUSED)] if c in (None, 64) else [(c, None)]
+        out += [(c, None), (c, STREAMING), (c, FUSED)] if c in (None, 64) else [(c, None)]
     return out
 
 
@@ -178,7 +183,7 @@ def test_unaligned_input_and_subviews(ppr):
         view = d[off:]
         g = ppr.parse(view, t, capacity=b.size)
         _same(g, oracle.csv_parse(b[off:], t), off)
-        assert g.path == (AUTO_PATH if off == 16 else ppr.PPR_PATH_SINGLE_PASS)
+        assert g.path == (auto_path(b.size - off) if off == 16 else ppr.PPR_PATH_SINGLE_PASS)
 
 
 def test_edge_cases(ppr):
@@ -220,7 +225,7 @@ def test_capacity_reported(ppr, path, cap):
                            ctypes.byref(out), P._ws_ptr(), P.ws_bytes, ctypes.byref(P.opts), None)
     assert rc == ppr.PPR_ECAPACITY
     assert out.n_fields == r["n_fields"] and out.n_records == r["n_records"]
-    assert out.path == (path or AUTO_PATH)
+    assert out.path == (path or auto_path(b.size))
     for a, key in zip(arrs, ("rec", "col", "off", "len")):
         got = _np(a)
         assert np.array_equal(got[:cap], r[key][:cap]), key
@@ -247,14 +252,17 @@ def test_repeatable(ppr, chunk, path):
 
 
 def test_path_reported(ppr):
-    """the table-driven kernels run for 64-byte chunks on aligned input with an encodable class map
-    (the fused kernel unless the streaming kernels are asked for); the single-pass kernel otherwise"""
+    """the table-driven kernels run for 64-byte chunks on aligned input with an encodable class map (left
+    to the library: the fused kernel up to 8 MiB, the streaming kernels above); the single-pass kernel
+    otherwise"""
+    big = W.generate(3, n=FUSED_MAX_AUTO + 64, seed=6)
+    assert ppr.parse(_dev(big), W.table("T5"), capacity=big.size + 1).path == STREAMING
     for name in ("T5", "T6"):
         t = W.table(name)
         b = W.generate(1 if name == "T5" else 4, n=300000, seed=5)
         r = oracle.csv_parse(b, t)
         g = ppr.parse(_dev(b), t, capacity=b.size + 1)
-        assert g.path == AUTO_PATH, name
+        assert g.path == FUSED, name
         for want in (ppr.PPR_PATH_FUSED, ppr.PPR_PATH_STREAMING, ppr.PPR_PATH_SINGLE_PASS):
             g = ppr.parse(_dev(b), t, capacity=b.size + 1, path=want)
             assert g.path == want, (name, want)
@@ -274,7 +282,7 @@ def test_path_reported(ppr):
     _same(g, oracle.csv_parse(b, t), "40 specials")
 
 
-@pytest.mark.parametrize("path,stages", [(None, 3), (3, 2)])
+@pytest.mark.parametrize("path,stages", [(STREAMING, 3), (FUSED, 2)])
 def test_stage_events(ppr, path, stages):
     """per-kernel HIP events recorded by the library between its kernels"""
     import torch
@@ -289,7 +297,7 @@ def test_stage_events(ppr, path, stages):
     P.launch(d, stage_events=ev)
     torch.cuda.synchronize()
     o = P.results(b.size)
-    assert o.path == (path or AUTO_PATH)
+    assert o.path == path
     times = [ev[i].elapsed_time(ev[i + 1]) for i in range(stages)]
     assert all(x >= 0 for x in times) and sum(times) > 0, times
     assert o.n_fields == oracle.csv_parse(b, t)["n_fields"]
@@ -299,21 +307,21 @@ def test_stage_events(ppr, path, stages):
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_full_size_workloads(ppr, cfg):
     """every output array at the workload's full size: in the launch configuration the benchmark times
-    (the default 64-byte chunks, streaming kernels), on the fused kernel, and at the workload's own
-    chunk size if it names one"""
+    (the default 64-byte chunks, the automatic path), on the streaming and the fused kernels, and at the
+    workload's own chunk size if it names one"""
     t = W.table(W.CONFIGS[cfg]["table"])
     _say("full", cfg, "generate")
     b = W.generate(cfg)
     _say("full", cfg, "oracle")
     r = oracle.csv_parse(b, t)
     d = _dev(b)
-    runs = [(None, None), (None, FUSED)]
+    runs = [(None, None), (None, STREAMING), (None, FUSED)]
     if W.CONFIGS[cfg].get("chunk_bytes"):
         runs.append((W.CONFIGS[cfg]["chunk_bytes"], None))
     for chunk, path in runs:
         _say("full", cfg, "gpu chunk", chunk, path, r["n_fields"])
         g = ppr.Parser(t, max_n=b.size, capacity=r["n_fields"], chunk_bytes=chunk, path=path)(d)
         if chunk is None:
-            assert g.path == (path or AUTO_PATH)
+            assert g.path == (path or auto_path(b.size))
         _same(g, r, ("full", cfg, chunk, path))
     del b, d
