@@ -424,6 +424,8 @@ static uint32_t lex_minimize(const std::vector<uint16_t>& fold, const std::vecto
     }
 }
 
+constexpr uint64_t kLexStreamMinAuto = 8ull << 20;
+
 static uint32_t lex_chunk_of(const ppr_parse_opts_t* o)
 {
     uint32_t L = o ? o->chunk_bytes : 0u;
@@ -582,8 +584,12 @@ extern "C" int ppr_lex_async(const uint8_t* d_bytes, uint64_t n, const ppr_lex_t
     WsHeader* hdr = (WsHeader*)ws;
 
     // the streaming kernels: 40-byte chunks, 8-byte aligned input, prepared fold rows
-    // (and positions up to the last tile's end below 2^32)
-    if (n && n <= 0xffff0000ull && want != PPR_PATH_SINGLE_PASS && L == (uint32_t)kLexFastChunk &&
+    // (and positions up to the last tile's end below 2^32); chosen automatically
+    // above kLexStreamMinAuto bytes, where their four launches pay off (the
+    // single-pass kernel: 56 against 65 us at 1 MiB, 74 against 81 us at 8 MiB;
+    // equal at 16 MiB, 176 against 135 us at 32 MiB)
+    const bool asked = want == PPR_PATH_STREAMING || want == PPR_PATH_FUSED;
+    if (n && n <= 0xffff0000ull && (asked || (want == 0 && n > kLexStreamMinAuto)) && L == (uint32_t)kLexFastChunk &&
         ((uintptr_t)d_bytes & 7u) == 0 && prep->n_rows && prep->n_states) {
         const LexFastLayout fl = lex_fast_layout(n);
         if (ws_bytes < fl.total) return PPR_EWORKSPACE;

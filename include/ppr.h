@@ -117,6 +117,7 @@ typedef struct ppr_parse_out {
  *                        range identifiers, boundary counts, tokens), no waiting
  *                        between workgroups; needs chunk_bytes 40, an 8-byte
  *                        aligned input and prepared fold rows (n_rows > 0);
+ *                        the automatic choice above 8 MiB;
  *   PPR_PATH_SINGLE_PASS any chunk size: 2 kernels (reset, one single-pass
  *                        kernel with decoupled look-back scans).
  */
@@ -138,7 +139,9 @@ enum { PPR_PATH_STREAMING = 1, PPR_PATH_SINGLE_PASS = 2, PPR_PATH_FUSED = 3 };
  *                   PPR_PATH_STREAMING ask for that path and fall back to the
  *                   single-pass path where it does not apply; PPR_PATH_SINGLE_PASS
  *                   forces the generic kernel. Any other value: PPR_EINVAL. The
- *                   lexer treats PPR_PATH_FUSED as PPR_PATH_STREAMING.
+ *                   lexer treats PPR_PATH_FUSED as PPR_PATH_STREAMING; its
+ *                   automatic choice is the streaming kernels above 8 MiB
+ *                   (where they apply), the single-pass kernel otherwise.
  */
 typedef struct ppr_parse_opts {
     uint32_t chunk_bytes;

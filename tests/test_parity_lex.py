@@ -17,6 +17,13 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 STREAMING, SINGLE_PASS = 1, 2
+STREAM_MIN_AUTO = 8 << 20  # the automatic choice: the streaming kernels above this many bytes (40-byte chunks)
+
+
+def auto_path(n, chunk=None):
+    return STREAMING if (chunk in (None, 40) and n > STREAM_MIN_AUTO) else SINGLE_PASS
+
+
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "lex_examples.jsonl")
 
 
@@ -59,9 +66,9 @@ def _same(g, r, what=""):
                 what, key, bad.size, a.size, bad[0], a[bad[0]], r[key][bad[0]]))
 
 
-# (chunk, path): the default 40-byte chunks run the streaming kernels; the
-# single-pass kernel is asked for explicitly or serves other chunk sizes
-PATHS = [(1, None), (2, None), (32, None), (None, None), (None, SINGLE_PASS)]
+# (chunk, path): the streaming kernels at the default 40-byte chunks, asked for
+# or left to the library; the single-pass kernel asked for or at other chunk sizes
+PATHS = [(1, None), (2, None), (32, None), (None, None), (None, STREAMING), (None, SINGLE_PASS)]
 
 
 def test_golden(ppr, tables):
@@ -76,7 +83,7 @@ def test_golden(ppr, tables):
 
 
 @pytest.mark.parametrize("chunk,path", [(1, None), (3, None), (16, None), (31, None), (32, None), (40, None),
-                                        (40, SINGLE_PASS), (64, None)])
+                                        (40, STREAMING), (40, SINGLE_PASS), (64, None)])
 def test_streams_several_tiles(ppr, tables, chunk, path):
     d, T = tables["lexer"]
     for seed in (1, 2):
@@ -85,7 +92,7 @@ def test_streams_several_tiles(ppr, tables, chunk, path):
         _say("stream", chunk, path, seed, n)
         g = ppr.lex(_dev(b), T, chunk_bytes=chunk, capacity=n + 1, path=path)
         _same(g, oracle.lex_restart(b, d), (chunk, path, seed))
-        assert g.path == (path or (STREAMING if chunk == 40 else SINGLE_PASS))
+        assert g.path == (path or auto_path(n, chunk))
 
 
 def test_random_bytes_and_edges(ppr, tables):
@@ -94,7 +101,7 @@ def test_random_bytes_and_edges(ppr, tables):
     cases = [b"", b"a", b"@", b"//" + b"x" * 70000, b'"' + b"q" * 70001, b" " * 100000, b"1." * 30000]
     cases += [rng.integers(0, 256, int(rng.integers(1, 50000)), dtype=np.uint8).tobytes() for _ in range(6)]
     for b in cases:
-        for chunk, path in [(1, None), (7, None), (32, None), (None, None), (None, SINGLE_PASS)]:
+        for chunk, path in [(1, None), (7, None), (32, None), (None, None), (None, STREAMING), (None, SINGLE_PASS)]:
             _say("edge", len(b), chunk, path)
             g = ppr.lex(_dev(b) if b else _dev(b"\0")[:0], T, chunk_bytes=chunk, capacity=len(b) + 1, path=path)
             _same(g, oracle.lex_restart(b, d), (len(b), chunk, path))
@@ -108,7 +115,7 @@ def test_streaming_ragged_tiles_and_ranges(ppr, tables):
     for n in (1, 39, 40, 41, tile - 1, tile, tile + 1, 3 * tile + 40 * 17 + 1, 1500 * tile + 12345):
         b = W.gen_tokens(7, n)
         _say("ragged", n)
-        g = ppr.lex(_dev(b), T, capacity=n + 1)
+        g = ppr.lex(_dev(b), T, capacity=n + 1, path=STREAMING)
         assert g.path == STREAMING
         _same(g, oracle.lex_restart(b, d), n)
 
@@ -118,10 +125,10 @@ def test_streaming_needs_aligned_input(ppr, tables):
     d, T = tables["lexer"]
     b = W.gen_tokens(8, 300000)
     buf = _dev(np.concatenate([np.zeros(3, np.uint8), b]))
-    g = ppr.lex(buf[3:], T, capacity=b.size + 1)
+    g = ppr.lex(buf[3:], T, capacity=b.size + 1, path=STREAMING)
     assert g.path == SINGLE_PASS
     _same(g, oracle.lex_restart(b, d), "misaligned")
-    assert ppr.lex(_dev(b), T, capacity=b.size + 1).path == STREAMING
+    assert ppr.lex(_dev(b), T, capacity=b.size + 1, path=STREAMING).path == STREAMING
 
 
 def test_minimal_automaton_and_identifier_fold(ppr, tables):
@@ -133,13 +140,13 @@ def test_minimal_automaton_and_identifier_fold(ppr, tables):
     assert 0 < T.prep.n_rows <= T.k, T.prep.n_rows
     b = W.gen_tokens(3, (1 << 20) + 5)
     r = oracle.lex_restart(b, d)
-    _same(ppr.lex(_dev(b), T, capacity=b.size + 1), r, "streaming")
+    _same(ppr.lex(_dev(b), T, capacity=b.size + 1, path=STREAMING), r, "streaming")
     _same(ppr.lex(_dev(b), T, capacity=b.size + 1, path=SINGLE_PASS), r, "minimal automaton")
     for field in ("n_rows", "n_states"):
         saved = getattr(T.prep, field)
         setattr(T.prep, field, 0)
         try:
-            g = ppr.lex(_dev(b), T, capacity=b.size + 1)
+            g = ppr.lex(_dev(b), T, capacity=b.size + 1, path=STREAMING)
             assert g.path == SINGLE_PASS
             _same(g, r, "without " + field)
         finally:
@@ -157,11 +164,12 @@ def test_full_size_lexer_workload(ppr, tables):
     d_b = _dev(b)
     for path in (None, SINGLE_PASS):
         g = ppr.Lexer(T, max_n=b.size, capacity=r["n_tokens"], path=path)(d_b)
-        assert g.path == (path or STREAMING)
+        assert g.path == (path or auto_path(b.size))
         _same(g, r, ("full", path))
 
 
-@pytest.mark.parametrize("path,cap", [(None, 1000), (None, 100000), (SINGLE_PASS, 1000), (SINGLE_PASS, 100000)])
+@pytest.mark.parametrize("path,cap", [(STREAMING, 1000), (STREAMING, 100000), (SINGLE_PASS, 1000),
+                                      (SINGLE_PASS, 100000)])
 def test_capacity_reported(ppr, tables, path, cap):
     """with too few output slots: PPR_ECAPACITY, the token count set, the first cap tokens written and nothing
     past them (guard words after each array stay untouched); the binding then resizes and fills"""
@@ -180,7 +188,7 @@ def test_capacity_reported(ppr, tables, path, cap):
     rc = ppr.lib.ppr_lex(ctypes.c_void_p(d_b.data_ptr()), b.size, ctypes.byref(T.c), ctypes.byref(T.prep),
                          ctypes.byref(o), Lx._ws_ptr(), Lx.ws_bytes, ctypes.byref(Lx.opts), None)
     assert rc == ppr.PPR_ECAPACITY
-    assert o.n_tokens == r["n_tokens"] and o.path == (path or STREAMING)
+    assert o.n_tokens == r["n_tokens"] and o.path == path
     for a, key in zip(arrs, ("kind", "start", "length")):
         got = _np(a)
         assert np.array_equal(got[:cap], r[key][:cap]), key
@@ -188,7 +196,7 @@ def test_capacity_reported(ppr, tables, path, cap):
     _same(Lx(d_b), r, "resized")
 
 
-@pytest.mark.parametrize("path", [None, SINGLE_PASS])
+@pytest.mark.parametrize("path", [STREAMING, SINGLE_PASS])
 def test_repeatable(ppr, tables, path):
     """the same workspace reused: nothing from the previous call leaks in (a shorter input, then the long one)"""
     d, T = tables["lexer"]
@@ -204,13 +212,25 @@ def test_repeatable(ppr, tables, path):
     _same(Lx(dev), r, "again")
 
 
+def test_automatic_path_by_size(ppr, tables):
+    """left to the library, the single-pass kernel up to 8 MiB and the streaming kernels above; both exact"""
+    d, T = tables["lexer"]
+    b = W.gen_tokens(14, STREAM_MIN_AUTO + 41)
+    dev = _dev(b)
+    for n in (STREAM_MIN_AUTO, STREAM_MIN_AUTO + 41):
+        _say("lex auto", n)
+        g = ppr.lex(dev[:n], T, capacity=n + 1)
+        assert g.path == auto_path(n), (n, g.path)
+        _same(g, oracle.lex_restart(b[:n], d), ("auto", n))
+
+
 def test_stage_events_streaming(ppr, tables):
     """the streaming lexer records an event before its kernels and after the first two, the count and the emit
     kernel"""
     import torch
     d, T = tables["lexer"]
     b = W.gen_tokens(13, 4 << 20)
-    Lx = ppr.Lexer(T, max_n=b.size, capacity=b.size + 1)
+    Lx = ppr.Lexer(T, max_n=b.size, capacity=b.size + 1, path=STREAMING)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     for e in ev:
         e.record()
