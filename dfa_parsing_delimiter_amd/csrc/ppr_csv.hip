@@ -157,7 +157,7 @@ __device__ void finish_tile(const LookCtx& c, const OutArrays& o, uint32_t n, ui
     }
     cr.lt = T ? chunk_abs + (uint32_t)(63 - __clzll((long long)T)) + 1u : 0u;
     cr.err = kNone;
-    if (err != kNone) atomicMin(&c.hdr->err_min, err);  // rare: only chunks holding an INVALID byte
+    wave_lower_min(&c.hdr->err_min, err);  // chunks holding an INVALID byte: one atomic per wave at most
     Carry cex, ctot;
     block_scan<NW>(cr, carry_identity(), cex, ctot, sh->wcar, CarryComb{});
 
@@ -536,6 +536,7 @@ extern "C" int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa
             f.range_vec = (uint64_t*)(ws + fl.range_vec);
             f.range_state = (uint32_t*)(ws + fl.range_state);
             f.range_carry = (uint4*)(ws + fl.range_carry);
+            f.range_err = (uint32_t*)(ws + fl.range_err);
             f.stat_vec = (uint64_t*)(ws + fl.stat_vec);
             f.stat_carry = (StatB*)(ws + fl.stat_carry);
             f.epoch = next_epoch();

@@ -123,6 +123,7 @@ struct FastParams {
     uint64_t* range_vec;   // per range: composite of its tile vectors
     uint32_t* range_state; // per range: state code before its first byte
     uint4* range_carry;    // per range: nf, nr, col (bit 31: absolute), lt
+    uint32_t* range_err;   // per range: its first INVALID byte (kNone: none)
     uint64_t* stat_vec;    // fused path: per tile, vector look-back status
     StatB* stat_carry;     // fused path: per tile, count-carry look-back status
     uint32_t epoch;        // fused path: call epoch carried by the status words
@@ -135,8 +136,8 @@ struct FastParams {
 constexpr uint32_t kMaxRanges = 1024;
 
 struct FastLayout {
-    uint64_t tiles, tabs, tile_vec, range_vec, range_state, range_carry, stat_vec, stat_carry, cvec_lo, cvec_hi, idx,
-        total;
+    uint64_t tiles, tabs, tile_vec, range_vec, range_state, range_carry, range_err, stat_vec, stat_carry, cvec_lo,
+        cvec_hi, idx, total;
 };
 
 // workspace of the fast path for n bytes (idx sized for 2-byte groups)
@@ -149,7 +150,8 @@ inline FastLayout fast_layout(uint64_t n)
     L.range_vec = align_up(L.tile_vec + L.tiles * 8, 256);
     L.range_state = align_up(L.range_vec + kMaxRanges * 8, 256);
     L.range_carry = align_up(L.range_state + kMaxRanges * 4, 256);
-    L.stat_vec = align_up(L.range_carry + kMaxRanges * 16, 256);
+    L.range_err = align_up(L.range_carry + kMaxRanges * 16, 256);
+    L.stat_vec = align_up(L.range_err + kMaxRanges * 4, 256);
     L.stat_carry = align_up(L.stat_vec + L.tiles * 8, 256);
     L.cvec_lo = align_up(L.stat_carry + L.tiles * sizeof(StatB), 256);
     L.cvec_hi = align_up(L.cvec_lo + L.tiles * (kFastBlock / 2) * 4, 256);

@@ -705,18 +705,19 @@ __device__ __forceinline__ void super_vecs(const FastParams& p, uint32_t st, uin
 }
 
 // Pass 2 for this thread's span: tags as bitmaps, the first INVALID byte (if
-// wanted). ts0 / ts1: the state before the super-tile's first / second tile.
+// wanted: err given and look true). ts0 / ts1: the state before the
+// super-tile's first / second tile.
 template <int CB, bool V8, bool FULL>
 __device__ __forceinline__ void span_tags(const FastParams& p, const PairPos& c, const IdxIn<CB, V8>& in,
                                           uint32_t ts0, uint32_t ts1, const Pass2Shared<V8, Geo<CB>::PAR>& sh,
-                                          uint64_t (&T)[2], uint64_t (&RD)[2], uint32_t* err)
+                                          uint64_t (&T)[2], uint64_t (&RD)[2], uint32_t* err, bool look = true)
 {
     const uint32_t nt = p.nt;
     const uint32_t s = vat(Vec{in.cvlo, in.cvhi}, threadIdx.x < kFastBlock / 2 ? ts0 : ts1);
     T[0] = T[1] = RD[0] = RD[1] = 0;
     if (FULL || c.full) {
         const uint32_t any = pass2_pair<CB>(in.pw, s, nt, sh.t2, T, RD);
-        if (err && (any & kP2Invalid)) *err = first_invalid<CB, 2>(in.pw, s, nt, sh.t2, c.abs);
+        if (err && look && (any & kP2Invalid)) *err = first_invalid<CB, 2>(in.pw, s, nt, sh.t2, c.abs);
     } else if (c.my_len) {
         uint32_t e = kNone;
         pass2_ragged<CB>(p, c, s, nt, sh.nxt, sh.tag, T, RD, e);
@@ -787,6 +788,7 @@ __global__ void __launch_bounds__(kFastBlock, kCarriesWavesPerSimd<CB>) csv_carr
     __shared__ uint32_t s_rd[2][kFastWaves];
     __shared__ Vec s_wv[kFastWaves];
     __shared__ uint4 s_red[kFastWaves];
+    __shared__ uint32_t s_err[kFastWaves];
 
     const uint32_t b = blockIdx.x;
     const uint32_t lane = (uint32_t)lane_id();
@@ -799,6 +801,11 @@ __global__ void __launch_bounds__(kFastBlock, kCarriesWavesPerSimd<CB>) csv_carr
     uint32_t run = vat(ranges_before<V8>(p, b, ident, s_wv), p.start_code);  // (its barrier publishes sh)
     if (threadIdx.x == 0) p.range_state[b] = run;
     uint32_t acc_nf = 0, acc_nr = 0, acc_col = 0, acc_lt = 0;
+    // the first INVALID byte of the wave's spans (wave-uniform): once found, later
+    // super-tiles (larger positions) are not searched; the range's (the waves'
+    // minimum) is stored, and the emit kernel takes the minimum over the ranges
+    // (atomics on one word from every wave would serialize)
+    uint32_t wave_err = kNone;
 
     auto step = [&](auto full_tag, uint32_t st, const IdxIn<CB, V8>& in, uint32_t it) {
         constexpr bool FULL = decltype(full_tag)::value;
@@ -808,8 +815,8 @@ __global__ void __launch_bounds__(kFastBlock, kCarriesWavesPerSimd<CB>) csv_carr
         const uint32_t ts1 = vat(v0, run);
         uint64_t T[2], RD[2];
         uint32_t err = kNone;
-        span_tags<CB, V8, FULL>(p, c, in, run, ts1, sh, T, RD, &err);
-        if (err != kNone) atomicMin(&p.hdr->err_min, err);
+        span_tags<CB, V8, FULL>(p, c, in, run, ts1, sh, T, RD, &err, wave_err == kNone);
+        if (wave_err == kNone) wave_err = wave_min_defined(err);
         if (c.my_len && c.abs + c.my_len == p.n)  // the thread holding the input's last byte
             p.hdr->last_rec = (uint32_t)((RD[(c.my_len - 1) >> 6] >> ((c.my_len - 1) & 63)) & 1u);
         const uint32_t nf = (uint32_t)(__popcll(T[0]) + __popcll(T[1]));
@@ -841,14 +848,18 @@ __global__ void __launch_bounds__(kFastBlock, kCarriesWavesPerSimd<CB>) csv_carr
     const uint32_t snf = wave_scan(acc_nf, 0u, AddComb{}), snr = wave_scan(acc_nr, 0u, AddComb{});
     const uint32_t scol = wave_scan(acc_col, 0u, AddComb{}), slt = wave_scan(acc_lt, 0u, MaxComb{});
     if (lane == kWave - 1) s_red[w] = make_uint4(snf, snr, scol, slt);
+    if (lane == 0) s_err[w] = wave_err;
     __syncthreads();
     if (threadIdx.x == 0) {
         uint4 r = s_red[0];
+        uint32_t e = s_err[0];
         for (int i = 1; i < kFastWaves; ++i) {
             const uint4 q = s_red[i];
             r = make_uint4(r.x + q.x, r.y + q.y, r.z + q.z, max(r.w, q.w));
+            e = min(e, s_err[i]);
         }
         p.range_carry[b] = make_uint4(r.x, r.y, r.z | (r.y ? 0x80000000u : 0u), r.w);
+        p.range_err[b] = e;
         if (b == p.num_ranges - 1) {
             const uint32_t e = min(run, 8u);
             p.hdr->end_state = p.state_of[e];
@@ -922,6 +933,7 @@ __global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_e
     __shared__ GCarry s_wc[kSpanScratch];
     __shared__ GCarry s_wg[kFastWaves];
     __shared__ uint32_t s_list[kFastWaves][kWaveList<CB>];
+    __shared__ uint32_t s_err[kFastWaves];
 
     const uint32_t lane = (uint32_t)lane_id();
     const uint32_t wv = threadIdx.x / kWave;
@@ -937,6 +949,18 @@ __global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_e
     const GCarryComb gcomb;
     // the input starts at column 0 of record 0: an absolute zero column offset
     GCarry P = gcomb(GCarry{0u, 0u, 0x80000000u, 0u}, carries_before(p, b, s_wg));  // (its barrier publishes sh)
+    if (b == 0) {  // the first INVALID byte: the smallest of the ranges' (stored by the carries kernel)
+        const uint32_t i0 = 2 * threadIdx.x, i1 = i0 + 1;
+        uint32_t e = i0 < p.num_ranges ? p.range_err[i0] : kNone;
+        if (i1 < p.num_ranges) e = min(e, p.range_err[i1]);
+        e = wave_min_defined(e);
+        if (lane == 0) s_err[wv] = e;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int i = 1; i < kFastWaves; ++i) e = min(e, s_err[i]);
+            p.hdr->err_min = e;
+        }
+    }
 
     auto step = [&](auto full_tag, uint32_t st, const IdxIn<CB, V8>& in, uint32_t it) {
         constexpr bool FULL = decltype(full_tag)::value;
@@ -1233,7 +1257,7 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
             } else if (c.my_len) {
                 pass2_ragged_chunk<CB>(p, c, s, nt, sh.p2.nxt, sh.p2.tag, T[0], RD[0], err);
             }
-            if (err != kNone) atomicMin(&p.hdr->err_min, err);
+            wave_lower_min(&p.hdr->err_min, err);
             if (c.my_len && c.chunk_abs + c.my_len == p.n)
                 sh.last_rec = (uint32_t)((RD[0] >> (c.my_len - 1)) & 1u);
             sc1 = span_carry<1>(T, RD, c.chunk_abs, sh.wc);

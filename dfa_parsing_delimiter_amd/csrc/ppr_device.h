@@ -112,6 +112,31 @@ __device__ __forceinline__ uint32_t shfl(uint32_t v, int src) { return (uint32_t
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
+// Smallest of the active lanes' values v (0xffffffff: the lane has none), in
+// every lane.
+__device__ __forceinline__ uint32_t wave_min_defined(uint32_t v)
+{
+    uint64_t m = __ballot(v != 0xffffffffu);
+    uint32_t best = 0xffffffffu;
+    while (m) {
+        best = min(best, (uint32_t)__builtin_amdgcn_readlane((int)v, __builtin_ctzll(m)));
+        m &= m - 1;
+    }
+    return best;
+}
+
+// Lowers *dst, a position that only ever decreases, to the smallest of the
+// wave's values v (0xffffffff: none): at most one atomic per wave, and none when
+// *dst already holds a smaller position (a stale read is only ever larger).
+__device__ __forceinline__ void wave_lower_min(uint32_t* dst, uint32_t v)
+{
+    const uint32_t best = wave_min_defined(v);
+    if (best == 0xffffffffu) return;
+    if (lane_id() == __builtin_ctzll(__ballot(1)) &&
+        __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > best)
+        atomicMin(dst, best);
+}
+
 // ---------------------------------------------------------------- wave-level output staging
 
 

@@ -204,6 +204,27 @@ def test_edge_cases(ppr):
             _same(g, oracle.csv_parse(b, t), (t["name"], len(b), chunk, path))
 
 
+def test_invalid_bytes_at_scale(ppr):
+    """the first INVALID byte over many tiles and ranges: at byte 1 of 12 MiB (every later byte stays in the
+    absorbing state, so every chunk after it holds INVALID bytes), deep inside the input (one bad byte after
+    9 MiB of valid CSV), and in the last tile"""
+    t = W.table("T5")
+    body = W.generate(3, n=12 << 20, seed=21)
+    deep = body.copy()
+    q = 9 * (1 << 20) + 12345
+    deep[q:q + 3] = np.frombuffer(b'x"y', np.uint8)  # a quote inside an unquoted field, then a non-delimiter
+    late = np.concatenate([body[: (12 << 20) - 40], np.frombuffer(b'1,2\n"a"b' + b"c" * 31, np.uint8)])
+    cases = [("at byte 1", np.concatenate([np.frombuffer(b'a"', np.uint8), body])), ("deep", deep),
+             ("last tile", late)]
+    for what, b in cases:
+        r = oracle.csv_parse(b, t)
+        assert 0 <= r["error_pos"] < b.size, (what, r["error_pos"])
+        for chunk, path in ((None, None), (64, STREAMING), (64, FUSED), (31, None)):
+            _say("invalid", what, b.size, chunk, path, r["error_pos"])
+            g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=r["n_fields"] + 1, path=path)
+            _same(g, r, (what, chunk, path))
+
+
 @pytest.mark.parametrize("path,cap", [(None, 100), (None, 20000), (FUSED, 20000), (SINGLE_PASS, 20000)])
 def test_capacity_reported(ppr, path, cap):
     """with too few output slots: PPR_ECAPACITY, the counts set, the first cap fields written and nothing past
