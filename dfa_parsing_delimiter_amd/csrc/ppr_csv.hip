@@ -485,7 +485,7 @@ using namespace ppr;
 extern "C" size_t ppr_parse_workspace_bytes(uint64_t n, const ppr_parse_opts_t* opts)
 {
     const uint32_t L = chunk_of(opts);
-    if (!L || n >= 0xffffffffull) return 0;
+    if (!L || n > kMaxInput) return 0;
     uint64_t total = csv_layout(n, L).total;
     if (L == (uint32_t)kFastChunk) total = std::max(total, fast_layout(n).total);
     return (size_t)total;
@@ -498,7 +498,7 @@ extern "C" int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa
     int rc = validate_dfa(dfa, class_map);
     if (rc) return rc;
     if (!out || !d_ws || (n && !d_bytes)) return PPR_EINVAL;
-    if (n >= 0xffffffffull) return PPR_ETOOBIG;
+    if (n > kMaxInput) return PPR_ETOOBIG;
     const uint32_t L = chunk_of(opts);
     if (!L) return PPR_EINVAL;
     if (out->cap_fields && (!out->record_idx || !out->column_ids || !out->field_offsets || !out->field_lengths))

@@ -36,6 +36,9 @@ inline void stage_event(const ppr_parse_opts_t* o, uint32_t i, hipStream_t s)
 // Upper bound on look-back polls per tile; beyond it the kernel records a fault
 // and finishes instead of waiting forever.
 constexpr uint32_t kSpinLimit = 1u << 22;
+// Largest input of one call: every byte position a kernel forms, up to the end
+// of the last (padded) tile, then fits 32 bits.
+constexpr uint64_t kMaxInput = 0xffff0000ull;
 
 // Count-carry status of one tile (second look-back). Every word is a relaxed
 // 64-bit atomic holding the call epoch (high half) and one 32-bit value, so a

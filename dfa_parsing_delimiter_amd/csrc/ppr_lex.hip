@@ -558,7 +558,7 @@ extern "C" int ppr_lex_prepare(const ppr_lex_tables_t* t, ppr_lex_prepared_t* pr
 extern "C" size_t ppr_lex_workspace_bytes(uint64_t n, const ppr_parse_opts_t* opts)
 {
     const uint32_t L = lex_chunk_of(opts);
-    if (!L || n >= 0xffffffffull) return 0;
+    if (!L || n > kMaxInput) return 0;
     uint64_t total = lex_layout(n, L).total;
     if (L == (uint32_t)kLexFastChunk) total = std::max(total, lex_fast_layout(n).total);
     return (size_t)total;
@@ -572,7 +572,7 @@ extern "C" int ppr_lex_async(const uint8_t* d_bytes, uint64_t n, const ppr_lex_t
     if (!t->merge_table || !t->final_states || !prep->d_fold || prep->k != t->k || prep->m == 0) return PPR_EINVAL;
     if (t->k == 0 || t->flag_mask != 0x8000u || t->identity >= t->k) return PPR_EINVAL;
     if (out->cap_tokens && (!out->kind || !out->start || !out->length)) return PPR_EINVAL;
-    if (n >= 0xffffffffull) return PPR_ETOOBIG;
+    if (n > kMaxInput) return PPR_ETOOBIG;
     const uint32_t L = lex_chunk_of(opts);
     if (!L) return PPR_EINVAL;
     const uint32_t want = opts ? opts->path : 0u;
@@ -583,13 +583,13 @@ extern "C" int ppr_lex_async(const uint8_t* d_bytes, uint64_t n, const ppr_lex_t
     uint8_t* ws = (uint8_t*)d_ws;
     WsHeader* hdr = (WsHeader*)ws;
 
-    // the streaming kernels: 40-byte chunks, 8-byte aligned input, prepared fold rows
-    // (and positions up to the last tile's end below 2^32); chosen automatically
+    // the streaming kernels: 40-byte chunks, 8-byte aligned input, prepared fold rows;
+    // chosen automatically
     // above kLexStreamMinAuto bytes, where their four launches pay off (the
     // single-pass kernel: 56 against 65 us at 1 MiB, 74 against 81 us at 8 MiB;
     // equal at 16 MiB, 176 against 135 us at 32 MiB)
     const bool asked = want == PPR_PATH_STREAMING || want == PPR_PATH_FUSED;
-    if (n && n <= 0xffff0000ull && (asked || (want == 0 && n > kLexStreamMinAuto)) && L == (uint32_t)kLexFastChunk &&
+    if (n && (asked || (want == 0 && n > kLexStreamMinAuto)) && L == (uint32_t)kLexFastChunk &&
         ((uintptr_t)d_bytes & 7u) == 0 && prep->n_rows && prep->n_states) {
         const LexFastLayout fl = lex_fast_layout(n);
         if (ws_bytes < fl.total) return PPR_EWORKSPACE;

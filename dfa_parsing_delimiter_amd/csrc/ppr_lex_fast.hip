@@ -241,18 +241,33 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_ids_kernel(LexFastParams p)
     // not a full tile; its copy then stores the same values).
     auto nth = [&](uint32_t t, uint32_t k) { return t + k * stride < tfull ? t + k * stride : t; };
     uint32_t it = 0;
-    for (uint32_t tile = blockIdx.x; tile < tfull; tile += kIdsTiles * stride, ++it) {
-        uint32_t w[kIdsTiles][kLexWords];
+    auto load_set = [&](uint32_t tile, uint32_t (&w)[kIdsTiles][kLexWords]) {
 #pragma unroll
         for (int k = 0; k < kIdsTiles; ++k)
             load_lex_chunk<true>(p.in + (size_t)nth(tile, k) * kLexFastTile + tid * kLexFastChunk, kLexFastChunk,
                                  w[k]);
+    };
+    uint32_t w[kIdsTiles][kLexWords];
+    if (blockIdx.x < tfull) load_set(blockIdx.x, w);
+    for (uint32_t tile = blockIdx.x; tile < tfull; tile += kIdsTiles * stride, ++it) {
+        // the next set's bytes load while this one is folded and scanned (the
+        // empty asm keeps the compiler from sinking the loads below the fold;
+        // the registers are free: the fold rows in LDS already hold the kernel
+        // to two workgroups per CU)
+        uint32_t wn[kIdsTiles][kLexWords];
+        const uint32_t next = tile + kIdsTiles * stride;
+        load_set(next < tfull ? next : tile, wn);
+        asm volatile("" ::: "memory");
         IdSet v, ident, excl, tot;
 #pragma unroll
         for (int k = 0; k < kIdsTiles; ++k) {
             v.v[k] = fold_lex_chunk<true>(p, w[k], kLexFastChunk, s_rows, s_col);
             ident.v[k] = p.identity;
         }
+#pragma unroll
+        for (int k = 0; k < kIdsTiles; ++k)
+#pragma unroll
+            for (int q = 0; q < kLexWords; ++q) w[k][q] = wn[k][q];
         block_scan<kLexFastWaves>(v, ident, excl, tot, s_set[it & 1], scomb);
 #pragma unroll
         for (int k = 0; k < kIdsTiles; ++k) {

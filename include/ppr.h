@@ -159,8 +159,9 @@ PPR_API size_t ppr_parse_workspace_bytes(uint64_t n, const ppr_parse_opts_t* opt
 
 /*
  * Parse n bytes at d_bytes with the DFA and the 256-entry class map (host
- * pointers, validated and copied at the call). n must be below 2^32 - 1
- * (PPR_ETOOBIG otherwise). d_bytes needs no particular alignment.
+ * pointers, validated and copied at the call). n must be at most
+ * 2^32 - 2^16 (PPR_ETOOBIG otherwise: every byte position then fits 32 bits,
+ * up to the end of the last tile). d_bytes needs no particular alignment.
  * Blocking: returns with out->n_fields, n_records, error_pos, end_state set.
  * Returns PPR_ECAPACITY (with the counts set) if n_fields > cap_fields.
  */
@@ -247,7 +248,7 @@ typedef struct ppr_tokens_out {
 
 PPR_API size_t ppr_lex_workspace_bytes(uint64_t n, const ppr_parse_opts_t* opts);
 
-/* Lex n bytes (n < 2^32 - 1). Blocking. PPR_ECAPACITY if n_tokens > cap_tokens. */
+/* Lex n bytes (n <= 2^32 - 2^16, else PPR_ETOOBIG). Blocking. PPR_ECAPACITY if n_tokens > cap_tokens. */
 PPR_API int ppr_lex(const uint8_t* d_bytes, uint64_t n, const ppr_lex_tables_t* tables, const ppr_lex_prepared_t* prep,
             ppr_tokens_out_t* out, void* d_ws, size_t ws_bytes, const ppr_parse_opts_t* opts, void* stream);
 

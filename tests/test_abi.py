@@ -45,6 +45,12 @@ def test_workspace_sizes():
     tiles = -(-(1 << 30) // (1024 * 31))  # single-pass tiles: 1024 threads x 31 bytes
     assert ws >= 256 + tiles * 72
     assert L.ppr_parse_workspace_bytes(1 << 32, ctypes.byref(o)) == 0
+    # the largest input of one call: 2^32 - 2^16 bytes (positions up to the last tile's end fit 32 bits)
+    assert L.ppr_parse_workspace_bytes((1 << 32) - (1 << 16) + 1, ctypes.byref(o)) == 0
+    assert L.ppr_parse_workspace_bytes((1 << 32) - (1 << 16), ctypes.byref(o)) > 0
+    o.chunk_bytes = 0
+    assert L.ppr_lex_workspace_bytes((1 << 32) - (1 << 16) + 1, ctypes.byref(o)) == 0
+    assert L.ppr_lex_workspace_bytes((1 << 32) - (1 << 16), ctypes.byref(o)) > 0
 
 
 def _call_parse(table, n=10, cm=None, chunk=0):
@@ -74,6 +80,7 @@ def test_bad_tables_rejected_on_host():
     assert _call_parse(t, cm=bytes(cm)) == ppr.PPR_EINVAL
     assert _call_parse(t, chunk=65) == ppr.PPR_EINVAL
     assert _call_parse(t, n=1 << 32) == ppr.PPR_ETOOBIG
+    assert _call_parse(t, n=(1 << 32) - (1 << 16) + 1) == ppr.PPR_ETOOBIG
 
 
 def _library_tables(d):
