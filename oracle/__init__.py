@@ -13,6 +13,11 @@ no code, header, table or helper with the GPU library, and it never imports it.
 * ``lex_closure.build_tables``: the merge tables written out from their
   definition with plain tuples (small grammars only).
 
+Beside the oracle, and not part of it: ``csv_parse_parallel`` and
+``lex_restart_parallel`` (cpu_parallel.c), the all-core CPU baseline that the
+benchmark times: the data-parallel method on host threads, checked bit-exact
+against the oracle by ``tests/test_cpu_parallel.py``.
+
 Every function is pinned by ``tests/test_oracle_*.py`` against hand-worked
 examples, exhaustive enumeration and independent readers; see those tests.
 """
@@ -26,15 +31,15 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_HERE, "_liboracle.so")
-_SRCS = [os.path.join(_HERE, "csv_oracle.c"), os.path.join(_HERE, "lex_oracle.c")]
+_SRCS = [os.path.join(_HERE, "csv_oracle.c"), os.path.join(_HERE, "lex_oracle.c"), os.path.join(_HERE, "cpu_parallel.c")]
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with plain gcc -O2."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.run(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", "-o", tmp] + _SRCS,
-                       check=True)
+        subprocess.run(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", "-pthread", "-o", tmp]
+                       + _SRCS, check=True)
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -61,6 +66,11 @@ def lib():
         L.oracle_lex_restart.restype = ctypes.c_int
         L.oracle_lex_fold.argtypes = [_P, _U64, _P, _P, _P, _U32, ctypes.c_uint16, _P, _P, _P, _U64, _P]
         L.oracle_lex_fold.restype = ctypes.c_int
+        L.cpu_parallel_csv_parse.argtypes = [_P, _U64, _U32, _U32, _U32, _U32, _P, _P, _P, _P, _P, _P, _P, _U64,
+                                             _U32, _P, _P, _P, _P]
+        L.cpu_parallel_csv_parse.restype = ctypes.c_int
+        L.cpu_parallel_lex_restart.argtypes = [_P, _U64, _U32, _U32, _P, _P, _P, _P, _P, _U64, _U32, _P]
+        L.cpu_parallel_lex_restart.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -173,4 +183,48 @@ def lex_fold(data, initial_state, merge_table, final_states, k: int, flag_mask: 
     assert rc == 0
     res = {key: v[:kk] for key, v in out.items()}
     res["n_tokens"] = kk
+    return res
+
+
+def csv_parse_parallel(data, d: dict, threads: int, cap: int | None = None) -> dict:
+    """The all-core CPU baseline (not the oracle): csv_parse's result, computed
+    by the data-parallel method on `threads` host threads."""
+    b = _as_u8(data)
+    n = b.size
+    nxt, tag, cm = _tables(d)
+    cap = n + 1 if cap is None else cap
+    out = {k: np.empty(cap, dtype=np.uint32) for k in ("rec", "col", "off", "len")}
+    nf, nr, err, es = _U64(), _U64(), ctypes.c_int64(), _U32()
+    rc = lib().cpu_parallel_csv_parse(b.ctypes.data, n, d["n_states"], d["n_classes"], d["start"], d["accept_mask"],
+                                      nxt.ctypes.data, tag.ctypes.data, cm.ctypes.data, out["rec"].ctypes.data,
+                                      out["col"].ctypes.data, out["off"].ctypes.data, out["len"].ctypes.data, cap,
+                                      threads, ctypes.byref(nf), ctypes.byref(nr), ctypes.byref(err),
+                                      ctypes.byref(es))
+    k = int(nf.value)
+    if rc == -1:
+        raise ValueError("cpu_parallel_csv_parse: invalid table or thread count")
+    res = {key: v[:min(k, cap)] for key, v in out.items()}
+    res.update(n_fields=k, n_records=int(nr.value), error_pos=int(err.value), end_state=int(es.value), rc=rc)
+    return res
+
+
+def lex_restart_parallel(data, d: dict, threads: int, cap: int | None = None) -> dict:
+    """The all-core CPU baseline (not the oracle): lex_restart's result, computed
+    by the data-parallel method on `threads` host threads."""
+    b = _as_u8(data)
+    n = b.size
+    cap = n + 1 if cap is None else cap
+    out = _tok_out(cap)
+    delta = np.ascontiguousarray(d["delta"], dtype=np.int16)
+    kind = np.ascontiguousarray(d["kind"], dtype=np.uint16)
+    nt = _U64()
+    rc = lib().cpu_parallel_lex_restart(b.ctypes.data, n, delta.shape[0], d["q0"], delta.ctypes.data,
+                                        kind.ctypes.data, out["kind"].ctypes.data, out["start"].ctypes.data,
+                                        out["length"].ctypes.data, cap, threads, ctypes.byref(nt))
+    k = int(nt.value)
+    if rc == -1:
+        raise ValueError("cpu_parallel_lex_restart: invalid table or thread count")
+    res = {key: v[:min(k, cap)] for key, v in out.items()}
+    res["n_tokens"] = k
+    res["rc"] = rc
     return res
