@@ -112,8 +112,8 @@ def cpu_oracle_baseline(kind, data, spec, max_seconds=30.0):
         "value": round(data.size / statistics.median(par_runs) / 1e9, 3), "unit": "GB/s", "cores": cores,
         "kind": "all-core CPU baseline",
         "sample": "the whole input, the data-parallel method on %d host threads (per-slice state-transition "
-                  "vectors, their serial composition, a counting pass and a writing pass per slice; gcc -O2), "
-                  "median of %d run(s)" % (cores, len(par_runs)),
+                  "vectors, their serial composition, a tagging pass listing each slice's terminators, prefixes, "
+                  "a parallel write; gcc -O2), median of %d run(s)" % (cores, len(par_runs)),
         "parity_vs_oracle": "bit-exact" if exact else "MISMATCH"}
 
 
