@@ -51,7 +51,8 @@ class ParseOut(ctypes.Structure):
     _fields_ = [("record_idx", ctypes.c_void_p), ("column_ids", ctypes.c_void_p),
                 ("field_offsets", ctypes.c_void_p), ("field_lengths", ctypes.c_void_p),
                 ("cap_fields", ctypes.c_uint64), ("n_fields", ctypes.c_uint64), ("n_records", ctypes.c_uint64),
-                ("error_pos", ctypes.c_int64), ("end_state", ctypes.c_uint32), ("path", ctypes.c_uint32)]
+                ("error_pos", ctypes.c_int64), ("end_state", ctypes.c_uint32), ("path", ctypes.c_uint32),
+                ("min_columns", ctypes.c_uint32), ("max_columns", ctypes.c_uint32)]
 
 
 class ParseOpts(ctypes.Structure):
@@ -181,6 +182,8 @@ class ParseResult:
     error_pos: int
     end_state: int
     path: int                    # the kernels that ran: a PPR_PATH_* value
+    min_columns: int             # fewest / most fields of a record (0 / 0 without records): the inferred
+    max_columns: int             # number of columns is max_columns; all records conform iff the two are equal
 
 
 class Parser:
@@ -251,7 +254,7 @@ class Parser:
             _check(rc, "ppr_parse")
             k = int(o.n_fields)
             return ParseResult(*[a[:k] for a in self.out_arrays], k, int(o.n_records), int(o.error_pos),
-                               int(o.end_state), int(o.path))
+                               int(o.end_state), int(o.path), int(o.min_columns), int(o.max_columns))
         raise PprError(PPR_ECAPACITY, "ppr_parse")
 
 

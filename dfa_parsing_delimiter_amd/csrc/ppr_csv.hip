@@ -106,6 +106,7 @@ struct TileShared {
     Carry prefix;
     uint32_t state;
     uint32_t last_rec;
+    uint32_t cols[2][NW];
 };
 
 // Tile start state from the block's vector scan: tile 0 starts in the DFA's
@@ -185,6 +186,7 @@ __device__ void finish_tile(const LookCtx& c, const OutArrays& o, uint32_t n, ui
         uint64_t fi = base.nf;
         uint32_t rec = base.nr, col = base.colv, off = base.lt;
         uint64_t bits = T;
+        uint32_t cmin = 0xffffffffu, cmax = 0;  // fields per record, over the records this chunk's fields end
         while (bits) {
             const uint32_t j = (uint32_t)__ffsll((unsigned long long)bits) - 1u;
             const uint32_t pos = chunk_abs + j;
@@ -197,12 +199,34 @@ __device__ void finish_tile(const LookCtx& c, const OutArrays& o, uint32_t n, ui
             ++fi;
             off = pos + 1;
             if ((RD >> j) & 1u) {
+                cmin = min(cmin, col + 1u);
+                cmax = max(cmax, col + 1u);
                 ++rec;
                 col = 0;
             } else {
                 ++col;
             }
             bits &= bits - 1;
+        }
+        if (tile == num_tiles - 1 && tid == 0 && !sh->last_rec) {  // the final field ends the last record
+            const Carry I = carry_op(P, ctot);
+            cmin = min(cmin, I.colv + 1u);
+            cmax = max(cmax, I.colv + 1u);
+        }
+        // the tile's fewest and most fields per record, into the call's
+        wave_min_max(cmin, cmax);
+        const int w = tid / kWave;
+        if (lane_id() == 0) {
+            sh->cols[0][w] = cmin;
+            sh->cols[1][w] = cmax;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            for (int i = 1; i < NW; ++i) {
+                cmin = min(cmin, sh->cols[0][i]);
+                cmax = max(cmax, sh->cols[1][i]);
+            }
+            widen_range(&c.hdr->cols_min, &c.hdr->cols_max, cmin, cmax);
         }
     }
 
@@ -230,6 +254,8 @@ __global__ void csv_reset_kernel(WsHeader* hdr, uint32_t n, uint32_t start_state
         hdr->err_min = 0xffffffffu;
         hdr->last_rec = 0;
         hdr->path = PPR_PATH_SINGLE_PASS;
+        hdr->cols_min = 0xffffffffu;
+        hdr->cols_max = 0;
         if (n == 0) {  // nothing to parse: the results of an empty input
             hdr->n_fields = 0;
             hdr->n_records = 0;
@@ -600,6 +626,8 @@ extern "C" int ppr_parse_results(const void* d_ws, uint64_t n, ppr_parse_out_t* 
     out->error_pos = h.err_min != 0xffffffffu ? (int64_t)h.err_min : h.error_pos;
     out->end_state = h.end_state;
     out->path = h.path;
+    out->min_columns = h.cols_min != 0xffffffffu ? h.cols_min : 0u;
+    out->max_columns = h.cols_max;
     if (h.fault) return PPR_EHIP;
     return out->n_fields > out->cap_fields ? PPR_ECAPACITY : PPR_OK;
 }

@@ -24,6 +24,8 @@ struct WsHeader {
     uint32_t err_min;   // first INVALID byte (atomic minimum over tiles), 0xffffffff: none
     uint32_t last_rec;  // the input's last byte is a record delimiter (multi-kernel parse)
     uint32_t path;      // which kernels ran (PPR_PATH_*)
+    uint32_t cols_min;  // fewest fields of a record (atomic minimum), 0xffffffff: no record yet
+    uint32_t cols_max;  // most fields of a record (atomic maximum)
 };
 
 // Records stage event i of the call on the stream, if the caller asked for it.

@@ -67,6 +67,30 @@ __device__ __forceinline__ T wave_scan(T x, const T& id, const Comb& comb)
     return x;
 }
 
+struct MinU32 {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
+};
+struct MaxU32 {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
+};
+
+// the wave's minimum of mn and maximum of mx, in every lane
+__device__ __forceinline__ void wave_min_max(uint32_t& mn, uint32_t& mx)
+{
+    mn = readlane_t(wave_scan(mn, 0xffffffffu, MinU32{}), kWave - 1);
+    mx = readlane_t(wave_scan(mx, 0u, MaxU32{}), kWave - 1);
+}
+
+// Widens the stored range [*dmin, *dmax] (it only ever widens) to hold [mn, mx]
+// (mn = 0xffffffff, mx = 0: nothing to add). One thread calls it; it makes an
+// atomic only where the stored bound would change (a stale read understates the
+// range, so at worst an atomic is made that was not needed).
+__device__ __forceinline__ void widen_range(uint32_t* dmin, uint32_t* dmax, uint32_t mn, uint32_t mx)
+{
+    if (mn < __hip_atomic_load(dmin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMin(dmin, mn);
+    if (mx > __hip_atomic_load(dmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(dmax, mx);
+}
+
 // value of the previous lane (lane 0: id)
 template <typename T>
 __device__ __forceinline__ T wave_shr1(const T& id, const T& x)

@@ -98,6 +98,12 @@ typedef struct ppr_parse_out {
     int64_t error_pos;  /* out: first INVALID byte; else n if the end state is not accepting; else -1 */
     uint32_t end_state; /* out: DFA state after the last byte */
     uint32_t path;      /* out: the kernels that ran, a PPR_PATH_* value */
+    /* out: the fewest and the most fields of any record (0 and 0 without records).
+     * [ParPaRaw Sec. 4, "Inferring or validating number of columns"]: the
+     * largest is the inferred number of columns; the records all conform to one
+     * number of columns exactly when the two are equal. */
+    uint32_t min_columns;
+    uint32_t max_columns;
 } ppr_parse_out_t;
 
 /*

@@ -5,7 +5,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 no code, header, table or helper with the GPU library, and it never imports it.
 
 * ``csv_parse``: one sequential DFA run over the whole input
-  (csv_oracle.c; ParPaRaw, Sec. 3 and "validating format").
+  (csv_oracle.c; ParPaRaw, Sec. 3 and "validating format"), and the fewest and
+  most fields of any record, counted from its per-field record indices
+  (ParPaRaw, Sec. 4, "Inferring or validating number of columns").
 * ``lex_restart``: the restart lexer, one state variable over the bytes
   (lex_oracle.c; "Lexing on the GPU", "A lexer is a prefix scan").
 * ``lex_fold``: the sequential table-driven fold over initial/merge/final
@@ -67,7 +69,7 @@ def lib():
         L.oracle_lex_fold.argtypes = [_P, _U64, _P, _P, _P, _U32, ctypes.c_uint16, _P, _P, _P, _U64, _P]
         L.oracle_lex_fold.restype = ctypes.c_int
         L.cpu_parallel_csv_parse.argtypes = [_P, _U64, _U32, _U32, _U32, _U32, _P, _P, _P, _P, _P, _P, _P, _U64,
-                                             _U32, _P, _P, _P, _P]
+                                             _U32, _P, _P, _P, _P, _P, _P]
         L.cpu_parallel_csv_parse.restype = ctypes.c_int
         L.cpu_parallel_lex_restart.argtypes = [_P, _U64, _U32, _U32, _P, _P, _P, _P, _P, _U64, _U32, _P]
         L.cpu_parallel_lex_restart.restype = ctypes.c_int
@@ -91,6 +93,15 @@ def _tables(d):
     return np.ascontiguousarray(nxt), np.ascontiguousarray(tag), np.ascontiguousarray(cm)
 
 
+def _columns(rec, n_records):
+    """fewest and most fields of any record (0, 0 without records): the fields
+    of record r are those whose record index is r"""
+    if n_records == 0:
+        return 0, 0
+    per_record = np.bincount(rec.astype(np.int64), minlength=n_records)
+    return int(per_record.min()), int(per_record.max())
+
+
 def csv_parse(data, d: dict, start_state: int | None = None, cap: int | None = None) -> dict:
     """Sequential parse of one input under DFA table d (workloads.dfa format).
     Returns the four per-field arrays (uint32) and the scalars."""
@@ -110,6 +121,7 @@ def csv_parse(data, d: dict, start_state: int | None = None, cap: int | None = N
         raise ValueError("oracle capacity too small: %d fields" % k)
     res = {key: v[:k] for key, v in out.items()}
     res.update(n_fields=k, n_records=int(nr.value), error_pos=int(err.value), end_state=int(es.value))
+    res["min_columns"], res["max_columns"] = _columns(res["rec"], res["n_records"])
     return res
 
 
@@ -139,6 +151,7 @@ def csv_parse_many(inputs, d: dict) -> list:
         lo, hi = int(base[j]), int(base[j + 1])
         r = {key: v[lo:hi] for key, v in out.items()}
         r.update(n_fields=hi - lo, n_records=int(nr[j]), error_pos=int(err[j]), end_state=int(es[j]))
+        r["min_columns"], r["max_columns"] = _columns(r["rec"], r["n_records"])
         res.append(r)
     return res
 
@@ -194,17 +207,18 @@ def csv_parse_parallel(data, d: dict, threads: int, cap: int | None = None) -> d
     nxt, tag, cm = _tables(d)
     cap = n + 1 if cap is None else cap
     out = {k: np.empty(cap, dtype=np.uint32) for k in ("rec", "col", "off", "len")}
-    nf, nr, err, es = _U64(), _U64(), ctypes.c_int64(), _U32()
+    nf, nr, err, es, cmin, cmax = _U64(), _U64(), ctypes.c_int64(), _U32(), _U32(), _U32()
     rc = lib().cpu_parallel_csv_parse(b.ctypes.data, n, d["n_states"], d["n_classes"], d["start"], d["accept_mask"],
                                       nxt.ctypes.data, tag.ctypes.data, cm.ctypes.data, out["rec"].ctypes.data,
                                       out["col"].ctypes.data, out["off"].ctypes.data, out["len"].ctypes.data, cap,
                                       threads, ctypes.byref(nf), ctypes.byref(nr), ctypes.byref(err),
-                                      ctypes.byref(es))
+                                      ctypes.byref(es), ctypes.byref(cmin), ctypes.byref(cmax))
     k = int(nf.value)
     if rc == -1:
         raise ValueError("cpu_parallel_csv_parse: invalid table or thread count")
     res = {key: v[:min(k, cap)] for key, v in out.items()}
-    res.update(n_fields=k, n_records=int(nr.value), error_pos=int(err.value), end_state=int(es.value), rc=rc)
+    res.update(n_fields=k, n_records=int(nr.value), error_pos=int(err.value), end_state=int(es.value), rc=rc,
+               min_columns=int(cmin.value), max_columns=int(cmax.value))
     return res
 
 

@@ -18,7 +18,11 @@
  *      counting its fields, records, column carry and first INVALID byte;
  *   4. one thread turns the counts into each slice's field index, record index,
  *      column and field start at its first byte (exclusive prefixes, the
- *      offsets of Fig. 4);
+ *      offsets of Fig. 4), and resolves the fields-per-record range as Sec. 4
+ *      ("Inferring or validating number of columns") describes: a slice counts
+ *      the field delimiters before its first record delimiter (relative: the
+ *      record began in an earlier slice) and the fewest and most fields of the
+ *      records after it; the carried column turns the relative count absolute;
  *   5. every thread writes its fields from its list at its field index.
  * Steps 3-5 give each field the record, column, offset and length the
  * sequential loop gives it, started from the slice's carried values.
@@ -170,6 +174,8 @@ typedef struct {
     uint64_t nr;        /* record delimiters */
     uint64_t col_tail;  /* field delimiters after the slice's last record delimiter (all of them if none) */
     int has_rec;
+    uint64_t col_head;  /* field delimiters before the slice's first record delimiter */
+    uint64_t cmin, cmax;  /* fewest / most fields of the records after the first record delimiter */
     int64_t err;        /* first INVALID byte (-1: none) */
     uint64_t f_in, r_in, c_in, start_in;  /* field index, record, column, field start at the first byte */
 } csv_slice_t;
@@ -199,7 +205,7 @@ static void csv_tags(void* p, uint32_t t)
     const uint64_t a = slice_lo(j->n, j->T, t), b = slice_lo(j->n, j->T, t + 1);
     const uint32_t C = j->d.n_classes;
     uint32_t s = c->s_in, last_tag = TAG_VALUE;
-    uint64_t nr = 0, col = 0;
+    uint64_t nr = 0, col = 0, col_head = 0, cmin = UINT64_MAX, cmax = 0;
     int64_t err = -1;
     int has_rec = 0;
     for (uint64_t i = a; i < b; ++i) {
@@ -212,6 +218,12 @@ static void csv_tags(void* p, uint32_t t)
         } else if (tg == TAG_RECORD) {
             list_push(&c->terms, (i << 1) | 1u);
             nr++;
+            if (has_rec) {
+                if (col + 1 < cmin) cmin = col + 1;
+                if (col + 1 > cmax) cmax = col + 1;
+            } else {
+                col_head = col;
+            }
             col = 0;
             has_rec = 1;
         } else if (tg == TAG_INVALID && err < 0) {
@@ -221,6 +233,9 @@ static void csv_tags(void* p, uint32_t t)
     }
     c->nr = nr;
     c->col_tail = col;
+    c->col_head = col_head;
+    c->cmin = cmin;
+    c->cmax = cmax;
     c->has_rec = has_rec;
     c->err = err;
     c->last_tag = last_tag;
@@ -256,7 +271,8 @@ int cpu_parallel_csv_parse(const uint8_t* bytes, uint64_t n, uint32_t n_states, 
                            uint32_t start_state, uint32_t accept_mask, const uint8_t* next, const uint8_t* tag,
                            const uint8_t* class_map, uint32_t* rec_out, uint32_t* col_out, uint32_t* off_out,
                            uint32_t* len_out, uint64_t cap, uint32_t n_threads, uint64_t* n_fields,
-                           uint64_t* n_records, int64_t* error_pos, uint32_t* end_state)
+                           uint64_t* n_records, int64_t* error_pos, uint32_t* end_state, uint32_t* min_columns,
+                           uint32_t* max_columns)
 {
     if (n_states == 0 || n_states > MAX_STATES || n_classes == 0 || start_state >= n_states || n_threads == 0)
         return -1;
@@ -286,13 +302,20 @@ int cpu_parallel_csv_parse(const uint8_t* bytes, uint64_t n, uint32_t n_states, 
     }
     if (rc == 0) {
         /* 4. prefixes */
-        uint64_t f = 0, r = 0, c = 0, start = 0;
+        uint64_t f = 0, r = 0, c = 0, start = 0, cmin = UINT64_MAX, cmax = 0;
         for (uint32_t t = 0; t < T; ++t) {
             csv_slice_t* x = &j.sl[t];
             x->f_in = f;
             x->r_in = r;
             x->c_in = c;
             x->start_in = start;
+            if (x->has_rec) {  /* the record its first record delimiter ends began at column c */
+                const uint64_t head = c + x->col_head + 1;
+                if (head < cmin) cmin = head;
+                if (head > cmax) cmax = head;
+                if (x->cmin < cmin) cmin = x->cmin;
+                if (x->cmax > cmax) cmax = x->cmax;
+            }
             f += x->terms.size;
             r += x->nr;
             c = x->has_rec ? x->col_tail : c + x->col_tail;
@@ -315,8 +338,12 @@ int cpu_parallel_csv_parse(const uint8_t* bytes, uint64_t n, uint32_t n_states, 
                 }
                 f++;
                 r++;
+                if (c + 1 < cmin) cmin = c + 1;
+                if (c + 1 > cmax) cmax = c + 1;
             }
             if (err < 0 && !((accept_mask >> s_end) & 1u)) err = (int64_t)n;
+            *min_columns = r ? (uint32_t)cmin : 0u;
+            *max_columns = r ? (uint32_t)cmax : 0u;
             *n_fields = f;
             *n_records = r;
             *error_pos = err;

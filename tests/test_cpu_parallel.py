@@ -20,7 +20,7 @@ THREADS = (1, 2, 3, 7, 16, 61)
 
 
 def _same_csv(a, r, what):
-    for key in ("n_fields", "n_records", "error_pos", "end_state"):
+    for key in ("n_fields", "n_records", "error_pos", "end_state", "min_columns", "max_columns"):
         assert a[key] == r[key], (what, key, a[key], r[key])
     for key in ("rec", "col", "off", "len"):
         assert np.array_equal(a[key], r[key]), (what, key)

@@ -49,6 +49,24 @@ def test_golden_examples():
         assert r["error_pos"] == c["error_pos"], c
 
 
+def _columns_of(fields, n_records):
+    """fewest and most fields of any record, counted from a field list (rec, col, off, len)"""
+    per = {}
+    for f in fields:
+        per[f[0]] = per.get(f[0], 0) + 1
+    return (min(per.values()), max(per.values())) if n_records else (0, 0)
+
+
+def test_column_count_examples():
+    """fields per record, worked by hand; the first is the pages' example of records with a varying number of
+    field delimiters (ParPaRaw, Sec. 4: "1,Apples" then "2")"""
+    t = W.table("T5")
+    for text, want in ((b"1,Apples\n2\n", (1, 2)), (b"", (0, 0)), (b"a,b,c\nd,e,f", (3, 3)), (b"\n\n", (1, 1)),
+                       (b'"x,y",z\n', (2, 2)), (b"a\nb,c,d\n,\n", (1, 3)), (b"a,b\nc", (1, 2))):
+        r = oracle.csv_parse(text, t)
+        assert (r["min_columns"], r["max_columns"]) == want, (text, r["min_columns"], r["max_columns"])
+
+
 @pytest.mark.parametrize("name,alphabet,max_len,reader", [
     ("T5", b',\n"a', 8, read_t5),
     ("T6", b'\t\n"#a', 7, read_t6),
@@ -60,7 +78,8 @@ def test_exhaustive_vs_recursive_descent(name, alphabet, max_len, reader):
     bad = 0
     for s, r in zip(inputs, got):
         fields, nrec, err = reader(s)
-        if _tuples(r) != fields or r["n_records"] != nrec or r["error_pos"] != err:
+        if _tuples(r) != fields or r["n_records"] != nrec or r["error_pos"] != err or \
+                (r["min_columns"], r["max_columns"]) != _columns_of(fields, nrec):
             bad += 1
             if bad < 5:
                 print("mismatch", s, _tuples(r), r["n_records"], r["error_pos"], "reader:", fields, nrec, err)
@@ -219,6 +238,7 @@ def test_valid_quoted_matches_csv_module():
         for (rec, col, off, ln) in _tuples(r):
             ours.setdefault(rec, []).append(_unquote(b[off:off + ln]).decode())
         assert [ours[i] for i in range(r["n_records"])] == rows, text
+        assert (r["min_columns"], r["max_columns"]) == (min(map(len, rows)), max(map(len, rows))), text
         checked += 1
     assert checked > 1000
 

@@ -52,6 +52,8 @@ def _same(g, r, what=""):
     assert g.n_records == r["n_records"], (what, g.n_records, r["n_records"])
     assert g.error_pos == r["error_pos"], (what, g.error_pos, r["error_pos"])
     assert g.end_state == r["end_state"], (what, g.end_state, r["end_state"])
+    assert (g.min_columns, g.max_columns) == (r["min_columns"], r["max_columns"]), (
+        what, g.min_columns, g.max_columns, r["min_columns"], r["max_columns"])
     for name, key in (("record_idx", "rec"), ("column_ids", "col"), ("field_offsets", "off"),
                       ("field_lengths", "len")):
         a = _np(getattr(g, name))
