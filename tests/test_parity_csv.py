@@ -206,6 +206,28 @@ def test_edge_cases(ppr):
             _same(g, oracle.csv_parse(b, t), (t["name"], len(b), chunk, path))
 
 
+def test_column_counts_at_scale(ppr):
+    """records of 1 to 40 fields (some quoted, with embedded delimiters) over many tiles and ranges: the fewest
+    and most fields per record on every path, with the narrowest and widest records placed deep inside; and a
+    conforming input (every record 7 fields)"""
+    t = W.table("T5")
+    rng = np.random.default_rng(31)
+    recs = []
+    for i in range(300000):
+        k = int(rng.integers(2, 39)) if i not in (123457, 200001) else (1 if i == 123457 else 40)
+        recs.append(b",".join(b'"a,\nb"' if rng.random() < 0.1 else b"x" * int(rng.integers(0, 6)) for _ in range(k)))
+    wide = b"\n".join(recs)  # no trailing newline: the final record is unterminated
+    conform = b"\n".join(b",".join(b"%d" % (i * 7 + j) for j in range(7)) for i in range(200000)) + b"\n"
+    for what, b in (("varied", wide), ("conforming", conform)):
+        r = oracle.csv_parse(b, t)
+        assert (what != "varied") or (r["min_columns"], r["max_columns"]) == (1, 40)
+        assert (what != "conforming") or (r["min_columns"], r["max_columns"]) == (7, 7)
+        for chunk, path in ((None, None), (64, STREAMING), (64, FUSED), (31, None)):
+            _say("columns", what, len(b), chunk, path)
+            g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=r["n_fields"] + 1, path=path)
+            _same(g, r, (what, chunk, path))
+
+
 def test_invalid_bytes_at_scale(ppr):
     """the first INVALID byte over many tiles and ranges: at byte 1 of 12 MiB (every later byte stays in the
     absorbing state, so every chunk after it holds INVALID bytes), deep inside the input (one bad byte after
