@@ -77,23 +77,54 @@ def algorithmic_bytes(stage, n, n_out, out_bytes_per_item):
     return 0
 
 
+def host_cpu():
+    """what the host offers this process: CPU model, nproc, the cores it may run on"""
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    allowed = sorted(os.sched_getaffinity(0))
+    return {"model": model, "nproc": os.cpu_count(), "allowed_cores": len(allowed)}, allowed
+
+
+def all_core_threads(allowed):
+    """threads for the all-core CPU baseline: every core this process may run on,
+    but no more than OMP_NUM_THREADS where it is set (the share of the host's
+    cores that one GPU's job is given)"""
+    k = len(allowed)
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        k = min(k, int(omp))
+    return max(1, k)
+
+
 def cpu_oracle_baseline(kind, data, spec, max_seconds=30.0):
-    """The oracle as it stands, on the host: one thread over the whole input
-    (median of up to 3 runs within the time bound); and the all-core CPU
-    baseline (the data-parallel method on host threads, at most 16), checked
+    """The oracle as it stands, on the host: one thread pinned to one core, over
+    the whole input (median of up to 3 runs within the time bound); and the
+    all-core CPU baseline (the data-parallel method on host threads), checked
     bit-exact against the oracle's result."""
     import numpy as np
     import oracle
+    info, allowed = host_cpu()
     runs, res = [], None
     t_end = time.time() + max_seconds
-    for _ in range(3):
-        t0 = time.perf_counter()
-        res = oracle.csv_parse(data, spec) if kind == "csv" else oracle.lex_restart(data, spec)
-        runs.append(time.perf_counter() - t0)
-        if time.time() + runs[-1] > t_end:
-            break
+    pin = allowed[len(allowed) // 2]
+    os.sched_setaffinity(0, {pin})  # this thread only: the oracle runs in it (ctypes)
+    try:
+        for _ in range(3):
+            t0 = time.perf_counter()
+            res = oracle.csv_parse(data, spec) if kind == "csv" else oracle.lex_restart(data, spec)
+            runs.append(time.perf_counter() - t0)
+            if time.time() + runs[-1] > t_end:
+                break
+    finally:
+        os.sched_setaffinity(0, set(allowed))  # the all-core run's threads inherit this mask
     single = data.size / statistics.median(runs) / 1e9
-    cores = min(16, os.cpu_count() or 1)
+    cores = all_core_threads(allowed)
     par_runs, par = [], None
     t_end = time.time() + max_seconds
     for _ in range(3):
@@ -107,14 +138,48 @@ def cpu_oracle_baseline(kind, data, spec, max_seconds=30.0):
         ("n_tokens", "kind", "start", "length")
     exact = all(np.array_equal(par[k], res[k]) for k in keys)
     return res, {"value": round(single, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                 "sample": "the whole %d-byte input, sequential C oracle (gcc -O2), median of %d run(s)" % (
-                     data.size, len(runs))}, {
+                 "sample": "the whole %d-byte input, sequential C oracle (gcc -O3), one thread pinned to core %d, "
+                           "median of %d run(s)" % (data.size, pin, len(runs)),
+                 "host": info}, {
         "value": round(data.size / statistics.median(par_runs) / 1e9, 3), "unit": "GB/s", "cores": cores,
         "kind": "all-core CPU baseline",
         "sample": "the whole input, the data-parallel method on %d host threads (per-slice state-transition "
                   "vectors, their serial composition, a tagging pass listing each slice's terminators, prefixes, "
-                  "a parallel write; gcc -O2), median of %d run(s)" % (cores, len(par_runs)),
+                  "a parallel write; gcc -O3), median of %d run(s)" % (cores, len(par_runs)),
+        "threads_rule": "the cores this process may run on (sched_getaffinity: %d), capped by OMP_NUM_THREADS "
+                        "(%s)" % (len(allowed), os.environ.get("OMP_NUM_THREADS", "unset")),
+        "host": info,
         "parity_vs_oracle": "bit-exact" if exact else "MISMATCH"}
+
+
+def bandwidth_ceilings(ppr, torch, dev, nbytes=1 << 30, iters=10):
+    """The device's own streaming rates (ppr_bandwidth_probe): read, write and
+    copy of nbytes, wave-contiguous 16-byte words (pattern 0) and 64 bytes per
+    lane (pattern 1), averaged over iters launches after 2 warm-ups."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(3)
+    props = torch.cuda.get_device_properties(dev)
+    grid = props.multi_processor_count * 8
+    stream = torch.cuda.current_stream()
+    out = {"bytes": nbytes, "grid": grid, "block": 256}
+    for pat, pname in ((0, "wave_contiguous_16B"), (1, "lane_contiguous_64B")):
+        r = {}
+        for mode, mname in ((0, "read"), (1, "write"), (2, "copy")):
+            for _ in range(2):
+                ppr.bandwidth_probe(mode, pat, src, dst, nbytes, grid)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(iters):
+                ppr.bandwidth_probe(mode, pat, src, dst, nbytes, grid)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / iters
+            moved = nbytes * (2 if mode == 2 else 1)
+            r[mname] = {"us": round(ms * 1e3, 1), "GBps": round(moved / (ms * 1e-3) / 1e9, 1)}
+        out[pname] = r
+    del src, dst
+    return out
 
 
 def read_pmc(d, counter):
@@ -208,6 +273,8 @@ def main():
     ap.add_argument("--path", choices=["auto", "fused", "streaming", "single-pass"], default="auto",
                     help="parse kernels to ask the library for (default: its automatic choice)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline and the full-size parity check")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the device bandwidth probe (read / write / copy of 1 GiB)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -274,16 +341,21 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # (1) the metric: K blocking calls, timed on the stream
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # (1) the metric: K blocking calls, each bracketed by events on the stream;
+    # ms_per_step is their median
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    for a, b in step_ev:
+        a.record(stream)
         o = step()
-    ev1.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    ms = ev0.elapsed_time(ev1) / args.steps
+    step_ms = [a.elapsed_time(b) for a, b in step_ev]
+    ms = statistics.median(step_ms)
+    ms_mean = statistics.mean(step_ms)
     got = int(o.n_fields if kind == "csv" else o.n_tokens)
     assert got == n_out, (got, n_out)
 
@@ -309,7 +381,7 @@ def main():
     gbs = n / (ms * 1e-3) / 1e9
     alg_dom = algorithmic_bytes(dominant, n, n_out, out_bytes_per_item)
     alg_step = n + out_bytes_per_item * n_out
-    traffic = measured_traffic(args.workload, chunk, dominant) if kind == "csv" else None
+    traffic = measured_traffic(args.workload, chunk, dominant)
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -337,9 +409,14 @@ def main():
                               "achieved": round(alg_step / (ms * 1e-3) / 1e9, 2),
                               "frac": round(alg_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
                      "ms_per_step_pipelined": round(ms_pipelined, 4),
-                     "timing": "HIP events on the launch stream: %d blocking calls (wall %.3fs); per-kernel events "
-                               "recorded by the library over %d pipelined calls" % (args.steps, wall, args.steps)},
+                     "ms_per_step_mean": round(ms_mean, 4),
+                     "ms_per_step_min_max": [round(min(step_ms), 4), round(max(step_ms), 4)],
+                     "timing": "HIP events on the launch stream around each of %d blocking calls (median; wall "
+                               "%.3fs); per-kernel events recorded by the library over %d pipelined calls" % (
+                                   args.steps, wall, args.steps)},
     }
+    if not args.no_probe:
+        line["bandwidth_ceilings"] = bandwidth_ceilings(ppr, torch, dev)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -106,6 +106,8 @@ def _load():
     L.ppr_lex_build_tables.restype = ctypes.c_int
     L.ppr_version.argtypes = []
     L.ppr_version.restype = ctypes.c_char_p
+    L.ppr_bandwidth_probe.argtypes = [U32, U32, P, P, U64, U32, P]
+    L.ppr_bandwidth_probe.restype = ctypes.c_int
     return L
 
 
@@ -114,6 +116,14 @@ lib = _load()
 
 def version() -> str:
     return lib.ppr_version().decode()
+
+
+def bandwidth_probe(mode: int, pattern: int, src, dst, nbytes: int, grid: int, stream=None):
+    """Enqueue one probe kernel (ppr_bandwidth_probe): mode 0 read, 1 write,
+    2 copy; pattern 0 wave-contiguous 16-byte words, 1 64 bytes per lane."""
+    _check(lib.ppr_bandwidth_probe(mode, pattern, ctypes.c_void_p(0 if src is None else src.data_ptr()),
+                                   ctypes.c_void_p(dst.data_ptr()), nbytes, grid, _stream_handle(stream)),
+           "ppr_bandwidth_probe")
 
 
 def _check(code: int, where: str):

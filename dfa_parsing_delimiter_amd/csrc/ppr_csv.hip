@@ -289,7 +289,9 @@ __global__ void __launch_bounds__(kBlock) csv_generic_kernel(CsvParams p)
 
     const int tid = threadIdx.x;
     if (tid == 0) {
-        s_tile = blockIdx.x;
+        // tiles in the order workgroups start (not blockIdx order): a tile only
+        // waits in its look-backs on tiles that running workgroups already hold
+        s_tile = atomicAdd(&p.look.hdr->tile_counter, 1u);
         sh.last_rec = 0;
     }
     if (tid < 256) s_cls[tid] = p.cls[tid];

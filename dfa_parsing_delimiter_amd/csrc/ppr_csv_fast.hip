@@ -48,21 +48,28 @@ struct Geo {
 
 
 // Count carries [ParPaRaw Sec. 3, offsets, Fig. 4] of a run of bytes: nf
-// terminators, nr record delimiters, col the column offset handed on (bit 31:
-// absolute, a record delimiter was seen), lt = 1 + position of the last
-// terminator (0: none).
+// terminators, nr record delimiters, col the column offset handed on, lt = 1 +
+// position of the last terminator (0: none). The column offset is absolute
+// (field delimiters after the run's last record delimiter) exactly when the
+// run holds a record delimiter, nr > 0, and relative (all its field
+// delimiters) otherwise, so the relative/absolute flag needs no bit of its
+// own and a column offset may take all 32 bits. The input's start is column 0
+// of record 0, so a prefix that starts there is absolute either way.
 struct GCarry {
     uint32_t nf, nr, col, lt;
 };
 
-// x earlier, y later: an absolute later column offset wins, a relative one adds
-// (the earlier offset's absolute flag stays in bit 31)
-__device__ __forceinline__ uint32_t col_op(uint32_t x, uint32_t y) { return (int32_t)y < 0 ? y : x + y; }
+// column offset after x then y (y later, holding ynr record delimiters): an
+// absolute later offset wins, a relative one adds to the earlier offset
+__device__ __forceinline__ uint32_t col_after(uint32_t xcol, uint32_t ycol, uint32_t ynr)
+{
+    return ynr ? ycol : xcol + ycol;
+}
 
 struct GCarryComb {
     __device__ GCarry operator()(const GCarry& x, const GCarry& y) const
     {
-        return {x.nf + y.nf, x.nr + y.nr, col_op(x.col, y.col), max(x.lt, y.lt)};
+        return {x.nf + y.nf, x.nr + y.nr, col_after(x.col, y.col, y.nr), max(x.lt, y.lt)};
     }
 };
 
@@ -117,7 +124,7 @@ __device__ __forceinline__ SpanCarry span_carry(const uint64_t (&T)[NCH], const 
     const uint32_t max_rd =
         has_r ? (uint32_t)__builtin_amdgcn_readlane((excl & 0xffffu) + rdl, 63 - __clzll((long long)has_r)) : 0u;
     const uint32_t wnf = tot & 0xffffu;
-    const GCarry wc{wnf, tot >> 16, max_rd ? (wnf - max_rd) | 0x80000000u : wnf, max_lt};
+    const GCarry wc{wnf, tot >> 16, max_rd ? wnf - max_rd : wnf, max_lt};
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const GCarry zero{0, 0, 0, 0};
     if (lane_id() == 0) s_wave[w] = wc;
@@ -860,7 +867,7 @@ __global__ void __launch_bounds__(kFastBlock, kCarriesWavesPerSimd<CB>) csv_carr
             r = make_uint4(r.x + q.x, r.y + q.y, r.z + q.z, max(r.w, q.w));
             e = min(e, s_err[i]);
         }
-        p.range_carry[b] = make_uint4(r.x, r.y, r.z | (r.y ? 0x80000000u : 0u), r.w);
+        p.range_carry[b] = make_uint4(r.x, r.y, r.z, r.w);
         p.range_err[b] = e;
         if (b == p.num_ranges - 1) {
             const uint32_t e = min(run, 8u);
@@ -955,8 +962,8 @@ __global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_e
     uint32_t* list = s_list[wv];
     load_pass2<CB, V8>(p, sh);
     const GCarryComb gcomb;
-    // the input starts at column 0 of record 0: an absolute zero column offset
-    GCarry P = gcomb(GCarry{0u, 0u, 0x80000000u, 0u}, carries_before(p, b, s_wg));  // (its barrier publishes sh)
+    // the count prefix of the range (the input starts at column 0 of record 0)
+    GCarry P = carries_before(p, b, s_wg);  // (its barrier publishes sh)
     if (b == 0) {  // the first INVALID byte: the smallest of the ranges' (stored by the carries kernel)
         const uint32_t i0 = 2 * threadIdx.x, i1 = i0 + 1;
         uint32_t e = i0 < p.num_ranges ? p.range_err[i0] : kNone;
@@ -984,7 +991,7 @@ __global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_e
         const uint32_t mine = sc.mine, first = sc.wave_excl.nf + sc.excl_nf;
         const uint32_t wfirst = sc.wave_excl.nf;
         const uint32_t wend = __builtin_amdgcn_readlane(first + mine, kWave - 1);
-        FieldRun fr{P.nr + sc.wave_excl.nr, col_op(P.col, sc.wave_excl.col) & 0x7fffffffu,
+        FieldRun fr{P.nr + sc.wave_excl.nr, col_after(P.col, sc.wave_excl.col, sc.wave_excl.nr),
                     (uint32_t)max(P.lt, sc.wave_excl.lt)};
         const uint32_t st_abs = st * (uint32_t)(2 * kFastTile);
         const uint32_t rel0 = c.abs - st_abs;
@@ -1022,13 +1029,13 @@ __global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_e
         const uint32_t final_field = p.hdr->last_rec ? 0u : 1u;
         if (final_field && P.nf < o.cap) {
             o.rec[P.nf] = P.nr;
-            o.col[P.nf] = P.col & 0x7fffffffu;
+            o.col[P.nf] = P.col;
             o.off[P.nf] = P.lt;
             o.len[P.nf] = p.n - P.lt;
         }
         if (final_field) {  // the final field ends the last record
-            cmin = min(cmin, (P.col & 0x7fffffffu) + 1u);
-            cmax = max(cmax, (P.col & 0x7fffffffu) + 1u);
+            cmin = min(cmin, P.col + 1u);
+            cmax = max(cmax, P.col + 1u);
         }
         p.hdr->n_fields = (uint64_t)P.nf + final_field;
         p.hdr->n_records = (uint64_t)P.nr + final_field;
@@ -1072,8 +1079,8 @@ __global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_e
 // is taken, never behind a wait, so waits do not feed back into later tiles.
 
 // Count-carry statuses. Aggregate (tile-local): nf | nr << 16 (a 32 KiB tile
-// has at most 2^15 of each), col (bit 31: absolute), lt. Inclusive prefix: nf,
-// nr, col, lt, all absolute.
+// has at most 2^15 of each), col (absolute when nr > 0), lt. Inclusive prefix:
+// nf, nr, col, lt, all absolute.
 __device__ __forceinline__ void publish_gagg(StatB& s, const GCarry& c, uint32_t epoch)
 {
     st_relaxed(&s.agg[0], ew(epoch, c.nf | (c.nr << 16)));
@@ -1158,7 +1165,7 @@ __device__ void pass2_ragged_chunk(const FastParams& p, const ChunkPos& c, uint3
 }
 
 constexpr int kFusedList = 1024;  // per-wave terminator list entries (LDS)
-constexpr int kFusedWavesPerSimd = 4;  // 3 resident workgroups per CU: the register budget the kernel is cut to
+constexpr int kFusedWavesPerSimd = 4;  // 2 resident workgroups per CU (8 waves each): the register budget the kernel is cut to
 
 template <int CB, bool V8>
 struct FusedShared {
@@ -1292,8 +1299,8 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
             T1 = T[0];
             RD1 = RD[0];
             if (tid == 0) {
-                if (t1 == 0)  // the input starts at column 0 of record 0
-                    publish_gincl(p.stat_carry[0], gcomb(GCarry{0u, 0u, 0x80000000u, 0u}, sc1.total), p.epoch);
+                if (t1 == 0)  // the input starts at column 0 of record 0: its prefix is the tile's carry
+                    publish_gincl(p.stat_carry[0], sc1.total, p.epoch);
                 else
                     publish_gagg(p.stat_carry[t1], sc1.total, p.epoch);
             }
@@ -1301,7 +1308,7 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
 
         // ---- phase 3 (tile t2): count prefix, fields
         if (t2 < num_tiles) {
-            GCarry P{0u, 0u, 0x80000000u, 0u};
+            GCarry P{0u, 0u, 0u, 0u};
             if (t2 != 0) {
                 P = lookback_pre<kFastWaves>(t2, zero, cpoll, gcomb, sh.pc, sh.first, &p.hdr->fault,
                                              look_first<kFastWaves>(t2, cpoll));
@@ -1313,7 +1320,7 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
             const uint32_t mine = sc2.mine, first = sc2.wave_excl.nf + sc2.excl_nf;
             const uint32_t wfirst = sc2.wave_excl.nf;
             const uint32_t wend = __builtin_amdgcn_readlane(first + mine, kWave - 1);
-            FieldRun fr{P.nr + sc2.wave_excl.nr, col_op(P.col, sc2.wave_excl.col) & 0x7fffffffu,
+            FieldRun fr{P.nr + sc2.wave_excl.nr, col_after(P.col, sc2.wave_excl.col, sc2.wave_excl.nr),
                         (uint32_t)max(P.lt, sc2.wave_excl.lt)};
             const uint32_t rel0 = (uint32_t)tid * (uint32_t)kFastChunk;
             for (uint32_t w0 = wfirst; w0 < wend; w0 += kFusedList) {
@@ -1342,13 +1349,13 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
                 const uint32_t final_field = sh.last_rec ? 0u : 1u;
                 if (final_field && I.nf < o.cap) {
                     o.rec[I.nf] = I.nr;
-                    o.col[I.nf] = I.col & 0x7fffffffu;
+                    o.col[I.nf] = I.col;
                     o.off[I.nf] = I.lt;
                     o.len[I.nf] = p.n - I.lt;
                 }
                 if (final_field) {  // the final field ends the last record
-                    cmin = min(cmin, (I.col & 0x7fffffffu) + 1u);
-                    cmax = max(cmax, (I.col & 0x7fffffffu) + 1u);
+                    cmin = min(cmin, I.col + 1u);
+                    cmax = max(cmax, I.col + 1u);
                 }
                 const uint32_t e = min(end2, 8u);
                 p.hdr->n_fields = (uint64_t)I.nf + final_field;

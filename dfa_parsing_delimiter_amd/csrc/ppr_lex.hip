@@ -160,7 +160,9 @@ __global__ void __launch_bounds__(kLexBlock) lex_kernel(LexParams p)
     __shared__ TokCarry s_prefix;
 
     const int tid = threadIdx.x;
-    if (tid == 0) s_tile = blockIdx.x;
+    // tiles in the order workgroups start (not blockIdx order): a tile only waits
+    // in its look-backs on tiles that running workgroups already hold
+    if (tid == 0) s_tile = atomicAdd(&p.hdr->tile_counter, 1u);
     if (tid < 256) s_col[tid] = p.col[tid];
     if (lds_final)
         for (uint32_t i = tid; i < p.k; i += kLexBlock) s_final[i] = p.final_[i];

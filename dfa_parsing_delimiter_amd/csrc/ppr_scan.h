@@ -22,6 +22,7 @@
 
 #include "ppr_device.h"
 #include "ppr_host.h"
+#include "ppr_walk.h"
 
 namespace ppr {
 
@@ -169,74 +170,89 @@ __device__ T block_reduce(const T& v, const T& ident, T* s_wave, const Comb& com
     return readlane_t(row_scan<NW>(lane_value<NW>(s_wave, ident), ident, comb), NW - 1);
 }
 
+// One round of a look-back at `base` (see walk_predecessors): lane l of wave w
+// looks at tile base - 64 w - (63 - l). first_raw(u, v) / repoll(u, v) give the
+// status of tile u (kFlagIncl: v = inclusive prefix through u, kFlagAgg: v = u's
+// aggregate, 0: not yet published). A wave only waits for the statuses it needs
+// (those between the nearest inclusive prefix and the tile); after kSpinLimit
+// polls (counted in `spins` over the whole walk) the missing ones count as empty
+// aggregates and a fault is recorded, so the kernel always finishes. Returns the
+// combination of the statuses used; found: one of them was an inclusive prefix.
+template <int NW, typename T, typename First, typename Repoll, typename Comb>
+__device__ __forceinline__ T lookback_round(int64_t base, const T& ident, const First& first_raw,
+                                            const Repoll& repoll, const Comb& comb, T* s_part, int* s_found,
+                                            uint32_t* fault, uint32_t& spins, bool& found)
+{
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    const int64_t u = base - (int64_t)(w * kWave + (kWave - 1 - lane));
+    const bool valid = u >= 0;
+    T v = ident;
+    uint32_t f = 0;
+    if (valid) f = first_raw(u, v);
+    const uint64_t vmask = __ballot(valid);
+    for (;;) {
+        const uint64_t ready = __ballot(f != 0);
+        const uint64_t inclm = __ballot(f == kFlagIncl);
+        // statuses needed: from the nearest inclusive prefix up to the tile
+        const uint64_t need = inclm ? vmask & (~0ull << (63 - __clzll((long long)inclm))) : vmask;
+        if ((ready & need) == need) break;
+        if (++spins > kSpinLimit) {
+            if (lane == 0) atomicOr(fault, 1u);
+            if (valid && f == 0) {
+                f = kFlagAgg;
+                v = ident;
+            }
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        if (valid && f == 0) f = repoll(u, v);
+    }
+    const uint64_t inclm = __ballot(f == kFlagIncl);
+    const int j = inclm ? 63 - __clzll((long long)inclm) : -1;
+    if (!(valid && lane >= j)) v = ident;
+    const T part = readlane_t(wave_scan(v, ident, comb), kWave - 1);
+    if (lane == 0) {
+        s_part[w] = part;
+        s_found[w] = j >= 0;
+    }
+    __syncthreads();
+    // wave i covers tiles base-64i-63 .. base-64i; the nearest wave holding an
+    // inclusive prefix ends the walk, and farther waves are not needed
+    int wi = NW;
+#pragma unroll
+    for (int i = NW - 1; i >= 0; --i)
+        if (s_found[i]) wi = i;
+    const int last = wi < NW ? wi : NW - 1;
+    T r = s_part[last];
+    for (int i = last - 1; i >= 0; --i) r = comb(r, s_part[i]);
+    __syncthreads();
+    found = wi < NW;
+    return r;
+}
+
 // Decoupled look-back; every thread of the workgroup calls it, tile > 0.
 // poll(u, out) returns kFlagIncl (out = inclusive prefix through tile u),
 // kFlagAgg (out = tile u's aggregate) or 0 (not yet published). Returns the
-// combination of all tiles before `tile`. Lane 63 of wave 0 reads the nearest
-// predecessor. Gives up after kSpinLimit polls per wave, recording a fault, so
-// the kernel always finishes.
+// combination of all tiles before `tile`. Bounded: see lookback_round and
+// walk_predecessors.
 template <int NW, typename T, typename Poll, typename Comb>
 __device__ T lookback(uint32_t tile, const T& ident, const Poll& poll, const Comb& comb, T* s_part, int* s_found,
                       uint32_t* fault)
 {
-    const int lane = lane_id(), w = threadIdx.x / kWave;
-    T acc = ident;
-    int64_t base = (int64_t)tile - 1;
     uint32_t spins = 0;
-    for (;;) {
-        const int64_t u = base - (int64_t)(w * kWave + (kWave - 1 - lane));
-        const bool valid = u >= 0;
-        T v = ident;
-        uint32_t f = 0;
-        if (valid) f = poll(u, v);
-        const uint64_t vmask = __ballot(valid);
-        for (;;) {
-            const uint64_t ready = __ballot(f != 0);
-            const uint64_t inclm = __ballot(f == kFlagIncl);
-            // statuses needed: from the nearest inclusive prefix up to the tile
-            const uint64_t need = inclm ? vmask & (~0ull << (63 - __clzll((long long)inclm))) : vmask;
-            if ((ready & need) == need) break;
-            if (++spins > kSpinLimit) {
-                if (lane == 0) atomicOr(fault, 1u);
-                if (valid && f == 0) {
-                    f = kFlagAgg;
-                    v = ident;
-                }
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-            if (valid && f == 0) f = poll(u, v);
-        }
-        const uint64_t inclm = __ballot(f == kFlagIncl);
-        const int j = inclm ? 63 - __clzll((long long)inclm) : -1;
-        if (!(valid && lane >= j)) v = ident;
-        const T part = readlane_t(wave_scan(v, ident, comb), kWave - 1);
-        if (lane == 0) {
-            s_part[w] = part;
-            s_found[w] = j >= 0;
-        }
-        __syncthreads();
-        // wave i covers tiles base-64i-63 .. base-64i; the nearest wave holding an
-        // inclusive prefix ends the walk, and farther waves are not needed
-        int wi = NW;
-#pragma unroll
-        for (int i = NW - 1; i >= 0; --i)
-            if (s_found[i]) wi = i;
-        const int last = wi < NW ? wi : NW - 1;
-        T r = s_part[last];
-        for (int i = last - 1; i >= 0; --i) r = comb(r, s_part[i]);
-        acc = comb(r, acc);
-        __syncthreads();
-        if (wi < NW) return acc;
-        base -= (int64_t)NW * kWave;
-    }
+    return walk_predecessors(
+        tile, ident, (int64_t)NW * kWave,
+        [&](int64_t base, bool& found) {
+            return lookback_round<NW>(base, ident, poll, poll, comb, s_part, s_found, fault, spins, found);
+        },
+        comb);
 }
 
 // Look-back whose first round of polls the caller issued earlier (look_first),
 // so that those loads travel while the caller does other work. A poller has
 // load(u) -> Raw (the status words of tile u, all loads issued at once) and
 // decode(raw, out) -> kFlagIncl / kFlagAgg / 0, as poll() above. Otherwise as
-// lookback(): every thread calls it, tile > 0, bounded by kSpinLimit.
+// lookback(): every thread calls it, tile > 0, bounded.
 template <int NW, typename P>
 __device__ __forceinline__ typename P::Raw look_first(uint32_t tile, const P& poller)
 {
@@ -249,54 +265,18 @@ template <int NW, typename T, typename P, typename Comb>
 __device__ T lookback_pre(uint32_t tile, const T& ident, const P& poller, const Comb& comb, T* s_part, int* s_found,
                           uint32_t* fault, const typename P::Raw& raw0)
 {
-    const int lane = lane_id(), w = threadIdx.x / kWave;
-    T acc = ident;
-    int64_t base = (int64_t)tile - 1;
     uint32_t spins = 0;
-    for (bool first_round = true;; first_round = false) {
-        const int64_t u = base - (int64_t)(w * kWave + (kWave - 1 - lane));
-        const bool valid = u >= 0;
-        T v = ident;
-        uint32_t f = 0;
-        if (valid) f = poller.decode(first_round ? raw0 : poller.load(u), v);
-        const uint64_t vmask = __ballot(valid);
-        for (;;) {
-            const uint64_t ready = __ballot(f != 0);
-            const uint64_t inclm = __ballot(f == kFlagIncl);
-            const uint64_t need = inclm ? vmask & (~0ull << (63 - __clzll((long long)inclm))) : vmask;
-            if ((ready & need) == need) break;
-            if (++spins > kSpinLimit) {
-                if (lane == 0) atomicOr(fault, 1u);
-                if (valid && f == 0) {
-                    f = kFlagAgg;
-                    v = ident;
-                }
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-            if (valid && f == 0) f = poller.decode(poller.load(u), v);
-        }
-        const uint64_t inclm = __ballot(f == kFlagIncl);
-        const int j = inclm ? 63 - __clzll((long long)inclm) : -1;
-        if (!(valid && lane >= j)) v = ident;
-        const T part = readlane_t(wave_scan(v, ident, comb), kWave - 1);
-        if (lane == 0) {
-            s_part[w] = part;
-            s_found[w] = j >= 0;
-        }
-        __syncthreads();
-        int wi = NW;
-#pragma unroll
-        for (int i = NW - 1; i >= 0; --i)
-            if (s_found[i]) wi = i;
-        const int last = wi < NW ? wi : NW - 1;
-        T r = s_part[last];
-        for (int i = last - 1; i >= 0; --i) r = comb(r, s_part[i]);
-        acc = comb(r, acc);
-        __syncthreads();
-        if (wi < NW) return acc;
-        base -= (int64_t)NW * kWave;
-    }
+    bool first_round = true;
+    auto repoll = [&](int64_t u, T& v) { return poller.decode(poller.load(u), v); };
+    return walk_predecessors(
+        tile, ident, (int64_t)NW * kWave,
+        [&](int64_t base, bool& found) {
+            const bool fr = first_round;
+            first_round = false;
+            auto first_raw = [&](int64_t u, T& v) { return fr ? poller.decode(raw0, v) : repoll(u, v); };
+            return lookback_round<NW>(base, ident, first_raw, repoll, comb, s_part, s_found, fault, spins, found);
+        },
+        comb);
 }
 
 }  // namespace ppr

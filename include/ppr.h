@@ -99,7 +99,7 @@ typedef struct ppr_parse_out {
     uint32_t end_state; /* out: DFA state after the last byte */
     uint32_t path;      /* out: the kernels that ran, a PPR_PATH_* value */
     /* out: the fewest and the most fields of any record (0 and 0 without records).
-     * [ParPaRaw Sec. 4, "Inferring or validating number of columns"]: the
+     * [ParPaRaw, "Inferring or validating number of columns"]: the
      * largest is the inferred number of columns; the records all conform to one
      * number of columns exactly when the two are equal. */
     uint32_t min_columns;
@@ -281,6 +281,25 @@ PPR_API int ppr_lex_build_tables(const int16_t* delta, const uint16_t* kind, uin
 
 /* Library version string. */
 PPR_API const char* ppr_version(void);
+
+/* ------------------------------------------------------------ diagnostics */
+
+/*
+ * Bandwidth probe (not part of the method): enqueues one kernel on `stream`
+ * that streams `bytes` (a multiple of 16 KiB) of device memory in 16-byte
+ * words, so that the caller can time the device's own read / write / copy rate
+ * with events and judge the kernels' traffic against it.
+ *   mode 0: read d_src; d_dst receives one 32-bit word per thread
+ *           (grid * 256 * 4 bytes), so the loads are not optimised away;
+ *   mode 1: write d_dst (d_src unused, may be NULL);
+ *   mode 2: copy d_src to d_dst (`bytes` each).
+ *   pattern 0: wave-contiguous words (one instruction covers 1 KiB);
+ *   pattern 1: 64 contiguous bytes per lane (the CSV codes kernel's layout).
+ *   grid: workgroups of 256 threads (a grid-stride loop covers the buffer).
+ * Pointers must be 16-byte aligned. PPR_EINVAL on bad arguments.
+ */
+PPR_API int ppr_bandwidth_probe(uint32_t mode, uint32_t pattern, const void* d_src, void* d_dst, uint64_t bytes,
+                                uint32_t grid, void* stream);
 
 #ifdef __cplusplus
 }

@@ -7,7 +7,7 @@ no code, header, table or helper with the GPU library, and it never imports it.
 * ``csv_parse``: one sequential DFA run over the whole input
   (csv_oracle.c; ParPaRaw, Sec. 3 and "validating format"), and the fewest and
   most fields of any record, counted from its per-field record indices
-  (ParPaRaw, Sec. 4, "Inferring or validating number of columns").
+  (ParPaRaw, "Inferring or validating number of columns").
 * ``lex_restart``: the restart lexer, one state variable over the bytes
   (lex_oracle.c; "Lexing on the GPU", "A lexer is a prefix scan").
 * ``lex_fold``: the sequential table-driven fold over initial/merge/final
@@ -37,10 +37,10 @@ _SRCS = [os.path.join(_HERE, "csv_oracle.c"), os.path.join(_HERE, "lex_oracle.c"
 
 
 def build(force: bool = True) -> str:
-    """Compile the oracle with plain gcc -O2."""
+    """Compile the oracle with plain gcc -O3."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.run(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", "-pthread", "-o", tmp]
+        subprocess.run(["gcc", "-O3", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", "-pthread", "-o", tmp]
                        + _SRCS, check=True)
         os.replace(tmp, _LIB)
     return _LIB

@@ -18,7 +18,7 @@
  *      counting its fields, records, column carry and first INVALID byte;
  *   4. one thread turns the counts into each slice's field index, record index,
  *      column and field start at its first byte (exclusive prefixes, the
- *      offsets of Fig. 4), and resolves the fields-per-record range as Sec. 4
+ *      offsets of Fig. 4), and resolves the fields-per-record range as the passage "Inferring or validating number of columns"
  *      ("Inferring or validating number of columns") describes: a slice counts
  *      the field delimiters before its first record delimiter (relative: the
  *      record began in an earlier slice) and the fewest and most fields of the

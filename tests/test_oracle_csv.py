@@ -59,7 +59,7 @@ def _columns_of(fields, n_records):
 
 def test_column_count_examples():
     """fields per record, worked by hand; the first is the pages' example of records with a varying number of
-    field delimiters (ParPaRaw, Sec. 4: "1,Apples" then "2")"""
+    field delimiters (ParPaRaw, "Inferring or validating number of columns": "1,Apples" then "2")"""
     t = W.table("T5")
     for text, want in ((b"1,Apples\n2\n", (1, 2)), (b"", (0, 0)), (b"a,b,c\nd,e,f", (3, 3)), (b"\n\n", (1, 1)),
                        (b'"x,y",z\n', (2, 2)), (b"a\nb,c,d\n,\n", (1, 3)), (b"a,b\nc", (1, 2))):
