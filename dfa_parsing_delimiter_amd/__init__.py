@@ -88,6 +88,9 @@ def _load():
         getattr(L, f).argtypes = [P, U64, ctypes.POINTER(Dfa), ctypes.c_char_p, ctypes.POINTER(ParseOut), P,
                                   ctypes.c_size_t, ctypes.POINTER(ParseOpts), P]
         getattr(L, f).restype = ctypes.c_int
+    L.ppr_parse_noalloc.argtypes = [P, U64, ctypes.POINTER(Dfa), ctypes.c_char_p, ctypes.POINTER(ParseOut),
+                                    ctypes.POINTER(ParseOpts), P]
+    L.ppr_parse_noalloc.restype = ctypes.c_int
     L.ppr_parse_results.argtypes = [P, U64, ctypes.POINTER(ParseOut), P]
     L.ppr_parse_results.restype = ctypes.c_int
     L.ppr_lex_fold_bytes.argtypes = [U32]

@@ -519,9 +519,16 @@ extern "C" size_t ppr_parse_workspace_bytes(uint64_t n, const ppr_parse_opts_t* 
     return (size_t)total;
 }
 
-extern "C" int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, const uint8_t class_map[256],
-                               const ppr_parse_out_t* out, void* d_ws, size_t ws_bytes, const ppr_parse_opts_t* opts,
-                               void* stream)
+namespace ppr {
+
+// Enqueues one parse. compact: the workspace is a fixed scratch buffer that
+// only holds the single-pass paths' statuses, so the streaming kernels (whose
+// intermediates take a quarter of the input) are never chosen; a
+// table-driven input then runs the fused kernel, whose workspace is the
+// header, the step tables and 72 bytes per 32 KiB tile.
+int parse_enqueue(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, const uint8_t class_map[256],
+                  const ppr_parse_out_t* out, void* d_ws, size_t ws_bytes, const ppr_parse_opts_t* opts, void* stream,
+                  bool compact)
 {
     int rc = validate_dfa(dfa, class_map);
     if (rc) return rc;
@@ -547,7 +554,10 @@ extern "C" int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa
         int cb = 0;
         bool v8 = false;
         if (prepare_fast(dfa, class_map, f, cb, v8)) {
-            const FastLayout fl = fast_layout(n);
+            const uint32_t path =
+                compact ? PPR_PATH_FUSED
+                        : want == PPR_PATH_STREAMING || want == PPR_PATH_FUSED ? want : auto_table_path(n);
+            const FastLayout fl = path == PPR_PATH_FUSED ? fused_layout(n) : fast_layout(n);
             if (ws_bytes < fl.total) return PPR_EWORKSPACE;
             f.in = d_bytes;
             f.n = (uint32_t)n;
@@ -568,7 +578,7 @@ extern "C" int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa
             f.stat_vec = (uint64_t*)(ws + fl.stat_vec);
             f.stat_carry = (StatB*)(ws + fl.stat_carry);
             f.epoch = next_epoch();
-            f.path = want == PPR_PATH_STREAMING || want == PPR_PATH_FUSED ? want : auto_table_path(n);
+            f.path = path;
             return launch_csv_fast(f, cb, v8, opts, s);
         }
     }
@@ -612,6 +622,15 @@ extern "C" int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa
     stage_event(opts, 2, s);
     if (hipGetLastError() != hipSuccess) return PPR_EHIP;
     return PPR_OK;
+}
+
+}  // namespace ppr
+
+extern "C" int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, const uint8_t class_map[256],
+                               const ppr_parse_out_t* out, void* d_ws, size_t ws_bytes, const ppr_parse_opts_t* opts,
+                               void* stream)
+{
+    return parse_enqueue(d_bytes, n, dfa, class_map, out, d_ws, ws_bytes, opts, stream, false);
 }
 
 extern "C" int ppr_parse_results(const void* d_ws, uint64_t n, ppr_parse_out_t* out, void* stream)

@@ -122,7 +122,7 @@ struct FastParams {
     uint64_t* tile_vec;    // per tile: state-transition vector (lo | hi << 32)
     uint64_t* range_vec;   // per range: composite of its tile vectors
     uint32_t* range_state; // per range: state code before its first byte
-    uint4* range_carry;    // per range: nf, nr, col (bit 31: absolute), lt
+    uint4* range_carry;    // per range: nf, nr, col (absolute when nr > 0), lt
     uint32_t* range_err;   // per range: its first INVALID byte (kNone: none)
     uint64_t* stat_vec;    // fused path: per tile, vector look-back status
     StatB* stat_carry;     // fused path: per tile, count-carry look-back status
@@ -160,7 +160,28 @@ inline FastLayout fast_layout(uint64_t n)
     return L;
 }
 
+// workspace of the fused path alone (header, step tables, look-back statuses;
+// the streaming kernels' arrays are left out: their offsets repeat the last one)
+inline FastLayout fused_layout(uint64_t n)
+{
+    FastLayout L;
+    L.tiles = (n + kFastTile - 1) / kFastTile;
+    L.tabs = 256;
+    L.stat_vec = align_up(L.tabs + kTabWords * 4, 256);
+    L.stat_carry = align_up(L.stat_vec + L.tiles * 8, 256);
+    L.total = align_up(L.stat_carry + L.tiles * sizeof(StatB), 256);
+    L.tile_vec = L.range_vec = L.range_state = L.range_carry = L.range_err = L.cvec_lo = L.cvec_hi = L.idx = L.total;
+    return L;
+}
+
 // Enqueue the fast path (CB symbol-code bits, V8: more than 4 tracked states).
 int launch_csv_fast(const FastParams& f, int cb, bool v8, const ppr_parse_opts_t* opts, hipStream_t s);
+
+// Enqueue one parse into the workspace d_ws (see ppr_parse_async); compact:
+// d_ws is a fixed scratch buffer, so only the single-pass paths (fused kernel
+// for table-driven inputs, else the generic kernel) are used.
+int parse_enqueue(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, const uint8_t class_map[256],
+                  const ppr_parse_out_t* out, void* d_ws, size_t ws_bytes, const ppr_parse_opts_t* opts, void* stream,
+                  bool compact);
 
 }  // namespace ppr

@@ -182,6 +182,28 @@ PPR_API int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t*
 /* Wait on `stream` and copy the scalars of the last ppr_parse_async on d_ws into out. */
 PPR_API int ppr_parse_results(const void* d_ws, uint64_t n, ppr_parse_out_t* out, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the parse of
+ * ppr_parse, blocking, with no workspace argument. Its workspace is a fixed
+ * array of PPR_NOALLOC_SCRATCH_BYTES in the library's own device memory (one
+ * per GPU, held until the process ends); the call allocates nothing. The
+ * caller still provides the input and the output arrays.
+ *   - The streaming kernels are never used (their workspace grows with n):
+ *     table-driven inputs run the fused kernel, others the generic kernel;
+ *     opts->path PPR_PATH_STREAMING is read as PPR_PATH_FUSED.
+ *   - PPR_ETOOBIG if the call's look-back statuses do not fit the scratch: never
+ *     for table-driven inputs up to 2^32 - 2^16 bytes; with the generic kernel,
+ *     above about 233,000 tiles of 1024 chunks of chunk_bytes.
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *     time on one GPU (other streams, other host threads) race and must not be
+ *     made. The first call on a GPU clears its scratch with a kernel on `stream`.
+ * Otherwise as ppr_parse (arguments, results, PPR_ECAPACITY).
+ */
+#define PPR_NOALLOC_SCRATCH_BYTES (16u << 20)
+PPR_API int ppr_parse_noalloc(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, const uint8_t class_map[256],
+                              ppr_parse_out_t* out, const ppr_parse_opts_t* opts, void* stream);
+
 /* ------------------------------------------------------------------ lexer */
 
 /*
