@@ -7,7 +7,10 @@ no code, header, table or helper with the GPU library, and it never imports it.
 * ``csv_parse``: one sequential DFA run over the whole input
   (csv_oracle.c; ParPaRaw, Sec. 3 and "validating format"), and the fewest and
   most fields of any record, counted from its per-field record indices
-  (ParPaRaw, "Inferring or validating number of columns").
+  (ParPaRaw, "Inferring or validating number of columns"); given an expected
+  number of columns, the records that do not have it: how many, and the first
+  (same passage, and the specialisations passage: rejecting records with an
+  inconsistent number of field delimiters).
 * ``lex_restart``: the restart lexer, one state variable over the bytes
   (lex_oracle.c; "Lexing on the GPU", "A lexer is a prefix scan").
 * ``lex_fold``: the sequential table-driven fold over initial/merge/final
@@ -102,9 +105,22 @@ def _columns(rec, n_records):
     return int(per_record.min()), int(per_record.max())
 
 
-def csv_parse(data, d: dict, start_state: int | None = None, cap: int | None = None) -> dict:
+def _conformance(rec, n_records, expected):
+    """records whose number of fields is not `expected` (0: no expectation):
+    how many, and the index of the first (-1: none)"""
+    if not expected or n_records == 0:
+        return 0, -1
+    per_record = np.bincount(rec.astype(np.int64), minlength=n_records)
+    bad = np.nonzero(per_record != expected)[0]
+    return int(bad.size), (int(bad[0]) if bad.size else -1)
+
+
+def csv_parse(data, d: dict, start_state: int | None = None, cap: int | None = None,
+              expected_columns: int = 0) -> dict:
     """Sequential parse of one input under DFA table d (workloads.dfa format).
-    Returns the four per-field arrays (uint32) and the scalars."""
+    Returns the four per-field arrays (uint32) and the scalars; with
+    expected_columns > 0 also bad_records / first_bad_record (records whose
+    number of fields differs from it)."""
     b = _as_u8(data)
     n = b.size
     nxt, tag, cm = _tables(d)
@@ -122,10 +138,11 @@ def csv_parse(data, d: dict, start_state: int | None = None, cap: int | None = N
     res = {key: v[:k] for key, v in out.items()}
     res.update(n_fields=k, n_records=int(nr.value), error_pos=int(err.value), end_state=int(es.value))
     res["min_columns"], res["max_columns"] = _columns(res["rec"], res["n_records"])
+    res["bad_records"], res["first_bad_record"] = _conformance(res["rec"], res["n_records"], expected_columns)
     return res
 
 
-def csv_parse_many(inputs, d: dict) -> list:
+def csv_parse_many(inputs, d: dict, expected_columns: int = 0) -> list:
     """Parse many independent inputs (each from the start state) in one call."""
     blobs = [bytes(x) for x in inputs]
     starts = np.zeros(len(blobs) + 1, dtype=np.uint64)
@@ -152,6 +169,7 @@ def csv_parse_many(inputs, d: dict) -> list:
         r = {key: v[lo:hi] for key, v in out.items()}
         r.update(n_fields=hi - lo, n_records=int(nr[j]), error_pos=int(err[j]), end_state=int(es[j]))
         r["min_columns"], r["max_columns"] = _columns(r["rec"], r["n_records"])
+        r["bad_records"], r["first_bad_record"] = _conformance(r["rec"], r["n_records"], expected_columns)
         res.append(r)
     return res
 

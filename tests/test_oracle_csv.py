@@ -67,6 +67,50 @@ def test_column_count_examples():
         assert (r["min_columns"], r["max_columns"]) == want, (text, r["min_columns"], r["max_columns"])
 
 
+def test_conformance_examples():
+    """records that do not have the expected number of fields, worked by hand (ParPaRaw, "Inferring or
+    validating number of columns", and the specialisations passage on rejecting records with an inconsistent
+    number of field delimiters): how many, and the first one's index"""
+    t = W.table("T5")
+    cases = (
+        (b"1,Apples\n2\n", 2, (1, 1)),   # the pages' example: the second record has one field
+        (b"1,Apples\n2\n", 1, (1, 0)),
+        (b"1,Apples\n2\n", 3, (2, 0)),
+        (b"", 3, (0, -1)),
+        (b"\n\n", 1, (0, -1)),           # an empty line is a record of one empty field
+        (b"\n\n", 2, (2, 0)),
+        (b"a,b\nc,d\ne", 2, (1, 2)),     # the unterminated final record
+        (b'"x,y",z\n"p\nq",r', 2, (0, -1)),
+        (b'"x,y",z\n"p\nq",r', 3, (2, 0)),
+        (b"a,b,c\nd,e\nf,g,h\n,,,\n", 3, (2, 1)),
+        (b"a,b\nc,d", 0, (0, -1)),         # no expectation
+    )
+    for text, expect, want in cases:
+        r = oracle.csv_parse(text, t, expected_columns=expect)
+        assert (r["bad_records"], r["first_bad_record"]) == want, (text, expect, r["bad_records"],
+                                                                   r["first_bad_record"])
+
+
+def _conformance_of(fields, n_records, expect):
+    per = {}
+    for f in fields:
+        per[f[0]] = per.get(f[0], 0) + 1
+    bad = [i for i in range(n_records) if per.get(i, 0) != expect]
+    return len(bad), (bad[0] if bad else -1)
+
+
+@pytest.mark.parametrize("name,alphabet,max_len,reader", [("T5", b',\n"a', 7, read_t5), ("T6", b'\t\n"#a', 6, read_t6)])
+def test_conformance_exhaustive_vs_recursive_descent(name, alphabet, max_len, reader):
+    """every input up to max_len bytes, expected counts 1 to 3: the independent reader's records"""
+    t = W.table(name)
+    inputs = list(_all_strings(alphabet, max_len))
+    for expect in (1, 2, 3):
+        got = oracle.csv_parse_many(inputs, t, expected_columns=expect)
+        for s, r in zip(inputs, got):
+            fields, nrec, err = reader(s)
+            assert (r["bad_records"], r["first_bad_record"]) == _conformance_of(fields, nrec, expect), (s, expect)
+
+
 @pytest.mark.parametrize("name,alphabet,max_len,reader", [
     ("T5", b',\n"a', 8, read_t5),
     ("T6", b'\t\n"#a', 7, read_t6),
@@ -239,6 +283,10 @@ def test_valid_quoted_matches_csv_module():
             ours.setdefault(rec, []).append(_unquote(b[off:off + ln]).decode())
         assert [ours[i] for i in range(r["n_records"])] == rows, text
         assert (r["min_columns"], r["max_columns"]) == (min(map(len, rows)), max(map(len, rows))), text
+        expect = len(rows[0])
+        rc = oracle.csv_parse(b, t, expected_columns=expect)
+        bad = [i for i, row in enumerate(rows) if len(row) != expect]
+        assert (rc["bad_records"], rc["first_bad_record"]) == (len(bad), bad[0] if bad else -1), text
         checked += 1
     assert checked > 1000
 

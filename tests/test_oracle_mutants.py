@@ -186,3 +186,46 @@ def test_unmutated_lex_source_passes_same_pins():
     with tempfile.TemporaryDirectory() as tmp:
         L = _compile("lex_oracle.c", ("int oracle_lex_fold(", "int oracle_lex_fold("), tmp)
         assert _lex_pins_pass(L)
+
+
+# Planted mistakes in the oracle's count of records that do not have the
+# expected number of fields (oracle._conformance): each must fail the
+# hand-worked or exhaustive pins of tests/test_oracle_csv.py.
+CONFORMANCE_MUTANTS = {
+    "count_fields_not_records": lambda rec, n, e: (int(np.count_nonzero(np.bincount(rec.astype(np.int64), minlength=n)
+                                                                         != e)) if e and n else 0,
+                                                    -1),
+    "first_off_by_one": lambda rec, n, e: _conf_with(rec, n, e, lambda bad: int(bad[0]) + 1),
+    "last_not_first": lambda rec, n, e: _conf_with(rec, n, e, lambda bad: int(bad[-1])),
+    "fewer_only": lambda rec, n, e: _conf_with(rec, n, e, None, cmp=lambda per: per < e),
+    "columns_not_fields": lambda rec, n, e: _conf_with(rec, n, e, None, shift=1),
+}
+
+
+def _conf_with(rec, n, e, first=None, cmp=None, shift=0):
+    if not e or n == 0:
+        return 0, -1
+    per = np.bincount(rec.astype(np.int64), minlength=n) - shift
+    bad = np.nonzero(cmp(per) if cmp else per != e)[0]
+    return int(bad.size), ((first or (lambda b: int(b[0])))(bad) if bad.size else -1)
+
+
+def _conformance_pins_pass():
+    from tests import test_oracle_csv as T
+    try:
+        T.test_conformance_examples()
+        T.test_conformance_exhaustive_vs_recursive_descent("T5", b',\n"a', 5, read_t5)
+    except AssertionError:
+        return False
+    return True
+
+
+@pytest.mark.parametrize("mutant", sorted(CONFORMANCE_MUTANTS))
+def test_conformance_mutant_is_caught(mutant, monkeypatch):
+    import oracle
+    monkeypatch.setattr(oracle, "_conformance", CONFORMANCE_MUTANTS[mutant])
+    assert not _conformance_pins_pass(), mutant
+
+
+def test_unmutated_conformance_passes_same_pins():
+    assert _conformance_pins_pass()
