@@ -52,12 +52,14 @@ class ParseOut(ctypes.Structure):
                 ("field_offsets", ctypes.c_void_p), ("field_lengths", ctypes.c_void_p),
                 ("cap_fields", ctypes.c_uint64), ("n_fields", ctypes.c_uint64), ("n_records", ctypes.c_uint64),
                 ("error_pos", ctypes.c_int64), ("end_state", ctypes.c_uint32), ("path", ctypes.c_uint32),
-                ("min_columns", ctypes.c_uint32), ("max_columns", ctypes.c_uint32)]
+                ("min_columns", ctypes.c_uint32), ("max_columns", ctypes.c_uint32),
+                ("bad_records", ctypes.c_uint64), ("first_bad_record", ctypes.c_int64)]
 
 
 class ParseOpts(ctypes.Structure):
     _fields_ = [("chunk_bytes", ctypes.c_uint32), ("n_stage_events", ctypes.c_uint32),
-                ("stage_events", ctypes.c_void_p), ("path", ctypes.c_uint32)]
+                ("stage_events", ctypes.c_void_p), ("path", ctypes.c_uint32),
+                ("expected_columns", ctypes.c_uint32)]
 
 
 class LexTablesC(ctypes.Structure):
@@ -139,10 +141,11 @@ def _stream_handle(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _opts(chunk_bytes, path=None):
+def _opts(chunk_bytes, path=None, expected_columns=0):
     o = ParseOpts()
     o.chunk_bytes = int(chunk_bytes or 0)
     o.path = int(path or 0)
+    o.expected_columns = int(expected_columns or 0)
     return o
 
 
@@ -152,6 +155,7 @@ def _opts_with_events(opts, events):
     o = ParseOpts()
     o.chunk_bytes = opts.chunk_bytes
     o.path = opts.path
+    o.expected_columns = opts.expected_columns
     if not events:
         return o, None
     handles = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
@@ -197,15 +201,17 @@ class ParseResult:
     path: int                    # the kernels that ran: a PPR_PATH_* value
     min_columns: int             # fewest / most fields of a record (0 / 0 without records): the inferred
     max_columns: int             # number of columns is max_columns; all records conform iff the two are equal
+    bad_records: int = 0         # with expected_columns: records with another number of fields,
+    first_bad_record: int = -1   # and the first of them (-1: none)
 
 
 class Parser:
     """Reusable workspace and output buffers for inputs of up to max_n bytes."""
 
     def __init__(self, table: dict, max_n: int, capacity: int | None = None, chunk_bytes: int | None = None,
-                 device=None, path: int | None = None):
+                 device=None, path: int | None = None, expected_columns: int = 0):
         self.dfa, self.class_map = make_dfa(table)
-        self.opts = _opts(chunk_bytes, path)
+        self.opts = _opts(chunk_bytes, path, expected_columns)
         self.device = torch.device("cuda") if device is None else torch.device(device)
         self.max_n = int(max_n)
         ws = lib.ppr_parse_workspace_bytes(self.max_n, ctypes.byref(self.opts))
@@ -267,18 +273,20 @@ class Parser:
             _check(rc, "ppr_parse")
             k = int(o.n_fields)
             return ParseResult(*[a[:k] for a in self.out_arrays], k, int(o.n_records), int(o.error_pos),
-                               int(o.end_state), int(o.path), int(o.min_columns), int(o.max_columns))
+                               int(o.end_state), int(o.path), int(o.min_columns), int(o.max_columns),
+                               int(o.bad_records), int(o.first_bad_record))
         raise PprError(PPR_ECAPACITY, "ppr_parse")
 
 
 def parse(data: torch.Tensor, table: dict, chunk_bytes: int | None = None, capacity: int | None = None,
-          stream=None, path: int | None = None) -> ParseResult:
+          stream=None, path: int | None = None, expected_columns: int = 0) -> ParseResult:
     """Parse one input (device uint8 tensor) with a DFA table; path: a
-    PPR_PATH_* value to ask for (None: the library's automatic choice)."""
+    PPR_PATH_* value to ask for (None: the library's automatic choice);
+    expected_columns > 0: count the records with another number of fields."""
     _check_input(data)
     n = data.numel()
     cap = capacity if capacity is not None else min(n + 1, max(4096, n // 4))
-    return Parser(table, n, cap, chunk_bytes, data.device, path)(data, stream)
+    return Parser(table, n, cap, chunk_bytes, data.device, path, expected_columns)(data, stream)
 
 
 # ------------------------------------------------------------------ lexer

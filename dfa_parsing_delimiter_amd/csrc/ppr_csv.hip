@@ -35,6 +35,7 @@ struct LookCtx {
     uint64_t* statA;
     StatB* statB;
     uint32_t epoch;
+    uint32_t expect_cols;  // expected fields per record (0: none)
 };
 
 // Publish a tile's carry. The aggregate holds tile-local counts (a tile has at
@@ -106,7 +107,7 @@ struct TileShared {
     Carry prefix;
     uint32_t state;
     uint32_t last_rec;
-    uint32_t cols[2][NW];
+    uint32_t cols[4 * NW];
 };
 
 // Tile start state from the block's vector scan: tile 0 starts in the DFA's
@@ -186,7 +187,7 @@ __device__ void finish_tile(const LookCtx& c, const OutArrays& o, uint32_t n, ui
         uint64_t fi = base.nf;
         uint32_t rec = base.nr, col = base.colv, off = base.lt;
         uint64_t bits = T;
-        uint32_t cmin = 0xffffffffu, cmax = 0;  // fields per record, over the records this chunk's fields end
+        RecStats st = rec_stats_none();  // fields per record, over the records this chunk's fields end
         while (bits) {
             const uint32_t j = (uint32_t)__ffsll((unsigned long long)bits) - 1u;
             const uint32_t pos = chunk_abs + j;
@@ -199,8 +200,7 @@ __device__ void finish_tile(const LookCtx& c, const OutArrays& o, uint32_t n, ui
             ++fi;
             off = pos + 1;
             if ((RD >> j) & 1u) {
-                cmin = min(cmin, col + 1u);
-                cmax = max(cmax, col + 1u);
+                note_record(st, col + 1u, rec, c.expect_cols);
                 ++rec;
                 col = 0;
             } else {
@@ -210,24 +210,11 @@ __device__ void finish_tile(const LookCtx& c, const OutArrays& o, uint32_t n, ui
         }
         if (tile == num_tiles - 1 && tid == 0 && !sh->last_rec) {  // the final field ends the last record
             const Carry I = carry_op(P, ctot);
-            cmin = min(cmin, I.colv + 1u);
-            cmax = max(cmax, I.colv + 1u);
+            note_record(st, I.colv + 1u, I.nr, c.expect_cols);
         }
-        // the tile's fewest and most fields per record, into the call's
-        wave_min_max(cmin, cmax);
-        const int w = tid / kWave;
-        if (lane_id() == 0) {
-            sh->cols[0][w] = cmin;
-            sh->cols[1][w] = cmax;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            for (int i = 1; i < NW; ++i) {
-                cmin = min(cmin, sh->cols[0][i]);
-                cmax = max(cmax, sh->cols[1][i]);
-            }
-            widen_range(&c.hdr->cols_min, &c.hdr->cols_max, cmin, cmax);
-        }
+        // the tile's per-record counts, into the call's
+        publish_rec_stats<NW>(st.cmin, st.cmax, st.bad, st.fbad, sh->cols, &c.hdr->cols_min, &c.hdr->cols_max,
+                              &c.hdr->bad_records, &c.hdr->first_bad);
     }
 
     if (tile == num_tiles - 1 && tid == 0) {
@@ -256,6 +243,8 @@ __global__ void csv_reset_kernel(WsHeader* hdr, uint32_t n, uint32_t start_state
         hdr->path = PPR_PATH_SINGLE_PASS;
         hdr->cols_min = 0xffffffffu;
         hdr->cols_max = 0;
+        hdr->bad_records = 0;
+        hdr->first_bad = 0xffffffffu;
         if (n == 0) {  // nothing to parse: the results of an empty input
             hdr->n_fields = 0;
             hdr->n_records = 0;
@@ -547,6 +536,7 @@ int parse_enqueue(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, cons
 
     const uint32_t want = opts ? opts->path : 0u;
     if (want > PPR_PATH_FUSED) return PPR_EINVAL;
+    const uint32_t expect = opts ? opts->expected_columns : 0u;
     // table-driven paths: 64-byte chunks, 16-byte aligned input, a table they can encode
     if (n && want != PPR_PATH_SINGLE_PASS && L == (uint32_t)kFastChunk && ((uintptr_t)d_bytes & 15u) == 0) {
         FastParams f;
@@ -579,6 +569,7 @@ int parse_enqueue(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, cons
             f.stat_carry = (StatB*)(ws + fl.stat_carry);
             f.epoch = next_epoch();
             f.path = path;
+            f.expect_cols = expect;
             return launch_csv_fast(f, cb, v8, opts, s);
         }
     }
@@ -590,7 +581,7 @@ int parse_enqueue(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, cons
     stage_event(opts, 1, s);
     if (hipGetLastError() != hipSuccess) return PPR_EHIP;
     if (n == 0) return PPR_OK;
-    LookCtx lc{hdr, (uint64_t*)(ws + lay.off_a), (StatB*)(ws + lay.off_b), next_epoch()};
+    LookCtx lc{hdr, (uint64_t*)(ws + lay.off_a), (StatB*)(ws + lay.off_b), next_epoch(), expect};
 
     CsvParams p;
     memset(&p, 0, sizeof p);
@@ -649,6 +640,8 @@ extern "C" int ppr_parse_results(const void* d_ws, uint64_t n, ppr_parse_out_t* 
     out->path = h.path;
     out->min_columns = h.cols_min != 0xffffffffu ? h.cols_min : 0u;
     out->max_columns = h.cols_max;
+    out->bad_records = h.bad_records;
+    out->first_bad_record = h.first_bad != 0xffffffffu ? (int64_t)h.first_bad : (int64_t)-1;
     if (h.fault) return PPR_EHIP;
     return out->n_fields > out->cap_fields ? PPR_ECAPACITY : PPR_OK;
 }

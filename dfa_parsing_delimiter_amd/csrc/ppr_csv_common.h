@@ -89,6 +89,26 @@ __device__ __forceinline__ Vec vunpack(uint32_t p)
     return v;
 }
 
+// Fields per record, over the records whose last field a lane writes
+// [ParPaRaw, "Inferring or validating number of columns"]: the fewest and the
+// most, and, given an expected number (expect > 0), how many records have
+// another number and the index of the first of them.
+struct RecStats {
+    uint32_t cmin, cmax, bad, fbad;
+};
+
+__device__ __forceinline__ RecStats rec_stats_none() { return {kNone, 0u, 0u, kNone}; }
+
+// record `rec` ends with this field and has `fields` fields
+__device__ __forceinline__ void note_record(RecStats& st, uint32_t fields, uint32_t rec, uint32_t expect)
+{
+    st.cmin = min(st.cmin, fields);
+    st.cmax = max(st.cmax, fields);
+    const bool bad = expect != 0u && fields != expect;
+    st.bad += bad ? 1u : 0u;
+    st.fbad = bad ? min(st.fbad, rec) : st.fbad;
+}
+
 struct OutArrays {
     uint32_t* rec;
     uint32_t* col;
@@ -128,6 +148,7 @@ struct FastParams {
     StatB* stat_carry;     // fused path: per tile, count-carry look-back status
     uint32_t epoch;        // fused path: call epoch carried by the status words
     uint32_t path;         // PPR_PATH_* the call runs
+    uint32_t expect_cols;  // expected fields per record (0: none)
     uint8_t state_of[16];  // DFA state of each code (index 8: absorbing)
     uint8_t nxt[9][16];    // [state code, row nt = absorbing][symbol code] -> next code
     uint8_t tag[9][16];

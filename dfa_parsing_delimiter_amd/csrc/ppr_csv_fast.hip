@@ -457,6 +457,8 @@ __device__ __forceinline__ void reset_header(const FastParams& p)
     p.hdr->path = p.path;
     p.hdr->cols_min = kNone;
     p.hdr->cols_max = 0;
+    p.hdr->bad_records = 0;
+    p.hdr->first_bad = kNone;
 }
 
 // Pass-1 table: entry e (the codes of G bytes) -> composite vector from every
@@ -892,11 +894,11 @@ struct FieldRun {
 // written through wave-uniform base pointers, so every store is one scalar
 // base plus the lane's offset. Only the window's first `slots` fields are
 // written (those below the capacity); rel: the round's offset in the window.
-// lt_mask: the lanes below this one. A lane whose field ends a record counts
-// that record's fields (its column + 1) into its running cmin / cmax.
+// lt_mask: the lanes below this one. A lane whose field ends a record notes
+// that record's fields (its column + 1) in its running record counts.
 __device__ __forceinline__ void field_round(const OutArrays& o, uint32_t g0, uint32_t rel, uint32_t slots,
                                             uint32_t cnt, uint32_t e, uint32_t base, uint32_t lane, uint64_t lt_mask,
-                                            FieldRun& fr, uint32_t& cmin, uint32_t& cmax)
+                                            FieldRun& fr, RecStats& st, uint32_t expect)
 {
     const uint32_t pos = base + (e >> 1);
     const uint64_t m = __ballot(lane < cnt && (e & 1u));
@@ -907,8 +909,7 @@ __device__ __forceinline__ void field_round(const OutArrays& o, uint32_t g0, uin
     const uint32_t prev = dpp_t<0x138, 0xf>(0u, pos);  // wave_shr:1: the previous lane's terminator
     const uint32_t off = lane ? prev + 1u : fr.off;
     const bool ends_record = (m >> lane) & 1ull;
-    cmin = ends_record ? min(cmin, col + 1u) : cmin;
-    cmax = ends_record ? max(cmax, col + 1u) : cmax;
+    if (ends_record) note_record(st, col + 1u, rec, expect);
     g0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)g0);  // (wave-uniform: the store addresses stay scalar)
     if (rel + lane < slots) {
         store_u32(o.rec + g0, lane, rec);
@@ -947,12 +948,12 @@ __global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_e
     __shared__ GCarry s_wg[kFastWaves];
     __shared__ uint32_t s_list[kFastWaves][kWaveList<CB>];
     __shared__ uint32_t s_err[kFastWaves];
-    __shared__ uint32_t s_cols[2][kFastWaves];
+    __shared__ uint32_t s_cols[4 * kFastWaves];
 
     const uint32_t lane = (uint32_t)lane_id();
     const uint32_t wv = threadIdx.x / kWave;
     const uint32_t b = blockIdx.x;
-    uint32_t cmin = kNone, cmax = 0;  // fields per record, over the records this lane's fields end
+    RecStats rs = rec_stats_none();  // fields per record, over the records this lane's fields end
     uint32_t s0, s1;
     range_of(p, b, s0, s1);
     const Vec ident = fast_ident<V8>(p.nt);
@@ -1013,7 +1014,7 @@ __global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_e
             for (uint32_t r = w0; r < w1; r += kWave) {
                 const uint32_t cnt = min((uint32_t)kWave, w1 - r);
                 field_round(o, P.nf + r, r - w0, slots, cnt, list[r - w0 + min(lane, cnt - 1u)], st_abs, lane, lt_mask,
-                            fr, cmin, cmax);
+                            fr, rs, p.expect_cols);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -1033,27 +1034,13 @@ __global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_e
             o.off[P.nf] = P.lt;
             o.len[P.nf] = p.n - P.lt;
         }
-        if (final_field) {  // the final field ends the last record
-            cmin = min(cmin, P.col + 1u);
-            cmax = max(cmax, P.col + 1u);
-        }
+        if (final_field) note_record(rs, P.col + 1u, P.nr, p.expect_cols);  // the final field ends the last record
         p.hdr->n_fields = (uint64_t)P.nf + final_field;
         p.hdr->n_records = (uint64_t)P.nr + final_field;
     }
-    // the range's fewest and most fields per record, into the call's
-    wave_min_max(cmin, cmax);
-    if (lane == 0) {
-        s_cols[0][wv] = cmin;
-        s_cols[1][wv] = cmax;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int i = 1; i < kFastWaves; ++i) {
-            cmin = min(cmin, s_cols[0][i]);
-            cmax = max(cmax, s_cols[1][i]);
-        }
-        widen_range(&p.hdr->cols_min, &p.hdr->cols_max, cmin, cmax);
-    }
+    // the range's per-record counts, into the call's
+    publish_rec_stats<kFastWaves>(rs.cmin, rs.cmax, rs.bad, rs.fbad, s_cols, &p.hdr->cols_min, &p.hdr->cols_max,
+                                  &p.hdr->bad_records, &p.hdr->first_bad);
 }
 
 // ================================================================ fused single pass
@@ -1177,7 +1164,7 @@ struct FusedShared {
     GCarry pc[kFastWaves];
     int first[kFastWaves];
     uint32_t next, state, last_rec;
-    uint32_t cols[2][kFastWaves];
+    uint32_t cols[4 * kFastWaves];
     uint32_t list[kFastWaves][kFusedList];
 };
 
@@ -1195,7 +1182,7 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
     const OutArrays& o = p.out;
     const uint64_t lt_mask = (1ull << lane) - 1ull;
     const GCarryComb gcomb;
-    uint32_t cmin = kNone, cmax = 0;  // fields per record, over the records this lane's fields end
+    RecStats rs = rec_stats_none();  // fields per record, over the records this lane's fields end
     const GCarry zero{0u, 0u, 0u, 0u};
     if (tid == 0) {
         sh.next = atomicAdd(&p.hdr->tile_counter, 1u);
@@ -1337,7 +1324,7 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
                 for (uint32_t r = w0; r < w1; r += kWave) {
                     const uint32_t cnt = min((uint32_t)kWave, w1 - r);
                     field_round(o, P.nf + r, r - w0, slots, cnt, list[r - w0 + min(lane, cnt - 1u)], tile_start,
-                                lane, lt_mask, fr, cmin, cmax);
+                                lane, lt_mask, fr, rs, p.expect_cols);
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
@@ -1353,10 +1340,7 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
                     o.off[I.nf] = I.lt;
                     o.len[I.nf] = p.n - I.lt;
                 }
-                if (final_field) {  // the final field ends the last record
-                    cmin = min(cmin, I.col + 1u);
-                    cmax = max(cmax, I.col + 1u);
-                }
+                if (final_field) note_record(rs, I.col + 1u, I.nr, p.expect_cols);  // the final field ends the last record
                 const uint32_t e = min(end2, 8u);
                 p.hdr->n_fields = (uint64_t)I.nf + final_field;
                 p.hdr->n_records = (uint64_t)I.nr + final_field;
@@ -1380,20 +1364,9 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
         if (t0 < num_tiles) load_chunk(t0, w);
         __syncthreads();  // sh.next and the scan scratch are rewritten next round
     }
-    // the workgroup's fewest and most fields per record, into the call's
-    wave_min_max(cmin, cmax);
-    if (lane == 0) {
-        sh.cols[0][wv] = cmin;
-        sh.cols[1][wv] = cmax;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        for (int i = 1; i < kFastWaves; ++i) {
-            cmin = min(cmin, sh.cols[0][i]);
-            cmax = max(cmax, sh.cols[1][i]);
-        }
-        widen_range(&p.hdr->cols_min, &p.hdr->cols_max, cmin, cmax);
-    }
+    // the workgroup's per-record counts, into the call's
+    publish_rec_stats<kFastWaves>(rs.cmin, rs.cmax, rs.bad, rs.fbad, sh.cols, &p.hdr->cols_min, &p.hdr->cols_max,
+                                  &p.hdr->bad_records, &p.hdr->first_bad);
 }
 
 // workgroups of the codes kernel (all resident at once: 4 per CU)

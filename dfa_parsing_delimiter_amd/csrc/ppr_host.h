@@ -26,6 +26,8 @@ struct WsHeader {
     uint32_t path;      // which kernels ran (PPR_PATH_*)
     uint32_t cols_min;  // fewest fields of a record (atomic minimum), 0xffffffff: no record yet
     uint32_t cols_max;  // most fields of a record (atomic maximum)
+    uint32_t bad_records;  // records whose number of fields is not the expected one (atomic sum)
+    uint32_t first_bad;    // the first of them (atomic minimum), 0xffffffff: none
 };
 
 // Records stage event i of the call on the stream, if the caller asked for it.

@@ -92,6 +92,43 @@ __device__ __forceinline__ void widen_range(uint32_t* dmin, uint32_t* dmax, uint
     if (mx > __hip_atomic_load(dmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(dmax, mx);
 }
 
+struct AddU32 {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+
+// The workgroup's per-record counts (fewest / most fields, records not of the
+// expected number, the first of them) into the call's, held at dmin, dmax, dbad
+// and dfirst. Every thread calls it; s_stats holds 4 x NW words.
+template <int NW>
+__device__ __forceinline__ void publish_rec_stats(uint32_t cmin, uint32_t cmax, uint32_t bad, uint32_t fbad,
+                                                  uint32_t* s_stats, uint32_t* dmin, uint32_t* dmax, uint32_t* dbad,
+                                                  uint32_t* dfirst)
+{
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    cmin = readlane_t(wave_scan(cmin, 0xffffffffu, MinU32{}), kWave - 1);
+    cmax = readlane_t(wave_scan(cmax, 0u, MaxU32{}), kWave - 1);
+    bad = readlane_t(wave_scan(bad, 0u, AddU32{}), kWave - 1);
+    fbad = readlane_t(wave_scan(fbad, 0xffffffffu, MinU32{}), kWave - 1);
+    if (lane == 0) {
+        s_stats[w] = cmin;
+        s_stats[NW + w] = cmax;
+        s_stats[2 * NW + w] = bad;
+        s_stats[3 * NW + w] = fbad;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int i = 1; i < NW; ++i) {
+            cmin = min(cmin, s_stats[i]);
+            cmax = max(cmax, s_stats[NW + i]);
+            bad += s_stats[2 * NW + i];
+            fbad = min(fbad, s_stats[3 * NW + i]);
+        }
+        widen_range(dmin, dmax, cmin, cmax);
+        if (bad) atomicAdd(dbad, bad);
+        if (fbad < __hip_atomic_load(dfirst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMin(dfirst, fbad);
+    }
+}
+
 // value of the previous lane (lane 0: id)
 template <typename T>
 __device__ __forceinline__ T wave_shr1(const T& id, const T& x)

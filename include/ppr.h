@@ -104,6 +104,14 @@ typedef struct ppr_parse_out {
      * number of columns exactly when the two are equal. */
     uint32_t min_columns;
     uint32_t max_columns;
+    /* out, with opts->expected_columns > 0 (else 0 and -1): the records whose
+     * number of fields is not expected_columns, how many and the index of the
+     * first (-1: none). [ParPaRaw, "Inferring or validating number of columns",
+     * and the specialisations passage: rejecting records that have an
+     * inconsistent number of field delimiters.] Their fields are still written;
+     * a caller that rejects them drops the fields of those records. */
+    uint64_t bad_records;
+    int64_t first_bad_record;
 } ppr_parse_out_t;
 
 /*
@@ -154,6 +162,7 @@ typedef struct ppr_parse_opts {
     uint32_t n_stage_events;
     void* const* stage_events;
     uint32_t path;
+    uint32_t expected_columns; /* 0: none; else records are checked against it (ppr_parse_out_t.bad_records) */
 } ppr_parse_opts_t;
 
 /*

@@ -54,6 +54,8 @@ def _same(g, r, what=""):
     assert g.end_state == r["end_state"], (what, g.end_state, r["end_state"])
     assert (g.min_columns, g.max_columns) == (r["min_columns"], r["max_columns"]), (
         what, g.min_columns, g.max_columns, r["min_columns"], r["max_columns"])
+    assert (g.bad_records, g.first_bad_record) == (r["bad_records"], r["first_bad_record"]), (
+        what, g.bad_records, g.first_bad_record, r["bad_records"], r["first_bad_record"])
     for name, key in (("record_idx", "rec"), ("column_ids", "col"), ("field_offsets", "off"),
                       ("field_lengths", "len")):
         a = _np(getattr(g, name))
@@ -127,9 +129,11 @@ def test_workloads_several_tiles_ragged(ppr, cfg, chunk, path):
     t = W.table(W.CONFIGS[cfg]["table"])
     n = (3 << 20) + 12345
     b = W.generate(cfg, n=n, seed=77 + cfg)
+    # checked against the workload's number of columns: comment lines and the unterminated final record differ
+    expect = W.CONFIGS[cfg]["n_cols"]
     _say("workload", cfg, chunk, path, n)
-    g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=n + 1, path=path)
-    _same(g, oracle.csv_parse(b, t), (cfg, chunk, path))
+    g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=n + 1, path=path, expected_columns=expect)
+    _same(g, oracle.csv_parse(b, t, expected_columns=expect), (cfg, chunk, path))
 
 
 def _random_table(rng, absorbing, n_special):
@@ -219,13 +223,17 @@ def test_column_counts_at_scale(ppr):
     wide = b"\n".join(recs)  # no trailing newline: the final record is unterminated
     conform = b"\n".join(b",".join(b"%d" % (i * 7 + j) for j in range(7)) for i in range(200000)) + b"\n"
     for what, b in (("varied", wide), ("conforming", conform)):
-        r = oracle.csv_parse(b, t)
-        assert (what != "varied") or (r["min_columns"], r["max_columns"]) == (1, 40)
-        assert (what != "conforming") or (r["min_columns"], r["max_columns"]) == (7, 7)
-        for chunk, path in ((None, None), (64, STREAMING), (64, FUSED), (31, None)):
-            _say("columns", what, len(b), chunk, path)
-            g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=r["n_fields"] + 1, path=path)
-            _same(g, r, (what, chunk, path))
+        for expect in (0, 7, 40):
+            r = oracle.csv_parse(b, t, expected_columns=expect)
+            assert (what != "varied") or (r["min_columns"], r["max_columns"]) == (1, 40)
+            assert (what != "conforming") or (r["min_columns"], r["max_columns"]) == (7, 7)
+            assert (what != "conforming" or expect != 7) or r["bad_records"] == 0
+            assert (what != "varied" or expect != 40) or r["first_bad_record"] == 0
+            for chunk, path in ((None, None), (64, STREAMING), (64, FUSED), (31, None)):
+                _say("columns", what, len(b), expect, chunk, path)
+                g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=r["n_fields"] + 1, path=path,
+                              expected_columns=expect)
+                _same(g, r, (what, expect, chunk, path))
 
 
 def test_invalid_bytes_at_scale(ppr):
