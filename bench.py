@@ -182,6 +182,36 @@ def bandwidth_ceilings(ppr, torch, dev, nbytes=1 << 30, iters=10):
     return out
 
 
+def stream_bench(args, cfg_id, cfg, ppr, torch, W, np):
+    """host-to-host GB/s of ppr_parse_stream: the input in pinned host memory, the
+    per-field results returned into pinned host arrays (64-bit offsets and
+    lengths); wall clock around each call, median of the timed calls"""
+    assert cfg["kind"] == "csv", "streaming covers the delimiter-separated parse"
+    log("generating", cfg["name"], cfg["n"], "bytes")
+    data = W.generate(cfg_id)
+    host = torch.empty(data.size, dtype=torch.uint8, pin_memory=True)
+    host.numpy()[:] = data
+    table = W.table(cfg["table"])
+    pb = args.stream << 20
+    first = ppr.parse_stream(host, table, pb)
+    for _ in range(args.warmup):
+        ppr.parse_stream(host, table, pb, capacity=first.n_fields)
+    times = []
+    for _ in range(args.steps):
+        t0 = time.perf_counter()
+        g = ppr.parse_stream(host, table, pb, capacity=first.n_fields)
+        times.append(time.perf_counter() - t0)
+    assert g.n_fields == first.n_fields
+    ms = statistics.median(times) * 1e3
+    print(json.dumps({"metric": "host-to-host GB/s parsed with overlapped transfers (ppr_parse_stream)",
+                      "value": round(data.size / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "ms_per_call": round(ms, 3),
+                      "steps": args.steps, "warmup": args.warmup, "partition_bytes": pb,
+                      "partitions": g.partitions, "fields": g.n_fields,
+                      "config": {"workload": "%s_%dMiB" % (cfg["name"], data.size >> 20), "n_bytes": data.size},
+                      "timing": "host wall clock around each blocking call (allocation of the driver's device "
+                                "buffers included), median"}), flush=True)
+
+
 def read_pmc(d, counter):
     """counter value of every dispatch, by kernel name, from a rocprofv3 csv output directory"""
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -273,6 +303,9 @@ def main():
     ap.add_argument("--path", choices=["auto", "fused", "streaming", "single-pass"], default="auto",
                     help="parse kernels to ask the library for (default: its automatic choice)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline and the full-size parity check")
+    ap.add_argument("--stream", type=int, default=0, metavar="PARTITION_MIB",
+                    help="instead: time ppr_parse_stream over the workload in pinned HOST memory, partitions of this "
+                         "many MiB (transfers, parse and returns overlapped; PCIe-inclusive, not the metric)")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the device bandwidth probe (read / write / copy of 1 GiB)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -299,6 +332,8 @@ def main():
     cfg = W.CONFIGS[cfg_id]
     kind = "csv" if cfg["kind"] == "csv" else "lex"
     dev = torch.device("cuda:0")
+    if args.stream:
+        return stream_bench(args, cfg_id, cfg, ppr, torch, W, np)
     log("generating", cfg["name"], cfg["n"], "bytes")
     t0 = time.time()
     data = W.generate(cfg_id)

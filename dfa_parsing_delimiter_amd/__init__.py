@@ -31,6 +31,7 @@ LIB_PATH = os.environ.get("PPR_LIB_PATH") or os.path.join(_HERE, "libppr.so")
 
 PPR_OK, PPR_EINVAL, PPR_ECAPACITY, PPR_ETOOBIG, PPR_EHIP, PPR_EWORKSPACE = 0, -1, -2, -3, -4, -5
 PPR_PATH_STREAMING, PPR_PATH_SINGLE_PASS, PPR_PATH_FUSED = 1, 2, 3
+PPR_PARSE_CONTINUE, PPR_PARSE_PARTIAL = 1, 2
 _ERRNAMES = {-1: "PPR_EINVAL", -2: "PPR_ECAPACITY", -3: "PPR_ETOOBIG", -4: "PPR_EHIP", -5: "PPR_EWORKSPACE"}
 TAG_VALUE, TAG_FIELD, TAG_RECORD, TAG_INVALID = 0, 1, 2, 3
 
@@ -53,13 +54,23 @@ class ParseOut(ctypes.Structure):
                 ("cap_fields", ctypes.c_uint64), ("n_fields", ctypes.c_uint64), ("n_records", ctypes.c_uint64),
                 ("error_pos", ctypes.c_int64), ("end_state", ctypes.c_uint32), ("path", ctypes.c_uint32),
                 ("min_columns", ctypes.c_uint32), ("max_columns", ctypes.c_uint32),
-                ("bad_records", ctypes.c_uint64), ("first_bad_record", ctypes.c_int64)]
+                ("bad_records", ctypes.c_uint64), ("first_bad_record", ctypes.c_int64),
+                ("tail_start", ctypes.c_uint32), ("tail_column", ctypes.c_uint32)]
 
 
 class ParseOpts(ctypes.Structure):
     _fields_ = [("chunk_bytes", ctypes.c_uint32), ("n_stage_events", ctypes.c_uint32),
                 ("stage_events", ctypes.c_void_p), ("path", ctypes.c_uint32),
-                ("expected_columns", ctypes.c_uint32)]
+                ("expected_columns", ctypes.c_uint32), ("flags", ctypes.c_uint32), ("start_state", ctypes.c_uint32),
+                ("start_column", ctypes.c_uint32)]
+
+
+class StreamOut(ctypes.Structure):
+    _fields_ = [("record_idx", ctypes.c_void_p), ("column_ids", ctypes.c_void_p), ("field_offsets", ctypes.c_void_p),
+                ("field_lengths", ctypes.c_void_p), ("cap_fields", ctypes.c_uint64), ("n_fields", ctypes.c_uint64),
+                ("n_records", ctypes.c_uint64), ("error_pos", ctypes.c_int64), ("end_state", ctypes.c_uint32),
+                ("min_columns", ctypes.c_uint32), ("max_columns", ctypes.c_uint32), ("partitions", ctypes.c_uint32),
+                ("bad_records", ctypes.c_uint64), ("first_bad_record", ctypes.c_int64)]
 
 
 class LexTablesC(ctypes.Structure):
@@ -93,6 +104,9 @@ def _load():
     L.ppr_parse_noalloc.argtypes = [P, U64, ctypes.POINTER(Dfa), ctypes.c_char_p, ctypes.POINTER(ParseOut),
                                     ctypes.POINTER(ParseOpts), P]
     L.ppr_parse_noalloc.restype = ctypes.c_int
+    L.ppr_parse_stream.argtypes = [P, U64, ctypes.POINTER(Dfa), ctypes.c_char_p, ctypes.POINTER(StreamOut), U64,
+                                   ctypes.POINTER(ParseOpts)]
+    L.ppr_parse_stream.restype = ctypes.c_int
     L.ppr_parse_results.argtypes = [P, U64, ctypes.POINTER(ParseOut), P]
     L.ppr_parse_results.restype = ctypes.c_int
     L.ppr_lex_fold_bytes.argtypes = [U32]
@@ -156,6 +170,7 @@ def _opts_with_events(opts, events):
     o.chunk_bytes = opts.chunk_bytes
     o.path = opts.path
     o.expected_columns = opts.expected_columns
+    o.flags, o.start_state, o.start_column = opts.flags, opts.start_state, opts.start_column
     if not events:
         return o, None
     handles = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
@@ -287,6 +302,60 @@ def parse(data: torch.Tensor, table: dict, chunk_bytes: int | None = None, capac
     n = data.numel()
     cap = capacity if capacity is not None else min(n + 1, max(4096, n // 4))
     return Parser(table, n, cap, chunk_bytes, data.device, path, expected_columns)(data, stream)
+
+
+@dataclass
+class StreamResult:
+    record_idx: np.ndarray       # uint64, length n_fields (host)
+    column_ids: np.ndarray       # uint32
+    field_offsets: np.ndarray    # uint64
+    field_lengths: np.ndarray    # uint64
+    n_fields: int
+    n_records: int
+    error_pos: int
+    end_state: int
+    min_columns: int
+    max_columns: int
+    partitions: int
+    bad_records: int = 0
+    first_bad_record: int = -1
+
+
+def parse_stream(data, table: dict, partition_bytes: int, capacity: int | None = None,
+                 chunk_bytes: int | None = None, path: int | None = None, expected_columns: int = 0,
+                 pinned: bool = True) -> StreamResult:
+    """Parse host bytes (a uint8 numpy array or a CPU torch tensor, pinned for
+    overlapped transfers) in partitions of partition_bytes through
+    ppr_parse_stream; the results are those of one parse of the whole input,
+    in host arrays (pinned torch memory when pinned)."""
+    if isinstance(data, torch.Tensor):
+        if data.is_cuda or data.dtype != torch.uint8 or not data.is_contiguous():
+            raise TypeError("host input must be a contiguous CPU uint8 tensor or numpy array")
+        ptr, n = data.data_ptr(), data.numel()
+    else:
+        data = np.ascontiguousarray(data, dtype=np.uint8)
+        ptr, n = data.ctypes.data, data.size
+    dfa, cm = make_dfa(table)
+    opts = _opts(chunk_bytes, path, expected_columns)
+    for _ in range(2):  # size, then fill
+        cap = max(1, int(capacity if capacity is not None else min(n + 1, max(4096, n // 4))))
+        arrs = [torch.empty(cap, dtype=dt, pin_memory=pinned) for dt in (torch.int64, torch.int32, torch.int64,
+                                                                          torch.int64)]
+        o = StreamOut()
+        o.record_idx, o.column_ids, o.field_offsets, o.field_lengths = [a.data_ptr() for a in arrs]
+        o.cap_fields = cap
+        rc = lib.ppr_parse_stream(ctypes.c_void_p(ptr), n, ctypes.byref(dfa), cm, ctypes.byref(o), partition_bytes,
+                                  ctypes.byref(opts))
+        if rc == PPR_ECAPACITY and capacity is None:
+            capacity = int(o.n_fields)
+            continue
+        _check(rc, "ppr_parse_stream")
+        k = int(o.n_fields)
+        return StreamResult(arrs[0][:k].numpy().view(np.uint64), arrs[1][:k].numpy().view(np.uint32),
+                            arrs[2][:k].numpy().view(np.uint64), arrs[3][:k].numpy().view(np.uint64), k,
+                            int(o.n_records), int(o.error_pos), int(o.end_state), int(o.min_columns),
+                            int(o.max_columns), int(o.partitions), int(o.bad_records), int(o.first_bad_record))
+    raise PprError(PPR_ECAPACITY, "ppr_parse_stream")
 
 
 # ------------------------------------------------------------------ lexer

@@ -36,6 +36,8 @@ struct LookCtx {
     StatB* statB;
     uint32_t epoch;
     uint32_t expect_cols;  // expected fields per record (0: none)
+    uint32_t start_col;    // column of the field open at the input's start (0: a record starts there)
+    uint32_t partial;      // more input follows: no final field, the end state may be non-accepting
 };
 
 // Publish a tile's carry. The aggregate holds tile-local counts (a tile has at
@@ -166,7 +168,8 @@ __device__ void finish_tile(const LookCtx& c, const OutArrays& o, uint32_t n, ui
     if (tile == 0) {
         if (tid == 0) {
             Carry z = carry_identity();
-            z.colabs = 1;  // the input starts at column 0 of record 0
+            z.colabs = 1;  // the input starts in record 0 at column start_col
+            z.colv = c.start_col;
             sh->prefix = z;
             publish_incl(c.statB[0], carry_op(z, ctot), c.epoch);
         }
@@ -208,7 +211,7 @@ __device__ void finish_tile(const LookCtx& c, const OutArrays& o, uint32_t n, ui
             }
             bits &= bits - 1;
         }
-        if (tile == num_tiles - 1 && tid == 0 && !sh->last_rec) {  // the final field ends the last record
+        if (tile == num_tiles - 1 && tid == 0 && !sh->last_rec && !c.partial) {  // the final field ends the last record
             const Carry I = carry_op(P, ctot);
             note_record(st, I.colv + 1u, I.nr, c.expect_cols);
         }
@@ -219,7 +222,9 @@ __device__ void finish_tile(const LookCtx& c, const OutArrays& o, uint32_t n, ui
 
     if (tile == num_tiles - 1 && tid == 0) {
         const Carry I = carry_op(P, ctot);
-        const uint32_t final_field = sh->last_rec ? 0u : 1u;
+        const uint32_t final_field = (c.partial || sh->last_rec) ? 0u : 1u;
+        c.hdr->tail_start = I.lt;
+        c.hdr->tail_col = I.colv;
         if (final_field && I.nf < o.cap) {
             o.rec[I.nf] = I.nr;
             o.col[I.nf] = I.colv;
@@ -229,11 +234,12 @@ __device__ void finish_tile(const LookCtx& c, const OutArrays& o, uint32_t n, ui
         c.hdr->n_fields = (uint64_t)I.nf + final_field;
         c.hdr->n_records = (uint64_t)I.nr + final_field;
         c.hdr->end_state = end_state;
-        c.hdr->error_pos = end_accepting ? (int64_t)-1 : (int64_t)n;  // before err_min is applied
+        c.hdr->error_pos = (c.partial || end_accepting) ? (int64_t)-1 : (int64_t)n;  // before err_min is applied
     }
 }
 
-__global__ void csv_reset_kernel(WsHeader* hdr, uint32_t n, uint32_t start_state, uint32_t accept_mask)
+__global__ void csv_reset_kernel(WsHeader* hdr, uint32_t n, uint32_t start_state, uint32_t accept_mask,
+                                 uint32_t start_col, uint32_t partial)
 {
     if (threadIdx.x == 0) {
         hdr->tile_counter = 0;
@@ -249,7 +255,9 @@ __global__ void csv_reset_kernel(WsHeader* hdr, uint32_t n, uint32_t start_state
             hdr->n_fields = 0;
             hdr->n_records = 0;
             hdr->end_state = start_state;
-            hdr->error_pos = ((accept_mask >> start_state) & 1u) ? -1 : 0;
+            hdr->error_pos = (partial || ((accept_mask >> start_state) & 1u)) ? -1 : 0;
+            hdr->tail_start = 0;
+            hdr->tail_col = start_col;
         }
     }
 }
@@ -521,6 +529,19 @@ int parse_enqueue(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, cons
 {
     int rc = validate_dfa(dfa, class_map);
     if (rc) return rc;
+    // a parse that continues an earlier call's input: its start state and the open field's column
+    const uint32_t flags = opts ? opts->flags : 0u;
+    if (flags & ~(uint32_t)(PPR_PARSE_CONTINUE | PPR_PARSE_PARTIAL)) return PPR_EINVAL;
+    ppr_dfa_t dfa_cont;
+    uint32_t start_col = 0;
+    if (flags & PPR_PARSE_CONTINUE) {
+        if (opts->start_state >= dfa->n_states) return PPR_EINVAL;
+        dfa_cont = *dfa;
+        dfa_cont.start_state = opts->start_state;
+        dfa = &dfa_cont;
+        start_col = opts->start_column;
+    }
+    const uint32_t partial = (flags & PPR_PARSE_PARTIAL) ? 1u : 0u;
     if (!out || !d_ws || (n && !d_bytes)) return PPR_EINVAL;
     if (n > kMaxInput) return PPR_ETOOBIG;
     const uint32_t L = chunk_of(opts);
@@ -570,6 +591,8 @@ int parse_enqueue(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, cons
             f.epoch = next_epoch();
             f.path = path;
             f.expect_cols = expect;
+            f.start_col = start_col;
+            f.partial = partial;
             return launch_csv_fast(f, cb, v8, opts, s);
         }
     }
@@ -577,11 +600,12 @@ int parse_enqueue(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, cons
     const WsLayout lay = csv_layout(n, L);
     if (ws_bytes < lay.total) return PPR_EWORKSPACE;
     stage_event(opts, 0, s);
-    hipLaunchKernelGGL(csv_reset_kernel, dim3(1), dim3(64), 0, s, hdr, (uint32_t)n, dfa->start_state, accept);
+    hipLaunchKernelGGL(csv_reset_kernel, dim3(1), dim3(64), 0, s, hdr, (uint32_t)n, dfa->start_state, accept,
+                       start_col, partial);
     stage_event(opts, 1, s);
     if (hipGetLastError() != hipSuccess) return PPR_EHIP;
     if (n == 0) return PPR_OK;
-    LookCtx lc{hdr, (uint64_t*)(ws + lay.off_a), (StatB*)(ws + lay.off_b), next_epoch(), expect};
+    LookCtx lc{hdr, (uint64_t*)(ws + lay.off_a), (StatB*)(ws + lay.off_b), next_epoch(), expect, start_col, partial};
 
     CsvParams p;
     memset(&p, 0, sizeof p);
@@ -642,6 +666,8 @@ extern "C" int ppr_parse_results(const void* d_ws, uint64_t n, ppr_parse_out_t* 
     out->max_columns = h.cols_max;
     out->bad_records = h.bad_records;
     out->first_bad_record = h.first_bad != 0xffffffffu ? (int64_t)h.first_bad : (int64_t)-1;
+    out->tail_start = h.tail_start;
+    out->tail_column = h.tail_col;
     if (h.fault) return PPR_EHIP;
     return out->n_fields > out->cap_fields ? PPR_ECAPACITY : PPR_OK;
 }

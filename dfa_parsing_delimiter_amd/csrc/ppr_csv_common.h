@@ -149,6 +149,8 @@ struct FastParams {
     uint32_t epoch;        // fused path: call epoch carried by the status words
     uint32_t path;         // PPR_PATH_* the call runs
     uint32_t expect_cols;  // expected fields per record (0: none)
+    uint32_t start_col;    // column of the field open at the input's start (0: a record starts there)
+    uint32_t partial;      // more input follows: no final field, the end state may be non-accepting
     uint8_t state_of[16];  // DFA state of each code (index 8: absorbing)
     uint8_t nxt[9][16];    // [state code, row nt = absorbing][symbol code] -> next code
     uint8_t tag[9][16];

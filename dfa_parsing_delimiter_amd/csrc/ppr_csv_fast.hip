@@ -874,7 +874,7 @@ __global__ void __launch_bounds__(kFastBlock, kCarriesWavesPerSimd<CB>) csv_carr
         if (b == p.num_ranges - 1) {
             const uint32_t e = min(run, 8u);
             p.hdr->end_state = p.state_of[e];
-            p.hdr->error_pos = ((p.accept_codes >> e) & 1u) ? (int64_t)-1 : (int64_t)p.n;  // before err_min
+            p.hdr->error_pos = (p.partial || ((p.accept_codes >> e) & 1u)) ? (int64_t)-1 : (int64_t)p.n;  // before err_min
         }
     }
 }
@@ -963,8 +963,8 @@ __global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_e
     uint32_t* list = s_list[wv];
     load_pass2<CB, V8>(p, sh);
     const GCarryComb gcomb;
-    // the count prefix of the range (the input starts at column 0 of record 0)
-    GCarry P = carries_before(p, b, s_wg);  // (its barrier publishes sh)
+    // the count prefix of the range (the input starts in record 0, at column start_col)
+    GCarry P = gcomb(GCarry{0u, 0u, p.start_col, 0u}, carries_before(p, b, s_wg));  // (its barrier publishes sh)
     if (b == 0) {  // the first INVALID byte: the smallest of the ranges' (stored by the carries kernel)
         const uint32_t i0 = 2 * threadIdx.x, i1 = i0 + 1;
         uint32_t e = i0 < p.num_ranges ? p.range_err[i0] : kNone;
@@ -1027,7 +1027,9 @@ __global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_e
         p, s0, s1, [&](uint32_t st, const IdxIn<CB, V8>& in, uint32_t it) { step(std::true_type{}, st, in, it); },
         [&](uint32_t st, const IdxIn<CB, V8>& in, uint32_t it) { step(std::false_type{}, st, in, it); });
     if (threadIdx.x == 0 && b == p.num_ranges - 1) {
-        const uint32_t final_field = p.hdr->last_rec ? 0u : 1u;
+        const uint32_t final_field = (p.partial || p.hdr->last_rec) ? 0u : 1u;
+        p.hdr->tail_start = P.lt;
+        p.hdr->tail_col = P.col;
         if (final_field && P.nf < o.cap) {
             o.rec[P.nf] = P.nr;
             o.col[P.nf] = P.col;
@@ -1286,8 +1288,8 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
             T1 = T[0];
             RD1 = RD[0];
             if (tid == 0) {
-                if (t1 == 0)  // the input starts at column 0 of record 0: its prefix is the tile's carry
-                    publish_gincl(p.stat_carry[0], sc1.total, p.epoch);
+                if (t1 == 0)  // the input starts in record 0 at column start_col
+                    publish_gincl(p.stat_carry[0], gcomb(GCarry{0u, 0u, p.start_col, 0u}, sc1.total), p.epoch);
                 else
                     publish_gagg(p.stat_carry[t1], sc1.total, p.epoch);
             }
@@ -1295,7 +1297,7 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
 
         // ---- phase 3 (tile t2): count prefix, fields
         if (t2 < num_tiles) {
-            GCarry P{0u, 0u, 0u, 0u};
+            GCarry P{0u, 0u, p.start_col, 0u};
             if (t2 != 0) {
                 P = lookback_pre<kFastWaves>(t2, zero, cpoll, gcomb, sh.pc, sh.first, &p.hdr->fault,
                                              look_first<kFastWaves>(t2, cpoll));
@@ -1333,7 +1335,9 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
             // the input's last tile: the unterminated final field and the results
             if (t2 == num_tiles - 1 && tid == 0) {
                 const GCarry I = gcomb(P, sc2.total);
-                const uint32_t final_field = sh.last_rec ? 0u : 1u;
+                const uint32_t final_field = (p.partial || sh.last_rec) ? 0u : 1u;
+                p.hdr->tail_start = I.lt;
+                p.hdr->tail_col = I.col;
                 if (final_field && I.nf < o.cap) {
                     o.rec[I.nf] = I.nr;
                     o.col[I.nf] = I.col;
@@ -1345,7 +1349,8 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
                 p.hdr->n_fields = (uint64_t)I.nf + final_field;
                 p.hdr->n_records = (uint64_t)I.nr + final_field;
                 p.hdr->end_state = p.state_of[e];
-                p.hdr->error_pos = ((p.accept_codes >> e) & 1u) ? (int64_t)-1 : (int64_t)p.n;  // before err_min
+                p.hdr->error_pos =
+                    (p.partial || ((p.accept_codes >> e) & 1u)) ? (int64_t)-1 : (int64_t)p.n;  // before err_min
             }
         }
 

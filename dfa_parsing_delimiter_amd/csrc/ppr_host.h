@@ -28,6 +28,8 @@ struct WsHeader {
     uint32_t cols_max;  // most fields of a record (atomic maximum)
     uint32_t bad_records;  // records whose number of fields is not the expected one (atomic sum)
     uint32_t first_bad;    // the first of them (atomic minimum), 0xffffffff: none
+    uint32_t tail_start;   // the unterminated tail: start of its field (1 + last terminator, 0: none)
+    uint32_t tail_col;     // and that field's column
 };
 
 // Records stage event i of the call on the stream, if the caller asked for it.

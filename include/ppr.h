@@ -112,6 +112,11 @@ typedef struct ppr_parse_out {
      * a caller that rejects them drops the fields of those records. */
     uint64_t bad_records;
     int64_t first_bad_record;
+    /* out: the unterminated tail of the input (after its last terminator, 0
+     * if none): where it starts and the column of its field. With
+     * PPR_PARSE_PARTIAL, the next call continues from there. */
+    uint32_t tail_start;
+    uint32_t tail_column;
 } ppr_parse_out_t;
 
 /*
@@ -163,7 +168,23 @@ typedef struct ppr_parse_opts {
     void* const* stage_events;
     uint32_t path;
     uint32_t expected_columns; /* 0: none; else records are checked against it (ppr_parse_out_t.bad_records) */
+    /* Resuming a parse across calls (input cut into partitions, ParPaRaw's
+     * streaming passage; ppr_parse_stream is built on it):
+     *   PPR_PARSE_CONTINUE: the bytes continue an earlier call's input: start in
+     *     DFA state start_state, inside a record whose open field has column
+     *     start_column (the earlier call's end_state and tail_column);
+     *   PPR_PARSE_PARTIAL: more input follows: the unterminated tail (after the
+     *     last terminator) is not emitted as a field, no record is closed at the
+     *     end, and a non-accepting end state is not an error (error_pos is only
+     *     an INVALID byte); tail_start / tail_column describe the open field.
+     * Offsets, record indices and columns are those of this call's bytes: a
+     * field continued from an earlier call starts at offset 0 here. */
+    uint32_t flags;
+    uint32_t start_state;
+    uint32_t start_column;
 } ppr_parse_opts_t;
+
+enum { PPR_PARSE_CONTINUE = 1, PPR_PARSE_PARTIAL = 2 };
 
 /*
  * Workspace bytes ppr_parse needs for n input bytes (opts may be NULL).
@@ -212,6 +233,46 @@ PPR_API int ppr_parse_results(const void* d_ws, uint64_t n, ppr_parse_out_t* out
 #define PPR_NOALLOC_SCRATCH_BYTES (16u << 20)
 PPR_API int ppr_parse_noalloc(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, const uint8_t class_map[256],
                               ppr_parse_out_t* out, const ppr_parse_opts_t* opts, void* stream);
+
+/*
+ * Host streaming [ParPaRaw, the end-to-end streaming passage, Fig. 7]: parse
+ * n bytes of HOST memory, any size, by cutting them into partitions of
+ * partition_bytes and running, on three HIP streams, the transfer of one
+ * partition to the device, the parse of the one before and the return of
+ * the one before that, with two device buffers used in turn. A partition
+ * continues the previous one's parse (PPR_PARSE_CONTINUE with its end state
+ * and open column, PPR_PARSE_PARTIAL on all but the last), so no incomplete
+ * record has to be copied over and parsed again and records may span any
+ * number of partitions. The results are those of one parse over the whole
+ * input, with 64-bit record indices, offsets and lengths.
+ *   out: host arrays of cap_fields entries each (pinned memory lets the
+ *        returns overlap the parse); n_fields etc. as for ppr_parse.
+ *   opts: chunk_bytes, path and expected_columns as for ppr_parse (flags,
+ *        start_state, start_column must be 0; stage events are ignored).
+ * Unlike ppr_parse, this driver allocates (and frees before it returns) its
+ * device buffers (2 x (partition + workspace + outputs)) and streams.
+ * PPR_ECAPACITY with the counts set if n_fields > cap_fields; PPR_EINVAL for
+ * partition_bytes of 0 or above 2^32 - 2^16.
+ */
+typedef struct ppr_stream_out {
+    uint64_t* record_idx;
+    uint32_t* column_ids;
+    uint64_t* field_offsets;
+    uint64_t* field_lengths;
+    uint64_t cap_fields;
+    uint64_t n_fields;      /* out */
+    uint64_t n_records;     /* out */
+    int64_t error_pos;      /* out */
+    uint32_t end_state;     /* out */
+    uint32_t min_columns;   /* out */
+    uint32_t max_columns;   /* out */
+    uint32_t partitions;    /* out: partitions parsed */
+    uint64_t bad_records;   /* out */
+    int64_t first_bad_record; /* out */
+} ppr_stream_out_t;
+
+PPR_API int ppr_parse_stream(const uint8_t* h_bytes, uint64_t n, const ppr_dfa_t* dfa, const uint8_t class_map[256],
+                             ppr_stream_out_t* out, uint64_t partition_bytes, const ppr_parse_opts_t* opts);
 
 /* ------------------------------------------------------------------ lexer */
 
