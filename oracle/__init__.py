@@ -17,6 +17,9 @@ no code, header, table or helper with the GPU library, and it never imports it.
   tables (lex_oracle.c; same page, tables and harness).
 * ``lex_closure.build_tables``: the merge tables written out from their
   definition with plain tuples (small grammars only).
+* ``columns.partition``: the columnar partition of one parse's fields into
+  per-column concatenated symbol strings and their index (ParPaRaw, Sec. 3,
+  Fig. 5; inline-terminated and vector-delimited variants, Fig. 6).
 
 Beside the oracle, and not part of it: ``csv_parse_parallel`` and
 ``lex_restart_parallel`` (cpu_parallel.c), the all-core CPU baseline that the

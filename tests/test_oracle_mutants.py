@@ -229,3 +229,49 @@ def test_conformance_mutant_is_caught(mutant, monkeypatch):
 
 def test_unmutated_conformance_passes_same_pins():
     assert _conformance_pins_pass()
+
+
+# Planted mistakes in the columnar-partition oracle (oracle/columns.py): each
+# copy of its source with one change must fail the pins of
+# tests/test_oracle_columns.py.
+COLUMNS_MUTANTS = {
+    "unstable_within_column": ('order = np.argsort(col, kind="stable")', 'order = np.argsort(-col, kind="stable")[::-1]'),
+    "slot_not_counted": ("pos += int(lens[j]) + slot", "pos += int(lens[j])"),
+    "empty_fields_dropped": ("    for j in range(nf):\n", "    for j in [i for i in range(nf) if lens[i] > 0]:\n"),
+    "aux_one_late": ("aux += bytes(int(lens[j]))", "aux += bytes(int(lens[j]) + 1)"),
+    "column_bound_off_by_one": ("css_off[f] if f < nf else pos", "css_off[f] + 1 if f < nf else pos"),
+    "terminator_before_field": ("        css += b[offs[j]:offs[j] + lens[j]].tobytes()\n        aux += bytes(int(lens[j]))\n        if slot:\n            css.append(terminator if mode == MODE_INLINE else 0)\n            aux.append(1)\n",
+                                "        if slot:\n            css.append(terminator if mode == MODE_INLINE else 0)\n            aux.append(1)\n        css += b[offs[j]:offs[j] + lens[j]].tobytes()\n        aux += bytes(int(lens[j]))\n"),
+}
+
+
+def _columns_mutant(name):
+    import types
+    src = open(os.path.join(ORACLE_DIR, "columns.py")).read()
+    old, new = COLUMNS_MUTANTS[name]
+    assert src.count(old) == 1, (name, old)
+    mod = types.ModuleType("columns_mutant")
+    exec(compile(src.replace(old, new), "columns_mutant.py", "exec"), mod.__dict__)
+    return mod.partition
+
+
+def _columns_pins_pass():
+    from tests import test_oracle_columns as T
+    try:
+        T.test_hand_worked()
+        T.test_exhaustive_vs_recursive_descent()
+        T.test_variant_invariants()
+    except (AssertionError, IndexError, ValueError):
+        return False
+    return True
+
+
+@pytest.mark.parametrize("mutant", sorted(COLUMNS_MUTANTS))
+def test_columns_mutant_is_caught(mutant, monkeypatch):
+    from oracle import columns
+    monkeypatch.setattr(columns, "partition", _columns_mutant(mutant))
+    assert not _columns_pins_pass(), mutant
+
+
+def test_unmutated_columns_passes_same_pins():
+    assert _columns_pins_pass()
