@@ -212,6 +212,119 @@ def stream_bench(args, cfg_id, cfg, ppr, torch, W, np):
                                 "buffers included), median"}), flush=True)
 
 
+COLUMN_STAGES = ["cols_reset_kernel", "cols_hist_kernel", "cols_scan_kernel#1", "cols_scatter_kernel",
+                 "cols_scan_kernel#2", "cols_bounds_kernel", "cols_copy_kernel"]
+
+
+def columns_bench(args, cfg_id, cfg, ppr, torch, W, np):
+    """GB/s of the columnar partition (ppr_columns) of the workload's parse: the
+    parse's field arrays and the bytes resident in HBM, one blocking call per
+    step (every kernel: histogram, scans, scatter, bounds, byte copy)"""
+    import oracle
+    assert cfg["kind"] == "csv", "the columnar partition follows a delimiter-separated parse"
+    mode = {"indexed": ppr.PPR_CSS_INDEXED, "inline": ppr.PPR_CSS_INLINE, "vector": ppr.PPR_CSS_VECTOR}[args.columns]
+    log("generating", cfg["name"], cfg["n"], "bytes")
+    data = W.generate(cfg_id)
+    sha = W.sha256(data)
+    n = data.size
+    dev = torch.device("cuda:0")
+    d = torch.from_numpy(data).to(dev)
+    table = W.table(cfg["table"])
+    g = ppr.Parser(table, max_n=n, capacity=n // 8 + 4096, device=dev)(d)
+    nf, nc = g.n_fields, g.max_columns
+    cols = ppr.Columns(nf, nc, n, mode=mode, terminator=0x1E)
+    first = cols(d, g)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        cols(d, g)
+    torch.cuda.synchronize()
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    for a, b in step_ev:
+        a.record(stream)
+        cols(d, g)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = statistics.median(a.elapsed_time(b) for a, b in step_ev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(COLUMN_STAGES) + 1)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for row in evs:
+        cols(d, g, stage_events=row)
+    torch.cuda.synchronize()
+    stage_ms = {k: statistics.mean(row[i].elapsed_time(row[i + 1]) for row in evs) for i, k in enumerate(COLUMN_STAGES)}
+    slot = 0 if mode == ppr.PPR_CSS_INDEXED else 1
+    css = first.css_bytes
+    field_bytes = css - slot * nf  # the fields' own bytes, read once from the input
+    aux = css if mode == ppr.PPR_CSS_VECTOR else 0
+    # algorithmic bytes, each attributed to the kernel that moves it: the four field arrays read once (16 B per
+    # field: the histogram reads the columns, the scatter the rest), the index written once (rec and length by the
+    # scatter, css_off by the second scan: 12 B per field), the field bytes read once and the CSS (and aux) written
+    # once (the copy kernel), the bounds (8 B per column)
+    alg = {"cols_hist_kernel": 4 * nf, "cols_scatter_kernel": 12 * nf + 8 * nf, "cols_scan_kernel#2": 4 * nf,
+           "cols_bounds_kernel": 8 * (nc + 1), "cols_copy_kernel": field_bytes + css + aux}
+    step_alg = 16 * nf + 12 * nf + field_bytes + css + aux + 8 * (nc + 1)
+    dominant = max(stage_ms, key=stage_ms.get)
+    t_dom = stage_ms[dominant] * 1e-3
+    alg_dom = alg.get(dominant, 0)
+    line = {"metric": "columnar partition GB/s (input bytes of the parse partitioned per second, ppr_columns)",
+            "value": round(n / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "%s_%dMiB_columns_%s" % (cfg["name"], n >> 20, args.columns), "n_bytes": n,
+                       "fields": nf, "columns": nc, "css_bytes": css, "input_sha256": sha[:16],
+                       "kernels": COLUMN_STAGES},
+            "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(alg_dom / t_dom / 1e9, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(alg_dom / t_dom / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes_per_launch": alg_dom, "kernel_ms": round(stage_ms[dominant], 4),
+                         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+                         "step": {"algorithmic_bytes": step_alg,
+                                  "achieved": round(step_alg / (ms * 1e-3) / 1e9, 2),
+                                  "frac": round(step_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                         "timing": "HIP events on the launch stream around each of %d blocking calls (median); "
+                                   "per-kernel events recorded by the library" % args.steps}}
+    if not args.no_cpu:
+        from oracle import columns as C
+        log("cpu oracle baseline (columns)")
+        r = oracle.csv_parse(data, table)
+        # the oracle as it stands (a Python loop per field) on a bounded sample: the first records' fields
+        info, allowed = host_cpu()
+        k = min(nf, 3 << 20)
+        end = int(r["off"][k - 1] + r["len"][k - 1]) + 1
+        t0 = time.perf_counter()
+        C.partition(data[:end], r["rec"][:k], r["col"][:k], r["off"][:k], r["len"][:k], mode, 0x1E)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(end / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                                "sample": "the first %d fields (%d input bytes) of the same parse, oracle partition "
+                                          "(numpy stable argsort, then a Python loop per field), one run" % (k, end),
+                                "host": info}
+        # parity at full size: counts and bounds exactly, every index entry against the oracle parse's fields in
+        # stable column order, and 2000 sampled CSS fields byte for byte
+        col = r["col"].astype(np.int64)
+        order = np.argsort(col, kind="stable")
+        lens = r["len"].astype(np.int64)[order]
+        offs = np.concatenate([[0], np.cumsum(lens + slot)])
+        u32 = lambda t: t.cpu().numpy().view(np.uint32).astype(np.int64)  # noqa: E731
+        res = cols(d, g)
+        ok = res.css_bytes == int(offs[-1]) and nf == r["n_fields"]
+        ok = ok and np.array_equal(u32(res.rec), r["rec"].astype(np.int64)[order])
+        ok = ok and np.array_equal(u32(res.length), lens) and np.array_equal(u32(res.css_off), offs[:-1])
+        ok = ok and np.array_equal(u32(res.col_first_field),
+                                   np.concatenate([[0], np.cumsum(np.bincount(col, minlength=nc))]))
+        rng = np.random.default_rng(3)
+        css_h = res.css
+        for j in rng.integers(0, nf, 2000):
+            f = order[j]
+            seg = css_h[offs[j]:offs[j] + lens[j]].cpu().numpy().tobytes()
+            ok = ok and seg == data[r["off"][f]:r["off"][f] + r["len"][f]].tobytes()
+        line["parity_vs_oracle"] = ("bit-exact (index, bounds, CSS size; 2000 sampled CSS fields)" if ok
+                                    else "MISMATCH")
+    print(json.dumps(line), flush=True)
+
+
 def read_pmc(d, counter):
     """counter value of every dispatch, by kernel name, from a rocprofv3 csv output directory"""
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -306,6 +419,8 @@ def main():
     ap.add_argument("--stream", type=int, default=0, metavar="PARTITION_MIB",
                     help="instead: time ppr_parse_stream over the workload in pinned HOST memory, partitions of this "
                          "many MiB (transfers, parse and returns overlapped; PCIe-inclusive, not the metric)")
+    ap.add_argument("--columns", choices=["indexed", "inline", "vector"], default=None,
+                    help="instead: time the columnar partition (ppr_columns) of the workload's parse in this mode")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the device bandwidth probe (read / write / copy of 1 GiB)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -334,6 +449,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.stream:
         return stream_bench(args, cfg_id, cfg, ppr, torch, W, np)
+    if args.columns:
+        return columns_bench(args, cfg_id, cfg, ppr, torch, W, np)
     log("generating", cfg["name"], cfg["n"], "bytes")
     t0 = time.time()
     data = W.generate(cfg_id)

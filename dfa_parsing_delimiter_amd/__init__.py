@@ -32,6 +32,7 @@ LIB_PATH = os.environ.get("PPR_LIB_PATH") or os.path.join(_HERE, "libppr.so")
 PPR_OK, PPR_EINVAL, PPR_ECAPACITY, PPR_ETOOBIG, PPR_EHIP, PPR_EWORKSPACE = 0, -1, -2, -3, -4, -5
 PPR_PATH_STREAMING, PPR_PATH_SINGLE_PASS, PPR_PATH_FUSED = 1, 2, 3
 PPR_PARSE_CONTINUE, PPR_PARSE_PARTIAL = 1, 2
+PPR_CSS_INDEXED, PPR_CSS_INLINE, PPR_CSS_VECTOR = 0, 1, 2
 _ERRNAMES = {-1: "PPR_EINVAL", -2: "PPR_ECAPACITY", -3: "PPR_ETOOBIG", -4: "PPR_EHIP", -5: "PPR_EWORKSPACE"}
 TAG_VALUE, TAG_FIELD, TAG_RECORD, TAG_INVALID = 0, 1, 2, 3
 
@@ -63,6 +64,13 @@ class ParseOpts(ctypes.Structure):
                 ("stage_events", ctypes.c_void_p), ("path", ctypes.c_uint32),
                 ("expected_columns", ctypes.c_uint32), ("flags", ctypes.c_uint32), ("start_state", ctypes.c_uint32),
                 ("start_column", ctypes.c_uint32)]
+
+
+class ColumnsOut(ctypes.Structure):
+    _fields_ = [("css", ctypes.c_void_p), ("aux", ctypes.c_void_p), ("css_cap", ctypes.c_uint64),
+                ("rec", ctypes.c_void_p), ("css_off", ctypes.c_void_p), ("length", ctypes.c_void_p),
+                ("col_first_field", ctypes.c_void_p), ("col_first_byte", ctypes.c_void_p),
+                ("css_bytes", ctypes.c_uint64)]
 
 
 class StreamOut(ctypes.Structure):
@@ -107,6 +115,11 @@ def _load():
     L.ppr_parse_stream.argtypes = [P, U64, ctypes.POINTER(Dfa), ctypes.c_char_p, ctypes.POINTER(StreamOut), U64,
                                    ctypes.POINTER(ParseOpts)]
     L.ppr_parse_stream.restype = ctypes.c_int
+    L.ppr_columns_workspace_bytes.argtypes = [U64, U32]
+    L.ppr_columns_workspace_bytes.restype = ctypes.c_size_t
+    L.ppr_columns.argtypes = [P, U64, P, P, P, P, U64, U32, U32, U32, ctypes.POINTER(ColumnsOut), P, ctypes.c_size_t,
+                              ctypes.POINTER(ParseOpts), P]
+    L.ppr_columns.restype = ctypes.c_int
     L.ppr_parse_results.argtypes = [P, U64, ctypes.POINTER(ParseOut), P]
     L.ppr_parse_results.restype = ctypes.c_int
     L.ppr_lex_fold_bytes.argtypes = [U32]
@@ -232,8 +245,7 @@ class Parser:
         ws = lib.ppr_parse_workspace_bytes(self.max_n, ctypes.byref(self.opts))
         if ws == 0:
             raise PprError(PPR_EINVAL, "ppr_parse_workspace_bytes")
-        # zero-filled before first use, as the ABI requires
-        self.ws = torch.zeros(ws + 256, dtype=torch.uint8, device=self.device)
+        self.ws = torch.empty(ws + 256, dtype=torch.uint8, device=self.device)
         self.ws_off = (-self.ws.data_ptr()) % 256
         self.ws_bytes = ws
         self._alloc(self.max_n + 1 if capacity is None else int(capacity))
@@ -302,6 +314,71 @@ def parse(data: torch.Tensor, table: dict, chunk_bytes: int | None = None, capac
     n = data.numel()
     cap = capacity if capacity is not None else min(n + 1, max(4096, n // 4))
     return Parser(table, n, cap, chunk_bytes, data.device, path, expected_columns)(data, stream)
+
+
+@dataclass
+class ColumnsResult:
+    css: torch.Tensor              # uint8, css_bytes (device)
+    aux: torch.Tensor | None       # uint8, css_bytes (vector-delimited mode)
+    rec: torch.Tensor              # int32 views of uint32, one entry per field grouped by column
+    css_off: torch.Tensor
+    length: torch.Tensor
+    col_first_field: torch.Tensor  # n_columns + 1
+    col_first_byte: torch.Tensor
+    css_bytes: int
+    n_columns: int
+
+
+class Columns:
+    """Reusable workspace and outputs for the columnar partition (ppr_columns)
+    of parses of up to max_fields fields and max_bytes input bytes."""
+
+    def __init__(self, max_fields: int, n_columns: int, max_bytes: int, mode: int = PPR_CSS_INDEXED,
+                 terminator: int = 0x1F, device=None, css_capacity: int | None = None):
+        self.device = torch.device("cuda") if device is None else torch.device(device)
+        self.mode, self.terminator, self.n_columns = int(mode), int(terminator), int(n_columns)
+        ws = lib.ppr_columns_workspace_bytes(max_fields, self.n_columns)
+        if ws == 0:
+            raise PprError(PPR_EINVAL, "ppr_columns_workspace_bytes")
+        self.ws = torch.empty(ws + 256, dtype=torch.uint8, device=self.device)
+        self.ws_off = (-self.ws.data_ptr()) % 256
+        self.ws_bytes = ws
+        cap = css_capacity if css_capacity is not None else max_bytes + (max_fields if mode != PPR_CSS_INDEXED else 0)
+        self.css_cap = max(1, int(cap))
+        self.css = torch.empty(self.css_cap, dtype=torch.uint8, device=self.device)
+        self.aux = torch.empty(self.css_cap, dtype=torch.uint8, device=self.device) if mode == PPR_CSS_VECTOR else None
+        f = max(1, int(max_fields))
+        self.ent = [torch.empty(f, dtype=torch.int32, device=self.device) for _ in range(3)]
+        self.bounds = [torch.empty(self.n_columns + 1, dtype=torch.int32, device=self.device) for _ in range(2)]
+
+    def __call__(self, data: torch.Tensor, res: "ParseResult", stream=None, stage_events=None) -> ColumnsResult:
+        """stage_events: optional list of 8 torch.cuda.Event recorded before and after the call's kernels"""
+        _check_input(data)
+        opts, keep = _opts_with_events(_opts(None), stage_events)
+        o = ColumnsOut()
+        o.css, o.css_cap = self.css.data_ptr(), self.css_cap
+        o.aux = self.aux.data_ptr() if self.aux is not None else None
+        o.rec, o.css_off, o.length = [a.data_ptr() for a in self.ent]
+        o.col_first_field, o.col_first_byte = [a.data_ptr() for a in self.bounds]
+        nf = int(res.n_fields)
+        rc = lib.ppr_columns(ctypes.c_void_p(data.data_ptr()), data.numel(), ctypes.c_void_p(res.record_idx.data_ptr()),
+                             ctypes.c_void_p(res.column_ids.data_ptr()), ctypes.c_void_p(res.field_offsets.data_ptr()),
+                             ctypes.c_void_p(res.field_lengths.data_ptr()), nf, self.n_columns, self.mode,
+                             self.terminator, ctypes.byref(o), ctypes.c_void_p(self.ws.data_ptr() + self.ws_off),
+                             self.ws_bytes, ctypes.byref(opts), _stream_handle(stream))
+        del keep
+        _check(rc, "ppr_columns")
+        k = int(o.css_bytes)
+        return ColumnsResult(self.css[:k], self.aux[:k] if self.aux is not None else None,
+                             *[a[:nf] for a in self.ent], *self.bounds, k, self.n_columns)
+
+
+def columns(data: torch.Tensor, res: "ParseResult", n_columns: int | None = None, mode: int = PPR_CSS_INDEXED,
+            terminator: int = 0x1F, stream=None) -> ColumnsResult:
+    """Partition a parse's fields by column into per-column symbol strings and
+    their index (one call; n_columns defaults to the parse's max_columns)."""
+    nc = int(res.max_columns if n_columns is None else n_columns)
+    return Columns(res.n_fields, nc, data.numel(), mode, terminator, data.device)(data, res, stream)
 
 
 @dataclass
@@ -428,7 +505,7 @@ class Lexer:
         ws = lib.ppr_lex_workspace_bytes(self.max_n, ctypes.byref(self.opts))
         if ws == 0:
             raise PprError(PPR_EINVAL, "ppr_lex_workspace_bytes")
-        self.ws = torch.zeros(ws + 256, dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(ws + 256, dtype=torch.uint8, device=dev)
         self.ws_off = (-self.ws.data_ptr()) % 256
         self.ws_bytes = ws
         self.device = dev

@@ -238,10 +238,13 @@ __device__ void finish_tile(const LookCtx& c, const OutArrays& o, uint32_t n, ui
     }
 }
 
+// Resets the workspace header (workgroup 0) and clears the look-back statuses
+// (all workgroups: n_stat 16-byte words from stat).
 __global__ void csv_reset_kernel(WsHeader* hdr, uint32_t n, uint32_t start_state, uint32_t accept_mask,
-                                 uint32_t start_col, uint32_t partial)
+                                 uint32_t start_col, uint32_t partial, uint4* stat, uint64_t n_stat)
 {
-    if (threadIdx.x == 0) {
+    clear_status(stat, n_stat);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
         hdr->tile_counter = 0;
         hdr->fault = 0;
         hdr->err_min = 0xffffffffu;
@@ -600,8 +603,9 @@ int parse_enqueue(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, cons
     const WsLayout lay = csv_layout(n, L);
     if (ws_bytes < lay.total) return PPR_EWORKSPACE;
     stage_event(opts, 0, s);
-    hipLaunchKernelGGL(csv_reset_kernel, dim3(1), dim3(64), 0, s, hdr, (uint32_t)n, dfa->start_state, accept,
-                       start_col, partial);
+    const uint64_t stat_bytes = lay.total - lay.off_a;  // statuses A and B, with their padding
+    hipLaunchKernelGGL(csv_reset_kernel, dim3(clear_grid(stat_bytes)), dim3(256), 0, s, hdr, (uint32_t)n,
+                       dfa->start_state, accept, start_col, partial, (uint4*)(ws + lay.off_a), stat_bytes / 16);
     stage_event(opts, 1, s);
     if (hipGetLastError() != hipSuccess) return PPR_EHIP;
     if (n == 0) return PPR_OK;

@@ -512,12 +512,16 @@ __device__ void build_pass2(uint32_t* t2, const uint8_t* s_nxt, const uint8_t* s
     }
 }
 
-// The fused path's tables (in the workspace, read by every workgroup) and the
-// reset of the workspace header. One workgroup.
+// The fused path's tables (in the workspace, read by every workgroup), built
+// by workgroup 0, which also resets the workspace header; every workgroup
+// clears a share of the two look-back status arrays.
 template <int CB, bool V8>
 __global__ void csv_fast_tables_kernel(FastParams p)
 {
     __shared__ uint8_t s_nxt[9 * 16], s_tag[9 * 16];
+    clear_status(reinterpret_cast<uint4*>(p.stat_vec), ((uint64_t)p.num_tiles + 1) / 2);
+    clear_status(reinterpret_cast<uint4*>(p.stat_carry), (uint64_t)p.num_tiles * (sizeof(StatB) / 16));
+    if (blockIdx.x != 0) return;
     if (threadIdx.x < 9 * 16) {
         s_nxt[threadIdx.x] = (&p.nxt[0][0])[threadIdx.x];
         s_tag[threadIdx.x] = (&p.tag[0][0])[threadIdx.x];
@@ -1418,7 +1422,8 @@ template <int CB, bool V8>
 static void launch_fused(const FastParams& f, const ppr_parse_opts_t* o, hipStream_t s)
 {
     stage_event(o, 0, s);
-    hipLaunchKernelGGL((csv_fast_tables_kernel<CB, V8>), dim3(1), dim3(256), 0, s, f);
+    hipLaunchKernelGGL((csv_fast_tables_kernel<CB, V8>), dim3(clear_grid((uint64_t)f.num_tiles * (8 + sizeof(StatB)))),
+                       dim3(256), 0, s, f);
     stage_event(o, 1, s);
     const uint32_t grid = std::min<uint32_t>(f.num_tiles, fused_grid<CB, V8>());
     hipLaunchKernelGGL((csv_fused_kernel<CB, V8>), dim3(grid), dim3(kFastBlock), 0, s, f);

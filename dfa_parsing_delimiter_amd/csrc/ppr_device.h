@@ -82,9 +82,11 @@ __device__ __forceinline__ void st_release(uint64_t* p, uint64_t v)
 //
 // Decoupled look-back (single-pass prefix scan with a per-tile status that is
 // either the tile's own aggregate or its inclusive prefix). A status word is
-// [63:34] call epoch, [33:32] flag, [31:0] payload. Statuses left over from an
-// earlier call carry another epoch and read as "not yet published", so the
-// status arrays never need clearing between calls.
+// [63:34] call epoch, [33:32] flag, [31:0] payload. Every call clears its
+// status arrays (clear_status) before its first tile starts: a workspace that
+// served another call, another entry point or another input size can hold any
+// bit pattern where the statuses now lie, small integers that happen to match
+// the epoch field included. The epoch is a second guard.
 
 constexpr uint32_t kFlagAgg = 1;
 constexpr uint32_t kFlagIncl = 2;
@@ -99,6 +101,14 @@ __device__ __forceinline__ uint32_t status_flag(uint64_t w, uint32_t epoch)
     return (uint32_t)(w >> 34) == (epoch & kEpochMask) ? (uint32_t)(w >> 32) & 3u : 0u;
 }
 __device__ __forceinline__ uint32_t status_payload(uint64_t w) { return (uint32_t)w; }
+
+// Zero n 16-byte words, spread over the launch's grid (each workgroup a
+// stride of the array).
+__device__ __forceinline__ void clear_status(uint4* p, uint64_t n)
+{
+    const uint64_t step = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += step) p[i] = make_uint4(0, 0, 0, 0);
+}
 
 // self-validating status word: call epoch in the high half, value in the low half
 __device__ __forceinline__ uint64_t ew(uint32_t epoch, uint32_t v) { return ((uint64_t)epoch << 32) | v; }

@@ -64,6 +64,14 @@ struct WsLayout {
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
+// Workgroups of 256 threads for a kernel that clears `bytes` of look-back
+// statuses (clear_status): about one 16-byte word per thread, at most 1024.
+inline uint32_t clear_grid(uint64_t bytes)
+{
+    const uint64_t g = (bytes + 16 * 256 - 1) / (16 * 256);
+    return (uint32_t)(g < 1 ? 1 : g > 1024 ? 1024 : g);
+}
+
 // Call epochs tag look-back statuses so stale ones from earlier calls read as
 // unpublished. 0 never occurs (a zero-filled workspace holds no valid status).
 inline uint32_t next_epoch()

@@ -128,9 +128,12 @@ __device__ __forceinline__ void publish_tok(StatB& s, TokCarry c, uint32_t epoch
     st_relaxed(&w[1], ew(epoch, c.lb));
 }
 
-__global__ void lex_reset_kernel(WsHeader* hdr)
+// Resets the workspace header (workgroup 0) and clears the look-back statuses
+// (all workgroups: n_stat 16-byte words from stat).
+__global__ void lex_reset_kernel(WsHeader* hdr, uint4* stat, uint64_t n_stat)
 {
-    if (threadIdx.x == 0) {
+    clear_status(stat, n_stat);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
         hdr->tile_counter = 0;
         hdr->n_fields = 0;
         hdr->fault = 0;
@@ -631,7 +634,9 @@ extern "C" int ppr_lex_async(const uint8_t* d_bytes, uint64_t n, const ppr_lex_t
         return launch_lex_fast(f, opts, s);
     }
     stage_event(opts, 0, s);
-    hipLaunchKernelGGL(lex_reset_kernel, dim3(1), dim3(64), 0, s, hdr);
+    const uint64_t stat_bytes = lay.total - lay.off_a;  // statuses A and B, with their padding
+    hipLaunchKernelGGL(lex_reset_kernel, dim3(clear_grid(stat_bytes)), dim3(256), 0, s, hdr, (uint4*)(ws + lay.off_a),
+                       stat_bytes / 16);
     stage_event(opts, 1, s);
     if (hipGetLastError() != hipSuccess) return PPR_EHIP;
     if (n == 0) return PPR_OK;

@@ -29,18 +29,11 @@ constexpr int kMaxDevices = 64;
 uint8_t* scratch_ptr[kMaxDevices];
 std::mutex scratch_mu;
 
-// zero fill with a kernel (not hipMemsetAsync, which does not replay
-// correctly inside captured graphs); one pass at set-up
-__global__ void scratch_clear_kernel(uint4* p, uint64_t words)
-{
-    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (uint64_t)gridDim.x * blockDim.x)
-        p[i] = make_uint4(0u, 0u, 0u, 0u);
-}
-
-// The current device's scratch (its address from hipGetSymbolAddress; the
-// first call on a device also clears it, on `s`, before any parse uses it).
-// NULL on a HIP error.
-uint8_t* device_scratch(hipStream_t s)
+// The current device's scratch (its address from hipGetSymbolAddress, taken
+// at the first call on the device). Nothing in it needs to start at zero: a
+// parse resets its header and clears its look-back statuses itself. NULL on a
+// HIP error.
+uint8_t* device_scratch()
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
@@ -48,9 +41,6 @@ uint8_t* device_scratch(hipStream_t s)
     if (!scratch_ptr[dev]) {
         void* ptr = nullptr;
         if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
-        hipLaunchKernelGGL(scratch_clear_kernel, dim3(256), dim3(256), 0, s, (uint4*)ptr,
-                           (uint64_t)(kScratchBytes / sizeof(uint4)));
-        if (hipGetLastError() != hipSuccess) return nullptr;
         scratch_ptr[dev] = (uint8_t*)ptr;
     }
     return scratch_ptr[dev];
@@ -66,8 +56,7 @@ extern "C" PPR_API int ppr_parse_noalloc(const uint8_t* d_bytes, uint64_t n, con
                                          const ppr_parse_opts_t* opts, void* stream)
 {
     if (!out) return PPR_EINVAL;
-    hipStream_t s = (hipStream_t)stream;
-    uint8_t* ws = device_scratch(s);
+    uint8_t* ws = device_scratch();
     if (!ws) return PPR_EHIP;
     // an input whose statuses exceed the scratch is refused before anything is enqueued
     const int rc = parse_enqueue(d_bytes, n, dfa, class_map, out, ws, kScratchBytes, opts, stream, true);

@@ -188,8 +188,9 @@ enum { PPR_PARSE_CONTINUE = 1, PPR_PARSE_PARTIAL = 2 };
 
 /*
  * Workspace bytes ppr_parse needs for n input bytes (opts may be NULL).
- * The workspace must be 256-byte aligned and zero-filled before its first use
- * (afterwards the library keeps it consistent); 0 on invalid arguments.
+ * The workspace must be 256-byte aligned; it needs no initialisation (every
+ * call clears what it reads before writing it, so one workspace may serve
+ * calls of any size and any entry point in turn); 0 on invalid arguments.
  */
 PPR_API size_t ppr_parse_workspace_bytes(uint64_t n, const ppr_parse_opts_t* opts);
 
@@ -227,7 +228,8 @@ PPR_API int ppr_parse_results(const void* d_ws, uint64_t n, ppr_parse_out_t* out
  *     above about 233,000 tiles of 1024 chunks of chunk_bytes.
  *   - Every call on one GPU shares that GPU's scratch: calls that overlap in
  *     time on one GPU (other streams, other host threads) race and must not be
- *     made. The first call on a GPU clears its scratch with a kernel on `stream`.
+ *     made. Each call clears what it needs at zero (its header and look-back
+ *     statuses) with kernels on `stream`; the scratch keeps the last call's contents.
  * Otherwise as ppr_parse (arguments, results, PPR_ECAPACITY).
  */
 #define PPR_NOALLOC_SCRATCH_BYTES (16u << 20)
@@ -273,6 +275,56 @@ typedef struct ppr_stream_out {
 
 PPR_API int ppr_parse_stream(const uint8_t* h_bytes, uint64_t n, const ppr_dfa_t* dfa, const uint8_t class_map[256],
                              ppr_stream_out_t* out, uint64_t partition_bytes, const ppr_parse_opts_t* opts);
+
+/*
+ * Columnar partition [P Sec. 3: symbols partitioned by column with a stable
+ * sort on their column tags, each column's concatenated symbol string (CSS),
+ * and an index of each field's record, offset and number of symbols, Fig. 5;
+ * the specialisations passage: inline-terminated and vector-delimited CSS,
+ * Fig. 6]. Input: the bytes a parse read and its per-field arrays (device,
+ * n_fields entries each; column ids below n_columns, at most 4096; a parse's
+ * max_columns is the right n_columns). Output, all device memory the caller
+ * provides:
+ *   rec, css_off, length [n_fields]: one entry per field, grouped by column
+ *     (column 0's fields, in input order, then column 1's, ...): the field's
+ *     record, the offset of its first byte in css, its length;
+ *   col_first_field, col_first_byte [n_columns + 1]: where each column's
+ *     entries and bytes start (the last element: n_fields and css_bytes);
+ *   css [css_cap]: the fields' raw spans (quotes included) in that order.
+ *     mode PPR_CSS_INDEXED: nothing between fields; PPR_CSS_INLINE: each field
+ *     followed by the byte `terminator` (e.g. 0x1E or 0x1F); PPR_CSS_VECTOR:
+ *     each field followed by a 0 byte, and aux[css_cap] holds 1 at those slots
+ *     and 0 elsewhere (so a field may hold any byte).
+ * Blocking; returns css_bytes. PPR_ECAPACITY (css_bytes set, nothing written
+ * at or beyond css_cap) if css_bytes > css_cap; PPR_EINVAL if a column id is
+ * not below n_columns (detected on the device: the outputs are then
+ * undefined); PPR_ETOOBIG if a CSS offset could exceed 32 bits. The workspace
+ * (ppr_columns_workspace_bytes, 256-byte aligned) needs no initialisation.
+ * opts may be NULL; only its stage_events are read: events recorded before
+ * the first and after each of the seven kernels (reset, histogram, scan,
+ * scatter, scan, bounds, copy; recorded in place of those skipped when
+ * n_fields is 0).
+ */
+enum { PPR_CSS_INDEXED = 0, PPR_CSS_INLINE = 1, PPR_CSS_VECTOR = 2 };
+
+typedef struct ppr_columns_out {
+    uint8_t* css;
+    uint8_t* aux;
+    uint64_t css_cap;
+    uint32_t* rec;
+    uint32_t* css_off;
+    uint32_t* length;
+    uint32_t* col_first_field;
+    uint32_t* col_first_byte;
+    uint64_t css_bytes; /* out */
+} ppr_columns_out_t;
+
+PPR_API size_t ppr_columns_workspace_bytes(uint64_t n_fields, uint32_t n_columns);
+
+PPR_API int ppr_columns(const uint8_t* d_bytes, uint64_t n, const uint32_t* d_rec, const uint32_t* d_col,
+                        const uint32_t* d_off, const uint32_t* d_len, uint64_t n_fields, uint32_t n_columns,
+                        uint32_t mode, uint32_t terminator, ppr_columns_out_t* out, void* d_ws, size_t ws_bytes,
+                        const ppr_parse_opts_t* opts, void* stream);
 
 /* ------------------------------------------------------------------ lexer */
 
@@ -344,6 +396,8 @@ typedef struct ppr_tokens_out {
     uint32_t path;     /* out: the kernels that ran (PPR_PATH_STREAMING or PPR_PATH_SINGLE_PASS) */
 } ppr_tokens_out_t;
 
+/* Workspace bytes ppr_lex needs for n input bytes (opts may be NULL): 256-byte
+ * aligned, no initialisation needed; 0 on invalid arguments. */
 PPR_API size_t ppr_lex_workspace_bytes(uint64_t n, const ppr_parse_opts_t* opts);
 
 /* Lex n bytes (n <= 2^32 - 2^16, else PPR_ETOOBIG). Blocking. PPR_ECAPACITY if n_tokens > cap_tokens. */
