@@ -212,8 +212,8 @@ def stream_bench(args, cfg_id, cfg, ppr, torch, W, np):
                                 "buffers included), median"}), flush=True)
 
 
-COLUMN_STAGES = ["cols_reset_kernel", "cols_hist_kernel", "cols_scan_kernel#1", "cols_scatter_kernel",
-                 "cols_scan_kernel#2", "cols_bounds_kernel", "cols_copy_kernel"]
+COLUMN_STAGES = ["cols_reset_kernel", "cols_hist_kernel", "cols_scan_kernel#counts", "cols_scan_kernel#bytes",
+                 "cols_part_kernel", "cols_bounds_kernel"]
 
 
 def columns_bench(args, cfg_id, cfg, ppr, torch, W, np):
@@ -260,11 +260,11 @@ def columns_bench(args, cfg_id, cfg, ppr, torch, W, np):
     field_bytes = css - slot * nf  # the fields' own bytes, read once from the input
     aux = css if mode == ppr.PPR_CSS_VECTOR else 0
     # algorithmic bytes, each attributed to the kernel that moves it: the four field arrays read once (16 B per
-    # field: the histogram reads the columns, the scatter the rest), the index written once (rec and length by the
-    # scatter, css_off by the second scan: 12 B per field), the field bytes read once and the CSS (and aux) written
-    # once (the copy kernel), the bounds (8 B per column)
-    alg = {"cols_hist_kernel": 4 * nf, "cols_scatter_kernel": 12 * nf + 8 * nf, "cols_scan_kernel#2": 4 * nf,
-           "cols_bounds_kernel": 8 * (nc + 1), "cols_copy_kernel": field_bytes + css + aux}
+    # field: the histogram reads columns and lengths, the partition kernel the rest), the index written once (12 B per
+    # field), the field bytes read once and the CSS (and aux) written once (all three by the partition kernel),
+    # the bounds (8 B per column)
+    alg = {"cols_hist_kernel": 8 * nf, "cols_part_kernel": 8 * nf + 12 * nf + field_bytes + css + aux,
+           "cols_bounds_kernel": 8 * (nc + 1)}
     step_alg = 16 * nf + 12 * nf + field_bytes + css + aux + 8 * (nc + 1)
     dominant = max(stage_ms, key=stage_ms.get)
     t_dom = stage_ms[dominant] * 1e-3

@@ -352,7 +352,7 @@ class Columns:
         self.bounds = [torch.empty(self.n_columns + 1, dtype=torch.int32, device=self.device) for _ in range(2)]
 
     def __call__(self, data: torch.Tensor, res: "ParseResult", stream=None, stage_events=None) -> ColumnsResult:
-        """stage_events: optional list of 8 torch.cuda.Event recorded before and after the call's kernels"""
+        """stage_events: optional list of 7 torch.cuda.Event recorded before and after the call's kernels"""
         _check_input(data)
         opts, keep = _opts_with_events(_opts(None), stage_events)
         o = ColumnsOut()

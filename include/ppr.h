@@ -301,9 +301,9 @@ PPR_API int ppr_parse_stream(const uint8_t* h_bytes, uint64_t n, const ppr_dfa_t
  * undefined); PPR_ETOOBIG if a CSS offset could exceed 32 bits. The workspace
  * (ppr_columns_workspace_bytes, 256-byte aligned) needs no initialisation.
  * opts may be NULL; only its stage_events are read: events recorded before
- * the first and after each of the seven kernels (reset, histogram, scan,
- * scatter, scan, bounds, copy; recorded in place of those skipped when
- * n_fields is 0).
+ * the first and after each of the six kernels (reset, histogram, scan of the
+ * counts, scan of the bytes, partition, bounds; recorded in place of those
+ * skipped when n_fields is 0).
  */
 enum { PPR_CSS_INDEXED = 0, PPR_CSS_INLINE = 1, PPR_CSS_VECTOR = 2 };
 
