@@ -15,9 +15,11 @@ state map f, a map p telling from which states its last byte ends a token:
                               delta(q0, c)           otherwise (restart),
                       p_c(q) = 1 if delta(q, c) is undefined, else 0;
   product (earlier a, later b):  (f_b o f_a,  p_b o f_a)  for non-empty a, b;
-  identity: the empty string's element, neutral on both sides. (It is written
-  (id, 0), but the product rule would turn a.(id, 0) into (f_a, 0) and drop
-  a's flag, so the empty element is special-cased: a.e = a, e.b = b.)
+  identity: the empty string's element, neutral on both sides: a.e = a,
+  e.b = b. It is an element of its own, apart from every non-empty element,
+  even one whose maps are (id, 0): the product rule turns a.(id, 0) into
+  (f_a, 0), clearing a's flag (a byte that keeps every state and ends no
+  token), while a.e keeps it.
 
 Table entries: merge[a][b] = id(a.b), with the flag bit set when p_{a.b}(q0)
 is 1; initial_state[c] = id(element of c) (with the same flag rule);
@@ -34,16 +36,17 @@ def element_of_byte(d, c):
     return f, p
 
 
+EMPTY = ()  # the empty string's element (non-empty elements are (f, p) pairs)
+
+
 def identity(Q):
-    return tuple(range(Q)), (0,) * Q
+    return EMPTY
 
 
 def product(a, b):
-    Q = len(a[0])
-    e = identity(Q)
-    if b == e:
+    if b == EMPTY:
         return a
-    if a == e:
+    if a == EMPTY:
         return b
     (fa, pa), (fb, pb) = a, b
     return tuple(fb[x] for x in fa), tuple(pb[x] for x in fa)
@@ -74,10 +77,10 @@ def build_tables(d, flag=0x8000, max_k=20000):
     k = len(order)
 
     def entry(e):
-        return ids[e] | (flag if e[1][q0] else 0)
+        return ids[e] | (flag if e != EMPTY and e[1][q0] else 0)
 
     merge = [[entry(product(a, b)) for b in order] for a in order]
     init = [entry(e) for e in byte_elem]
-    final = [int(d["kind"][f[q0]]) for f, _ in order]
+    final = [int(d["kind"][q0 if e == EMPTY else e[0][q0]]) for e in order]
     return {"k": k, "identity": 0, "initial_state": init, "merge_table": merge, "final_states": final,
             "elements": order}

@@ -246,3 +246,24 @@ def toy_dfa():
     """Three rules: ID=[a-z]+, NUM=[0-9]+, WS=' '+ (a small hand-checkable grammar)."""
     rules = [("ID", plus(Set(rng("a", "z")))), ("NUM", plus(Set(DIGIT))), ("WS", plus(Set(b" ")))]
     return compile_rules(rules)
+
+
+def random_token_dfa(seed: int, n_states: int, n_cols: int, p_undefined: float = 0.3, n_kinds: int = 6):
+    """A seeded random token DFA (same dict format as compile_rules): the 256
+    bytes fall into n_cols byte classes (every class used), each state has a
+    random successor or none (-1) per class, the start state 0 has a successor
+    for every class, and every state a random kind in [0, n_kinds)."""
+    r = np.random.default_rng(seed)
+    col_of = np.concatenate([np.arange(n_cols), r.integers(0, n_cols, 256 - n_cols)])
+    r.shuffle(col_of)
+    table = r.integers(0, n_states, (n_states, n_cols))
+    undefined = r.random((n_states, n_cols)) < p_undefined
+    undefined[0, :] = False
+    table[undefined] = -1
+    return {
+        "n_states": n_states,
+        "q0": 0,
+        "delta": table[:, col_of].astype(np.int16),
+        "kind": r.integers(0, n_kinds, n_states).astype(np.uint16),
+        "kind_names": tuple("K%d" % i for i in range(n_kinds)),
+    }
