@@ -188,6 +188,7 @@ def sha256(a: np.ndarray) -> str:
 lexer_dfa = _lexgrammar.lexer_dfa
 toy_dfa = _lexgrammar.toy_dfa
 random_token_dfa = _lexgrammar.random_token_dfa
+keyword_chain_dfa = _lexgrammar.keyword_chain_dfa
 
 _PATTERN_FIRST = {
     1: set(_lexgrammar.ALPHA),

@@ -267,3 +267,23 @@ def random_token_dfa(seed: int, n_states: int, n_cols: int, p_undefined: float =
         "kind": r.integers(0, n_kinds, n_states).astype(np.uint16),
         "kind_names": tuple("K%d" % i for i in range(n_kinds)),
     }
+
+
+def keyword_chain_dfa(length: int, seed: int):
+    """A token DFA for one keyword of `length` distinct bytes (a seeded
+    permutation of 1..255): state i has read the keyword's first i bytes, the
+    keyword's next byte moves on, anything else ends the token; the start row
+    sends every other byte to the dead state E. Kinds: KEYWORD for the whole
+    keyword, PART for a proper prefix, ERROR for E. Returns (dfa, keyword)."""
+    r = np.random.default_rng(seed)
+    word = r.permutation(np.arange(1, 256))[:length]
+    Q, E = length + 2, length + 1
+    delta = np.full((Q, 256), -1, dtype=np.int16)
+    delta[0, :] = E
+    delta[0, word[0]] = 1
+    for i in range(1, length):
+        delta[i, word[i]] = i + 1
+    kind = np.full(Q, 2, dtype=np.uint16)
+    kind[length], kind[E], kind[0] = 1, 0, 0
+    return ({"n_states": Q, "q0": 0, "delta": delta, "kind": kind, "kind_names": ("ERROR", "KEYWORD", "PART")},
+            bytes(word.astype(np.uint8)))
