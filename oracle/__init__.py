@@ -20,6 +20,10 @@ no code, header, table or helper with the GPU library, and it never imports it.
 * ``columns.partition``: the columnar partition of one parse's fields into
   per-column concatenated symbol strings and their index (ParPaRaw, Sec. 3,
   Fig. 5; inline-terminated and vector-delimited variants, Fig. 6).
+* ``numbers.infer`` / ``numbers.convert``: each field's minimal numeric type
+  and each column's (the maximum over its fields), and the fields' values in
+  their column's type (ParPaRaw, "Type inference", "Default values for empty
+  strings"; Sec. 3, conversion to the column's type).
 
 Beside the oracle, and not part of it: ``csv_parse_parallel`` and
 ``lex_restart_parallel`` (cpu_parallel.c), the all-core CPU baseline that the

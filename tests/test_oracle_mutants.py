@@ -275,3 +275,51 @@ def test_columns_mutant_is_caught(mutant, monkeypatch):
 
 def test_unmutated_columns_passes_same_pins():
     assert _columns_pins_pass()
+
+
+NUMBERS_MUTANTS = {
+    "width_top_inclusive": ("-(1 << (bits - 1)) <= v < (1 << (bits - 1))", "-(1 << (bits - 1)) <= v <= (1 << (bits - 1))"),
+    "fraction_digits_added": ("- len(fp) +", "+ len(fp) +"),
+    "trailing_zeros_kept": ('stripped = digits.rstrip(b"0")', "stripped = digits"),
+    "column_minimum": ("ct[c] = max(ct[c], t)", "ct[c] = min(ct[c], t)"),
+    "exponent_bound_23": ("    if -22 <= e10 <= 22:\n", "    if -23 <= e10 <= 23:\n"),
+    "mantissa_bound_2_54": ("if w > 1 << 53:", "if w > 1 << 54:"),
+    "int64_overflow_text": ("        return FLOAT64\n    if _FLOAT", "        return TEXT\n    if _FLOAT"),
+    "mismatch_only_text": ("        elif t > ct:", "        elif t > ct and t == TEXT:"),
+}
+
+
+def _numbers_mutant(name):
+    import types
+    src = open(os.path.join(ORACLE_DIR, "numbers.py")).read()
+    old, new = NUMBERS_MUTANTS[name]
+    assert src.count(old) == 1, (name, old)
+    mod = types.ModuleType("numbers_mutant")
+    exec(compile(src.replace(old, new), "numbers_mutant.py", "exec"), mod.__dict__)
+    return mod
+
+
+def _numbers_pins_pass(mod, monkeypatch):
+    from tests import test_oracle_numbers as T
+    monkeypatch.setattr(T, "N", mod)
+    try:
+        for text, want in T.HAND_TYPES:
+            T.test_hand_worked_types(text, want)
+        T.test_width_boundaries()
+        T.test_decompose_against_fractions()
+        T.test_exact_class_one_rounding()
+        T.test_infer_reduction()
+        T.test_convert_hand_worked()
+    except (AssertionError, IndexError, ValueError):
+        return False
+    return True
+
+
+@pytest.mark.parametrize("mutant", sorted(NUMBERS_MUTANTS))
+def test_numbers_mutant_is_caught(mutant, monkeypatch):
+    assert not _numbers_pins_pass(_numbers_mutant(mutant), monkeypatch), mutant
+
+
+def test_unmutated_numbers_passes_same_pins(monkeypatch):
+    from oracle import numbers
+    assert _numbers_pins_pass(numbers, monkeypatch)
