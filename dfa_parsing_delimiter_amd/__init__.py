@@ -33,6 +33,8 @@ PPR_OK, PPR_EINVAL, PPR_ECAPACITY, PPR_ETOOBIG, PPR_EHIP, PPR_EWORKSPACE = 0, -1
 PPR_PATH_STREAMING, PPR_PATH_SINGLE_PASS, PPR_PATH_FUSED = 1, 2, 3
 PPR_PARSE_CONTINUE, PPR_PARSE_PARTIAL = 1, 2
 PPR_CSS_INDEXED, PPR_CSS_INLINE, PPR_CSS_VECTOR = 0, 1, 2
+PPR_NUM_EMPTY, PPR_NUM_INT8, PPR_NUM_INT16, PPR_NUM_INT32, PPR_NUM_INT64, PPR_NUM_FLOAT64, PPR_NUM_TEXT = range(7)
+PPR_NUM_OK, PPR_NUM_DEFAULTED, PPR_NUM_MISMATCH, PPR_NUM_INEXACT, PPR_NUM_NOT_CONVERTED = range(5)
 _ERRNAMES = {-1: "PPR_EINVAL", -2: "PPR_ECAPACITY", -3: "PPR_ETOOBIG", -4: "PPR_EHIP", -5: "PPR_EWORKSPACE"}
 TAG_VALUE, TAG_FIELD, TAG_RECORD, TAG_INVALID = 0, 1, 2, 3
 
@@ -71,6 +73,12 @@ class ColumnsOut(ctypes.Structure):
                 ("rec", ctypes.c_void_p), ("css_off", ctypes.c_void_p), ("length", ctypes.c_void_p),
                 ("col_first_field", ctypes.c_void_p), ("col_first_byte", ctypes.c_void_p),
                 ("css_bytes", ctypes.c_uint64)]
+
+
+class FieldsC(ctypes.Structure):
+    _fields_ = [("bytes", ctypes.c_void_p), ("n_bytes", ctypes.c_uint64), ("off", ctypes.c_void_p),
+                ("len", ctypes.c_void_p), ("col", ctypes.c_void_p), ("col_first", ctypes.c_void_p),
+                ("n_fields", ctypes.c_uint64), ("n_columns", ctypes.c_uint32)]
 
 
 class StreamOut(ctypes.Structure):
@@ -120,6 +128,13 @@ def _load():
     L.ppr_columns.argtypes = [P, U64, P, P, P, P, U64, U32, U32, U32, ctypes.POINTER(ColumnsOut), P, ctypes.c_size_t,
                               ctypes.POINTER(ParseOpts), P]
     L.ppr_columns.restype = ctypes.c_int
+    L.ppr_numbers_workspace_bytes.argtypes = [U32]
+    L.ppr_numbers_workspace_bytes.restype = ctypes.c_size_t
+    L.ppr_infer_types.argtypes = [ctypes.POINTER(FieldsC), P, P, P, ctypes.c_size_t, P]
+    L.ppr_infer_types.restype = ctypes.c_int
+    L.ppr_convert.argtypes = [ctypes.POINTER(FieldsC), P, ctypes.c_int64, ctypes.c_double, P, P, P, P, ctypes.c_size_t,
+                              P]
+    L.ppr_convert.restype = ctypes.c_int
     L.ppr_parse_results.argtypes = [P, U64, ctypes.POINTER(ParseOut), P]
     L.ppr_parse_results.restype = ctypes.c_int
     L.ppr_lex_fold_bytes.argtypes = [U32]
@@ -379,6 +394,71 @@ def columns(data: torch.Tensor, res: "ParseResult", n_columns: int | None = None
     their index (one call; n_columns defaults to the parse's max_columns)."""
     nc = int(res.max_columns if n_columns is None else n_columns)
     return Columns(res.n_fields, nc, data.numel(), mode, terminator, data.device)(data, res, stream)
+
+
+class Fields:
+    """Spans (off, len) of a device byte tensor, with their columns: col (per
+    field) or col_first (fields grouped by column) or neither (one column)."""
+
+    def __init__(self, data: torch.Tensor, off: torch.Tensor, length: torch.Tensor, n_columns: int = 1,
+                 col: torch.Tensor | None = None, col_first: torch.Tensor | None = None):
+        _check_input(data)
+        self.keep = (data, off, length, col, col_first)
+        self.c = FieldsC(data.data_ptr(), data.numel(), off.data_ptr() if off.numel() else None,
+                         length.data_ptr() if length.numel() else None,
+                         col.data_ptr() if col is not None and col.numel() else None,
+                         col_first.data_ptr() if col_first is not None else None, off.numel(), int(n_columns))
+        self.device = data.device
+
+    @classmethod
+    def of_parse(cls, data: torch.Tensor, res: "ParseResult", n_columns: int | None = None):
+        return cls(data, res.field_offsets, res.field_lengths, max(1, res.max_columns if n_columns is None else n_columns),
+                   col=res.column_ids)
+
+    @classmethod
+    def of_columns(cls, cols: "ColumnsResult"):
+        return cls(cols.css, cols.css_off, cols.length, max(1, cols.n_columns), col_first=cols.col_first_field)
+
+
+def _num_ws(n_columns, device):
+    nbytes = lib.ppr_numbers_workspace_bytes(int(n_columns))
+    if nbytes == 0:
+        raise PprError(PPR_EINVAL, "ppr_numbers_workspace_bytes")
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    return ws, (-ws.data_ptr()) % 256, nbytes
+
+
+def infer_types(fields: Fields, field_types: bool = False, stream=None):
+    """(column types as a numpy uint32 array, per-field types as a device uint8 tensor or None)"""
+    ws, off, nbytes = _num_ws(fields.c.n_columns, fields.device)
+    ft = torch.empty(max(1, fields.c.n_fields), dtype=torch.uint8, device=fields.device) if field_types else None
+    ct = np.zeros(fields.c.n_columns, dtype=np.uint32)
+    _check(lib.ppr_infer_types(ctypes.byref(fields.c), ctypes.c_void_p(ft.data_ptr()) if ft is not None else None,
+                               ct.ctypes.data, ctypes.c_void_p(ws.data_ptr() + off), nbytes, _stream_handle(stream)),
+           "ppr_infer_types")
+    return ct, (ft[:fields.c.n_fields] if ft is not None else None)
+
+
+@dataclass
+class Converted:
+    values: torch.Tensor   # int64 per field (device): the value, or the double's bits for FLOAT64 columns
+    status: torch.Tensor   # uint8 per field (device): PPR_NUM_OK ... PPR_NUM_NOT_CONVERTED
+    counts: np.ndarray     # fields with status 1..4
+
+
+def convert(fields: Fields, column_types, int_default: int = 0, float_default: float = 0.0, stream=None) -> Converted:
+    ws, off, nbytes = _num_ws(fields.c.n_columns, fields.device)
+    n = fields.c.n_fields
+    vals = torch.empty(max(1, n), dtype=torch.int64, device=fields.device)
+    st = torch.empty(max(1, n), dtype=torch.uint8, device=fields.device)
+    ct = np.ascontiguousarray(column_types, dtype=np.uint32)
+    if ct.size != fields.c.n_columns:
+        raise ValueError("one type per column")
+    counts = np.zeros(4, dtype=np.uint64)
+    _check(lib.ppr_convert(ctypes.byref(fields.c), ct.ctypes.data, int(int_default), float(float_default),
+                           ctypes.c_void_p(vals.data_ptr()), ctypes.c_void_p(st.data_ptr()), counts.ctypes.data,
+                           ctypes.c_void_p(ws.data_ptr() + off), nbytes, _stream_handle(stream)), "ppr_convert")
+    return Converted(vals[:n], st[:n], counts)
 
 
 @dataclass

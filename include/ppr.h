@@ -447,6 +447,76 @@ PPR_API const char* ppr_version(void);
 PPR_API int ppr_bandwidth_probe(uint32_t mode, uint32_t pattern, const void* d_src, void* d_dst, uint64_t bytes,
                                 uint32_t grid, void* stream);
 
+/*
+ * Numeric type inference and conversion [P "Type inference" (each field's
+ * minimal numerical type, a reduction over the column's fields), "Default
+ * values for empty strings", and Sec. 3 (fields converted to their column's
+ * type, threads alone on short fields and collaborating on long ones)].
+ *
+ * A field is a span (off, len) of `bytes` (device): a parse's fields in the
+ * input, or a CSS index's entries in the CSS. Its text is the raw span (quotes
+ * included: a quoted number is TEXT). Types, ordered:
+ *   EMPTY (no symbols) < INT8 < INT16 < INT32 < INT64 < FLOAT64 < TEXT.
+ * INT: optional sign and decimal digits, typed by the smallest signed width
+ * holding the value (beyond int64: FLOAT64). FLOAT64: optional sign, digits
+ * with a point (a digit on at least one side) or without, then an optional
+ * exponent (e/E, optional sign, digits), with a point or an exponent present.
+ * Anything else is TEXT. A column's type is the largest of its fields'.
+ *
+ * Columns: col[j] per field (device, may be NULL); else col_first[n_columns +
+ * 1] (device: fields grouped by column, as ppr_columns' col_first_field); else
+ * a single column. 1 <= n_columns <= 4096. A column id >= n_columns counts in
+ * no column (its field converts to PPR_NUM_NOT_CONVERTED). A span past
+ * n_bytes is TEXT (never for a parse's own fields).
+ */
+enum { PPR_NUM_EMPTY = 0, PPR_NUM_INT8 = 1, PPR_NUM_INT16 = 2, PPR_NUM_INT32 = 3, PPR_NUM_INT64 = 4,
+       PPR_NUM_FLOAT64 = 5, PPR_NUM_TEXT = 6 };
+/* per-field conversion status */
+enum { PPR_NUM_OK = 0, PPR_NUM_DEFAULTED = 1, PPR_NUM_MISMATCH = 2, PPR_NUM_INEXACT = 3, PPR_NUM_NOT_CONVERTED = 4 };
+
+typedef struct ppr_fields {
+    const uint8_t* bytes;
+    uint64_t n_bytes;
+    const uint32_t* off;
+    const uint32_t* len;
+    const uint32_t* col;
+    const uint32_t* col_first;
+    uint64_t n_fields;
+    uint32_t n_columns;
+} ppr_fields_t;
+
+/* Workspace bytes of ppr_infer_types / ppr_convert (256-byte aligned, no
+ * initialisation needed); 0 if n_columns is 0 or above 4096. */
+PPR_API size_t ppr_numbers_workspace_bytes(uint32_t n_columns);
+
+/*
+ * Blocking. column_type (host, n_columns): each column's type. d_field_type
+ * (device, n_fields bytes, may be NULL): each field's type.
+ */
+PPR_API int ppr_infer_types(const ppr_fields_t* f, uint8_t* d_field_type, uint32_t* column_type, void* d_ws,
+                            size_t ws_bytes, void* stream);
+
+/*
+ * Blocking. Converts every field to its column's type (column_type: host,
+ * n_columns, PPR_NUM_* values, e.g. from ppr_infer_types). d_values (device,
+ * n_fields x 8 bytes): int64 for EMPTY and INT columns, the double's bits for
+ * FLOAT64 columns, 0 for TEXT columns. d_status (device, n_fields bytes):
+ *   PPR_NUM_OK            converted;
+ *   PPR_NUM_DEFAULTED     empty field: int_default or float_default;
+ *   PPR_NUM_MISMATCH      the field's own type is above the column's: the default;
+ *   PPR_NUM_INEXACT       a FLOAT64 column's number outside the exactly converted
+ *                         class: NaN. The class: with w the mantissa's digits
+ *                         without leading and trailing zeros and |value| =
+ *                         w * 10^e, w <= 2^53 and |e| <= 22, or e > 22 and
+ *                         w * 10^(e - 22) <= 2^53 (one IEEE operation on exact
+ *                         doubles rounds correctly, to nearest even), or w = 0;
+ *   PPR_NUM_NOT_CONVERTED a TEXT column (or a column id >= n_columns): 0.
+ * counts (host, may be NULL): fields with status 1, 2, 3 and 4.
+ */
+PPR_API int ppr_convert(const ppr_fields_t* f, const uint32_t* column_type, int64_t int_default, double float_default,
+                        uint64_t* d_values, uint8_t* d_status, uint64_t counts[4], void* d_ws, size_t ws_bytes,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

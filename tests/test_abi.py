@@ -29,7 +29,8 @@ def test_library_exports_every_declared_symbol():
                             "ppr_lex_fold_bytes", "ppr_lex_prepare", "ppr_lex_workspace_bytes", "ppr_lex",
                             "ppr_lex_async", "ppr_lex_results", "ppr_lex_build_tables", "ppr_version",
                             "ppr_bandwidth_probe", "ppr_parse_noalloc", "ppr_parse_stream", "ppr_columns",
-                            "ppr_columns_workspace_bytes"]), names
+                            "ppr_columns_workspace_bytes", "ppr_numbers_workspace_bytes", "ppr_infer_types",
+                            "ppr_convert"]), names
     for nm in names:
         assert hasattr(ppr.lib, nm), nm
     assert "gfx950" in ppr.version()

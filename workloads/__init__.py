@@ -190,6 +190,10 @@ toy_dfa = _lexgrammar.toy_dfa
 random_token_dfa = _lexgrammar.random_token_dfa
 keyword_chain_dfa = _lexgrammar.keyword_chain_dfa
 
+from . import numtext as _numtext  # noqa: E402
+
+numeric_csv = _numtext.numeric_csv
+
 _PATTERN_FIRST = {
     1: set(_lexgrammar.ALPHA),
     2: set(_lexgrammar.DIGIT),
