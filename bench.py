@@ -325,6 +325,92 @@ def columns_bench(args, cfg_id, cfg, ppr, torch, W, np):
     print(json.dumps(line), flush=True)
 
 
+def numbers_bench(args, cfg_id, cfg, ppr, torch, W, np):
+    """GB/s of numeric type inference plus conversion (ppr_infer_types, then
+    ppr_convert to the inferred types) over a workload's parse: the input and
+    the parse's field arrays resident in HBM, one blocking call of each per
+    step"""
+    import oracle
+    from oracle import numbers as N
+    assert cfg["kind"] == "csv", "numbers follow a delimiter-separated parse"
+    log("generating", cfg["name"], cfg["n"], "bytes")
+    data = W.generate(cfg_id)
+    sha = W.sha256(data)
+    n = data.size
+    dev = torch.device("cuda:0")
+    d = torch.from_numpy(data).to(dev)
+    table = W.table(cfg["table"])
+    g = ppr.Parser(table, max_n=n, capacity=n // 4 + 4096, device=dev)(d)
+    F = ppr.Fields.of_parse(d, g)
+    nf = g.n_fields
+    types, _ = ppr.infer_types(F)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        ppr.infer_types(F)
+        ppr.convert(F, types)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for a, b, c in ev:
+        a.record(stream)
+        ppr.infer_types(F)
+        b.record(stream)
+        cv = ppr.convert(F, types)
+        c.record(stream)
+    torch.cuda.synchronize()
+    t_inf = [a.elapsed_time(b) for a, b, _ in ev]
+    t_cnv = [b.elapsed_time(c) for _, b, c in ev]
+    ms = statistics.median([x + y for x, y in zip(t_inf, t_cnv)])
+    field_bytes = int(g.field_lengths.to(torch.int64).sum().item())
+    # algorithmic bytes: each call reads the field arrays it needs (offset, length, column: 12 B per field) and the
+    # fields' bytes; conversion writes 9 B per field (value and status)
+    alg = {"num_kernel<infer>": 12 * nf + field_bytes, "num_kernel<convert>": 12 * nf + field_bytes + 9 * nf}
+    stage_ms = {"num_kernel<infer>": statistics.mean(t_inf), "num_kernel<convert>": statistics.mean(t_cnv)}
+    dominant = max(stage_ms, key=stage_ms.get)
+    t_dom = stage_ms[dominant] * 1e-3
+    step_alg = sum(alg.values())
+    line = {"metric": "numeric type inference + conversion GB/s (input bytes of the parse per second)",
+            "value": round(n / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "%s_%dMiB_numbers" % (cfg["name"], n >> 20), "n_bytes": n, "fields": nf,
+                       "columns": int(types.size), "column_types": [N.TYPE_NAMES[int(t)] for t in types],
+                       "input_sha256": sha[:16], "kernels": list(alg)},
+            "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(alg[dominant] / t_dom / 1e9, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(alg[dominant] / t_dom / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes_per_launch": alg[dominant], "kernel_ms": round(stage_ms[dominant], 4),
+                         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+                         "step": {"algorithmic_bytes": step_alg, "achieved": round(step_alg / (ms * 1e-3) / 1e9, 2),
+                                  "frac": round(step_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                         "statuses": {"defaulted": int(cv.counts[0]), "mismatch": int(cv.counts[1]),
+                                      "inexact": int(cv.counts[2]), "not_converted": int(cv.counts[3])},
+                         "timing": "HIP events on the launch stream around each blocking call (a reset kernel and "
+                                   "the main kernel each), median of %d steps" % args.steps}}
+    if not args.no_cpu:
+        log("cpu oracle baseline (numbers)")
+        info, _ = host_cpu()
+        k = min(nf, 1 << 20)
+        off = g.field_offsets[:k].cpu().numpy().view(np.uint32).astype(np.int64)
+        ln = g.field_lengths[:k].cpu().numpy().view(np.uint32).astype(np.int64)
+        r = oracle.csv_parse(data[:int(off[-1] + ln[-1]) + 1], table)
+        t0 = time.perf_counter()
+        oft, _ = N.infer(data, r["off"][:k], r["len"][:k], r["col"][:k], int(types.size))
+        ov, ost = N.convert(data, r["off"][:k], r["len"][:k], r["col"][:k], types, 0, 0.0)
+        dt = time.perf_counter() - t0
+        span = int(r["off"][k - 1] + r["len"][k - 1])
+        line["cpu_baseline"] = {"value": round(span / dt / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                                "sample": "the first %d fields (%d input bytes), oracle inference and conversion "
+                                          "(Python regular expressions, int(), float()), one run" % (k, span),
+                                "host": info}
+        _, ft = ppr.infer_types(F, field_types=True)
+        ok = np.array_equal(ft[:k].cpu().numpy(), oft)
+        ok = ok and np.array_equal(cv.status[:k].cpu().numpy(), ost)
+        ok = ok and np.array_equal(cv.values[:k].cpu().numpy(), ov)
+        line["parity_vs_oracle"] = ("bit-exact (types, values, statuses) on the first %d fields" % k if ok
+                                    else "MISMATCH")
+    print(json.dumps(line), flush=True)
+
+
 def read_pmc(d, counter):
     """counter value of every dispatch, by kernel name, from a rocprofv3 csv output directory"""
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -421,6 +507,8 @@ def main():
                          "many MiB (transfers, parse and returns overlapped; PCIe-inclusive, not the metric)")
     ap.add_argument("--columns", choices=["indexed", "inline", "vector"], default=None,
                     help="instead: time the columnar partition (ppr_columns) of the workload's parse in this mode")
+    ap.add_argument("--numbers", action="store_true",
+                    help="instead: time numeric type inference and conversion over the workload's parse")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the device bandwidth probe (read / write / copy of 1 GiB)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -451,6 +539,8 @@ def main():
         return stream_bench(args, cfg_id, cfg, ppr, torch, W, np)
     if args.columns:
         return columns_bench(args, cfg_id, cfg, ppr, torch, W, np)
+    if args.numbers:
+        return numbers_bench(args, cfg_id, cfg, ppr, torch, W, np)
     log("generating", cfg["name"], cfg["n"], "bytes")
     t0 = time.time()
     data = W.generate(cfg_id)

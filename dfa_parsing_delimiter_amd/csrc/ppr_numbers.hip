@@ -63,10 +63,16 @@ constexpr uint32_t kOnSign[10] = {NSIGN, NX, NX, NX, NX, NX, NESIGN, NX, NX, NX}
 constexpr uint32_t kOnPoint[10] = {NPOINT, NPOINT, NDOT, NX, NX, NX, NX, NX, NX, NX};
 constexpr uint32_t kOnExp[10] = {NX, NX, NE, NE, NX, NE, NX, NX, NX, NX};
 constexpr uint32_t kOnOther[10] = {NX, NX, NX, NX, NX, NX, NX, NX, NX, NX};
-__constant__ uint64_t kNumNext[5] = {pack_next(kOnDigit), pack_next(kOnSign), pack_next(kOnPoint), pack_next(kOnExp),
-                                     pack_next(kOnOther)};
+constexpr uint64_t kNextDigit = pack_next(kOnDigit), kNextSign = pack_next(kOnSign), kNextPoint = pack_next(kOnPoint),
+                   kNextExp = pack_next(kOnExp), kNextOther = pack_next(kOnOther);
 
-__device__ __forceinline__ uint32_t num_step(uint32_t s, uint32_t c) { return (uint32_t)(kNumNext[c] >> (4 * s)) & 15u; }
+// the transitions of class c, from immediates (a per-lane index into a table
+// in memory would be a vector load per byte)
+__device__ __forceinline__ uint64_t num_next(uint32_t c)
+{
+    return c == 0u ? kNextDigit : c == 1u ? kNextSign : c == 2u ? kNextPoint : c == 3u ? kNextExp : kNextOther;
+}
+__device__ __forceinline__ uint32_t num_step(uint32_t s, uint32_t c) { return (uint32_t)(num_next(c) >> (4 * s)) & 15u; }
 
 constexpr uint64_t kTwo53 = 1ull << 53;
 constexpr uint64_t kTwo63 = 1ull << 63;
@@ -83,13 +89,8 @@ struct NumAcc {
 
 __device__ __forceinline__ NumAcc num_init() { return NumAcc{NS0, 0u, 0u, 0u, 0u, 0u, 0ull, 0ull, 0ull, 0ull}; }
 
-__device__ __forceinline__ void num_fold_sig(NumAcc& a, uint32_t d)
+__device__ __forceinline__ void num_fold_sig_slow(NumAcc& a, uint32_t d)
 {
-    if (a.big) return;
-    if (d == 0) {
-        if (a.w) ++a.z;  // (a leading zero adds nothing)
-        return;
-    }
     uint64_t w = a.w;
     for (uint32_t k = 0; k <= a.z; ++k) {  // w * 10^(z + 1), stopping beyond 2^53
         w *= 10u;
@@ -107,6 +108,51 @@ __device__ __forceinline__ void num_fold_sig(NumAcc& a, uint32_t d)
     a.z = 0;
 }
 
+// a significant digit into (w, z): zeros stay pending, a nonzero digit
+// multiplies them in; the common case (no pending zeros, w far below 2^53)
+// is one multiply-add
+__device__ __forceinline__ void num_fold_sig(NumAcc& a, uint32_t d)
+{
+    if (a.big) return;
+    if (d == 0) {
+        if (a.w) ++a.z;  // (a leading zero adds nothing)
+    } else if (a.z == 0 && a.w < kTwo53 / 10u) {
+        a.w = a.w * 10u + d;
+    } else {
+        num_fold_sig_slow(a, d);
+    }
+}
+
+// One byte, without branches (selects) where the thread is active (act); the
+// rare slow fold (pending zeros, or w near 2^53) is the only branch.
+__device__ __forceinline__ void num_byte_p(NumAcc& a, uint32_t b, bool act)
+{
+    const uint32_t c = num_class(b), s = a.s, d = b - '0';
+    const bool dig = act && c == 0u;
+    const bool in_int = s <= NINT, in_frac = s >= NDOT && s <= NFRAC, in_exp = s >= NE && s <= NEXP;
+    const bool minus = b == '-';
+    a.neg = (act && c == 1u && s == NS0) ? minus : a.neg;
+    a.eneg = (act && c == 1u && s == NE) ? minus : a.eneg;
+    // integer magnitude, up to 2^63
+    const bool upd = dig && in_int && !a.mag_ovf;
+    const bool fits = a.mag < kTwo63 / 10u || (a.mag == kTwo63 / 10u && d <= 8u);
+    const uint64_t m10 = a.mag * 10u + d;
+    a.mag = upd && fits ? m10 : a.mag;
+    a.mag_ovf |= (upd && !fits) ? 1u : 0u;
+    // fraction digits and exponent
+    a.frac += (dig && in_frac) ? 1u : 0u;
+    const uint64_t e10 = min(a.ev * 10u + d, kExpCap);
+    a.ev = (dig && in_exp) ? e10 : a.ev;
+    // significant digits: zeros pending, one multiply-add in the common case
+    const bool sig = dig && (in_int || in_frac) && !a.big;
+    const bool zero = d == 0u;
+    const bool fast = sig && !zero && a.z == 0u && a.w < kTwo53 / 10u;
+    a.z += (sig && zero && a.w != 0u) ? 1u : 0u;
+    a.w = fast ? a.w * 10u + d : a.w;
+    if (sig && !zero && !fast) num_fold_sig_slow(a, d);
+    a.s = act ? num_step(s, c) : s;
+}
+
 __device__ __forceinline__ void num_byte(NumAcc& a, uint32_t b)
 {
     const uint32_t c = num_class(b), s = a.s;
@@ -116,9 +162,10 @@ __device__ __forceinline__ void num_byte(NumAcc& a, uint32_t b)
     } else if (c == 0u) {
         const uint32_t d = b - '0';
         if (s <= NINT) {  // integer part (S0, SIGN, INT)
-            if (!a.mag_ovf) {
-                if (a.mag > (kTwo63 - d) / 10u) a.mag_ovf = 1;
-                else a.mag = a.mag * 10u + d;
+            if (!a.mag_ovf) {  // up to 2^63: below 2^63 / 10 the next digit always fits
+                if (a.mag < kTwo63 / 10u) a.mag = a.mag * 10u + d;
+                else if (a.mag == kTwo63 / 10u && d <= 8u) a.mag = a.mag * 10u + d;
+                else a.mag_ovf = 1;
             }
             num_fold_sig(a, d);
         } else if (s <= NFRAC) {  // fraction (DOT, POINT, FRAC)
@@ -188,26 +235,28 @@ struct NumParams {
     unsigned long long* counts;  // convert: fields per status 1..4
 };
 
-__device__ __forceinline__ uint32_t column_of(const NumParams& p, uint64_t j)
+// s_cf: the columns' first fields in LDS (when the fields are grouped by column)
+__device__ __forceinline__ uint32_t column_of(const NumParams& p, uint64_t j, const uint32_t* s_cf)
 {
     if (p.col) return p.col[j];
     if (!p.col_first) return 0u;
     uint32_t lo = 0;  // the last column whose first field is at or before j
     for (uint32_t step = 1u << 12; step; step >>= 1)
-        if (lo + step < p.n_columns && p.col_first[lo + step] <= j) lo += step;
+        if (lo + step < p.n_columns && s_cf[lo + step] <= j) lo += step;
     return lo;
 }
 
 // a field's result: its type (infer), or its value and status (convert)
+// (convert: returns the status)
 template <bool CONVERT>
-__device__ __forceinline__ void num_finish(const NumParams& p, uint64_t j, uint32_t c, uint32_t len, const NumAcc& a,
-                                           uint32_t* s_ct, uint32_t* s_cnt)
+__device__ __forceinline__ uint32_t num_finish(const NumParams& p, uint64_t j, uint32_t c, uint32_t len,
+                                               const NumAcc& a, uint32_t* s_ct)
 {
     const uint32_t t = len == 0 ? (uint32_t)PPR_NUM_EMPTY : num_type(a);
     if (!CONVERT) {
         if (p.field_type) p.field_type[j] = (uint8_t)t;
         if (c < p.n_columns && s_ct[c] < t) atomicMax(&s_ct[c], t);
-        return;
+        return 0u;
     }
     const uint32_t ct = c < p.n_columns ? s_ct[c] : (uint32_t)PPR_NUM_TEXT;
     const bool as_float = ct == PPR_NUM_FLOAT64;
@@ -238,7 +287,7 @@ __device__ __forceinline__ void num_finish(const NumParams& p, uint64_t j, uint3
     }
     p.values[j] = v;
     p.status[j] = (uint8_t)st;
-    if (st) atomicAdd(&s_cnt[st], 1u);
+    return st;
 }
 
 // a field's bytes [from, to) folded into a, one by one (stops once rejected)
@@ -255,7 +304,7 @@ __device__ __forceinline__ uint64_t piece_map(const uint4& x, uint32_t nb)
     const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (uint32_t i = 0; i < 16; ++i) {
-        const uint64_t nx = kNumNext[num_class((wd[i >> 2] >> (8 * (i & 3u))) & 0xffu)];
+        const uint64_t nx = num_next(num_class((wd[i >> 2] >> (8 * (i & 3u))) & 0xffu));
         uint64_t r = 0;
 #pragma unroll
         for (uint32_t s = 0; s < 10; ++s) r |= ((nx >> (4 * ((m >> (4 * s)) & 15u))) & 15u) << (4 * s);
@@ -277,36 +326,79 @@ struct MapComb {  // x earlier, y later: y after x
 template <bool CONVERT>
 __global__ void __launch_bounds__(kNumBlock) num_kernel(NumParams p)
 {
-    __shared__ uint32_t s_ct[kNumMaxColumns];
+    // dynamic LDS: the column types, then (fields grouped by column) the columns' first fields
+    extern __shared__ __align__(16) uint32_t s_num_dyn[];
+    uint32_t* s_ct = s_num_dyn;
+    uint32_t* s_cf = s_num_dyn + p.n_columns;
     __shared__ uint32_t s_q[kNumQueue];
     __shared__ NumAcc s_qa[kNumQueue];
     __shared__ uint32_t s_qn, s_cnt[8];
     const uint32_t tid = threadIdx.x, lane = (uint32_t)lane_id(), w = tid / kWave;
     for (uint32_t c = tid; c < p.n_columns; c += kNumBlock) s_ct[c] = CONVERT ? p.column_type[c] : 0u;
+    if (!p.col && p.col_first)
+        for (uint32_t c = tid; c <= p.n_columns; c += kNumBlock) s_cf[c] = p.col_first[c];
     if (tid < 8) s_cnt[tid] = 0;
     if (tid == 0) s_qn = 0;
     __syncthreads();
 
-    // (1) thread-exclusive: each thread's fields, up to 32 bytes of each
+    // statuses 1-4 of this thread's fields (16 bits each; convert only)
+    uint32_t n12 = 0, n34 = 0;
+    auto count = [&](uint32_t st) {
+        n12 += st == 1u ? 1u : st == 2u ? 0x10000u : 0u;
+        n34 += st == 3u ? 1u : st == 4u ? 0x10000u : 0u;
+    };
+
+    // (1) thread-exclusive: each thread's fields, up to 32 bytes of each. The
+    // loads run ahead of the work: a field's offset, length and column two
+    // fields ahead, its first 32 bytes one field ahead.
     const uint64_t j0 = (uint64_t)blockIdx.x * (kNumBlock * kNumPer);
+    struct FieldAt {
+        uint32_t o, L, c;
+    };
+    auto load_field = [&](uint32_t k) {
+        FieldAt f{0u, 0u, 0u};
+        const uint64_t j = j0 + (uint64_t)k * kNumBlock + tid;
+        if (k < (uint32_t)kNumPer && j < p.n_fields) {
+            f.o = p.off[j];
+            f.L = p.len[j];
+            f.c = column_of(p, j, s_cf);
+        }
+        return f;
+    };
+    auto load_head = [&](const FieldAt& f, uint4 (&x)[2]) {
+        if ((uint64_t)f.o + kNumThread <= p.n_bytes) {
+            __builtin_memcpy(&x[0], p.bytes + f.o, 16);
+            __builtin_memcpy(&x[1], p.bytes + f.o + 16, 16);
+        } else {
+            x[0] = x[1] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    FieldAt f_next = load_field(0), f_after = load_field(1);
+    uint4 x_next[2];
+    load_head(f_next, x_next);
 #pragma unroll 1
     for (uint32_t k = 0; k < (uint32_t)kNumPer; ++k) {
         const uint64_t j = j0 + (uint64_t)k * kNumBlock + tid;
         if (j >= p.n_fields) break;
-        const uint32_t o = p.off[j], L = p.len[j], c = column_of(p, j);
+        const FieldAt f = f_next;
+        const uint4 x[2] = {x_next[0], x_next[1]};
+        f_next = f_after;
+        f_after = load_field(k + 2);
+        load_head(f_next, x_next);
+        const uint32_t o = f.o, L = f.L, c = f.c;
         NumAcc a = num_init();
         if ((uint64_t)o + L > p.n_bytes) a.s = NX;  // (a span past the text: never for a parse's own fields)
         const uint32_t head = min(L, kNumThread);
-        if (a.s != NX) {
-            if ((uint64_t)o + kNumThread <= p.n_bytes) {
-                uint4 x[2];
-                __builtin_memcpy(&x[0], p.bytes + o, 16);
-                __builtin_memcpy(&x[1], p.bytes + o + 16, 16);
-                const uint32_t wd[8] = {x[0].x, x[0].y, x[0].z, x[0].w, x[1].x, x[1].y, x[1].z, x[1].w};
-                for (uint32_t i = 0; i < head && a.s != NX; ++i) num_byte(a, (wd[i >> 2] >> (8 * (i & 3u))) & 0xffu);
-            } else {
-                num_fold_range(p, o, 0, head, a);
+        if ((uint64_t)o + kNumThread <= p.n_bytes) {
+            const uint32_t wd[8] = {x[0].x, x[0].y, x[0].z, x[0].w, x[1].x, x[1].y, x[1].z, x[1].w};
+#pragma unroll
+            for (uint32_t i = 0; i < kNumThread; ++i) {
+                const bool act = i < head && a.s != NX;
+                if (__ballot(act))  // (uniform: the wave skips bytes no lane still needs)
+                    num_byte_p(a, (wd[i >> 2] >> (8 * (i & 3u))) & 0xffu, act);
             }
+        } else if (a.s != NX) {
+            num_fold_range(p, o, 0, head, a);  // (the text's last 32 bytes)
         }
         if (L > kNumThread && a.s != NX) {
             const uint32_t qi = atomicAdd(&s_qn, 1u);
@@ -317,7 +409,7 @@ __global__ void __launch_bounds__(kNumBlock) num_kernel(NumParams p)
             }
             num_fold_range(p, o, kNumThread, L, a);  // (queue full: the thread goes on alone)
         }
-        num_finish<CONVERT>(p, j, c, L, a, s_ct, s_cnt);
+        count(num_finish<CONVERT>(p, j, c, L, a, s_ct));
     }
     __syncthreads();
 
@@ -325,7 +417,7 @@ __global__ void __launch_bounds__(kNumBlock) num_kernel(NumParams p)
     const uint32_t nq = min(s_qn, kNumQueue);
     for (uint32_t qi = w; qi < nq; qi += kNumWaves) {
         const uint64_t j = j0 + s_q[qi];
-        const uint32_t o = p.off[j], L = p.len[j], c = column_of(p, j);
+        const uint32_t o = p.off[j], L = p.len[j], c = column_of(p, j, s_cf);
         NumAcc a = s_qa[qi];
         uint32_t s = a.s;
         // the state after the bytes [32, L): pieces of 16 bytes, one per lane, composed by a wave scan
@@ -350,7 +442,17 @@ __global__ void __launch_bounds__(kNumBlock) num_kernel(NumParams p)
         }
         if (s != NX && lane == 0) num_fold_range(p, o, kNumThread, L, a);  // a long number: one lane folds the rest
         else a.s = NX;
-        if (lane == 0) num_finish<CONVERT>(p, j, c, L, a, s_ct, s_cnt);
+        if (lane == 0) count(num_finish<CONVERT>(p, j, c, L, a, s_ct));
+    }
+    if (CONVERT) {  // the wave's counts, into the workgroup's
+        n12 = readlane_t(wave_scan(n12, 0u, AddU32{}), kWave - 1);
+        n34 = readlane_t(wave_scan(n34, 0u, AddU32{}), kWave - 1);
+        if (lane == 0) {
+            atomicAdd(&s_cnt[1], n12 & 0xffffu);
+            atomicAdd(&s_cnt[2], n12 >> 16);
+            atomicAdd(&s_cnt[3], n34 & 0xffffu);
+            atomicAdd(&s_cnt[4], n34 >> 16);
+        }
     }
     __syncthreads();
 
@@ -412,6 +514,11 @@ NumParams num_params(const ppr_fields_t* f, uint8_t* ws)
     return p;
 }
 
+inline size_t num_lds(const NumParams& p)
+{
+    return (size_t)p.n_columns * 4u + (!p.col && p.col_first ? ((size_t)p.n_columns + 1u) * 4u : 0u);
+}
+
 inline uint32_t num_grid(uint64_t n_fields)
 {
     return (uint32_t)std::max<uint64_t>((n_fields + kNumBlock * kNumPer - 1) / (kNumBlock * kNumPer), 1);
@@ -438,7 +545,8 @@ extern "C" PPR_API int ppr_infer_types(const ppr_fields_t* f, uint8_t* d_field_t
     NumParams p = num_params(f, (uint8_t*)d_ws);
     p.field_type = d_field_type;
     hipLaunchKernelGGL(num_reset_kernel, dim3(1), dim3(256), 0, s, p.column_type, p.n_columns, p.counts);
-    if (f->n_fields) hipLaunchKernelGGL(num_kernel<false>, dim3(num_grid(f->n_fields)), dim3(kNumBlock), 0, s, p);
+    if (f->n_fields)
+        hipLaunchKernelGGL(num_kernel<false>, dim3(num_grid(f->n_fields)), dim3(kNumBlock), num_lds(p), s, p);
     if (hipGetLastError() != hipSuccess) return PPR_EHIP;
     if (hipMemcpyAsync(column_type, p.column_type, (size_t)f->n_columns * 4u, hipMemcpyDeviceToHost, s) != hipSuccess)
         return PPR_EHIP;
@@ -465,7 +573,8 @@ extern "C" PPR_API int ppr_convert(const ppr_fields_t* f, const uint32_t* column
     hipLaunchKernelGGL(num_reset_kernel, dim3(1), dim3(256), 0, s, p.column_type, 0u, p.counts);
     if (hipMemcpyAsync(p.column_type, column_type, (size_t)f->n_columns * 4u, hipMemcpyHostToDevice, s) != hipSuccess)
         return PPR_EHIP;
-    if (f->n_fields) hipLaunchKernelGGL(num_kernel<true>, dim3(num_grid(f->n_fields)), dim3(kNumBlock), 0, s, p);
+    if (f->n_fields)
+        hipLaunchKernelGGL(num_kernel<true>, dim3(num_grid(f->n_fields)), dim3(kNumBlock), num_lds(p), s, p);
     if (hipGetLastError() != hipSuccess) return PPR_EHIP;
     unsigned long long h[4];
     if (hipMemcpyAsync(h, p.counts, sizeof h, hipMemcpyDeviceToHost, s) != hipSuccess) return PPR_EHIP;
