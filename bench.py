@@ -28,6 +28,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -52,10 +53,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_sha():
-    """hash of every kernel source file: counter summaries taken on other sources are stale"""
+def kernel_file(name):
+    """the kernel source file that defines kernel `name` (None: not found)"""
+    pat = re.compile(r"__global__[^;{]{0,200}?\b%s\s*\(" % re.escape(name))
+    for p in sorted(glob.glob(os.path.join(ROOT, "dfa_parsing_delimiter_amd", "csrc", "*.hip"))):
+        if pat.search(open(p).read()):
+            return p
+    return None
+
+
+def source_sha(kernel=None):
+    """hash of the sources a kernel is built from (its .hip file and every shared
+    header; every source when no kernel is named): counter summaries taken on other
+    sources are stale"""
+    csrc = os.path.join(ROOT, "dfa_parsing_delimiter_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(csrc, "*.h")))
+    kf = kernel_file(kernel) if kernel else None
+    files += [kf] if kf else sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.cpp")))
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "dfa_parsing_delimiter_amd", "csrc", "*"))):
+    for p in files:
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
@@ -461,7 +477,8 @@ def summarize_pmc(args, chunk):
         fb = fetch.get(k, 0.0) * 1024.0 * f_scale
         wb = write.get(k, 0.0) * 1024.0 * w_scale
         kernels[s] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "hbm_bytes": round(fb + wb),
-                      "fetch_kib_raw": round(fetch.get(k, 0.0), 1), "write_kib_raw": round(write.get(k, 0.0), 1)}
+                      "fetch_kib_raw": round(fetch.get(k, 0.0), 1), "write_kib_raw": round(write.get(k, 0.0), 1),
+                      "source_sha": source_sha(s)}
     out = {"workload": args.workload, "chunk_bytes": chunk, "source_sha": source_sha(),
            "copy_calibration": {"bytes_each_way": COPY_BYTES, "fetch_kib_raw": round(copy_f, 1),
                                 "write_kib_raw": round(copy_w, 1), "fetch_scale": round(f_scale, 4),
@@ -486,10 +503,10 @@ def measured_traffic(workload, chunk, stage):
     if not os.path.exists(path):
         return None
     c = json.load(open(path))
-    if c.get("source_sha") != source_sha():
-        return None
     k = c.get("kernels", {}).get(stage)
-    return None if k is None else k["hbm_bytes"]
+    if k is None or k.get("source_sha", c.get("source_sha")) != source_sha(stage):
+        return None
+    return k["hbm_bytes"]
 
 
 def main():
