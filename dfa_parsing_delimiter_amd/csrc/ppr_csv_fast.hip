@@ -144,42 +144,50 @@ __device__ __forceinline__ SpanCarry span_carry(const uint64_t (&T)[NCH], const 
     return r;
 }
 
-// symbol codes of four bytes: a 3-bit slot from two bit fields of each byte, the
-// slot's special byte and code by v_perm, and an exact compare (SWAR zero-byte
-// test); bytes that are not special get the catch-all code
+// Symbol codes (times 4) of four bytes: a 3-bit slot from two bit fields of
+// each byte; by v_perm, the slot's special byte (XORed with a key) and its
+// code; then one more v_perm of the difference decides whether the byte is
+// that special byte: selector `key` (the byte equals it) picks 0x00 from the
+// hit table, every other selector gives 0xff (the host picked the slot bits so
+// that the one other selector that yields 0x00, 12, cannot occur). Bytes that
+// are not special get the catch-all code.
 template <int CB>
 __device__ __forceinline__ uint32_t classify4(uint32_t w, const FastParams& p)
 {
     const uint32_t h = ((w >> p.sh1) & p.m1) | ((w >> p.sh2) & p.m2);
-    const uint32_t e = perm(p.exp_hi, p.exp_lo, h);
-    const uint32_t c = perm(p.cls_hi, p.cls_lo, h);
-    const uint32_t d = w ^ e;
-    const uint32_t t = (((d & 0x7f7f7f7fu) + 0x7f7f7f7fu) | d) & 0x80808080u;  // 0x80: not a special byte
-    const uint32_t x = t >> 7;
-    return c | ((x << CB) - x);
+    const uint32_t miss = perm(p.hit_hi, p.hit_lo, w ^ perm(p.exp_hi, p.exp_lo, h));
+    return (miss & (Geo<CB>::CM * 0x04040404u)) | perm(p.cls_hi, p.cls_lo, h);
 }
 
-// the group indices of a full chunk (one byte per group of G symbol codes:
-// c0 + 4 c1 + 16 c2 + 64 c3, or c0 + 2^CB c1), also packed four per word
+// symbol code of one byte (the ragged paths)
+template <int CB>
+__device__ __forceinline__ uint32_t classify1(uint32_t b, const FastParams& p)
+{
+    return (classify4<CB>(b * 0x01010101u, p) >> 2) & Geo<CB>::CM;
+}
+
+// The table addresses (4 x the group index: c0 + 4 c1 + 16 c2 + 64 c3, or
+// c0 + 2^CB c1) of a full chunk's groups, and the group indices packed four
+// per word (one byte per group).
 template <int CB>
 __device__ __forceinline__ void chunk_codes(const uint32_t (&w)[Geo<CB>::ND], const FastParams& p,
-                                            uint32_t (&idx)[Geo<CB>::NI], uint32_t (&pw)[Geo<CB>::NP])
+                                            uint32_t (&ia)[Geo<CB>::NI], uint32_t (&pw)[Geo<CB>::NP])
 {
     using Gm = Geo<CB>;
 #pragma unroll
     for (int k = 0; k < Gm::ND; ++k) {
-        const uint32_t code = classify4<CB>(w[k], p);
+        const uint32_t code4 = classify4<CB>(w[k], p);
         if constexpr (Gm::G == 4) {
-            idx[k] = __builtin_amdgcn_udot4(code, 0x40100401u, 0u, false);
+            ia[k] = __builtin_amdgcn_udot4(code4, 0x40100401u, 0u, false);
         } else {
             constexpr uint32_t W = 1u << CB;
-            idx[2 * k] = __builtin_amdgcn_udot4(code, 0x00000001u | (W << 8), 0u, false);
-            idx[2 * k + 1] = __builtin_amdgcn_udot4(code, 0x00010000u | (W << 24), 0u, false);
+            ia[2 * k] = __builtin_amdgcn_udot4(code4, 0x00000001u | (W << 8), 0u, false);
+            ia[2 * k + 1] = __builtin_amdgcn_udot4(code4, 0x00010000u | (W << 24), 0u, false);
         }
     }
 #pragma unroll
     for (int q = 0; q < Gm::NP; ++q)
-        pw[q] = idx[4 * q] | (idx[4 * q + 1] << 8) | (idx[4 * q + 2] << 16) | (idx[4 * q + 3] << 24);
+        pw[q] = (ia[4 * q] >> 2) | (ia[4 * q + 1] << 6) | (ia[4 * q + 2] << 14) | (ia[4 * q + 3] << 22);
 }
 
 // identity vector over the tracked state codes; the rest is absorbing
@@ -215,17 +223,17 @@ __device__ __forceinline__ ChunkPos chunk_pos(uint32_t n, uint32_t tile)
     return c;
 }
 
-// the chunk's vector from its group indices: independent table reads, then a
-// tree of composites (group 2i before group 2i+1)
+// the chunk's vector from its table addresses: independent table reads, then
+// a tree of composites (group 2i before group 2i+1)
 template <int CB, bool V8>
-__device__ __forceinline__ Vec tree_vector(const uint32_t (&idx)[Geo<CB>::NI], const uint32_t* s_t1)
+__device__ __forceinline__ Vec tree_vector(const uint32_t (&ia)[Geo<CB>::NI], const uint32_t* s_t1)
 {
     constexpr int E = Geo<CB>::E, NI = Geo<CB>::NI;
     uint32_t tl[NI], th[NI];
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
-        tl[k] = s_t1[idx[k]];
-        if (V8) th[k] = s_t1[E + idx[k]];
+        tl[k] = lds_at(s_t1, ia[k]);
+        if (V8) th[k] = lds_at(s_t1 + E, ia[k]);
     }
 #pragma unroll
     for (int width = NI; width > 1; width >>= 1) {
@@ -249,7 +257,7 @@ template <int CB, bool V8>
 __device__ Vec ragged_vector(const FastParams& p, const ChunkPos& c, Vec v, const uint8_t* s_nxt)
 {
     for (uint32_t j = 0; j < c.my_len; ++j) {
-        const uint32_t code = classify4<CB>(p.in[c.chunk_abs + j] * 0x01010101u, p) & Geo<CB>::CM;
+        const uint32_t code = classify1<CB>(p.in[c.chunk_abs + j], p);
         uint32_t lo = 0, hi = 0;
         for (int i = 0; i < 8; ++i) {
             uint32_t s = vat(v, (uint32_t)i);
@@ -403,7 +411,7 @@ __device__ void pass2_ragged(const FastParams& p, const PairPos& c, uint32_t s, 
 {
     T[0] = T[1] = RD[0] = RD[1] = 0;
     for (uint32_t j = 0; j < c.my_len; ++j) {
-        const uint32_t code = classify4<CB>(p.in[c.abs + j] * 0x01010101u, p) & Geo<CB>::CM;
+        const uint32_t code = classify1<CB>(p.in[c.abs + j], p);
         const uint32_t row = min(s, nt);
         const uint32_t t = s_tag[row * 16 + code];
         s = s_nxt[row * 16 + code];
@@ -616,13 +624,13 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
 
     // classify, store the indices, the chunk's vector
     auto full_chunk = [&](uint32_t tile, const uint32_t (&wc)[ND]) {
-        uint32_t idx[NI], pw[NP];
-        chunk_codes<CB>(wc, p, idx, pw);
+        uint32_t ia[NI], pw[NP];
+        chunk_codes<CB>(wc, p, ia, pw);
         uint4* dst = reinterpret_cast<uint4*>(p.idx + ((size_t)tile * kFastBlock + tid) * NI);
 #pragma unroll
         for (int q = 0; q < NP / 4; ++q)
             dst[q] = make_uint4(pw[4 * q], pw[4 * q + 1], pw[4 * q + 2], pw[4 * q + 3]);
-        return tree_vector<CB, V8>(idx, s_t1);
+        return tree_vector<CB, V8>(ia, s_t1);
     };
     // scan the tile's chunk vectors, store those of the even chunks (where the
     // carries and emit kernels' two-chunk spans start) and the tile vector
@@ -1147,7 +1155,7 @@ __device__ void pass2_ragged_chunk(const FastParams& p, const ChunkPos& c, uint3
 {
     T = RD = 0;
     for (uint32_t j = 0; j < c.my_len; ++j) {
-        const uint32_t code = classify4<CB>(p.in[c.chunk_abs + j] * 0x01010101u, p) & Geo<CB>::CM;
+        const uint32_t code = classify1<CB>(p.in[c.chunk_abs + j], p);
         const uint32_t row = min(s, nt);
         const uint32_t t = s_tag[row * 16 + code];
         s = s_nxt[row * 16 + code];
@@ -1243,9 +1251,9 @@ __global__ void __launch_bounds__(kFastBlock, kFusedWavesPerSimd) csv_fused_kern
             const ChunkPos c = chunk_pos(p.n, t0);
             Vec v = ident;
             if (c.full) {
-                uint32_t idx[NI];
-                chunk_codes<CB>(w, p, idx, pw0);
-                v = tree_vector<CB, V8>(idx, sh.t1);
+                uint32_t ia[NI];
+                chunk_codes<CB>(w, p, ia, pw0);
+                v = tree_vector<CB, V8>(ia, sh.t1);
             } else if (c.my_len) {
                 v = ragged_vector<CB, V8>(p, c, ident, sh.p2.nxt);
             }

@@ -25,6 +25,12 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// LDS word at a byte address
+__device__ __forceinline__ uint32_t lds_at(const uint32_t* base, uint32_t byte_addr)
+{
+    return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(base) + byte_addr);
+}
+
 __device__ __forceinline__ Vec vec_identity() { return {0x03020100u, 0x07060504u}; }
 
 // composite: a earlier, b later; result[i] = b[a[i]]
@@ -189,21 +195,21 @@ __device__ __forceinline__ uint32_t slots_from(uint64_t cap, uint64_t first, uin
 // its terminator / record bitmaps as 32-bit words (bit j of word q = byte
 // 32 q + j). When all of them fall in the window (the usual case) the loop
 // runs without index checks.
-template <int NWORDS>
-__device__ __forceinline__ void list_terminators(uint32_t* list, const uint32_t (&tw)[NWORDS],
+template <int NWORDS, typename Entry>
+__device__ __forceinline__ void list_terminators(Entry* list, const uint32_t (&tw)[NWORDS],
                                                  const uint32_t (&rw)[NWORDS], uint32_t rel0, uint32_t first,
                                                  uint32_t mine, uint32_t w0, uint32_t w1)
 {
     if (!(mine && first < w1 && first + mine > w0)) return;
     if (first >= w0 && first + mine <= w1) {
-        uint32_t* dst = list + (first - w0);
+        Entry* dst = list + (first - w0);
 #pragma unroll
         for (int q = 0; q < NWORDS; ++q) {
             uint32_t bits = tw[q];
             const uint32_t base2 = (rel0 + 32u * q) << 1;
             while (bits) {
                 const uint32_t j = (uint32_t)__builtin_ctz(bits);
-                *dst++ = base2 + (j << 1) + ((rw[q] >> j) & 1u);
+                *dst++ = (Entry)(base2 + (j << 1) + ((rw[q] >> j) & 1u));
                 bits &= bits - 1u;
             }
         }
@@ -215,7 +221,7 @@ __device__ __forceinline__ void list_terminators(uint32_t* list, const uint32_t 
         uint32_t bits = tw[q];
         while (bits && li < w1) {
             const uint32_t j = (uint32_t)__builtin_ctz(bits);
-            if (li >= w0) list[li - w0] = ((rel0 + 32u * q + j) << 1) | ((rw[q] >> j) & 1u);
+            if (li >= w0) list[li - w0] = (Entry)(((rel0 + 32u * q + j) << 1) | ((rw[q] >> j) & 1u));
             ++li;
             bits &= bits - 1u;
         }

@@ -97,26 +97,71 @@ __device__ __forceinline__ uint32_t fold_lex_chunk(const LexFastParams& p, const
     return p.row_id[r + c];
 }
 
-// Pass 2 from the automaton state q (times m): bit j of the result is set when
-// a token ends before byte j. With kinds, the ending token's kind (bits 24-31 of
-// the step entry: the kind of the state before the byte) goes to kinds[j].
-template <bool FULL>
-__device__ __forceinline__ uint64_t lex_pass2(const uint32_t (&w)[kLexWords], uint32_t len, uint32_t q,
-                                              const uint32_t* s_step, const uint8_t* s_col, uint8_t* kinds)
+// Pass 1 for N full chunks at once: their folds step in lockstep, so each
+// step's N row reads are independent and wait on the LDS once.
+template <int N>
+__device__ __forceinline__ void fold_lex_chunks(const LexFastParams& p, const uint32_t (&w)[N][kLexWords],
+                                                const uint16_t* s_rows, const uint8_t* s_col, uint32_t (&id)[N])
 {
-    uint32_t b0 = 0, b1 = 0;
+    uint32_t r[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) r[k] = p.row0;
+#pragma unroll
+    for (int j = 0; j + 1 < kLexFastChunk; ++j)
+#pragma unroll
+        for (int k = 0; k < N; ++k) r[k] = s_rows[r[k] + s_col[chunk_byte(w[k], j)]];
+#pragma unroll
+    for (int k = 0; k < N; ++k) id[k] = p.row_id[r[k] + s_col[chunk_byte(w[k], kLexFastChunk - 1)]];
+}
+
+// Pass 2 from the automaton state whose row starts at byte q4 of the step
+// table: bit j of the result is set when a token ends before byte j. Entries
+// are addressed by byte: entry = the successor's row offset | flag << 16 |
+// kind of the state before the byte << 24; s_col holds each byte's column (one
+// byte each: the 256-byte table is one word per LDS bank, so its reads never
+// conflict). A full chunk reads all its columns before the chain of steps
+// (they do not depend on the state) and gathers the flag bytes, and with kinds
+// the kind bytes, four per word by v_perm; the kind words go to kinds32
+// (garbage where no token ends: only flagged bytes' kinds are read).
+template <bool KINDS>
+__device__ __forceinline__ uint64_t lex_pass2_full(const uint32_t (&w)[kLexWords], uint32_t q4, const uint32_t* s_step,
+                                                   const uint8_t* s_col, uint32_t* kinds32)
+{
+    uint32_t c[kLexFastChunk];
+#pragma unroll
+    for (int j = 0; j < kLexFastChunk; ++j) c[j] = s_col[chunk_byte(w, j)];
+    uint32_t e = q4, fw = 0, kw = 0, b0 = 0, b1 = 0;
 #pragma unroll
     for (int j = 0; j < kLexFastChunk; ++j) {
-        if (FULL || (uint32_t)j < len) {
-            const uint32_t e = s_step[q + s_col[chunk_byte(w, j)]];
-            const uint32_t f = (e >> 16) & 1u;
-            if (kinds && f) kinds[j] = (uint8_t)(e >> 24);
-            if (j < 32) b0 |= f << j;
-            else b1 |= f << (j - 32);
-            q = e & 0xffffu;
+        e = lds_at(s_step, (e & 0xffffu) + (c[j] << 2));
+        const int i = j & 3;
+        const uint32_t keep = 0x03020100u & ~(0xffu << (8 * i));
+        fw = perm(e, fw, keep | (6u << (8 * i)));  // byte i <- the entry's flag byte
+        if (KINDS) kw = perm(e, kw, keep | (7u << (8 * i)));  // byte i <- the entry's kind byte
+        if (i == 3) {
+            const uint32_t nib = __builtin_amdgcn_udot4(fw, 0x08040201u, 0u, false);  // flag bytes (0/1) -> 4 bits
+            if (j < 32) b0 |= nib << (j - 3);
+            else b1 |= nib << (j - 35);
+            if (KINDS) kinds32[j >> 2] = kw;
         }
     }
     return (uint64_t)b0 | ((uint64_t)b1 << 32);
+}
+
+// Pass 2 over the input's ragged last chunk (bytes < len), one byte at a time.
+template <bool KINDS>
+__device__ __forceinline__ uint64_t lex_pass2_ragged(const uint32_t (&w)[kLexWords], uint32_t len, uint32_t q4,
+                                                     const uint32_t* s_step, const uint8_t* s_col, uint8_t* kinds)
+{
+    uint64_t bits = 0;
+    uint32_t e = q4;
+    for (uint32_t j = 0; j < len; ++j) {
+        e = lds_at(s_step, (e & 0xffffu) + ((uint32_t)s_col[chunk_byte(w, (int)j)] << 2));
+        const uint32_t f = (e >> 16) & 1u;
+        if (KINDS && f) kinds[j] = (uint8_t)(e >> 24);
+        bits |= (uint64_t)f << j;
+    }
+    return bits;
 }
 
 __device__ __forceinline__ void lex_range_of(const LexFastParams& p, uint32_t b, uint32_t& t0, uint32_t& t1)
@@ -182,17 +227,20 @@ __device__ LexTok lex_tokens_before(const LexFastParams& p, uint32_t b, LexTok* 
     return block_reduce<kLexFastWaves>(LexTok{x.x + y.x, max(x.y, y.y)}, LexTok{0u, 0u}, s_wave, LexTokComb{});
 }
 
-// The minimal automaton in LDS, successors times m: entry = successor * m |
-// flag << 16 | kind of the row's state << 24; and the state of each identifier,
-// times m.
-__device__ __forceinline__ void load_lex_automaton(const LexFastParams& p, uint32_t* s_step, uint16_t* s_state)
+// The minimal automaton in LDS, by byte offset: entry = the successor's row
+// offset (successor * m * 4) | flag << 16 | kind of the row's state << 24;
+// the row offset of each identifier's state; and each byte's column. (Row
+// offsets stay below 2^16: the table is held to 16 KiB.)
+__device__ __forceinline__ void load_lex_automaton(const LexFastParams& p, uint32_t* s_step, uint16_t* s_state,
+                                                   uint8_t* s_col)
 {
-    const uint32_t m = p.m;
-    for (uint32_t i = threadIdx.x; i < p.nq * m; i += kLexFastBlock) {
+    const uint32_t m4 = p.m * 4u;
+    for (uint32_t i = threadIdx.x; i < p.nq * p.m; i += kLexFastBlock) {
         const uint32_t e = p.step[i];
-        s_step[i] = (e & 0xffffu) * m | (e & 0x10000u) | ((uint32_t)p.state_kind[i / m] << 24);
+        s_step[i] = (e & 0xffffu) * m4 | (e & 0x10000u) | ((uint32_t)p.state_kind[i / p.m] << 24);
     }
-    for (uint32_t i = threadIdx.x; i < p.k; i += kLexFastBlock) s_state[i] = (uint16_t)(p.state_of[i] * m);
+    for (uint32_t i = threadIdx.x; i < p.k; i += kLexFastBlock) s_state[i] = (uint16_t)(p.state_of[i] * m4);
+    if (threadIdx.x < 256) s_col[threadIdx.x] = p.col[threadIdx.x];
 }
 
 // Several tiles' chunk identifiers, scanned together: the merges of the scans
@@ -259,11 +307,9 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_ids_kernel(LexFastParams p)
         load_set(next < tfull ? next : tile, wn);
         asm volatile("" ::: "memory");
         IdSet v, ident, excl, tot;
+        fold_lex_chunks<kIdsTiles>(p, w, s_rows, s_col, v.v);
 #pragma unroll
-        for (int k = 0; k < kIdsTiles; ++k) {
-            v.v[k] = fold_lex_chunk<true>(p, w[k], kLexFastChunk, s_rows, s_col);
-            ident.v[k] = p.identity;
-        }
+        for (int k = 0; k < kIdsTiles; ++k) ident.v[k] = p.identity;
 #pragma unroll
         for (int k = 0; k < kIdsTiles; ++k)
 #pragma unroll
@@ -311,8 +357,7 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_count_kernel(LexFastParams 
     __shared__ uint32_t s_wave[kLexFastWaves];
     __shared__ LexTok s_tw[kLexFastWaves];
     const uint32_t tid = threadIdx.x, b = blockIdx.x;
-    load_lex_automaton(p, s_step, s_state);
-    if (tid < 256) s_col[tid] = p.col[tid];
+    load_lex_automaton(p, s_step, s_state, s_col);
     const LexIdComb idc{p.merge, p.k, p.id_mask};
     uint32_t run = lex_ranges_before(p, b, s_wave, idc);  // (its barrier publishes the tables)
     uint32_t t0, t1;
@@ -328,7 +373,7 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_count_kernel(LexFastParams 
         p, t0, t1,
         [&](uint32_t tile, const LexIn& in, uint32_t) {
             const uint32_t q = s_state[idc(run, in.cid)];
-            count(tile, lex_pass2<true>(in.w, kLexFastChunk, q, s_step, s_col, nullptr));
+            count(tile, lex_pass2_full<false>(in.w, q, s_step, s_col, nullptr));
             run = idc(run, in.tid);
         },
         [&](uint32_t tile, uint32_t) {
@@ -337,7 +382,7 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_count_kernel(LexFastParams 
             uint32_t w[kLexWords];
             load_lex_chunk<false>(p.in + pos, len, w);
             const uint32_t q = s_state[idc(run, p.chunk_id[(size_t)tile * kLexFastBlock + tid])];
-            count(tile, lex_pass2<false>(w, len, q, s_step, s_col, nullptr));
+            count(tile, lex_pass2_ragged<false>(w, len, q, s_step, s_col, nullptr));
             run = idc(run, p.tile_id[tile]);
         });
     const LexTok r = block_reduce<kLexFastWaves>(acc, LexTok{0u, 0u}, s_tw, LexTokComb{});
@@ -349,7 +394,7 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_emit_kernel(LexFastParams p
     extern __shared__ __align__(16) uint32_t s_tab[];
     uint32_t* s_step = s_tab;
     uint16_t* s_state = reinterpret_cast<uint16_t*>(s_tab + p.nq * p.m);
-    __shared__ uint8_t s_kind[kLexFastTile];  // kind of the token ending before each byte of the tile
+    __shared__ uint32_t s_kind32[kLexFastTile / 4];  // kind of the token ending before each byte of the tile
     __shared__ uint32_t s_list[kLexFastWaves][kLexList];
     __shared__ uint8_t s_col[256];
     __shared__ uint32_t s_wave[kLexFastWaves];
@@ -357,8 +402,8 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_emit_kernel(LexFastParams p
     __shared__ LexTok s_tw[2][kLexFastWaves];
     const uint32_t tid = threadIdx.x, b = blockIdx.x;
     const uint32_t lane = (uint32_t)lane_id();
-    load_lex_automaton(p, s_step, s_state);
-    if (tid < 256) s_col[tid] = p.col[tid];
+    uint8_t* const s_kind = reinterpret_cast<uint8_t*>(s_kind32);
+    load_lex_automaton(p, s_step, s_state, s_col);
     const LexIdComb idc{p.merge, p.k, p.id_mask};
     uint32_t run = lex_ranges_before(p, b, s_wave, idc);  // (its barrier publishes the tables)
     LexTok P = lex_tokens_before(p, b, s_pre);
@@ -417,7 +462,7 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_emit_kernel(LexFastParams p
         p, t0, t1,
         [&](uint32_t tile, const LexIn& in, uint32_t it) {
             const uint32_t q = s_state[idc(run, in.cid)];
-            emit(tile, lex_pass2<true>(in.w, kLexFastChunk, q, s_step, s_col, s_kind + pos0), it);
+            emit(tile, lex_pass2_full<true>(in.w, q, s_step, s_col, s_kind32 + pos0 / 4u), it);
             run = idc(run, in.tid);
         },
         [&](uint32_t tile, uint32_t it) {
@@ -426,7 +471,7 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_emit_kernel(LexFastParams p
             uint32_t w[kLexWords];
             load_lex_chunk<false>(p.in + pos, len, w);
             const uint32_t q = s_state[idc(run, p.chunk_id[(size_t)tile * kLexFastBlock + tid])];
-            emit(tile, lex_pass2<false>(w, len, q, s_step, s_col, s_kind + pos0), it);
+            emit(tile, lex_pass2_ragged<true>(w, len, q, s_step, s_col, s_kind + pos0), it);
             run = idc(run, p.tile_id[tile]);
         });
     if (b == p.num_ranges - 1 && tid == 0) {  // the final token: from the last boundary to n

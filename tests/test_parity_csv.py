@@ -179,6 +179,55 @@ def test_random_tables(ppr, seed):
                 _same(g, r, (seed, trial, n, chunk, path))
 
 
+def _full_range_csv(rng, n, sep, quote=ord('"')):
+    """records of unquoted fields (any byte but the specials) and quoted fields
+    (any byte but the quote, doubled quotes, separators and newlines inside)"""
+    specials = {sep, 10, quote}
+    plain = np.array([b for b in range(256) if b not in specials], dtype=np.uint8)
+    inner = np.array([b for b in range(256) if b != quote], dtype=np.uint8)
+    out = bytearray()
+    while len(out) < n:
+        for f in range(int(rng.integers(1, 6))):
+            if f:
+                out.append(sep)
+            L = int(rng.integers(0, 40))
+            if rng.random() < 0.4:
+                body = bytearray(inner[rng.integers(0, inner.size, L)].tobytes())
+                for i in sorted(rng.integers(0, L + 1, int(rng.integers(0, 3))).tolist(), reverse=True):
+                    body[i:i] = bytes([quote, quote])
+                out += bytes([quote]) + body + bytes([quote])
+            else:
+                out += plain[rng.integers(0, plain.size, L)].tobytes()
+        out.append(10)
+    return np.frombuffer(bytes(out[:n]), dtype=np.uint8)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_every_byte_value(ppr, seed):
+    """every byte value at every position in a word, in unquoted and quoted
+    fields, for T5 and T6 and for random tables whose special bytes are anywhere
+    in 0..255 (the table-driven paths tell a special byte from all the others by
+    a slot of a few bits and an exact compare)"""
+    rng = np.random.default_rng(500 + seed)
+    cases = [(W.table("T5"), _full_range_csv(rng, 200003, ord(","))),
+             (W.table("T6"), _full_range_csv(rng, 200003, 9))]
+    for trial in range(4):
+        t = _random_table(rng, absorbing=bool(trial % 2), n_special=int(rng.choice([1, 3, 5, 8])))
+        K = max(set(t["class_map"]), key=t["class_map"].count)
+        specials = np.array([b for b in range(256) if t["class_map"][b] != K], dtype=np.uint8)
+        b = rng.integers(0, 256, 150001).astype(np.uint8)
+        if specials.size:
+            pick = rng.random(b.size) < 0.3
+            b[pick] = specials[rng.integers(0, specials.size, int(pick.sum()))]
+        cases.append((t, b))
+    for i, (t, b) in enumerate(cases):
+        r = oracle.csv_parse(b, t)
+        for chunk, path in _with_paths((64, 13)):
+            _say("every byte", seed, i, b.size, chunk, path)
+            g = ppr.parse(_dev(b), t, chunk_bytes=chunk, capacity=b.size + 1, path=path)
+            _same(g, r, (seed, i, chunk, path))
+
+
 def test_unaligned_input_and_subviews(ppr):
     import torch
     t = W.table("T5")
