@@ -170,8 +170,9 @@ def cpu_oracle_baseline(kind, data, spec, max_seconds=30.0):
 
 def bandwidth_ceilings(ppr, torch, dev, nbytes=1 << 30, iters=10):
     """The device's own streaming rates (ppr_bandwidth_probe): read, write and
-    copy of nbytes, wave-contiguous 16-byte words (pattern 0) and 64 bytes per
-    lane (pattern 1), averaged over iters launches after 2 warm-ups."""
+    copy of nbytes, wave-contiguous 16-byte words (pattern 0), 64 bytes per
+    lane (pattern 1) and wave-contiguous 4-byte words (pattern 2, the field and
+    token stores' shape), averaged over iters launches after 2 warm-ups."""
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     src.fill_(3)
@@ -179,7 +180,7 @@ def bandwidth_ceilings(ppr, torch, dev, nbytes=1 << 30, iters=10):
     grid = props.multi_processor_count * 8
     stream = torch.cuda.current_stream()
     out = {"bytes": nbytes, "grid": grid, "block": 256}
-    for pat, pname in ((0, "wave_contiguous_16B"), (1, "lane_contiguous_64B")):
+    for pat, pname in ((0, "wave_contiguous_16B"), (1, "lane_contiguous_64B"), (2, "wave_contiguous_4B")):
         r = {}
         for mode, mname in ((0, "read"), (1, "write"), (2, "copy")):
             for _ in range(2):

@@ -190,6 +190,12 @@ __device__ __forceinline__ void chunk_codes(const uint32_t (&w)[Geo<CB>::ND], co
         pw[q] = (ia[4 * q] >> 2) | (ia[4 * q + 1] << 6) | (ia[4 * q + 2] << 14) | (ia[4 * q + 3] << 22);
 }
 
+// the value of the even lane of this lane's pair (DPP quad_perm [0,0,2,2])
+__device__ __forceinline__ uint32_t even_lane(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xa0, 0xf, 0xf, false);
+}
+
 // identity vector over the tracked state codes; the rest is absorbing
 template <bool V8>
 __device__ __forceinline__ Vec fast_ident(uint32_t nt)
@@ -634,33 +640,46 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
     };
     // scan the tile's chunk vectors, store those of the even chunks (where the
     // carries and emit kernels' two-chunk spans start) and the tile vector
+    //
+    // Every lane issues the same stores (an odd lane writes its even
+    // neighbour's vector to the same word, every wave the tile vector): with
+    // no store skipped by a branch, the compiler knows how many memory
+    // operations follow each prefetch and waits for the prefetch alone, not for
+    // the previous tile's stores as well.
     auto finish = [&](uint32_t tile, const Vec& v, uint32_t it) {
         Vec excl, tot;
         block_scan<kFastWaves>(v, ident, excl, tot, s_wave[it & 1], VecComb<V8>{});
-        if ((tid & 1) == 0) {
-            const size_t ci = (size_t)tile * (kFastBlock / 2) + (uint32_t)tid / 2;
-            p.cvec_lo[ci] = excl.lo;
-            if (V8) p.cvec_hi[ci] = excl.hi;
-        }
-        if (tid == 0) p.tile_vec[tile] = (uint64_t)tot.lo | ((uint64_t)tot.hi << 32);
+        const size_t ci = (size_t)tile * (kFastBlock / 2) + (uint32_t)tid / 2;
+        p.cvec_lo[ci] = even_lane(excl.lo);
+        if (V8) p.cvec_hi[ci] = even_lane(excl.hi);
+        p.tile_vec[tile] = (uint64_t)tot.lo | ((uint64_t)tot.hi << 32);
     };
 
     // Two register buffers used in turn, and an unconditional prefetch (the
     // last full tile is read again at the end): no copy of a register still
     // being loaded and no branch around a load, either of which would make the
-    // compiler wait for the prefetch before the current tile's work.
+    // compiler wait for the prefetch before the current tile's work. The first
+    // tile is peeled off the loop, so that every entry to the loop body, like
+    // every other tile, follows a tile's stores: the wait for a prefetch then
+    // leaves those stores in flight.
     uint32_t w2[ND];
     uint32_t tile = t0;
     // the last full tile this workgroup takes
     const uint32_t tlast = tfull_all > t0 ? t0 + (tfull_all - 1 - t0) / stride * stride : t0;
-    while (tile < tfull_all) {
+    uint32_t it = 0;
+    if (tile < tfull_all) {
         load_full(min(tile + stride, tlast), w2);
-        finish(tile, full_chunk(tile, w), 0);
+        finish(tile, full_chunk(tile, w), it++);
         tile += stride;
-        if (tile >= tfull_all) break;
-        load_full(min(tile + stride, tlast), w);
-        finish(tile, full_chunk(tile, w2), 1);
-        tile += stride;
+        while (tile < tfull_all) {
+            load_full(min(tile + stride, tlast), w);
+            finish(tile, full_chunk(tile, w2), it++);
+            tile += stride;
+            if (tile >= tfull_all) break;
+            load_full(min(tile + stride, tlast), w2);
+            finish(tile, full_chunk(tile, w), it++);
+            tile += stride;
+        }
     }
     if (tile < p.num_tiles) {  // the input's ragged last tile
         const ChunkPos c = chunk_pos(p.n, tile);
@@ -671,7 +690,7 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
         } else if (c.my_len) {
             v = ragged_vector<CB, V8>(p, c, v, s_nxt);
         }
-        finish(tile, v, 0);
+        finish(tile, v, it);
     }
 }
 

@@ -432,15 +432,17 @@ PPR_API const char* ppr_version(void);
 
 /*
  * Bandwidth probe (not part of the method): enqueues one kernel on `stream`
- * that streams `bytes` (a multiple of 16 KiB) of device memory in 16-byte
- * words, so that the caller can time the device's own read / write / copy rate
- * with events and judge the kernels' traffic against it.
+ * that streams `bytes` (a multiple of 16 KiB) of device memory, so that the
+ * caller can time the device's own read / write / copy rate with events and
+ * judge the kernels' traffic against it.
  *   mode 0: read d_src; d_dst receives one 32-bit word per thread
  *           (grid * 256 * 4 bytes), so the loads are not optimised away;
  *   mode 1: write d_dst (d_src unused, may be NULL);
  *   mode 2: copy d_src to d_dst (`bytes` each).
- *   pattern 0: wave-contiguous words (one instruction covers 1 KiB);
- *   pattern 1: 64 contiguous bytes per lane (the CSV codes kernel's layout).
+ *   pattern 0: wave-contiguous 16-byte words (one instruction covers 1 KiB);
+ *   pattern 1: 64 contiguous bytes per lane (the CSV codes kernel's layout);
+ *   pattern 2: wave-contiguous 4-byte words (one instruction covers 256 bytes:
+ *              the shape of the field and token stores).
  *   grid: workgroups of 256 threads (a grid-stride loop covers the buffer).
  * Pointers must be 16-byte aligned. PPR_EINVAL on bad arguments.
  */
