@@ -485,8 +485,8 @@ def summarize_pmc(args, chunk):
                                 "write_kib_raw": round(copy_w, 1), "fetch_scale": round(f_scale, 4),
                                 "write_scale": round(w_scale, 4)},
            "kernels": kernels,
-           "commands": ["rocprofv3 --pmc %s -d %s -o run --output-format csv -- python bench.py --workload %s "
-                        "--chunk %d --no-cpu --steps 3 --warmup 1 --copy-calibration" % (c, d, args.workload, chunk)
+           "commands": ["rocprofv3 --pmc %s -d %s -o run --output-format csv -- python3 bench.py --workload %s "
+                        "--chunk %d --no-cpu --no-probe --steps 3 --warmup 1 --copy-calibration" % (c, d, args.workload, chunk)
                         for c, d in zip(("FETCH_SIZE", "WRITE_SIZE"), args.summarize_pmc)]
                        + ["python bench.py --workload %s --chunk %d --summarize-pmc %s %s" % (
                            args.workload, chunk, *args.summarize_pmc)]}

@@ -60,7 +60,7 @@ template <bool V8>
 __device__ __forceinline__ Vec comp(Vec a, Vec b)
 {
     if constexpr (V8) return compose(a, b);
-    else return {perm(b.lo, b.lo, a.lo), a.hi};
+    else return {perm(b.lo, b.lo, a.lo), 0xffffffffu};  // (entries 4-7 are never read with 4 tracked states)
 }
 
 template <bool V8>
