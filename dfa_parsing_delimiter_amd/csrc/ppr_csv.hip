@@ -399,7 +399,8 @@ static WsLayout csv_layout(uint64_t n, uint32_t L)
 }
 
 // Fast-path eligibility and its tables: a catch-all class, at most 8 other
-// bytes separable by a 3-bit slot (byte >> shift) & 7, at most 8 tracked states.
+// bytes separable by a 3-bit slot of two bit fields (ppr_slots.h), at most 8
+// tracked states.
 static bool prepare_fast(const ppr_dfa_t* d, const uint8_t* cm, FastParams& f, int& cb, bool& v8)
 {
     uint32_t count[PPR_MAX_CLASSES] = {0};
@@ -412,79 +413,14 @@ static bool prepare_fast(const ppr_dfa_t* d, const uint8_t* cm, FastParams& f, i
     for (int b = 0; b < 256; ++b)
         if (cm[b] != K) specials[ns++] = (uint8_t)b;
     if (ns > 8) return false;
-    // slot = ((b >> sh1) & m1) | ((b >> sh2) & m2): two bit fields, 3 bits in all.
-    // The kernels test a byte b against its slot's special byte x by one byte
-    // select of the difference b ^ x ^ key (key in {0, 2, 4, 6}): selector key
-    // picks the 0x00 of the hit table, every other selector below 12 a 0xff
-    // byte or the sign of one, 12 the constant 0x00 and the rest 0xff. A byte
-    // that differs from x by exactly 12 ^ key would so pass as x, so the slot
-    // function must change under that difference: it must read one of its bits.
-    int best_sh1 = -1, best_sh2 = 0;
-    uint32_t best_m1 = 0, best_key = 0;
-    for (int m1 = 7; m1 >= 1 && best_sh1 < 0; --m1) {
-        const uint32_t m2 = 7u & ~(uint32_t)m1;
-        for (int sh1 = 0; sh1 <= 5 && best_sh1 < 0; ++sh1) {
-            for (int sh2 = 0; sh2 <= 7 && best_sh1 < 0; ++sh2) {
-                if (m2 == 0 && sh2 != 0) continue;
-                if ((m2 & 4u) && sh2 > 5) continue;
-                if ((m2 & 2u) && sh2 > 6) continue;
-                auto slot = [&](uint32_t b) { return ((b >> sh1) & (uint32_t)m1) | ((b >> sh2) & m2); };
-                uint32_t used = 0;
-                bool ok = true;
-                for (int i = 0; i < ns && ok; ++i) {
-                    if (used & (1u << slot(specials[i]))) ok = false;
-                    used |= 1u << slot(specials[i]);
-                }
-                int key = -1;
-                for (uint32_t k = 0; k <= 6 && ok && key < 0; k += 2)
-                    if (slot(12u ^ k) != slot(0u)) key = (int)k;  // (the slot function is linear over XOR)
-                if (ok && key >= 0) {
-                    best_sh1 = sh1;
-                    best_sh2 = sh2;
-                    best_m1 = (uint32_t)m1;
-                    best_key = (uint32_t)key;
-                }
-            }
-        }
-    }
-    if (best_sh1 < 0) return false;
-    const uint32_t best_m2 = 7u & ~best_m1;
-    auto slot_of = [&](uint32_t b) { return ((b >> best_sh1) & best_m1) | ((b >> best_sh2) & best_m2); };
-    const uint32_t delta = 12u ^ best_key;  // the one difference the select would take for a hit
     cb = d->n_classes <= 4 ? 2 : d->n_classes <= 8 ? 3 : 4;
     const uint32_t catch_code = (1u << cb) - 1u;
     uint8_t code_of[PPR_MAX_CLASSES];
     uint32_t next_code = 0;
     for (uint32_t c = 0; c < d->n_classes; ++c) code_of[c] = c == K ? (uint8_t)catch_code : (uint8_t)next_code++;
-    // slot tables: the special byte of each slot (XORed with the key) and its
-    // code times 4 (the kernels index 4-byte table entries by byte address)
-    uint8_t exp[8], cls[8];
-    for (int sl = 0; sl < 8; ++sl) {
-        // a filler that no byte of the slot equals or differs from by delta
-        int other = -1;
-        for (int b = 0; b < 256 && other < 0; ++b)
-            if (slot_of((uint32_t)b) != (uint32_t)sl && slot_of((uint32_t)b ^ delta) != (uint32_t)sl) other = b;
-        if (other < 0) return false;
-        exp[sl] = (uint8_t)other;
-        cls[sl] = (uint8_t)(catch_code << 2);
-    }
-    for (int i = 0; i < ns; ++i) {
-        const uint32_t slot = slot_of(specials[i]);
-        exp[slot] = specials[i];
-        cls[slot] = (uint8_t)(code_of[cm[specials[i]]] << 2);
-    }
-    for (int sl = 0; sl < 8; ++sl) exp[sl] = (uint8_t)(exp[sl] ^ best_key);
-    f.sh1 = (uint32_t)best_sh1;
-    f.sh2 = (uint32_t)best_sh2;
-    f.m1 = best_m1 * 0x01010101u;
-    f.m2 = best_m2 * 0x01010101u;
-    f.exp_lo = exp[0] | exp[1] << 8 | exp[2] << 16 | (uint32_t)exp[3] << 24;
-    f.exp_hi = exp[4] | exp[5] << 8 | exp[6] << 16 | (uint32_t)exp[7] << 24;
-    f.cls_lo = cls[0] | cls[1] << 8 | cls[2] << 16 | (uint32_t)cls[3] << 24;
-    f.cls_hi = cls[4] | cls[5] << 8 | cls[6] << 16 | (uint32_t)cls[7] << 24;
-    // hit table: byte `key` 0x00, the others 0xff
-    f.hit_lo = best_key < 4 ? ~(0xffu << (8 * best_key)) : 0xffffffffu;
-    f.hit_hi = best_key >= 4 ? ~(0xffu << (8 * (best_key - 4))) : 0xffffffffu;
+    uint8_t special_code[8];
+    for (int i = 0; i < ns; ++i) special_code[i] = code_of[cm[specials[i]]];
+    if (!build_slot_tables(specials, special_code, ns, catch_code, f.slots)) return false;
     // states: one absorbing state (if any) becomes kAbs, the rest are tracked
     int abs_state = -1;
     for (uint32_t s = 0; s < d->n_states && abs_state < 0; ++s) {

@@ -9,6 +9,7 @@
 #include "ppr.h"
 #include "ppr_device.h"
 #include "ppr_host.h"
+#include "ppr_slots.h"
 
 namespace ppr {
 
@@ -128,10 +129,7 @@ struct FastParams {
     uint32_t n, num_tiles;
     uint32_t start_code, accept_codes;  // bit i: tracked code i accepting; bit 8: absorbing state accepting
     uint32_t nt;                        // tracked states
-    uint32_t sh1, m1, sh2, m2;          // slot = ((byte >> sh1) & m1) | ((byte >> sh2) & m2), 3 bits
-    uint32_t exp_lo, exp_hi;            // the special byte owning each slot (or a filler), XORed with the key
-    uint32_t cls_lo, cls_hi;            // 4 x the code of each slot's special byte
-    uint32_t hit_lo, hit_hi;            // byte select table: 0x00 at the key, 0xff elsewhere
+    SlotTables slots;                   // symbol classification (ppr_slots.h)
     OutArrays out;
     WsHeader* hdr;
     uint32_t* tabs;        // step tables built for this call

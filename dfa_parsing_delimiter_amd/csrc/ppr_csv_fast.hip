@@ -144,19 +144,18 @@ __device__ __forceinline__ SpanCarry span_carry(const uint64_t (&T)[NCH], const 
     return r;
 }
 
-// Symbol codes (times 4) of four bytes: a 3-bit slot from two bit fields of
-// each byte; by v_perm, the slot's special byte (XORed with a key) and its
-// code; then one more v_perm of the difference decides whether the byte is
-// that special byte: selector `key` (the byte equals it) picks 0x00 from the
-// hit table, every other selector gives 0xff (the host picked the slot bits so
-// that the one other selector that yields 0x00, 12, cannot occur). Bytes that
-// are not special get the catch-all code.
+// v_perm_b32, for the classification shared with the host check (ppr_slots.h)
+struct PermOp {
+    __device__ uint32_t operator()(uint32_t hi, uint32_t lo, uint32_t sel) const { return perm(hi, lo, sel); }
+};
+
+// Symbol codes (times 4) of four bytes (ppr_slots.h): the slot's special byte
+// and code by v_perm, and an exact match test by one more v_perm of the
+// difference; bytes that are not special get the catch-all code.
 template <int CB>
 __device__ __forceinline__ uint32_t classify4(uint32_t w, const FastParams& p)
 {
-    const uint32_t h = ((w >> p.sh1) & p.m1) | ((w >> p.sh2) & p.m2);
-    const uint32_t miss = perm(p.hit_hi, p.hit_lo, w ^ perm(p.exp_hi, p.exp_lo, h));
-    return (miss & (Geo<CB>::CM * 0x04040404u)) | perm(p.cls_hi, p.cls_lo, h);
+    return slot_codes4(w, p.slots, Geo<CB>::CM * 0x04040404u, PermOp{});
 }
 
 // symbol code of one byte (the ragged paths)
