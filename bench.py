@@ -199,6 +199,82 @@ def bandwidth_ceilings(ppr, torch, dev, nbytes=1 << 30, iters=10):
     return out
 
 
+def reread_probe(ppr, torch, dev, reps=3):
+    """Read probe (pattern 0) over the first `size` bytes of a buffer, cold (after
+    reading 1 GiB of other data) and warm (right after reading the same bytes):
+    how much a re-read gains from the caches beyond the L2. Prints one JSON line."""
+    big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    other = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    big.fill_(1)
+    other.fill_(2)
+    sink = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    grid = torch.cuda.get_device_properties(dev).multi_processor_count * 8
+
+    def read(buf, nbytes):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        ppr.bandwidth_probe(0, 0, buf, sink, nbytes, grid)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    out = {"probe": "reread", "grid": grid, "block": 256, "sizes": {}}
+    for mib in (64, 128, 192, 256, 384, 512):
+        nb = mib << 20
+        cold, warm = [], []
+        for _ in range(reps):
+            read(other, 1 << 30)
+            cold.append(read(big, nb))
+            warm.append(read(big, nb))
+        out["sizes"]["%dMiB" % mib] = {"cold_us": round(statistics.median(cold), 1),
+                                       "warm_us": round(statistics.median(warm), 1)}
+    print(json.dumps(out))
+
+
+def overlap_probe(args, cfg_id, cfg, ppr, torch, W, np, reps=10):
+    """Two parses of the workload with their own workspaces: back to back on one
+    stream, and on two streams with the second started once the first's first
+    stage (the codes kernel) is done, so that its memory-bound kernel runs beside
+    the first's later kernels. Median ms of each, one JSON line."""
+    dev = torch.device("cuda:0")
+    data = W.generate(cfg_id)
+    xa = torch.from_numpy(data).to(dev)
+    xb = xa.clone()
+    table = W.table(cfg["table"])
+    n = data.size
+    A = ppr.Parser(table, max_n=n, capacity=max(4096, n // 8), device=dev)
+    B = ppr.Parser(table, max_n=n, capacity=max(4096, n // 8), device=dev)
+    s1 = torch.cuda.current_stream()
+    s2 = torch.cuda.Stream()
+    ev = [torch.cuda.Event() for _ in range(8)]
+    for e in ev:
+        e.record(s1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def run(mode):
+        e0.record(s1)
+        if mode == "one_stream":
+            A.launch(xa, s1)
+            B.launch(xb, s1)
+        else:
+            s2.wait_stream(s1)
+            A.launch(xa, s1, stage_events=ev)
+            s2.wait_event(ev[1])
+            B.launch(xb, s2)
+            s1.wait_stream(s2)
+        e1.record(s1)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    out = {"probe": "overlap", "workload": cfg["name"], "n_bytes": n}
+    for mode in ("one_stream", "two_streams"):
+        for _ in range(3):
+            run(mode)
+        out[mode + "_ms"] = round(statistics.median([run(mode) for _ in range(reps)]), 4)
+    print(json.dumps(out))
+
+
 def stream_bench(args, cfg_id, cfg, ppr, torch, W, np):
     """host-to-host GB/s of ppr_parse_stream: the input in pinned host memory, the
     per-field results returned into pinned host arrays (64-bit offsets and
@@ -529,6 +605,10 @@ def main():
                     help="instead: time numeric type inference and conversion over the workload's parse")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the device bandwidth probe (read / write / copy of 1 GiB)")
+    ap.add_argument("--overlap-probe", action="store_true",
+                    help="instead: two parses back to back against two streams, the second after the first's codes kernel")
+    ap.add_argument("--reread-probe", action="store_true",
+                    help="instead: time the read probe over 64-512 MiB cold and right after a read of the same bytes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -553,6 +633,10 @@ def main():
     cfg = W.CONFIGS[cfg_id]
     kind = "csv" if cfg["kind"] == "csv" else "lex"
     dev = torch.device("cuda:0")
+    if args.reread_probe:
+        return reread_probe(ppr, torch, dev)
+    if args.overlap_probe:
+        return overlap_probe(args, cfg_id, cfg, ppr, torch, W, np)
     if args.stream:
         return stream_bench(args, cfg_id, cfg, ppr, torch, W, np)
     if args.columns:
