@@ -534,13 +534,14 @@ extern "C" int ppr_lex_prepare(const ppr_lex_tables_t* t, ppr_lex_prepared_t* pr
         prep->n_states = nq;
 
         // the streaming kernels' fold rows, where their tables fit the LDS budgets
-        // (the automaton's entries carry the 8-bit kinds, its states times m 16 bits)
+        // (the automaton's entries carry the 8-bit kinds, its states times m 16
+        // bits; a column times 4 is one byte, so m <= 64)
         uint32_t max_kind = 0;
         for (uint32_t q = 0; q < nq; ++q) max_kind = std::max<uint32_t>(max_kind, qkind[q]);
         std::vector<uint32_t> row_of, rrep;
         const uint32_t nr = lex_fold_rows(fold, t->k, m, id_mask, row_of, rrep);
         const RowLayout rl = row_layout(t->k, m, nq, nr);
-        if (max_kind < 256u && (uint64_t)nq * m * 4u <= kLexStepLds && (uint64_t)t->k * 2u <= kLexStateLds &&
+        if (max_kind < 256u && m <= 64u && (uint64_t)nq * m * 4u <= kLexStepLds && (uint64_t)t->k * 2u <= kLexStateLds &&
             (uint64_t)nr * m * 2u <= kLexRowLds && rl.end <= ppr_lex_fold_bytes(t->k)) {
             const size_t cells = align_up((uint64_t)nr * m * 2u, 16) / 2u;
             std::vector<uint16_t> next_row(cells, 0), row_id(cells, 0);

@@ -79,20 +79,28 @@ __device__ __forceinline__ void load_lex_chunk(const uint8_t* src, uint32_t len,
     }
 }
 
+// u16 at byte a of an LDS table
+__device__ __forceinline__ uint32_t lds_u16_at(const uint16_t* base, uint32_t a)
+{
+    return *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(base) + a);
+}
+
 // Pass 1: the chunk's identifier, folded from the identity. All but the last
 // byte step through the fold rows in LDS (entries: the next row times m); the
 // last byte reads the identifier itself from the same row in global memory.
+// s_col2 holds each byte's column times 2, and the rows lie at LDS address 0,
+// so a step's address is one v_lshl_add of the entry and the column.
 template <bool FULL>
 __device__ __forceinline__ uint32_t fold_lex_chunk(const LexFastParams& p, const uint32_t (&w)[kLexWords], uint32_t len,
-                                                   const uint16_t* s_rows, const uint8_t* s_col)
+                                                   const uint16_t* s_rows, const uint8_t* s_col2)
 {
     if (!FULL && len == 0) return p.identity;
     uint32_t r = p.row0, c = 0;
 #pragma unroll
     for (int j = 0; j < kLexFastChunk; ++j) {
-        const uint32_t cj = s_col[chunk_byte(w, j)];
-        if (FULL ? j + 1 < kLexFastChunk : (uint32_t)j + 1u < len) r = s_rows[r + cj];
-        else if (FULL || (uint32_t)j + 1u == len) c = cj;
+        const uint32_t cj = s_col2[chunk_byte(w, j)];
+        if (FULL ? j + 1 < kLexFastChunk : (uint32_t)j + 1u < len) r = lds_u16_at(s_rows, 2u * r + cj);
+        else if (FULL || (uint32_t)j + 1u == len) c = cj >> 1;
     }
     return p.row_id[r + c];
 }
@@ -101,7 +109,7 @@ __device__ __forceinline__ uint32_t fold_lex_chunk(const LexFastParams& p, const
 // step's N row reads are independent and wait on the LDS once.
 template <int N>
 __device__ __forceinline__ void fold_lex_chunks(const LexFastParams& p, const uint32_t (&w)[N][kLexWords],
-                                                const uint16_t* s_rows, const uint8_t* s_col, uint32_t (&id)[N])
+                                                const uint16_t* s_rows, const uint8_t* s_col2, uint32_t (&id)[N])
 {
     uint32_t r[N];
 #pragma unroll
@@ -109,31 +117,34 @@ __device__ __forceinline__ void fold_lex_chunks(const LexFastParams& p, const ui
 #pragma unroll
     for (int j = 0; j + 1 < kLexFastChunk; ++j)
 #pragma unroll
-        for (int k = 0; k < N; ++k) r[k] = s_rows[r[k] + s_col[chunk_byte(w[k], j)]];
+        for (int k = 0; k < N; ++k) r[k] = lds_u16_at(s_rows, 2u * r[k] + s_col2[chunk_byte(w[k], j)]);
 #pragma unroll
-    for (int k = 0; k < N; ++k) id[k] = p.row_id[r[k] + s_col[chunk_byte(w[k], kLexFastChunk - 1)]];
+    for (int k = 0; k < N; ++k) id[k] = p.row_id[r[k] + (s_col2[chunk_byte(w[k], kLexFastChunk - 1)] >> 1)];
 }
 
 // Pass 2 from the automaton state whose row starts at byte q4 of the step
 // table: bit j of the result is set when a token ends before byte j. Entries
 // are addressed by byte: entry = the successor's row offset | flag << 16 |
-// kind of the state before the byte << 24; s_col holds each byte's column (one
-// byte each: the 256-byte table is one word per LDS bank, so its reads never
-// conflict). A full chunk reads all its columns before the chain of steps
-// (they do not depend on the state) and gathers the flag bytes, and with kinds
-// the kind bytes, four per word by v_perm; the kind words go to kinds32
-// (garbage where no token ends: only flagged bytes' kinds are read).
+// kind of the state before the byte << 24; s_col4 holds each byte's column
+// times 4 (one byte each: the 256-byte table is one word per LDS bank, so its
+// reads never conflict). The step table sits at LDS address 0, so a step is
+// one add of the entry's low half and the column (v_add_u32 with a 16-bit
+// source select) and one LDS read. A full chunk reads all its columns before
+// the chain of steps (they do not depend on the state) and gathers the flag
+// bytes, and with kinds the kind bytes, four per word by v_perm; the kind words
+// go to kinds32 (garbage where no token ends: only flagged bytes' kinds are
+// read).
 template <bool KINDS>
 __device__ __forceinline__ uint64_t lex_pass2_full(const uint32_t (&w)[kLexWords], uint32_t q4, const uint32_t* s_step,
-                                                   const uint8_t* s_col, uint32_t* kinds32)
+                                                   const uint8_t* s_col4, uint32_t* kinds32)
 {
     uint32_t c[kLexFastChunk];
 #pragma unroll
-    for (int j = 0; j < kLexFastChunk; ++j) c[j] = s_col[chunk_byte(w, j)];
+    for (int j = 0; j < kLexFastChunk; ++j) c[j] = s_col4[chunk_byte(w, j)];
     uint32_t e = q4, fw = 0, kw = 0, b0 = 0, b1 = 0;
 #pragma unroll
     for (int j = 0; j < kLexFastChunk; ++j) {
-        e = lds_at(s_step, (e & 0xffffu) + (c[j] << 2));
+        e = lds_at(s_step, (e & 0xffffu) + c[j]);
         const int i = j & 3;
         const uint32_t keep = 0x03020100u & ~(0xffu << (8 * i));
         fw = perm(e, fw, keep | (6u << (8 * i)));  // byte i <- the entry's flag byte
@@ -151,12 +162,12 @@ __device__ __forceinline__ uint64_t lex_pass2_full(const uint32_t (&w)[kLexWords
 // Pass 2 over the input's ragged last chunk (bytes < len), one byte at a time.
 template <bool KINDS>
 __device__ __forceinline__ uint64_t lex_pass2_ragged(const uint32_t (&w)[kLexWords], uint32_t len, uint32_t q4,
-                                                     const uint32_t* s_step, const uint8_t* s_col, uint8_t* kinds)
+                                                     const uint32_t* s_step, const uint8_t* s_col4, uint8_t* kinds)
 {
     uint64_t bits = 0;
     uint32_t e = q4;
     for (uint32_t j = 0; j < len; ++j) {
-        e = lds_at(s_step, (e & 0xffffu) + ((uint32_t)s_col[chunk_byte(w, (int)j)] << 2));
+        e = lds_at(s_step, (e & 0xffffu) + (uint32_t)s_col4[chunk_byte(w, (int)j)]);
         const uint32_t f = (e >> 16) & 1u;
         if (KINDS && f) kinds[j] = (uint8_t)(e >> 24);
         bits |= (uint64_t)f << j;
@@ -227,20 +238,31 @@ __device__ LexTok lex_tokens_before(const LexFastParams& p, uint32_t b, LexTok* 
     return block_reduce<kLexFastWaves>(LexTok{x.x + y.x, max(x.y, y.y)}, LexTok{0u, 0u}, s_wave, LexTokComb{});
 }
 
+// The pass-2 kernels' LDS, one object so that the step table lies at LDS
+// address 0 (the entries' row offsets are then the addresses themselves).
+template <typename Rest>
+struct LexPass2Shared {
+    uint32_t step[kLexStepLds / 4];    // the minimal automaton (below)
+    uint16_t state[kLexStateLds / 2];  // row offset of each identifier's state
+    uint8_t col4[256];                 // each byte's column times 4
+    Rest rest;                         // the kernel's own
+};
+
 // The minimal automaton in LDS, by byte offset: entry = the successor's row
 // offset (successor * m * 4) | flag << 16 | kind of the row's state << 24;
-// the row offset of each identifier's state; and each byte's column. (Row
-// offsets stay below 2^16: the table is held to 16 KiB.)
-__device__ __forceinline__ void load_lex_automaton(const LexFastParams& p, uint32_t* s_step, uint16_t* s_state,
-                                                   uint8_t* s_col)
+// the row offset of each identifier's state; and each byte's column times 4.
+// (Row offsets stay below 2^16: the table is held to 16 KiB; columns times 4
+// fit a byte: the streaming kernels take m <= 64.)
+template <typename Rest>
+__device__ __forceinline__ void load_lex_automaton(const LexFastParams& p, LexPass2Shared<Rest>& sh)
 {
     const uint32_t m4 = p.m * 4u;
     for (uint32_t i = threadIdx.x; i < p.nq * p.m; i += kLexFastBlock) {
         const uint32_t e = p.step[i];
-        s_step[i] = (e & 0xffffu) * m4 | (e & 0x10000u) | ((uint32_t)p.state_kind[i / p.m] << 24);
+        sh.step[i] = (e & 0xffffu) * m4 | (e & 0x10000u) | ((uint32_t)p.state_kind[i / p.m] << 24);
     }
-    for (uint32_t i = threadIdx.x; i < p.k; i += kLexFastBlock) s_state[i] = (uint16_t)(p.state_of[i] * m4);
-    if (threadIdx.x < 256) s_col[threadIdx.x] = p.col[threadIdx.x];
+    for (uint32_t i = threadIdx.x; i < p.k; i += kLexFastBlock) sh.state[i] = (uint16_t)(p.state_of[i] * m4);
+    if (threadIdx.x < 256) sh.col4[threadIdx.x] = (uint8_t)(p.col[threadIdx.x] << 2);
 }
 
 // Several tiles' chunk identifiers, scanned together: the merges of the scans
@@ -262,12 +284,21 @@ struct LexIdSetComb {
     }
 };
 
+// The rest of the pass-1 kernel's LDS, after the fold rows (all of it is
+// dynamic, so the rows lie at LDS address 0).
+struct IdsShared {
+    uint8_t col2[256];  // each byte's column times 2
+    IdSet set[2][kLexFastWaves];
+    uint32_t wave[kLexFastWaves];
+};
+
 __global__ void __launch_bounds__(kLexFastBlock) lex_ids_kernel(LexFastParams p)
 {
     extern __shared__ __align__(16) uint16_t s_rows[];
-    __shared__ uint8_t s_col[256];
-    __shared__ IdSet s_set[2][kLexFastWaves];
-    __shared__ uint32_t s_wave[kLexFastWaves];
+    const uint32_t row_vecs = (p.n_rows * p.m + 7u) / 8u;  // (the rows are padded to 16 bytes)
+    IdsShared& sh = *reinterpret_cast<IdsShared*>(reinterpret_cast<uint4*>(s_rows) + row_vecs);
+    uint8_t* const s_col = sh.col2;
+    uint32_t* const s_wave = sh.wave;
     const uint32_t tid = threadIdx.x;
     if (blockIdx.x == 0 && tid == 0) {  // (no kernel of the call has read the header yet)
         p.hdr->tile_counter = 0;
@@ -275,10 +306,9 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_ids_kernel(LexFastParams p)
         p.hdr->fault = 0;
         p.hdr->path = PPR_PATH_STREAMING;
     }
-    const uint32_t row_vecs = (p.n_rows * p.m + 7u) / 8u;  // (the rows are padded to 16 bytes)
     for (uint32_t i = tid; i < row_vecs; i += kLexFastBlock)
         reinterpret_cast<uint4*>(s_rows)[i] = reinterpret_cast<const uint4*>(p.next_row)[i];
-    if (tid < 256) s_col[tid] = p.col[tid];
+    if (tid < 256) s_col[tid] = (uint8_t)(p.col[tid] << 1);
     __syncthreads();
     const LexIdComb idc{p.merge, p.k, p.id_mask};
     const LexIdSetComb scomb{idc};
@@ -314,7 +344,7 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_ids_kernel(LexFastParams p)
         for (int k = 0; k < kIdsTiles; ++k)
 #pragma unroll
             for (int q = 0; q < kLexWords; ++q) w[k][q] = wn[k][q];
-        block_scan<kLexFastWaves>(v, ident, excl, tot, s_set[it & 1], scomb);
+        block_scan<kLexFastWaves>(v, ident, excl, tot, sh.set[it & 1], scomb);
 #pragma unroll
         for (int k = 0; k < kIdsTiles; ++k) {
             p.chunk_id[(size_t)nth(tile, k) * kLexFastBlock + tid] = (uint16_t)excl.v[k];
@@ -350,14 +380,18 @@ __global__ void __launch_bounds__(kWave) lex_range_kernel(LexFastParams p)
 
 __global__ void __launch_bounds__(kLexFastBlock) lex_count_kernel(LexFastParams p)
 {
-    extern __shared__ __align__(16) uint32_t s_tab[];
-    uint32_t* s_step = s_tab;
-    uint16_t* s_state = reinterpret_cast<uint16_t*>(s_tab + p.nq * p.m);
-    __shared__ uint8_t s_col[256];
-    __shared__ uint32_t s_wave[kLexFastWaves];
-    __shared__ LexTok s_tw[kLexFastWaves];
+    struct Own {
+        uint32_t wave[kLexFastWaves];
+        LexTok tw[kLexFastWaves];
+    };
+    __shared__ __align__(16) LexPass2Shared<Own> sh;
+    const uint32_t* s_step = sh.step;
+    const uint16_t* s_state = sh.state;
+    const uint8_t* s_col4 = sh.col4;
+    uint32_t* s_wave = sh.rest.wave;
+    LexTok* s_tw = sh.rest.tw;
     const uint32_t tid = threadIdx.x, b = blockIdx.x;
-    load_lex_automaton(p, s_step, s_state, s_col);
+    load_lex_automaton(p, sh);
     const LexIdComb idc{p.merge, p.k, p.id_mask};
     uint32_t run = lex_ranges_before(p, b, s_wave, idc);  // (its barrier publishes the tables)
     uint32_t t0, t1;
@@ -373,7 +407,7 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_count_kernel(LexFastParams 
         p, t0, t1,
         [&](uint32_t tile, const LexIn& in, uint32_t) {
             const uint32_t q = s_state[idc(run, in.cid)];
-            count(tile, lex_pass2_full<false>(in.w, q, s_step, s_col, nullptr));
+            count(tile, lex_pass2_full<false>(in.w, q, s_step, s_col4, nullptr));
             run = idc(run, in.tid);
         },
         [&](uint32_t tile, uint32_t) {
@@ -382,7 +416,7 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_count_kernel(LexFastParams 
             uint32_t w[kLexWords];
             load_lex_chunk<false>(p.in + pos, len, w);
             const uint32_t q = s_state[idc(run, p.chunk_id[(size_t)tile * kLexFastBlock + tid])];
-            count(tile, lex_pass2_ragged<false>(w, len, q, s_step, s_col, nullptr));
+            count(tile, lex_pass2_ragged<false>(w, len, q, s_step, s_col4, nullptr));
             run = idc(run, p.tile_id[tile]);
         });
     const LexTok r = block_reduce<kLexFastWaves>(acc, LexTok{0u, 0u}, s_tw, LexTokComb{});
@@ -391,23 +425,28 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_count_kernel(LexFastParams 
 
 __global__ void __launch_bounds__(kLexFastBlock) lex_emit_kernel(LexFastParams p)
 {
-    extern __shared__ __align__(16) uint32_t s_tab[];
-    uint32_t* s_step = s_tab;
-    uint16_t* s_state = reinterpret_cast<uint16_t*>(s_tab + p.nq * p.m);
-    __shared__ uint32_t s_kind32[kLexFastTile / 4];  // kind of the token ending before each byte of the tile
-    __shared__ uint32_t s_list[kLexFastWaves][kLexList];
-    __shared__ uint8_t s_col[256];
-    __shared__ uint32_t s_wave[kLexFastWaves];
-    __shared__ LexTok s_pre[kLexFastWaves];
-    __shared__ LexTok s_tw[2][kLexFastWaves];
+    struct Own {
+        uint32_t kind32[kLexFastTile / 4];  // kind of the token ending before each byte of the tile
+        uint32_t list[kLexFastWaves][kLexList];
+        uint32_t wave[kLexFastWaves];
+        LexTok pre[kLexFastWaves];
+        LexTok tw[2][kLexFastWaves];
+    };
+    __shared__ __align__(16) LexPass2Shared<Own> sh;
+    const uint32_t* s_step = sh.step;
+    const uint16_t* s_state = sh.state;
+    const uint8_t* s_col4 = sh.col4;
+    uint32_t* s_kind32 = sh.rest.kind32;
+    uint32_t* s_wave = sh.rest.wave;
+    LexTok* s_pre = sh.rest.pre;
     const uint32_t tid = threadIdx.x, b = blockIdx.x;
     const uint32_t lane = (uint32_t)lane_id();
     uint8_t* const s_kind = reinterpret_cast<uint8_t*>(s_kind32);
-    load_lex_automaton(p, s_step, s_state, s_col);
+    load_lex_automaton(p, sh);
     const LexIdComb idc{p.merge, p.k, p.id_mask};
     uint32_t run = lex_ranges_before(p, b, s_wave, idc);  // (its barrier publishes the tables)
     LexTok P = lex_tokens_before(p, b, s_pre);
-    uint32_t* list = s_list[tid / kWave];
+    uint32_t* list = sh.rest.list[tid / kWave];
     const uint32_t pos0 = tid * (uint32_t)kLexFastChunk;  // the chunk's first byte in the tile
     uint32_t t0, t1;
     lex_range_of(p, b, t0, t1);
@@ -418,7 +457,7 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_emit_kernel(LexFastParams p
         if (pos == 0) B &= ~1ull;  // a flag at the input's first byte ends no token
         const LexTok c{(uint32_t)__popcll(B), B ? pos + (uint32_t)(63 - __clzll((long long)B)) : 0u};
         LexTok cex, ctot;
-        block_scan<kLexFastWaves>(c, LexTok{0u, 0u}, cex, ctot, s_tw[it & 1u], LexTokComb{});  // (publishes s_kind)
+        block_scan<kLexFastWaves>(c, LexTok{0u, 0u}, cex, ctot, sh.rest.tw[it & 1u], LexTokComb{});  // (publishes s_kind)
 
         // Tokens, written by waves: each lane lists its boundaries (tile
         // positions) in the wave's list, then lane l of a round takes token
@@ -462,7 +501,7 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_emit_kernel(LexFastParams p
         p, t0, t1,
         [&](uint32_t tile, const LexIn& in, uint32_t it) {
             const uint32_t q = s_state[idc(run, in.cid)];
-            emit(tile, lex_pass2_full<true>(in.w, q, s_step, s_col, s_kind32 + pos0 / 4u), it);
+            emit(tile, lex_pass2_full<true>(in.w, q, s_step, s_col4, s_kind32 + pos0 / 4u), it);
             run = idc(run, in.tid);
         },
         [&](uint32_t tile, uint32_t it) {
@@ -471,7 +510,7 @@ __global__ void __launch_bounds__(kLexFastBlock) lex_emit_kernel(LexFastParams p
             uint32_t w[kLexWords];
             load_lex_chunk<false>(p.in + pos, len, w);
             const uint32_t q = s_state[idc(run, p.chunk_id[(size_t)tile * kLexFastBlock + tid])];
-            emit(tile, lex_pass2_ragged<true>(w, len, q, s_step, s_col, s_kind + pos0), it);
+            emit(tile, lex_pass2_ragged<true>(w, len, q, s_step, s_col4, s_kind + pos0), it);
             run = idc(run, p.tile_id[tile]);
         });
     if (b == p.num_ranges - 1 && tid == 0) {  // the final token: from the last boundary to n
@@ -489,16 +528,15 @@ constexpr uint32_t kLexIdsGrid = 512;
 
 int launch_lex_fast(const LexFastParams& p, const ppr_parse_opts_t* o, hipStream_t s)
 {
-    const size_t rows_lds = (size_t)(p.n_rows * p.m + 7u) / 8u * 16u;
-    const size_t tab_lds = (size_t)p.nq * p.m * 4u + (size_t)p.k * 2u;
+    const size_t ids_lds = (size_t)(p.n_rows * p.m + 7u) / 8u * 16u + sizeof(IdsShared);
     stage_event(o, 0, s);
-    hipLaunchKernelGGL(lex_ids_kernel, dim3(std::min<uint32_t>(p.num_tiles, kLexIdsGrid)), dim3(kLexFastBlock), rows_lds,
+    hipLaunchKernelGGL(lex_ids_kernel, dim3(std::min<uint32_t>(p.num_tiles, kLexIdsGrid)), dim3(kLexFastBlock), ids_lds,
                        s, p);
     hipLaunchKernelGGL(lex_range_kernel, dim3(p.num_ranges), dim3(kWave), 0, s, p);
     stage_event(o, 1, s);
-    hipLaunchKernelGGL(lex_count_kernel, dim3(p.num_ranges), dim3(kLexFastBlock), tab_lds, s, p);
+    hipLaunchKernelGGL(lex_count_kernel, dim3(p.num_ranges), dim3(kLexFastBlock), 0, s, p);
     stage_event(o, 2, s);
-    hipLaunchKernelGGL(lex_emit_kernel, dim3(p.num_ranges), dim3(kLexFastBlock), tab_lds, s, p);
+    hipLaunchKernelGGL(lex_emit_kernel, dim3(p.num_ranges), dim3(kLexFastBlock), 0, s, p);
     stage_event(o, 3, s);
     return hipGetLastError() == hipSuccess ? PPR_OK : PPR_EHIP;
 }
