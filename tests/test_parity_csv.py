@@ -427,3 +427,30 @@ def test_full_size_workloads(ppr, cfg):
             assert g.path == (path or auto_path(b.size))
         _same(g, r, ("full", cfg, chunk, path))
     del b, d
+
+
+N_MAX = (1 << 32) - (1 << 16)  # the largest input ppr_parse takes
+
+
+@pytest.mark.slow
+def test_maximum_size(ppr):
+    """the largest input the library takes (2^32 - 2^16 bytes of the quote-heavy workload: positions, field
+    offsets and lengths near 2^32), every output array, on the streaming and the fused kernels; and a ragged
+    size just below it (a partial last tile) on the automatic path"""
+    import torch
+    t = W.table(W.CONFIGS[3]["table"])
+    _say("max: generate", N_MAX)
+    b = W.generate(3, n=N_MAX)
+    d = _dev(b)
+    for n, paths in ((N_MAX, (None, FUSED)), (N_MAX - 4093, (None,))):
+        _say("max: oracle", n)
+        r = oracle.csv_parse(b[:n], t, cap=n // 16)
+        for path in paths:
+            _say("max: gpu", n, path, r["n_fields"])
+            g = ppr.Parser(t, max_n=n, capacity=r["n_fields"], path=path)(d[:n])
+            assert g.path == (path or auto_path(n))
+            _same(g, r, ("max", n, path))
+            del g
+            torch.cuda.empty_cache()
+        del r
+    del b, d

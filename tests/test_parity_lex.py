@@ -242,3 +242,34 @@ def test_stage_events_streaming(ppr, tables):
     times = [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
     assert all(x >= 0 for x in times) and sum(times) > 0, times
     assert o.n_tokens == oracle.lex_restart(b, d)["n_tokens"]
+
+
+N_MAX = (1 << 32) - (1 << 16)  # the largest input ppr_lex takes
+
+
+@pytest.mark.slow
+def test_maximum_size(ppr, tables):
+    """the largest input the library takes (2^32 - 2^16 bytes: copies of the seeded token stream, token
+    starts near 2^32), every output array, on the streaming and the single-pass kernels; and a ragged size just
+    below it (a partial last tile) on the automatic path"""
+    import torch
+    d, T = tables["lexer"]
+    _say("max lexer: generate", N_MAX)
+    unit = W.generate(5)
+    b = np.empty(N_MAX, dtype=np.uint8)
+    for i in range(0, N_MAX, unit.size):
+        b[i:i + unit.size] = unit[:min(unit.size, N_MAX - i)]
+    del unit
+    d_b = _dev(b)
+    for n, paths in ((N_MAX, (None, SINGLE_PASS)), (N_MAX - 4093, (None,))):
+        _say("max lexer: oracle", n)
+        r = oracle.lex_restart(b[:n], d)
+        for path in paths:
+            _say("max lexer: gpu", n, path, r["n_tokens"])
+            g = ppr.Lexer(T, max_n=n, capacity=r["n_tokens"], path=path)(d_b[:n])
+            assert g.path == (path or auto_path(n))
+            _same(g, r, ("max", n, path))
+            del g
+            torch.cuda.empty_cache()
+        del r
+    del b, d_b
