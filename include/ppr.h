@@ -371,7 +371,8 @@ typedef struct ppr_lex_prepared {
     uint16_t flag_mask;
     uint8_t column_of[256]; /* out: column of each byte */
     uint32_t n_states;     /* out: states of the minimal automaton (0: it does not fit the buffer; not used) */
-    uint32_t n_rows;       /* out: fold rows (0: the streaming kernels' tables do not fit; they are not used) */
+    uint32_t n_rows;       /* out: fold rows (0: the streaming kernels are not used: their tables do not fit
+                              their LDS budgets, a token kind exceeds 255, or m exceeds 64) */
     uint32_t row0;         /* out: the identity's row, times m */
 } ppr_lex_prepared_t;
 
