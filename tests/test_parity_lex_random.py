@@ -11,7 +11,9 @@ the library.
   minimal automaton of 122 states x 121 columns, too large for LDS, so that the
   single-pass kernel steps the fold table and reads the final-state table from
   global memory);
-* tables naming an identifier at or beyond k are rejected (PPR_EINVAL).
+* tables naming an identifier at or beyond k are rejected (PPR_EINVAL);
+* grammars of 64 and 65 byte columns, either side of the streaming kernels'
+  limit (their column table holds each column times 4 in a byte).
 
 Expected tokens: the restart lexer over the DFA ("Lexing on the GPU: the scan
 is the easy part", "A lexer is a prefix scan"; no table is involved on that
@@ -154,3 +156,23 @@ def test_prepare_rejects_identifiers_out_of_range(ppr):
     with pytest.raises(ppr.PprError) as e:
         ppr.LexTables(init, merge, fin, k, k)  # identity beyond k
     assert e.value.code == ppr.PPR_EINVAL
+
+
+@pytest.mark.parametrize("n_cols", [64, 65])
+def test_column_limit_of_streaming_kernels(ppr, n_cols):
+    """64 byte columns (the largest column times 4 is 252) run on the streaming kernels; 65 fall back to the
+    single-pass kernel, on the automatic path and when the streaming kernels are asked for; the same tokens"""
+    d = W.many_columns_dfa(n_cols)
+    T = ppr.LexTables.from_dfa(d)
+    assert int(T.prep.m) == n_cols
+    assert (int(T.prep.n_rows) > 0) == (n_cols <= 64), (n_cols, int(T.prep.n_rows))
+    want = STREAMING if n_cols <= 64 else SINGLE_PASS
+    rng = np.random.default_rng(n_cols)
+    b = rng.integers(0, 256, (9 << 20) + 123, dtype=np.uint8).tobytes()  # above the automatic threshold
+    r = oracle.lex_restart(b, d)
+    x = _dev(b)
+    for path in (None, STREAMING):
+        print("columns", n_cols, "path", path, r["n_tokens"], flush=True)
+        g = ppr.lex(x, T, capacity=len(b) + 1, path=path)
+        assert g.path == want, (n_cols, path, g.path)
+        _same(g, r, (n_cols, path))

@@ -189,6 +189,7 @@ lexer_dfa = _lexgrammar.lexer_dfa
 toy_dfa = _lexgrammar.toy_dfa
 random_token_dfa = _lexgrammar.random_token_dfa
 keyword_chain_dfa = _lexgrammar.keyword_chain_dfa
+many_columns_dfa = _lexgrammar.many_columns_dfa
 
 from . import numtext as _numtext  # noqa: E402
 

@@ -287,3 +287,21 @@ def keyword_chain_dfa(length: int, seed: int):
     kind[length], kind[E], kind[0] = 1, 0, 0
     return ({"n_states": Q, "q0": 0, "delta": delta, "kind": kind, "kind_names": ("ERROR", "KEYWORD", "PART")},
             bytes(word.astype(np.uint8)))
+
+
+def many_columns_dfa(n_cols: int, seed: int = 5):
+    """A token DFA of 4 states whose 256 bytes fall into n_cols classes (byte b
+    in class b mod n_cols, 2 <= n_cols <= 192) with pairwise different columns,
+    so that the byte columns of its closure number exactly n_cols. Each class
+    is one of the 192 columns (successor of the start state in {1, 2, 3}, of
+    states 1-3 in {none, 1, 2, 3}), drawn without repetition; kinds 0-3."""
+    import itertools
+    combos = list(itertools.product([1, 2, 3], [-1, 1, 2, 3], [-1, 1, 2, 3], [-1, 1, 2, 3]))
+    if not 2 <= n_cols <= len(combos):
+        raise ValueError("n_cols out of range")
+    pick = np.random.default_rng(seed).permutation(len(combos))[:n_cols]
+    delta = np.empty((4, 256), dtype=np.int16)
+    for b in range(256):
+        delta[:, b] = combos[pick[b % n_cols]]
+    return {"n_states": 4, "q0": 0, "delta": delta, "kind": np.arange(4, dtype=np.uint16),
+            "kind_names": ("K0", "K1", "K2", "K3")}
