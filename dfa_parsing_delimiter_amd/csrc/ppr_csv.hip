@@ -544,6 +544,7 @@ int parse_enqueue(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, cons
             f.range_err = (uint32_t*)(ws + fl.range_err);
             f.stat_vec = (uint64_t*)(ws + fl.stat_vec);
             f.stat_carry = (StatB*)(ws + fl.stat_carry);
+            f.spec = (uint32_t*)(ws + fl.stat_carry);  // (8 of its 16 words per tile)
             f.epoch = next_epoch();
             f.path = path;
             f.expect_cols = expect;

@@ -145,6 +145,7 @@ struct FastParams {
     uint32_t* range_err;   // per range: its first INVALID byte (kNone: none)
     uint64_t* stat_vec;    // fused path: per tile, vector look-back status
     StatB* stat_carry;     // fused path: per tile, count-carry look-back status
+    uint32_t* spec;        // streaming path (the same memory): per tile, the carry of its agreed chunks (8 words)
     uint32_t epoch;        // fused path: call epoch carried by the status words
     uint32_t path;         // PPR_PATH_* the call runs
     uint32_t expect_cols;  // expected fields per record (0: none)

@@ -98,9 +98,15 @@ struct SpanCarry {
 
 constexpr int kSpanScratch = 2 * kFastWaves + 1;  // GCarry entries of span_carry's LDS scratch
 
+// The count carry of a wave's spans (every lane gets it), from each lane's
+// bitmaps; excl_nf: the terminators of the wave's earlier lanes, nf: the lane's.
+struct WaveCarry {
+    GCarry wc;
+    uint32_t excl_nf, nf;
+};
+
 template <int NCH>
-__device__ __forceinline__ SpanCarry span_carry(const uint64_t (&T)[NCH], const uint64_t (&RD)[NCH], uint32_t abs,
-                                                GCarry* s_wave)
+__device__ __forceinline__ WaveCarry wave_carry(const uint64_t (&T)[NCH], const uint64_t (&RD)[NCH], uint32_t abs)
 {
     uint32_t nr = 0, lt = 0, rdl = 0, before = 0;
 #pragma unroll
@@ -124,7 +130,15 @@ __device__ __forceinline__ SpanCarry span_carry(const uint64_t (&T)[NCH], const 
     const uint32_t max_rd =
         has_r ? (uint32_t)__builtin_amdgcn_readlane((excl & 0xffffu) + rdl, 63 - __clzll((long long)has_r)) : 0u;
     const uint32_t wnf = tot & 0xffffu;
-    const GCarry wc{wnf, tot >> 16, max_rd ? wnf - max_rd : wnf, max_lt};
+    return WaveCarry{GCarry{wnf, tot >> 16, max_rd ? wnf - max_rd : wnf, max_lt}, excl & 0xffffu, nf};
+}
+
+template <int NCH>
+__device__ __forceinline__ SpanCarry span_carry(const uint64_t (&T)[NCH], const uint64_t (&RD)[NCH], uint32_t abs,
+                                                GCarry* s_wave)
+{
+    const WaveCarry wcr = wave_carry<NCH>(T, RD, abs);
+    const GCarry wc = wcr.wc;
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const GCarry zero{0, 0, 0, 0};
     if (lane_id() == 0) s_wave[w] = wc;
@@ -137,8 +151,8 @@ __device__ __forceinline__ SpanCarry span_carry(const uint64_t (&T)[NCH], const 
     }
     __syncthreads();
     SpanCarry r;
-    r.excl_nf = excl & 0xffffu;
-    r.mine = nf;
+    r.excl_nf = wcr.excl_nf;
+    r.mine = wcr.nf;
     r.wave_excl = s_wave[kFastWaves + w];
     r.total = s_wave[2 * kFastWaves];
     return r;
@@ -194,6 +208,51 @@ __device__ __forceinline__ uint32_t even_lane(uint32_t v)
 {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xa0, 0xf, 0xf, false);
 }
+
+// Whether every live hypothesis of a prefix vector has reached one state: each
+// entry is either that state x or absorbing (kAbs). x = kAbs when every entry
+// is. Once a prefix agrees, every longer one does (the live hypotheses then
+// move together), so the agreed chunks of a tile are a suffix of it.
+template <bool V8>
+__device__ __forceinline__ bool vec_agreed(const Vec& v, uint32_t& x)
+{
+    uint32_t m = kAbs;
+#pragma unroll
+    for (int i = 0; i < (V8 ? 8 : 4); ++i) m = min(m, ((i < 4 ? v.lo : v.hi) >> (8 * (i & 3))) & 0xffu);
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < (V8 ? 8 : 4); ++i) {
+        const uint32_t e = ((i < 4 ? v.lo : v.hi) >> (8 * (i & 3))) & 0xffu;
+        ok = ok && (e == m || e == kAbs);
+    }
+    x = m;
+    return ok;
+}
+
+// Speculation [ParPaRaw Sec. 3, parsing context]: a chunk whose tile-exclusive
+// vector agrees starts in the agreed state whatever state the tile starts in,
+// unless the true path has died (reached the absorbing state) before it. The
+// codes kernel counts the fields of a tile's agreed chunks when the tile's own
+// vector agrees on a tracked state and it is not the input's last tile; the
+// carries kernel uses that count when the tile's true start state reaches
+// that same state at the tile's end (the true path is then alive at every
+// agreed chunk, so their starts are the agreed states), and otherwise runs
+// pass 2 over the whole tile.
+template <bool V8>
+__device__ __forceinline__ bool tile_speculates(const FastParams& p, uint32_t tile, const Vec& tv, uint32_t& x)
+{
+    return tile + 1u < p.num_tiles && vec_agreed<V8>(tv, x) && x != kAbs;
+}
+
+// words of a tile's speculative carry (p.spec, 8 per tile)
+// (nf, nr, col, lt; then the first INVALID byte of the agreed chunks)
+constexpr uint32_t kSpWords = 8;
+
+// Speculation runs for 4-byte groups and at most 4 tracked states (one VGPR
+// per vector); the other geometries need more registers in the codes kernel
+// than it can spare.
+template <int CB, bool V8>
+constexpr bool kSpeculates = CB == 2 && !V8;
 
 // identity vector over the tracked state codes; the rest is absorbing
 template <bool V8>
@@ -584,6 +643,26 @@ __device__ GCarry carries_before(const FastParams& p, uint32_t b, GCarry* s_wave
     return block_reduce<kFastWaves>(c, zero, s_wave, comb);
 }
 
+// pass-2 table rows (tracked states + the absorbing row, per table) and the byte tables
+template <bool V8, int PAR>
+struct Pass2Shared {
+    uint32_t t2[PAR * (V8 ? 9 : 5) * kRowStride];
+    uint8_t nxt[9 * 16], tag[9 * 16];
+};
+
+// The byte tables and the pass-2 tables in LDS, built by the workgroup (the
+// caller's next barrier publishes the pass-2 tables).
+template <int CB, bool V8>
+__device__ __forceinline__ void load_pass2(const FastParams& p, Pass2Shared<V8, Geo<CB>::PAR>& sh)
+{
+    if (threadIdx.x < 9 * 16) {
+        sh.nxt[threadIdx.x] = (&p.nxt[0][0])[threadIdx.x];
+        sh.tag[threadIdx.x] = (&p.tag[0][0])[threadIdx.x];
+    }
+    __syncthreads();
+    build_pass2<CB>(sh.t2, sh.nxt, sh.tag, p.nt);
+}
+
 // codes: symbol codes -> group indices (stored); the vector of the tile's bytes
 // before each even chunk, the tile vectors and the range vector (stored).
 //
@@ -600,6 +679,8 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
     __shared__ uint32_t s_t1[T1W];
     __shared__ uint8_t s_nxt[9 * 16];
     __shared__ Vec s_wave[2][kFastWaves];
+    __shared__ Pass2Shared<V8, Gm::PAR> s_p2;
+    __shared__ uint4 s_sx[2][kFastWaves][2];  // per wave: its speculative carry, its first INVALID byte
 
     const int tid = threadIdx.x;
     // workgroup b takes tiles b, b + G, b + 2G, ... (G = the grid): the workgroups
@@ -624,18 +705,65 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
     if (blockIdx.x == 0 && tid == 0) reset_header(p);  // (no kernel of the call has read it yet)
     __syncthreads();
     build_pass1<CB, V8>(s_t1, s_nxt, p.nt);
+    load_pass2<CB, V8>(p, s_p2);
     __syncthreads();
     const Vec ident = fast_ident<V8>(p.nt);
 
     // classify, store the indices, the chunk's vector
-    auto full_chunk = [&](uint32_t tile, const uint32_t (&wc)[ND]) {
-        uint32_t ia[NI], pw[NP];
+    auto full_chunk = [&](uint32_t tile, const uint32_t (&wc)[ND], uint32_t (&pw)[NP]) {
+        uint32_t ia[NI];
         chunk_codes<CB>(wc, p, ia, pw);
         uint4* dst = reinterpret_cast<uint4*>(p.idx + ((size_t)tile * kFastBlock + tid) * NI);
 #pragma unroll
         for (int q = 0; q < NP / 4; ++q)
             dst[q] = make_uint4(pw[4 * q], pw[4 * q + 1], pw[4 * q + 2], pw[4 * q + 3]);
         return tree_vector<CB, V8>(ia, s_t1);
+    };
+    // The speculative carry of a full tile (see tile_speculates): pass 2 over
+    // each chunk of an agreed span from its agreed state; each wave's count
+    // carry and first INVALID byte go to LDS, and thread 0 combines them and
+    // stores the tile's after the next barrier (the next tile's block scan, or
+    // the one at the end), so that this costs no barrier of its own.
+    int64_t spec_tile = -1;  // the tile whose wave carries wait in s_sx[spec_buf]
+    uint32_t spec_buf = 0;
+    auto speculate = [&](uint32_t tile, const Vec& excl, const uint32_t (&pw)[NP], uint32_t it) {
+        const Vec ev{even_lane(excl.lo), V8 ? even_lane(excl.hi) : 0xffffffffu};
+        uint32_t xs, x;
+        const bool mine = vec_agreed<V8>(ev, xs);  // the span's first chunk agrees
+        vec_agreed<V8>(excl, x);                   // this chunk's start (it agrees if that one does)
+        uint64_t T[1] = {0ull}, RD[1] = {0ull};
+        uint32_t err = kNone;
+        const uint32_t abs = tile * (uint32_t)kFastTile + (uint32_t)tid * (uint32_t)kFastChunk;
+        if (mine) {
+            const uint32_t any = pass2_run<CB, 1>(pw, x, p.nt, s_p2.t2, T, RD);
+            if (any & kP2Invalid) err = first_invalid<CB, 1>(pw, x, p.nt, s_p2.t2, abs);
+        }
+        const GCarry wc = wave_carry<1>(T, RD, abs).wc;
+        const uint32_t werr = wave_min_defined(err);
+        if (lane_id() == 0) {
+            s_sx[it & 1][tid / kWave][0] = make_uint4(wc.nf, wc.nr, wc.col, wc.lt);
+            s_sx[it & 1][tid / kWave][1] = make_uint4(werr, 0u, 0u, 0u);
+        }
+        spec_tile = tile;
+        spec_buf = it & 1;
+    };
+    // after a barrier: the pending tile's speculative carry
+    auto flush_spec = [&]() {
+        if (spec_tile >= 0 && tid == 0) {
+            const GCarryComb gc;
+            GCarry r{0u, 0u, 0u, 0u};
+            uint32_t e = kNone;
+#pragma unroll
+            for (int i = 0; i < kFastWaves; ++i) {
+                const uint4 q = s_sx[spec_buf][i][0];
+                r = gc(r, GCarry{q.x, q.y, q.z, q.w});
+                e = min(e, s_sx[spec_buf][i][1].x);
+            }
+            uint4* dst = reinterpret_cast<uint4*>(p.spec + (size_t)spec_tile * kSpWords);
+            dst[0] = make_uint4(r.nf, r.nr, r.col, r.lt);
+            dst[1] = make_uint4(e, 0u, 0u, 0u);
+        }
+        spec_tile = -1;
     };
     // scan the tile's chunk vectors, store those of the even chunks (where the
     // carries and emit kernels' two-chunk spans start) and the tile vector
@@ -645,13 +773,23 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
     // no store skipped by a branch, the compiler knows how many memory
     // operations follow each prefetch and waits for the prefetch alone, not for
     // the previous tile's stores as well.
-    auto finish = [&](uint32_t tile, const Vec& v, uint32_t it) {
-        Vec excl, tot;
+    auto finish = [&](uint32_t tile, const Vec& v, uint32_t it, Vec& excl, Vec& tot) {
         block_scan<kFastWaves>(v, ident, excl, tot, s_wave[it & 1], VecComb<V8>{});
+        flush_spec();  // (the block scan's barrier publishes the previous tile's wave carries)
         const size_t ci = (size_t)tile * (kFastBlock / 2) + (uint32_t)tid / 2;
         p.cvec_lo[ci] = even_lane(excl.lo);
         if (V8) p.cvec_hi[ci] = even_lane(excl.hi);
         p.tile_vec[tile] = (uint64_t)tot.lo | ((uint64_t)tot.hi << 32);
+    };
+    // a full tile: codes, indices, vectors, and the speculative carry where the
+    // tile vector (the block scan's total, the same in every thread) agrees
+    auto full_tile = [&](uint32_t tile, const uint32_t (&wc)[ND], uint32_t it) {
+        uint32_t pw[NP];
+        Vec excl, tot;
+        finish(tile, full_chunk(tile, wc, pw), it, excl, tot);
+        uint32_t xt;
+        if constexpr (kSpeculates<CB, V8>)
+            if (tile_speculates<V8>(p, tile, tot, xt)) speculate(tile, excl, pw, it);
     };
 
     // Two register buffers used in turn, and an unconditional prefetch (the
@@ -668,28 +806,34 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
     uint32_t it = 0;
     if (tile < tfull_all) {
         load_full(min(tile + stride, tlast), w2);
-        finish(tile, full_chunk(tile, w), it++);
+        full_tile(tile, w, it++);
         tile += stride;
         while (tile < tfull_all) {
             load_full(min(tile + stride, tlast), w);
-            finish(tile, full_chunk(tile, w2), it++);
+            full_tile(tile, w2, it++);
             tile += stride;
             if (tile >= tfull_all) break;
             load_full(min(tile + stride, tlast), w2);
-            finish(tile, full_chunk(tile, w), it++);
+            full_tile(tile, w, it++);
             tile += stride;
         }
     }
-    if (tile < p.num_tiles) {  // the input's ragged last tile
+    if (tile < p.num_tiles) {  // the input's ragged last tile (it never speculates)
         const ChunkPos c = chunk_pos(p.n, tile);
         Vec v = ident;
         if (c.full) {
             load_full(tile, w);
-            v = full_chunk(tile, w);
+            uint32_t pw[NP];
+            v = full_chunk(tile, w, pw);
         } else if (c.my_len) {
             v = ragged_vector<CB, V8>(p, c, v, s_nxt);
         }
-        finish(tile, v, it);
+        Vec excl, tot;
+        finish(tile, v, it, excl, tot);
+    }
+    if (spec_tile >= 0) {  // (uniform)
+        __syncthreads();
+        flush_spec();
     }
 }
 
@@ -709,26 +853,6 @@ __global__ void __launch_bounds__(kWave) csv_range_vec_kernel(FastParams p)
         rv = comp<V8>(rv, readlane_t(wave_scan(x, ident, VecComb<V8>{}), kWave - 1));
     }
     if (threadIdx.x == 0) p.range_vec[blockIdx.x] = (uint64_t)rv.lo | ((uint64_t)rv.hi << 32);
-}
-
-// pass-2 table rows (tracked states + the absorbing row, per table) and the byte tables
-template <bool V8, int PAR>
-struct Pass2Shared {
-    uint32_t t2[PAR * (V8 ? 9 : 5) * kRowStride];
-    uint8_t nxt[9 * 16], tag[9 * 16];
-};
-
-// The byte tables and the pass-2 tables in LDS, built by the workgroup (the
-// caller's next barrier publishes the pass-2 tables).
-template <int CB, bool V8>
-__device__ __forceinline__ void load_pass2(const FastParams& p, Pass2Shared<V8, Geo<CB>::PAR>& sh)
-{
-    if (threadIdx.x < 9 * 16) {
-        sh.nxt[threadIdx.x] = (&p.nxt[0][0])[threadIdx.x];
-        sh.tag[threadIdx.x] = (&p.tag[0][0])[threadIdx.x];
-    }
-    __syncthreads();
-    build_pass2<CB>(sh.t2, sh.nxt, sh.tag, p.nt);
 }
 
 // The tile vectors of super-tile st from the lane-wise prefetch (the second is
@@ -799,6 +923,222 @@ __device__ __forceinline__ uint32_t count_from(const uint64_t (&T)[2], uint32_t 
     return (uint32_t)(__popcll(T[0] & m0) + __popcll(T[1] & m1));
 }
 
+// A range's count carry from the codes kernel's speculative carries. A tile
+// qualifies when its speculative carry holds (see tile_speculates) and it
+// agrees from its span kSpecSpans - 1 on: then only the spans before its
+// agreed ones need pass 2, at most kSpecSpans - 1, and those of 32 qualifying
+// tiles run at once (16 threads per tile) instead of in the tiles' order. The
+// other tiles of the range run pass 2 over all their spans, two tiles at a
+// time (the input's last tile among them: it never qualifies). Ranges without a
+// qualifying tile take the walk over their super-tiles instead.
+constexpr uint32_t kSpecSpans = 16;
+constexpr uint32_t kRangeTilesMax = 128;  // tiles of a range for n < 2^32 (1024 ranges of whole super-tiles)
+
+struct FastRangeShared {
+    uint32_t ts[kRangeTilesMax];  // each tile's start state
+    uint4 tc[kRangeTilesMax];     // each tile's count carry
+    uint32_t te[kRangeTilesMax];  // each tile's first INVALID byte
+    uint8_t fastl[kRangeTilesMax], slowl[kRangeTilesMax];  // the qualifying tiles and the others, in order
+    uint32_t nfast, nslow;
+    uint32_t end;              // the state after the range
+    uint4 red[2][kFastWaves];  // wave partials of the other tiles
+};
+
+// v combined over the 16 lanes of its row (a butterfly: every lane gets it)
+template <typename Op>
+__device__ __forceinline__ uint32_t row16_all(uint32_t v, const Op& op)
+{
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) v = op(v, (uint32_t)__shfl_xor((int)v, m));
+    return v;
+}
+
+struct MinComb {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
+};
+
+// 1 + position of the last set bit of two consecutive 64-bit bitmaps of a span at abs (0: none)
+__device__ __forceinline__ uint32_t last_pos1(const uint64_t (&B)[2], uint32_t abs)
+{
+    if (B[1]) return abs + (uint32_t)kFastChunk + (uint32_t)(64 - __clzll((long long)B[1]));
+    if (B[0]) return abs + (uint32_t)(64 - __clzll((long long)B[0]));
+    return 0u;
+}
+
+// terminators of a span at abs after position L - 1 (all when L is 0 or before the span)
+__device__ __forceinline__ uint32_t terms_after(const uint64_t (&T)[2], uint32_t abs, uint32_t L)
+{
+    const uint32_t nf = (uint32_t)(__popcll(T[0]) + __popcll(T[1]));
+    return L == 0 || abs >= L ? nf : (abs + 2u * kFastChunk > L ? count_from(T, L - abs) : 0u);
+}
+
+// Pass 2 over span pair of a full tile from the tile's start state ts.
+template <int CB>
+__device__ __forceinline__ void span_pass2(const FastParams& p, size_t pair, uint32_t cv, uint32_t ts, uint32_t abs,
+                                           const Pass2Shared<false, Geo<CB>::PAR>& sh, uint64_t (&T)[2],
+                                           uint64_t (&RD)[2], uint32_t& err)
+{
+    constexpr int NP = Geo<CB>::NP, NI = Geo<CB>::NI;
+    uint32_t pw[2 * NP];
+    const uint4* src = reinterpret_cast<const uint4*>(p.idx + pair * (2 * NI));
+#pragma unroll
+    for (int q = 0; q < NP / 2; ++q) {
+        const uint4 v = src[q];
+        pw[4 * q] = v.x;
+        pw[4 * q + 1] = v.y;
+        pw[4 * q + 2] = v.z;
+        pw[4 * q + 3] = v.w;
+    }
+    const uint32_t st = vat(Vec{cv, 0xffffffffu}, ts);
+    const uint32_t any = pass2_pair<CB>(pw, st, p.nt, sh.t2, T, RD);
+    err = (any & kP2Invalid) ? first_invalid<CB, 2>(pw, st, p.nt, sh.t2, abs) : kNone;
+}
+
+// Every thread calls it; returns whether it stored the range's carry and first
+// INVALID byte (false: the range needs the walk over its super-tiles).
+template <int CB>
+__device__ bool carries_fast_range(const FastParams& p, uint32_t b, uint32_t s0, uint32_t s1, uint32_t run,
+                                   const Pass2Shared<false, Geo<CB>::PAR>& sh, FastRangeShared& fr)
+{
+    const uint32_t ta = 2 * s0, tb = min(2 * s1, p.num_tiles), nr_t = tb - ta;
+    if (nr_t > kRangeTilesMax) return false;
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t w = threadIdx.x / kWave;
+    const Vec ident = fast_ident<false>(p.nt);
+    if (w == 0) {  // the tiles' start states, and which qualify
+        uint32_t s = run, nf = 0, ns = 0;
+        for (uint32_t base = 0; base < nr_t; base += kWave) {
+            const uint32_t i = base + lane;
+            const bool valid = i < nr_t;
+            const Vec tv = unpack_vec(p.tile_vec[ta + (valid ? i : 0u)]);
+            const Vec inc = wave_scan(select_t(valid, tv, ident), ident, VecComb<false>{});
+            const uint32_t ts = vat(wave_shr1(ident, inc), s);
+            uint32_t x, x2;
+            bool f = valid && tile_speculates<false>(p, ta + i, tv, x) && vat(tv, ts) == x;
+            if (f) f = vec_agreed<false>(Vec{p.cvec_lo[(size_t)(ta + i) * (kFastBlock / 2) + (kSpecSpans - 1)],
+                                             0xffffffffu},
+                                         x2);
+            const uint64_t below = (1ull << lane) - 1ull;
+            const uint64_t mf = __ballot(f), ms = __ballot(valid && !f);
+            if (valid) {
+                fr.ts[i] = ts;
+                if (f) fr.fastl[nf + (uint32_t)__popcll(mf & below)] = (uint8_t)i;
+                else fr.slowl[ns + (uint32_t)__popcll(ms & below)] = (uint8_t)i;
+            }
+            nf += (uint32_t)__popcll(mf);
+            ns += (uint32_t)__popcll(ms);
+            s = vat(readlane_t(inc, kWave - 1), s);
+        }
+        if (lane == 0) {
+            fr.nfast = nf;
+            fr.nslow = ns;
+            fr.end = s;
+        }
+    }
+    __syncthreads();
+    const uint32_t nfast = fr.nfast, nslow = fr.nslow;
+    if (nfast == 0) return false;
+    const GCarryComb gc;
+    // qualifying tiles: the spans before the agreed ones, 16 threads per tile
+    for (uint32_t g = 0; g < nfast; g += kFastBlock / kSpecSpans) {
+        const uint32_t li = g + threadIdx.x / kSpecSpans, j = threadIdx.x % kSpecSpans;
+        const bool valid = li < nfast;
+        const uint32_t i = fr.fastl[valid ? li : g], t = ta + i;
+        const size_t pair = (size_t)t * (kFastBlock / 2) + j;
+        const uint32_t cv = p.cvec_lo[pair];
+        uint32_t xs;
+        const bool todo = valid && !vec_agreed<false>(Vec{cv, 0xffffffffu}, xs);
+        const uint32_t abs = t * (uint32_t)kFastTile + j * (uint32_t)(2 * kFastChunk);
+        uint64_t T[2] = {0ull, 0ull}, RD[2] = {0ull, 0ull};
+        uint32_t err = kNone;
+        if (todo) span_pass2<CB>(p, pair, cv, fr.ts[i], abs, sh, T, RD, err);
+        // their count carry: the last record delimiter L (a row maximum), the terminators after it
+        const uint32_t L = row16_all(last_pos1(RD, abs), MaxComb{});
+        const GCarry pre{row16_all((uint32_t)(__popcll(T[0]) + __popcll(T[1])), AddComb{}),
+                         row16_all((uint32_t)(__popcll(RD[0]) + __popcll(RD[1])), AddComb{}),
+                         row16_all(terms_after(T, abs, L), AddComb{}), row16_all(last_pos1(T, abs), MaxComb{})};
+        const uint32_t perr = row16_all(err, MinComb{});
+        if (valid && j == 0) {
+            const uint4* sp = reinterpret_cast<const uint4*>(p.spec + (size_t)t * kSpWords);
+            const uint4 a = sp[0], e = sp[1];
+            const GCarry c = gc(pre, GCarry{a.x, a.y, a.z, a.w});
+            fr.tc[i] = make_uint4(c.nf, c.nr, c.col, c.lt);
+            fr.te[i] = min(perr, e.x);
+        }
+    }
+    // the other tiles: every span, a tile per half of the workgroup
+    for (uint32_t k = 0; k < nslow; k += 2) {
+        const uint32_t h = threadIdx.x / (kFastBlock / 2), j = threadIdx.x % (kFastBlock / 2);
+        const bool valid = k + h < nslow;
+        const uint32_t i = fr.slowl[valid ? k + h : k], t = ta + i;
+        const size_t pair = (size_t)t * (kFastBlock / 2) + j;
+        const uint32_t abs = t * (uint32_t)kFastTile + j * (uint32_t)(2 * kFastChunk);
+        const uint32_t my_len = abs < p.n ? min((uint32_t)(2 * kFastChunk), p.n - abs) : 0u;
+        uint64_t T[2] = {0ull, 0ull}, RD[2] = {0ull, 0ull};
+        uint32_t err = kNone;
+        if (my_len == 2u * kFastChunk) {
+            span_pass2<CB>(p, pair, p.cvec_lo[pair], fr.ts[i], abs, sh, T, RD, err);
+        } else if (my_len) {  // the input's ragged last tile: from the bytes
+            PairPos c;
+            c.abs = abs;
+            c.my_len = my_len;
+            pass2_ragged<CB>(p, c, vat(Vec{p.cvec_lo[pair], 0xffffffffu}, fr.ts[i]), p.nt, sh.nxt, sh.tag, T, RD, err);
+        }
+        if (valid && my_len && abs + my_len == p.n)  // the thread holding the input's last byte
+            p.hdr->last_rec = (uint32_t)((RD[(my_len - 1) >> 6] >> ((my_len - 1) & 63)) & 1u);
+        // positions grow with the lanes: a wave's last is its last lane's holding one
+        const uint32_t rdp = last_pos1(RD, abs), ltp = last_pos1(T, abs);
+        const uint64_t hr = __ballot(rdp != 0), ht = __ballot(ltp != 0);
+        const uint32_t wrd = hr ? (uint32_t)__builtin_amdgcn_readlane(rdp, 63 - __clzll((long long)hr)) : 0u;
+        if (lane == 0) fr.red[0][w] = make_uint4(wrd, 0u, 0u, 0u);
+        __syncthreads();
+        const uint32_t w0 = h * (kFastWaves / 2);
+        uint32_t L = 0;
+#pragma unroll
+        for (int q = 0; q < kFastWaves / 2; ++q) L = max(L, fr.red[0][w0 + q].x);
+        const uint32_t nf = (uint32_t)(__popcll(T[0]) + __popcll(T[1]));
+        const uint32_t nr = (uint32_t)(__popcll(RD[0]) + __popcll(RD[1]));
+        const uint32_t cnt = readlane_t(wave_scan(nf | (nr << 16), 0u, AddComb{}), kWave - 1);
+        const uint32_t aft = readlane_t(wave_scan(terms_after(T, abs, L), 0u, AddComb{}), kWave - 1);
+        const uint32_t wlt = ht ? (uint32_t)__builtin_amdgcn_readlane(ltp, 63 - __clzll((long long)ht)) : 0u;
+        const uint32_t werr = wave_min_defined(err);
+        if (lane == 0) fr.red[1][w] = make_uint4(cnt, aft, wlt, werr);
+        __syncthreads();
+        if (valid && j == 0) {
+            uint32_t snf = 0, snr = 0, sc = 0, sl = 0, se = kNone;
+#pragma unroll
+            for (int q = 0; q < kFastWaves / 2; ++q) {
+                const uint4 v = fr.red[1][w0 + q];
+                snf += v.x & 0xffffu;
+                snr += v.x >> 16;
+                sc += v.y;
+                sl = max(sl, v.z);
+                se = min(se, v.w);
+            }
+            fr.tc[i] = make_uint4(snf, snr, sc, sl);
+            fr.te[i] = se;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        GCarry r{0u, 0u, 0u, 0u};
+        uint32_t e = kNone;
+        for (uint32_t i = 0; i < nr_t; ++i) {
+            const uint4 q = fr.tc[i];
+            r = gc(r, GCarry{q.x, q.y, q.z, q.w});
+            e = min(e, fr.te[i]);
+        }
+        p.range_carry[b] = make_uint4(r.nf, r.nr, r.col, r.lt);
+        p.range_err[b] = e;
+        if (b == p.num_ranges - 1) {
+            const uint32_t x = min(fr.end, 8u);
+            p.hdr->end_state = p.state_of[x];
+            p.hdr->error_pos = (p.partial || ((p.accept_codes >> x) & 1u)) ? (int64_t)-1 : (int64_t)p.n;  // before err_min
+        }
+    }
+    return true;
+}
+
 // Register budgets of the carries and emit kernels (waves per SIMD; a
 // workgroup is two per SIMD). With 4-byte groups both wait mostly on their
 // pass-2 lookup chains and fit 64 VGPRs, four workgroups per CU (the emit
@@ -841,6 +1181,10 @@ __global__ void __launch_bounds__(kFastBlock, kCarriesWavesPerSimd<CB>) csv_carr
     load_pass2<CB, V8>(p, sh);
     uint32_t run = vat(ranges_before<V8>(p, b, ident, s_wv), p.start_code);  // (its barrier publishes sh)
     if (threadIdx.x == 0) p.range_state[b] = run;
+    if constexpr (kSpeculates<CB, V8>) {
+        __shared__ FastRangeShared s_fr;
+        if (carries_fast_range<CB>(p, b, s0, s1, run, sh, s_fr)) return;
+    }
     uint32_t acc_nf = 0, acc_nr = 0, acc_col = 0, acc_lt = 0;
     // the first INVALID byte of the wave's spans (wave-uniform): once found, later
     // super-tiles (larger positions) are not searched; the range's (the waves'

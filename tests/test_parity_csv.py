@@ -306,6 +306,26 @@ def test_invalid_bytes_at_scale(ppr):
             _same(g, r, (what, chunk, path))
 
 
+def test_late_agreement_and_dead_paths(ppr):
+    """quoted fields of 1-6 KiB: tiles that start inside one agree on their start state only kilobytes in (the
+    streaming kernels then run pass 2 over every span of such a tile), among tiles that agree early; and the
+    same input with bytes that end the true path (a quote inside an unquoted field) while the other hypotheses
+    live on, in the middle of tiles, so that a tile's agreed state is not its true one; 256 MiB, so that each
+    range of the streaming kernels holds several tiles"""
+    t = W.table("T5")
+    b = W.long_field_csv(256 << 20, 7)
+    bad = b.copy()
+    for q in (100 << 20) + np.arange(5) * 700001:
+        bad[q:q + 3] = np.frombuffer(b'x"y', np.uint8)
+    for what, x in (("long fields", b), ("dead paths", bad)):
+        r = oracle.csv_parse(x, t)
+        for path in (None, FUSED):
+            _say("late agreement", what, x.size, path, r["n_fields"], r["error_pos"])
+            g = ppr.parse(_dev(x), t, capacity=r["n_fields"] + 1, path=path)
+            assert g.path == (path or auto_path(x.size))
+            _same(g, r, (what, path))
+
+
 @pytest.mark.parametrize("path,cap", [(None, 100), (None, 20000), (FUSED, 20000), (SINGLE_PASS, 20000)])
 def test_capacity_reported(ppr, path, cap):
     """with too few output slots: PPR_ECAPACITY, the counts set, the first cap fields written and nothing past

@@ -307,3 +307,37 @@ def gen_tokens(seed: int, n: int, truth: bool = False, out: np.ndarray | None = 
     if rc != 0:
         raise RuntimeError("wl_gen_tokens failed")
     return buf[:n]
+
+
+def long_field_csv(n: int, seed: int) -> np.ndarray:
+    """n bytes of T5 CSV whose records mix short fields with quoted fields of
+    1-6 KiB (commas, newlines and doubled quotes inside), so that chunks far
+    into a quoted field are ambiguous (inside or outside quotes) for several
+    KiB. Seeded; the last record may be cut at n bytes."""
+    r = np.random.default_rng(seed)
+    alnum = np.frombuffer(b"abcdefghijklmnopqrstuvwxyz0123456789", np.uint8)
+
+    def text(k):
+        return bytes(alnum[r.integers(0, alnum.size, k)])
+
+    templates = []
+    for _ in range(64):
+        fields = []
+        for _ in range(int(r.integers(2, 7))):
+            u = r.random()
+            if u < 0.3:
+                body = bytearray(text(int(r.integers(1024, 6144))))
+                for pos in r.integers(0, len(body), 6):
+                    body[pos] = b",\n"[int(r.integers(0, 2))]
+                if r.random() < 0.5:
+                    body[len(body) // 2:len(body) // 2] = b'""'
+                fields.append(b'"' + bytes(body) + b'"')
+            elif u < 0.6:
+                fields.append(b'"' + text(int(r.integers(0, 30))) + b'"')
+            else:
+                fields.append(text(int(r.integers(0, 30))))
+        templates.append(b",".join(fields) + b"\n")
+    out = bytearray()
+    while len(out) < n:
+        out += templates[int(r.integers(0, len(templates)))]
+    return np.frombuffer(bytes(out[:n]), np.uint8).copy()
