@@ -229,8 +229,10 @@ __device__ __forceinline__ bool vec_agreed(const Vec& v, uint32_t& x)
     return ok;
 }
 
-// Speculation [ParPaRaw Sec. 3, parsing context]: a chunk whose tile-exclusive
-// vector agrees starts in the agreed state whatever state the tile starts in,
+// Speculation (not a step of the pages' method, but built on its
+// state-transition vectors, ParPaRaw Sec. 3, parsing context; the outputs are
+// the plain method's): a chunk whose tile-exclusive vector agrees starts in the
+// agreed state whatever state the tile starts in,
 // unless the true path has died (reached the absorbing state) before it. The
 // codes kernel counts the fields of a tile's agreed chunks when the tile's own
 // vector agrees on a tracked state and it is not the input's last tile; the

@@ -1,5 +1,5 @@
 // Bandwidth probe: the device's own read, write and copy rates, against which
-// the parse and lex kernels' HBM traffic is judged. Not part of the method.
+// the parse and lex kernels' HBM traffic is measured. Not part of the method.
 //
 // Each kernel streams 16-byte words with a grid-stride loop, four loads or
 // stores in flight per lane. Access pattern 0: wave-contiguous (lane l of a

@@ -435,7 +435,7 @@ PPR_API const char* ppr_version(void);
  * Bandwidth probe (not part of the method): enqueues one kernel on `stream`
  * that streams `bytes` (a multiple of 16 KiB) of device memory, so that the
  * caller can time the device's own read / write / copy rate with events and
- * judge the kernels' traffic against it.
+ * compare the kernels' traffic with it.
  *   mode 0: read d_src; d_dst receives one 32-bit word per thread
  *           (grid * 256 * 4 bytes), so the loads are not optimised away;
  *   mode 1: write d_dst (d_src unused, may be NULL);
