@@ -456,6 +456,9 @@ static bool prepare_fast(const ppr_dfa_t* d, const uint8_t* cm, FastParams& f, i
             f.tag[row][code_of[c]] = d->tag[s][c];
         }
     }
+    f.quiet_abs = 1;
+    for (int c = 0; c < 16; ++c)
+        if (f.tag[nt][c] == PPR_TAG_FIELD || f.tag[nt][c] == PPR_TAG_RECORD) f.quiet_abs = 0;
     return true;
 }
 

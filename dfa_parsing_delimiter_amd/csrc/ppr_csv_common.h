@@ -151,6 +151,7 @@ struct FastParams {
     uint32_t expect_cols;  // expected fields per record (0: none)
     uint32_t start_col;    // column of the field open at the input's start (0: a record starts there)
     uint32_t partial;      // more input follows: no final field, the end state may be non-accepting
+    uint32_t quiet_abs;    // the absorbing state tags no byte FIELD or RECORD (tag bitmaps may replace indices)
     uint8_t state_of[16];  // DFA state of each code (index 8: absorbing)
     uint8_t nxt[9][16];    // [state code, row nt = absorbing][symbol code] -> next code
     uint8_t tag[9][16];

@@ -246,6 +246,23 @@ __device__ __forceinline__ bool tile_speculates(const FastParams& p, uint32_t ti
     return tile + 1u < p.num_tiles && vec_agreed<V8>(tv, x) && x != kAbs;
 }
 
+// What a span's index slot holds (speculating configurations). The codes
+// kernel stores the tag bitmaps of an agreed chunk (terminators, then record
+// delimiters, 8 bytes each: the 16 bytes its indices take) in place of its
+// indices, when its tile speculates and the absorbing state tags no byte as a
+// terminator. Readers take them when the tile's speculation holds (mode 1),
+// nothing when it does not (mode 2: the true path has died, so those chunks are
+// in the absorbing state and end no field), and run pass 2 on the indices of
+// every other span (mode 0).
+template <bool V8>
+__device__ __forceinline__ bool tile_bits(const FastParams& p, uint32_t tile, const Vec& tv, uint32_t& x)
+{
+    return p.quiet_abs && tile < p.num_tiles && tile_speculates<V8>(p, tile, tv, x);
+}
+
+template <int CB, bool V8>
+__device__ __forceinline__ int span_mode(bool bits, bool holds, uint32_t cvlo, uint32_t cvhi);
+
 // words of a tile's speculative carry (p.spec, 8 per tile)
 // (nf, nr, col, lt; then the first INVALID byte of the agreed chunks)
 constexpr uint32_t kSpWords = 8;
@@ -255,6 +272,34 @@ constexpr uint32_t kSpWords = 8;
 // than it can spare.
 template <int CB, bool V8>
 constexpr bool kSpeculates = CB == 2 && !V8;
+
+template <int CB, bool V8>
+__device__ __forceinline__ int span_mode(bool bits, bool holds, uint32_t cvlo, uint32_t cvhi)
+{
+    if constexpr (!kSpeculates<CB, V8>) {
+        return 0;
+    } else {
+        uint32_t x;
+        if (!bits || !vec_agreed<V8>(Vec{cvlo, cvhi}, x)) return 0;
+        return holds ? 1 : 2;
+    }
+}
+
+// A span vector that no prefix has (its entries are neither tracked states
+// nor absorbing): the carries kernel puts it in place of the vector of a span
+// whose slot it has filled with the span's tag bitmaps. It agrees (every entry
+// the same), so the emit kernel reads that slot as bitmaps (mode 1).
+constexpr uint32_t kBitsMark = 0xfefefefeu;
+
+// the tag bitmaps of a span's two chunks from its slot (mode 1)
+__device__ __forceinline__ void slot_bits(const uint32_t* pw, uint64_t (&T)[2], uint64_t (&RD)[2])
+{
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        T[h] = (uint64_t)pw[4 * h] | ((uint64_t)pw[4 * h + 1] << 32);
+        RD[h] = (uint64_t)pw[4 * h + 2] | ((uint64_t)pw[4 * h + 3] << 32);
+    }
+}
 
 // identity vector over the tracked state codes; the rest is absorbing
 template <bool V8>
@@ -712,13 +757,18 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
     const Vec ident = fast_ident<V8>(p.nt);
 
     // classify, store the indices, the chunk's vector
-    auto full_chunk = [&](uint32_t tile, const uint32_t (&wc)[ND], uint32_t (&pw)[NP]) {
-        uint32_t ia[NI];
-        chunk_codes<CB>(wc, p, ia, pw);
+    auto store_slot = [&](uint32_t tile, const uint32_t (&pw)[NP]) {
         uint4* dst = reinterpret_cast<uint4*>(p.idx + ((size_t)tile * kFastBlock + tid) * NI);
 #pragma unroll
         for (int q = 0; q < NP / 4; ++q)
             dst[q] = make_uint4(pw[4 * q], pw[4 * q + 1], pw[4 * q + 2], pw[4 * q + 3]);
+    };
+    // (speculating configurations store the slot after the block scan: indices
+    // or tag bitmaps)
+    auto full_chunk = [&](uint32_t tile, const uint32_t (&wc)[ND], uint32_t (&pw)[NP]) {
+        uint32_t ia[NI];
+        chunk_codes<CB>(wc, p, ia, pw);
+        if constexpr (!kSpeculates<CB, V8>) store_slot(tile, pw);
         return tree_vector<CB, V8>(ia, s_t1);
     };
     // The speculative carry of a full tile (see tile_speculates): pass 2 over
@@ -728,12 +778,13 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
     // the one at the end), so that this costs no barrier of its own.
     int64_t spec_tile = -1;  // the tile whose wave carries wait in s_sx[spec_buf]
     uint32_t spec_buf = 0;
-    auto speculate = [&](uint32_t tile, const Vec& excl, const uint32_t (&pw)[NP], uint32_t it) {
+    auto speculate = [&](uint32_t tile, const Vec& excl, const uint32_t (&pw)[NP], uint32_t it, uint64_t (&T)[1],
+                         uint64_t (&RD)[1]) {
         const Vec ev{even_lane(excl.lo), V8 ? even_lane(excl.hi) : 0xffffffffu};
         uint32_t xs, x;
         const bool mine = vec_agreed<V8>(ev, xs);  // the span's first chunk agrees
         vec_agreed<V8>(excl, x);                   // this chunk's start (it agrees if that one does)
-        uint64_t T[1] = {0ull}, RD[1] = {0ull};
+        T[0] = RD[0] = 0ull;
         uint32_t err = kNone;
         const uint32_t abs = tile * (uint32_t)kFastTile + (uint32_t)tid * (uint32_t)kFastChunk;
         if (mine) {
@@ -748,6 +799,7 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
         }
         spec_tile = tile;
         spec_buf = it & 1;
+        return mine;
     };
     // after a barrier: the pending tile's speculative carry
     auto flush_spec = [&]() {
@@ -789,9 +841,19 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
         uint32_t pw[NP];
         Vec excl, tot;
         finish(tile, full_chunk(tile, wc, pw), it, excl, tot);
-        uint32_t xt;
-        if constexpr (kSpeculates<CB, V8>)
-            if (tile_speculates<V8>(p, tile, tot, xt)) speculate(tile, excl, pw, it);
+        if constexpr (kSpeculates<CB, V8>) {
+            uint32_t xt;
+            if (tile_speculates<V8>(p, tile, tot, xt)) {
+                uint64_t T[1], RD[1];
+                if (speculate(tile, excl, pw, it, T, RD) && p.quiet_abs) {
+                    pw[0] = (uint32_t)T[0];
+                    pw[1] = (uint32_t)(T[0] >> 32);
+                    pw[2] = (uint32_t)RD[0];
+                    pw[3] = (uint32_t)(RD[0] >> 32);
+                }
+            }
+            store_slot(tile, pw);
+        }
     };
 
     // Two register buffers used in turn, and an unconditional prefetch (the
@@ -827,6 +889,7 @@ __global__ void __launch_bounds__(kFastBlock) csv_codes_kernel(FastParams p)
             load_full(tile, w);
             uint32_t pw[NP];
             v = full_chunk(tile, w, pw);
+            if constexpr (kSpeculates<CB, V8>) store_slot(tile, pw);
         } else if (c.my_len) {
             v = ragged_vector<CB, V8>(p, c, v, s_nxt);
         }
@@ -877,11 +940,17 @@ __device__ __forceinline__ void super_vecs(const FastParams& p, uint32_t st, uin
 template <int CB, bool V8, bool FULL>
 __device__ __forceinline__ void span_tags(const FastParams& p, const PairPos& c, const IdxIn<CB, V8>& in,
                                           uint32_t ts0, uint32_t ts1, const Pass2Shared<V8, Geo<CB>::PAR>& sh,
-                                          uint64_t (&T)[2], uint64_t (&RD)[2], uint32_t* err, bool look = true)
+                                          uint64_t (&T)[2], uint64_t (&RD)[2], uint32_t* err, bool look = true,
+                                          int mode = 0)
 {
     const uint32_t nt = p.nt;
     const uint32_t s = vat(Vec{in.cvlo, in.cvhi}, threadIdx.x < kFastBlock / 2 ? ts0 : ts1);
     T[0] = T[1] = RD[0] = RD[1] = 0;
+    if (mode == 2) return;
+    if (mode == 1) {
+        slot_bits(in.pw, T, RD);
+        return;
+    }
     if (FULL || c.full) {
         const uint32_t any = pass2_pair<CB>(in.pw, s, nt, sh.t2, T, RD);
         if (err && look && (any & kP2Invalid)) *err = first_invalid<CB, 2>(in.pw, s, nt, sh.t2, c.abs);
@@ -941,6 +1010,7 @@ struct FastRangeShared {
     uint4 tc[kRangeTilesMax];     // each tile's count carry
     uint32_t te[kRangeTilesMax];  // each tile's first INVALID byte
     uint8_t fastl[kRangeTilesMax], slowl[kRangeTilesMax];  // the qualifying tiles and the others, in order
+    uint8_t bits[kRangeTilesMax];  // 0: indices only; 1: bitmaps that hold; 2: bitmaps of a dead path (span_mode)
     uint32_t nfast, nslow;
     uint32_t end;              // the state after the range
     uint4 red[2][kFastWaves];  // wave partials of the other tiles
@@ -1016,7 +1086,9 @@ __device__ bool carries_fast_range(const FastParams& p, uint32_t b, uint32_t s0,
             const Vec inc = wave_scan(select_t(valid, tv, ident), ident, VecComb<false>{});
             const uint32_t ts = vat(wave_shr1(ident, inc), s);
             uint32_t x, x2;
-            bool f = valid && tile_speculates<false>(p, ta + i, tv, x) && vat(tv, ts) == x;
+            const bool sp = valid && tile_speculates<false>(p, ta + i, tv, x);
+            bool f = sp && vat(tv, ts) == x;
+            if (valid) fr.bits[i] = (uint8_t)(sp && p.quiet_abs ? (vat(tv, ts) == x ? 1 : 2) : 0);
             if (f) f = vec_agreed<false>(Vec{p.cvec_lo[(size_t)(ta + i) * (kFastBlock / 2) + (kSpecSpans - 1)],
                                              0xffffffffu},
                                          x2);
@@ -1053,7 +1125,15 @@ __device__ bool carries_fast_range(const FastParams& p, uint32_t b, uint32_t s0,
         const uint32_t abs = t * (uint32_t)kFastTile + j * (uint32_t)(2 * kFastChunk);
         uint64_t T[2] = {0ull, 0ull}, RD[2] = {0ull, 0ull};
         uint32_t err = kNone;
-        if (todo) span_pass2<CB>(p, pair, cv, fr.ts[i], abs, sh, T, RD, err);
+        if (todo) {
+            span_pass2<CB>(p, pair, cv, fr.ts[i], abs, sh, T, RD, err);
+            if (p.quiet_abs) {  // the span's bitmaps for the emit kernel, which then runs no pass 2 on this tile
+                uint4* dst = reinterpret_cast<uint4*>(p.idx + pair * (2 * Geo<CB>::NI));
+                dst[0] = make_uint4((uint32_t)T[0], (uint32_t)(T[0] >> 32), (uint32_t)RD[0], (uint32_t)(RD[0] >> 32));
+                dst[1] = make_uint4((uint32_t)T[1], (uint32_t)(T[1] >> 32), (uint32_t)RD[1], (uint32_t)(RD[1] >> 32));
+                p.cvec_lo[pair] = kBitsMark;
+            }
+        }
         // their count carry: the last record delimiter L (a row maximum), the terminators after it
         const uint32_t L = row16_all(last_pos1(RD, abs), MaxComb{});
         const GCarry pre{row16_all((uint32_t)(__popcll(T[0]) + __popcll(T[1])), AddComb{}),
@@ -1078,13 +1158,21 @@ __device__ bool carries_fast_range(const FastParams& p, uint32_t b, uint32_t s0,
         const uint32_t my_len = abs < p.n ? min((uint32_t)(2 * kFastChunk), p.n - abs) : 0u;
         uint64_t T[2] = {0ull, 0ull}, RD[2] = {0ull, 0ull};
         uint32_t err = kNone;
-        if (my_len == 2u * kFastChunk) {
-            span_pass2<CB>(p, pair, p.cvec_lo[pair], fr.ts[i], abs, sh, T, RD, err);
+        const uint32_t cv = p.cvec_lo[pair];
+        const int mode = span_mode<CB, false>(fr.bits[i] != 0, fr.bits[i] == 1, cv, 0xffffffffu);
+        if (mode == 1) {
+            const uint4* src = reinterpret_cast<const uint4*>(p.idx + pair * (2 * Geo<CB>::NI));
+            const uint4 a = src[0], c2 = src[1];
+            const uint32_t pw[8] = {a.x, a.y, a.z, a.w, c2.x, c2.y, c2.z, c2.w};
+            slot_bits(pw, T, RD);
+        } else if (mode == 2) {
+        } else if (my_len == 2u * kFastChunk) {
+            span_pass2<CB>(p, pair, cv, fr.ts[i], abs, sh, T, RD, err);
         } else if (my_len) {  // the input's ragged last tile: from the bytes
             PairPos c;
             c.abs = abs;
             c.my_len = my_len;
-            pass2_ragged<CB>(p, c, vat(Vec{p.cvec_lo[pair], 0xffffffffu}, fr.ts[i]), p.nt, sh.nxt, sh.tag, T, RD, err);
+            pass2_ragged<CB>(p, c, vat(Vec{cv, 0xffffffffu}, fr.ts[i]), p.nt, sh.nxt, sh.tag, T, RD, err);
         }
         if (valid && my_len && abs + my_len == p.n)  // the thread holding the input's last byte
             p.hdr->last_rec = (uint32_t)((RD[(my_len - 1) >> 6] >> ((my_len - 1) & 63)) & 1u);
@@ -1118,7 +1206,7 @@ __device__ bool carries_fast_range(const FastParams& p, uint32_t b, uint32_t s0,
                 se = min(se, v.w);
             }
             fr.tc[i] = make_uint4(snf, snr, sc, sl);
-            fr.te[i] = se;
+            fr.te[i] = fr.bits[i] == 1 ? min(se, p.spec[(size_t)t * kSpWords + 4]) : se;
         }
     }
     __syncthreads();
@@ -1188,6 +1276,7 @@ __global__ void __launch_bounds__(kFastBlock, kCarriesWavesPerSimd<CB>) csv_carr
         if (carries_fast_range<CB>(p, b, s0, s1, run, sh, s_fr)) return;
     }
     uint32_t acc_nf = 0, acc_nr = 0, acc_col = 0, acc_lt = 0;
+    uint32_t sp_err = kNone;  // from the speculative carries of tiles read from bitmaps (uniform)
     // the first INVALID byte of the wave's spans (wave-uniform): once found, later
     // super-tiles (larger positions) are not searched; the range's (the waves'
     // minimum) is stored, and the emit kernel takes the minimum over the ranges
@@ -1200,9 +1289,18 @@ __global__ void __launch_bounds__(kFastBlock, kCarriesWavesPerSimd<CB>) csv_carr
         Vec v0, v1;
         super_vecs<V8>(p, st, in.tvl, ident, v0, v1);
         const uint32_t ts1 = vat(v0, run);
+        uint32_t xa = 0, xb = 0;
+        const bool ba = kSpeculates<CB, V8> && tile_bits<V8>(p, 2 * st, v0, xa);
+        const bool bb = kSpeculates<CB, V8> && tile_bits<V8>(p, 2 * st + 1, v1, xb);
+        const bool ha = vat(v0, run) == xa, hb = vat(v1, ts1) == xb;
+        const bool upper = threadIdx.x >= kFastBlock / 2;
+        const int mode = span_mode<CB, V8>(upper ? bb : ba, upper ? hb : ha, in.cvlo, in.cvhi);
         uint64_t T[2], RD[2];
         uint32_t err = kNone;
-        span_tags<CB, V8, FULL>(p, c, in, run, ts1, sh, T, RD, &err, wave_err == kNone);
+        span_tags<CB, V8, FULL>(p, c, in, run, ts1, sh, T, RD, &err, wave_err == kNone, mode);
+        // a tile read from bitmaps: its agreed chunks' first INVALID byte is in its speculative carry
+        if (ba && ha) sp_err = min(sp_err, p.spec[(size_t)(2 * st) * kSpWords + 4]);
+        if (bb && hb) sp_err = min(sp_err, p.spec[(size_t)(2 * st + 1) * kSpWords + 4]);
         if (wave_err == kNone) wave_err = wave_min_defined(err);
         if (c.my_len && c.abs + c.my_len == p.n)  // the thread holding the input's last byte
             p.hdr->last_rec = (uint32_t)((RD[(c.my_len - 1) >> 6] >> ((c.my_len - 1) & 63)) & 1u);
@@ -1235,7 +1333,7 @@ __global__ void __launch_bounds__(kFastBlock, kCarriesWavesPerSimd<CB>) csv_carr
     const uint32_t snf = wave_scan(acc_nf, 0u, AddComb{}), snr = wave_scan(acc_nr, 0u, AddComb{});
     const uint32_t scol = wave_scan(acc_col, 0u, AddComb{}), slt = wave_scan(acc_lt, 0u, MaxComb{});
     if (lane == kWave - 1) s_red[w] = make_uint4(snf, snr, scol, slt);
-    if (lane == 0) s_err[w] = wave_err;
+    if (lane == 0) s_err[w] = min(wave_err, sp_err);
     __syncthreads();
     if (threadIdx.x == 0) {
         uint4 r = s_red[0];
@@ -1360,8 +1458,14 @@ __global__ void __launch_bounds__(kFastBlock, (kEmitWavesPerSimd<CB, V8>)) csv_e
         Vec v0, v1;
         super_vecs<V8>(p, st, in.tvl, ident, v0, v1);
         const uint32_t ts1 = vat(v0, run);
+        uint32_t xa = 0, xb = 0;
+        const bool ba = kSpeculates<CB, V8> && tile_bits<V8>(p, 2 * st, v0, xa);
+        const bool bb = kSpeculates<CB, V8> && tile_bits<V8>(p, 2 * st + 1, v1, xb);
+        const bool upper = threadIdx.x >= kFastBlock / 2;
+        const int mode = span_mode<CB, V8>(upper ? bb : ba, upper ? vat(v1, ts1) == xb : vat(v0, run) == xa,
+                                           in.cvlo, in.cvhi);
         uint64_t T[2], RD[2];
-        span_tags<CB, V8, FULL>(p, c, in, run, ts1, sh, T, RD, nullptr);
+        span_tags<CB, V8, FULL>(p, c, in, run, ts1, sh, T, RD, nullptr, true, mode);
         const SpanCarry sc = span_carry(T, RD, c.abs, s_wc);
 
         // the wave's fields: super-tile-local indices [wfirst, wend); the state at its first field
