@@ -326,6 +326,26 @@ def test_late_agreement_and_dead_paths(ppr):
             _same(g, r, (what, path))
 
 
+def test_absorbing_state_that_ends_fields(ppr):
+    """T5 with its absorbing state tagging field and record delimiters FIELD and RECORD (so that, after the first
+    INVALID byte, the rest of the input still ends fields): the streaming kernels must then keep the group indices
+    of agreed chunks (no tag bitmaps in their place) and, in tiles whose true path has died, run pass 2 from the
+    absorbing state; on a quote-heavy input with INVALID bytes in the middle of tiles"""
+    t = dict(W.table("T5"))
+    t["tag"] = [list(r) for r in t["tag"]]
+    t["tag"][4] = [1, 2, 3, 3]  # INV: FDELIM -> FIELD, RDELIM -> RECORD
+    b = W.generate(3, n=96 << 20, seed=29)
+    for q in (30 << 20) + np.arange(4) * 1000003:
+        b[q:q + 3] = np.frombuffer(b'x"y', np.uint8)
+    r = oracle.csv_parse(b, t)
+    assert 0 <= r["error_pos"] < b.size
+    for path in (None, FUSED):
+        _say("absorbing fields", b.size, path, r["n_fields"], r["error_pos"])
+        g = ppr.parse(_dev(b), t, capacity=r["n_fields"] + 1, path=path)
+        assert g.path == (path or auto_path(b.size))
+        _same(g, r, ("absorbing fields", path))
+
+
 @pytest.mark.parametrize("path,cap", [(None, 100), (None, 20000), (FUSED, 20000), (SINGLE_PASS, 20000)])
 def test_capacity_reported(ppr, path, cap):
     """with too few output slots: PPR_ECAPACITY, the counts set, the first cap fields written and nothing past
