@@ -615,7 +615,7 @@ def main():
                     help="write profiles/hbm_counters_<workload>_chunk<L>.json from two rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     chunk = args.chunk or (40 if args.workload == "lex5" else 64)  # the library's defaults
