@@ -609,14 +609,39 @@ extern "C" int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa
     return parse_enqueue(d_bytes, n, dfa, class_map, out, d_ws, ws_bytes, opts, stream, false);
 }
 
-extern "C" int ppr_parse_results(const void* d_ws, uint64_t n, ppr_parse_out_t* out, void* stream)
+namespace ppr {
+
+// The workspace header's host copy for blocking calls: one pinned buffer per
+// host thread, allocated on the thread's first call and kept until the process
+// ends (256 bytes). The copy is then one DMA into it; a pageable destination is
+// staged through the runtime's own pinned buffer, a second copy with its own
+// latency on every call. A thread's calls use it one at a time (each waits for
+// its copy). nullptr if the allocation failed: the caller reads into the stack.
+WsHeader* pinned_header()
 {
-    (void)n;
+    thread_local WsHeader* p = nullptr;
+    thread_local bool tried = false;
+    if (!tried) {
+        tried = true;
+        if (hipHostMalloc((void**)&p, sizeof(WsHeader), hipHostMallocPortable) != hipSuccess) {
+            p = nullptr;
+            (void)hipGetLastError();  // not left for a later launch check to report
+        }
+    }
+    return p;
+}
+
+// ppr_parse_results; may_alloc = false (the entry point that allocates nothing)
+// reads the header into the stack instead of the pinned buffer.
+int parse_results(const void* d_ws, ppr_parse_out_t* out, hipStream_t s, bool may_alloc)
+{
     if (!d_ws || !out) return PPR_EINVAL;
-    WsHeader h;
-    hipStream_t s = (hipStream_t)stream;
-    if (hipMemcpyAsync(&h, d_ws, sizeof h, hipMemcpyDeviceToHost, s) != hipSuccess) return PPR_EHIP;
+    WsHeader local;
+    WsHeader* dst = may_alloc ? pinned_header() : nullptr;
+    if (!dst) dst = &local;
+    if (hipMemcpyAsync(dst, d_ws, sizeof(WsHeader), hipMemcpyDeviceToHost, s) != hipSuccess) return PPR_EHIP;
     if (hipStreamSynchronize(s) != hipSuccess) return PPR_EHIP;
+    const WsHeader h = *dst;
     out->n_fields = h.n_fields;
     out->n_records = h.n_records;
     // the first INVALID byte wins over a non-accepting end state
@@ -631,6 +656,14 @@ extern "C" int ppr_parse_results(const void* d_ws, uint64_t n, ppr_parse_out_t* 
     out->tail_column = h.tail_col;
     if (h.fault) return PPR_EHIP;
     return out->n_fields > out->cap_fields ? PPR_ECAPACITY : PPR_OK;
+}
+
+}  // namespace ppr
+
+extern "C" int ppr_parse_results(const void* d_ws, uint64_t n, ppr_parse_out_t* out, void* stream)
+{
+    (void)n;
+    return parse_results(d_ws, out, (hipStream_t)stream, true);
 }
 
 extern "C" int ppr_parse(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa, const uint8_t class_map[256],

@@ -450,6 +450,8 @@ static WsLayout lex_layout(uint64_t n, uint32_t L)
     return w;
 }
 
+WsHeader* pinned_header();  // ppr_csv.hip: the blocking calls' pinned header buffer
+
 }  // namespace ppr
 
 using namespace ppr;
@@ -689,10 +691,13 @@ extern "C" int ppr_lex_results(const void* d_ws, uint64_t n, ppr_tokens_out_t* o
 {
     (void)n;
     if (!d_ws || !out) return PPR_EINVAL;
-    WsHeader h;
+    WsHeader local;
+    WsHeader* dst = pinned_header();  // (per host thread, pinned: one DMA)
+    if (!dst) dst = &local;
     hipStream_t s = (hipStream_t)stream;
-    if (hipMemcpyAsync(&h, d_ws, sizeof h, hipMemcpyDeviceToHost, s) != hipSuccess) return PPR_EHIP;
+    if (hipMemcpyAsync(dst, d_ws, sizeof(WsHeader), hipMemcpyDeviceToHost, s) != hipSuccess) return PPR_EHIP;
     if (hipStreamSynchronize(s) != hipSuccess) return PPR_EHIP;
+    const WsHeader h = *dst;
     out->n_tokens = h.n_fields;
     out->path = h.path;
     if (h.fault) return PPR_EHIP;

@@ -49,6 +49,10 @@ uint8_t* device_scratch()
 }  // namespace
 }  // namespace ppr
 
+namespace ppr {
+int parse_results(const void* d_ws, ppr_parse_out_t* out, hipStream_t s, bool may_alloc);  // ppr_csv.hip
+}  // namespace ppr
+
 using namespace ppr;
 
 extern "C" PPR_API int ppr_parse_noalloc(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t* dfa,
@@ -62,5 +66,5 @@ extern "C" PPR_API int ppr_parse_noalloc(const uint8_t* d_bytes, uint64_t n, con
     const int rc = parse_enqueue(d_bytes, n, dfa, class_map, out, ws, kScratchBytes, opts, stream, true);
     if (rc == PPR_EWORKSPACE) return PPR_ETOOBIG;
     if (rc) return rc;
-    return ppr_parse_results(ws, n, out, stream);
+    return parse_results(ws, out, (hipStream_t)stream, false);  // (no pinned header buffer: it allocates)
 }
