@@ -210,7 +210,12 @@ PPR_API int ppr_parse_async(const uint8_t* d_bytes, uint64_t n, const ppr_dfa_t*
                     const ppr_parse_out_t* out, void* d_ws, size_t ws_bytes, const ppr_parse_opts_t* opts,
                     void* stream);
 
-/* Wait on `stream` and copy the scalars of the last ppr_parse_async on d_ws into out. */
+/* Wait on `stream` and copy the scalars of the last ppr_parse_async on d_ws into out.
+ * The copy goes through a 256-byte pinned host buffer that belongs to the
+ * calling thread. It is allocated (hipHostMalloc) on the thread's first blocking
+ * call (ppr_parse, ppr_parse_results, ppr_lex, ppr_lex_results) and kept until
+ * the process ends. If that allocation fails, the copy goes into the stack
+ * instead. ppr_parse_noalloc never uses it. */
 PPR_API int ppr_parse_results(const void* d_ws, uint64_t n, ppr_parse_out_t* out, void* stream);
 
 /*
